@@ -1,0 +1,173 @@
+"""Decode attention by its plain definition, in fp64 (test infrastructure only).
+
+For every output row (b, h_q), with ``h_kv = h_q // g`` and ``g = H_q/H_kv``
+(M4.5 §0x03A, §0x04A):
+
+    s_t = (q . k_t) * scale,  scale = 1/sqrt(d_h)       (M4.5 §0x01, §0x05D)
+    O   = softmax(s over the visible set A_b) @ V        (M4.5 §0x01)
+    LSE = m + ln(sum_t e^(s_t - m)),  m = max s           (M4.5 §0x02B)
+
+and for an empty A_b (length 0 or everything masked): ``O = 0``, ``LSE = -inf``
+(M4.5 §0x02C).  The visible set comes from ``visibility.visible_positions``;
+rows are located through ``address`` with the oracle's own translation and
+decoded from the stored bytes (``numerics``); int8 rows are ``code * scale``
+with the K scale of the token's 128-token group and channel and the V scale
+of the token (M8.6 §0x03B, §0x03C), and the newest ``min(T_b, R)`` tokens
+come from the bf16 residual (M8.6 §0x06B/§0x06C: one shared softmax over
+both regions).
+
+``split_attend`` is the Flash-Decoding reference: it summarizes each
+physical split of the visible positions (M4.5 §0x02A, §0x03I), merges the
+states in the order given (§0x02B, §0x02C) and finalizes.  It exists to pin
+the algebra (partition invariance, §0x02E) and to check GPU workspace states.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .address import nhd_offset, paged_nhd_offset
+from .numerics import decode, decode_bf16, decode_f16
+from .state import EMPTY, finalize, merge_state, summarize_allowed
+from .visibility import visible_positions
+
+
+def _scale(prob) -> float:
+    return float(prob.softmax_scale) if prob.softmax_scale else 1.0 / math.sqrt(prob.head_dim)
+
+
+def gather_rows(prob, buf, b: int, h_kv: int, positions):
+    """K and V rows (fp64, ``[n, D]``) of the given logical positions of
+    request b and K/V head h_kv, plus the element offset of each row inside the
+    buffer it was read from and the region tag (0: main cache or int8 codes,
+    1: bf16 residual)."""
+    D = prob.head_dim
+    H = prob.num_kv_heads
+    positions = np.asarray(positions, dtype=np.int64)
+    n = positions.size
+    lane = np.arange(D, dtype=np.int64)
+    region = np.zeros(n, dtype=np.int8)
+    if prob.kv_format in ("f32", "bf16"):
+        if prob.layout == "contig":
+            offs = nhd_offset(b, positions, h_kv, 0, prob.kv_capacity, H, D)
+        elif prob.layout == "paged":
+            P = prob.page_size
+            table = buf["block_table"][b]
+            pages = table[positions // P].astype(np.int64)
+            offs = paged_nhd_offset(pages, positions % P, h_kv, 0, P, H, D)
+        else:
+            raise ValueError(prob.layout)
+        idx = offs[:, None] + lane[None, :]
+        kflat = buf["k"].reshape(-1)
+        vflat = buf["v"].reshape(-1)
+        K = decode(kflat[idx], prob.kv_format)
+        V = decode(vflat[idx], prob.kv_format)
+        return K.reshape(n, D), V.reshape(n, D), offs, region
+    if prob.kv_format == "i8":
+        if prob.layout != "contig":
+            raise ValueError("int8 format is contiguous")
+        T = int(buf["seq_lens"][b])
+        R = prob.residual_len
+        G = prob.k_group
+        n_q = T - min(T, R)
+        K = np.empty((n, D), dtype=np.float64)
+        V = np.empty((n, D), dtype=np.float64)
+        offs = np.empty(n, dtype=np.int64)
+        quant = positions < n_q
+        region[~quant] = 1
+        tq = positions[quant]
+        if tq.size:
+            o = nhd_offset(b, tq, h_kv, 0, prob.kv_capacity, H, D)
+            offs[quant] = o
+            idx = o[:, None] + lane[None, :]
+            kc = buf["k"].reshape(-1)[idx].astype(np.float64)
+            vc = buf["v"].reshape(-1)[idx].astype(np.float64)
+            ks = decode_f16(buf["k_scale"][b, tq // G, h_kv, :])          # [n, D]
+            vs = decode_f16(buf["v_scale"][b, tq, h_kv])                   # [n]
+            K[quant] = kc * ks
+            V[quant] = vc * vs[:, None]
+        tr = positions[~quant]
+        if tr.size:
+            o = nhd_offset(b, tr - n_q, h_kv, 0, R, H, D)
+            offs[~quant] = o
+            idx = o[:, None] + lane[None, :]
+            K[~quant] = decode_bf16(buf["k_resid"].reshape(-1)[idx])
+            V[~quant] = decode_bf16(buf["v_resid"].reshape(-1)[idx])
+        return K, V, offs, region
+    raise ValueError(prob.kv_format)
+
+
+def attend(prob, buf, heads=None, with_trace: bool = False):
+    """Exact decode attention.
+
+    Returns ``(O [B, H_q, D], LSE [B, H_q])`` in fp64, and with ``with_trace``
+    also ``{(b, h_kv): (positions, offsets, regions)}`` of every row read.
+    ``heads`` optionally restricts the work to a list of ``(b, h_q)`` rows
+    (the other rows are returned as NaN)."""
+    B, Hq, Hkv, D = prob.batch, prob.num_q_heads, prob.num_kv_heads, prob.head_dim
+    g = Hq // Hkv
+    scale = _scale(prob)
+    q = decode(buf["q"], prob.q_dtype).reshape(B, Hq, D)
+    O = np.full((B, Hq, D), np.nan)
+    LSE = np.full((B, Hq), np.nan)
+    trace = {}
+    want = None
+    if heads is not None:
+        want = {}
+        for (b, hq) in heads:
+            want.setdefault((int(b), int(hq) // g), []).append(int(hq) % g)
+    for b in range(B):
+        T = int(buf["seq_lens"][b])
+        A = visible_positions(T, prob.mask_kind, prob.n_sink, prob.window)
+        for h in range(Hkv):
+            if want is not None and (b, h) not in want:
+                continue
+            rows = range(g) if want is None else sorted(set(want[(b, h)]))
+            if A.size == 0:
+                for i in rows:
+                    O[b, h * g + i] = 0.0
+                    LSE[b, h * g + i] = -math.inf
+                if with_trace:
+                    trace[(b, h)] = (A, np.zeros(0, np.int64), np.zeros(0, np.int8))
+                continue
+            K, V, offs, region = gather_rows(prob, buf, b, h, A)
+            if with_trace:
+                trace[(b, h)] = (A, offs, region)
+            for i in rows:
+                s = (K @ q[b, h * g + i]) * scale
+                m = np.max(s)
+                w = np.exp(s - m)
+                l = np.sum(w)
+                O[b, h * g + i] = (w @ V) / l
+                LSE[b, h * g + i] = m + math.log(l)
+    if with_trace:
+        return O, LSE, trace
+    return O, LSE
+
+
+def split_attend(prob, buf, b: int, h_q: int, bounds, order=None):
+    """Flash-Decoding reference for one output row.
+
+    ``bounds`` is a list of half-open intervals ``[start, end)`` over the
+    visible positions of request b (indices into the sorted visible list, so
+    any disjoint exact cover is legal, M4.5 §0x02E).  Returns the per-split
+    states, the merged state and ``(O, LSE)``."""
+    g = prob.num_q_heads // prob.num_kv_heads
+    h = h_q // g
+    scale = _scale(prob)
+    q = decode(buf["q"], prob.q_dtype).reshape(prob.batch, prob.num_q_heads, prob.head_dim)[b, h_q]
+    T = int(buf["seq_lens"][b])
+    A = visible_positions(T, prob.mask_kind, prob.n_sink, prob.window)
+    states = []
+    for (lo, hi) in bounds:
+        pos = A[lo:hi]
+        if pos.size == 0:
+            states.append(EMPTY(prob.head_dim))
+            continue
+        K, V, _, _ = gather_rows(prob, buf, b, h, pos)
+        states.append(summarize_allowed((K @ q) * scale, V))
+    acc = EMPTY(prob.head_dim)
+    for i in (order if order is not None else range(len(states))):
+        acc = merge_state(acc, states[i])
+    return states, acc, finalize(acc)

@@ -1,0 +1,373 @@
+"""Seeded synthetic decode-attention workloads.
+
+This module only *produces inputs*: a problem description (the decode
+coordinate of "M4.5 - Decode Attention Kernels, Mask Programs, and Backend
+Boundaries", §0x00B/§0x07A) and the raw stored bytes of q, the K/V cache and
+its metadata.  It contains none of the attention arithmetic.  Both the CPU
+oracle and the GPU path consume exactly the arrays built here, so they see
+identical bytes.
+
+Storage conventions (the library's ABI, restated for the generators):
+
+* bf16 tensors are ``uint16`` arrays holding the bit patterns, produced from
+  float32 draws by round-to-nearest-even on the bits;
+* fp16 tensors are ``numpy.float16``; fp32 tensors are ``float32``;
+* q is ``[B, H_q, D]`` (the single decode row squeezed);
+* contiguous K/V is token-major NHD ``[B, T_cap, H_kv, D]``;
+* paged K/V is a page pool ``[N_pages, P, H_kv, D]`` addressed through a dense
+  ``block_table [B, max_pages_per_seq]`` (int32);
+* the int8 format stores K codes ``[B, T_cap, H_kv, D]`` with one fp16 scale per
+  (batch, K/V head, 128-token group, channel) in ``k_scale [B, ceil(T_cap/G),
+  H_kv, D]``, V codes ``[B, T_cap, H_kv, D]`` with one fp16 scale per (batch,
+  token, K/V head) in ``v_scale [B, T_cap, H_kv]``, and the newest
+  ``min(T_b, R)`` tokens of request b as bf16 rows in ``k_resid/v_resid
+  [B, R, H_kv, D]`` (residual row ``t - n_q`` holds token t, with
+  ``n_q = T_b - min(T_b, R)``).
+
+The int8 writer below is the cache *writer* (the producer of the stored
+format, "M8.6 - Live-Data Quantization: Activations and KV Cache", §0x02A
+quantizer rule applied along the axes of §0x06/§0x06A with the residual of
+§0x06B).  It is input production, not part of the decode path; the oracle
+package carries its own independent writer and the CPU tests require the two
+to agree byte for byte.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Problem", "Workload", "rng", "bf16_bits", "draw_bf16", "make_contiguous",
+    "make_paged", "make_int8", "config", "CONFIG_NAMES",
+]
+
+
+@dataclasses.dataclass
+class Problem:
+    """Static decode coordinate (one call).  Field names follow the C ABI."""
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    q_dtype: str = "bf16"          # "f32" | "bf16"
+    kv_format: str = "bf16"        # "f32" | "bf16" | "i8"
+    layout: str = "contig"         # "contig" | "paged"
+    kv_capacity: int = 0           # contiguous token capacity T_cap
+    page_size: int = 0             # paged only
+    max_pages_per_seq: int = 0
+    num_pages: int = 0
+    max_seq_len: int = 0           # bound on seq_lens (plan-time)
+    mask_kind: str = "causal"      # "causal" | "sink_window"
+    n_sink: int = 0
+    window: int = 0
+    softmax_scale: float = 0.0     # 0 -> 1/sqrt(head_dim)
+    num_splits: int = 0            # 0 -> auto
+    k_group: int = 0               # int8 only: tokens per K scale group
+    residual_len: int = 0          # int8 only: bf16 residual rows
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+@dataclasses.dataclass
+class Workload:
+    problem: Problem
+    buffers: dict          # name -> numpy array (stored bytes)
+    name: str = ""
+    note: str = ""
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        rounded[nan] = np.uint16(0x7FC0)
+    return rounded
+
+
+def draw_bf16(g: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return bf16_bits(x)
+
+
+def _draw(g, shape, dtype):
+    if dtype == "f32":
+        return g.standard_normal(size=shape, dtype=np.float32)
+    if dtype == "bf16":
+        return draw_bf16(g, shape)
+    raise ValueError(dtype)
+
+
+BF16_POISON = np.array([0x7FC0, 0x7F80, 0xFF80, 0x476A, 0xC76A], dtype=np.uint16)
+# quiet NaN, +Inf, -Inf, +59904, -59904 (bf16 bit patterns)
+
+
+def _poison_like(g, shape, dtype):
+    if dtype == "bf16":
+        return g.choice(BF16_POISON, size=shape)
+    if dtype == "f32":
+        return g.choice(np.array([np.nan, np.inf, -np.inf, 6e4, -6e4], np.float32), size=shape)
+    if dtype == "i8":
+        return g.integers(-128, 128, size=shape, dtype=np.int8)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# contiguous NHD cache
+# --------------------------------------------------------------------------
+def make_contiguous(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
+                    dtype: str = "bf16", kv_capacity: int | None = None,
+                    mask_kind: str = "causal", n_sink: int = 0, window: int = 0,
+                    num_splits: int = 0, q_scale: float = 1.0,
+                    poison_tail: bool = True) -> Workload:
+    """q, K, V ~ N(0,1) (q optionally multiplied by ``q_scale`` before rounding).
+
+    Token slots at or beyond ``seq_lens[b]`` (allocated, never visible) are
+    filled with NaN/Inf/huge values so that a read of them would show.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
+    T_cap = int(kv_capacity if kv_capacity is not None else max(1, int(seq_lens.max(initial=0))))
+    g = rng(seed)
+    qf = g.standard_normal(size=(B, H_q, D), dtype=np.float32) * np.float32(q_scale)
+    q = qf if dtype == "f32" else bf16_bits(qf)
+    k = _draw(g, (B, T_cap, H_kv, D), dtype)
+    v = _draw(g, (B, T_cap, H_kv, D), dtype)
+    if poison_tail:
+        for b in range(B):
+            T = int(seq_lens[b])
+            if T < T_cap:
+                k[b, T:] = _poison_like(g, k[b, T:].shape, dtype)
+                v[b, T:] = _poison_like(g, v[b, T:].shape, dtype)
+    prob = Problem(batch=B, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
+                   q_dtype=dtype, kv_format=dtype, layout="contig",
+                   kv_capacity=T_cap, max_seq_len=int(seq_lens.max(initial=0)),
+                   mask_kind=mask_kind, n_sink=n_sink, window=window,
+                   num_splits=num_splits)
+    return Workload(prob, dict(q=q, k=k, v=v, seq_lens=seq_lens))
+
+
+# --------------------------------------------------------------------------
+# paged NHD cache with a dense block table
+# --------------------------------------------------------------------------
+def make_paged(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
+               page_size: int = 16, dtype: str = "bf16",
+               max_pages_per_seq: int | None = None, spare_frac: float = 0.10,
+               mask_kind: str = "causal", n_sink: int = 0, window: int = 0,
+               num_splits: int = 0) -> Workload:
+    """Paged pool.  Every visible logical page maps to a seeded random
+    permutation of the pool; everything that is allocated but not visible holds
+    garbage:
+
+    * rows ``T_b mod P .. P-1`` of each request's last page: NaN/Inf/±59904;
+    * block-table slots ``>= ceil(T_b/P)``: out-of-pool ids (-1, N_pages+7,
+      INT32_MAX) and in-pool ids of other requests' pages;
+    * spare pool pages (``spare_frac`` beyond the pages in use): NaN/Inf.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
+    P = int(page_size)
+    g = rng(seed)
+    pages_needed = [(int(T) + P - 1) // P for T in seq_lens]
+    used = int(sum(pages_needed))
+    spare = int(math.ceil(used * spare_frac)) if used else 1
+    N_pages = max(1, used + spare)
+    maxp = int(max_pages_per_seq if max_pages_per_seq is not None
+               else max(1, max(pages_needed, default=1)))
+    qf = g.standard_normal(size=(B, H_q, D), dtype=np.float32)
+    q = qf if dtype == "f32" else bf16_bits(qf)
+    perm = g.permutation(N_pages).astype(np.int32)
+    table = np.empty((B, maxp), dtype=np.int32)
+    garbage_ids = np.array([-1, N_pages + 7, np.iinfo(np.int32).max], dtype=np.int64)
+    k = np.empty((N_pages, P, H_kv, D), dtype=np.float32 if dtype == "f32" else np.uint16)
+    v = np.empty_like(k)
+    # spare pages first get poison; used pages are overwritten below
+    cursor = 0
+    for b in range(B):
+        n = pages_needed[b]
+        phys = perm[cursor:cursor + n]
+        cursor += n
+        table[b, :n] = phys
+        tail = maxp - n
+        if tail > 0:
+            other = g.integers(0, N_pages, size=tail)
+            pick = g.integers(0, 2, size=tail).astype(bool)
+            junk = np.where(pick, other, g.choice(garbage_ids, size=tail))
+            table[b, n:] = junk.astype(np.int64).clip(np.iinfo(np.int32).min,
+                                                       np.iinfo(np.int32).max).astype(np.int32)
+    for pidx in perm[cursor:]:
+        k[pidx] = _poison_like(g, k[pidx].shape, dtype)
+        v[pidx] = _poison_like(g, v[pidx].shape, dtype)
+    # fill used pages in pool order (draw order is fixed by the seed)
+    used_pages = perm[:cursor]
+    chunk = 4096
+    for start in range(0, len(used_pages), chunk):
+        ids = used_pages[start:start + chunk]
+        k[ids] = _draw(g, (len(ids), P, H_kv, D), dtype)
+        v[ids] = _draw(g, (len(ids), P, H_kv, D), dtype)
+    for b in range(B):
+        T = int(seq_lens[b])
+        if T % P and pages_needed[b]:
+            last = table[b, pages_needed[b] - 1]
+            r0 = T % P
+            k[last, r0:] = _poison_like(g, k[last, r0:].shape, dtype)
+            v[last, r0:] = _poison_like(g, v[last, r0:].shape, dtype)
+    prob = Problem(batch=B, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
+                   q_dtype=dtype, kv_format=dtype, layout="paged",
+                   page_size=P, max_pages_per_seq=maxp, num_pages=N_pages,
+                   max_seq_len=int(seq_lens.max(initial=0)), mask_kind=mask_kind,
+                   n_sink=n_sink, window=window, num_splits=num_splits)
+    return Workload(prob, dict(q=q, k=k, v=v, block_table=table, seq_lens=seq_lens))
+
+
+# --------------------------------------------------------------------------
+# int8 K/V with fp16 scales and a bf16 residual window (cache writer)
+# --------------------------------------------------------------------------
+QMAX = 127
+
+
+def _store_scale_f16(amax: np.ndarray) -> np.ndarray:
+    """Effective stored scale: amax/127 rounded to fp16; all-zero -> 1."""
+    zero = amax == 0
+    ideal = np.where(zero, 1.0, amax / QMAX)
+    with np.errstate(over="ignore", under="ignore"):
+        s = ideal.astype(np.float16)
+    eff = s.astype(np.float64)
+    if (not np.isfinite(eff).all()) or np.any(eff < np.finfo(np.float16).tiny):
+        raise ValueError("stored fp16 scale is non-finite or subnormal")
+    return s
+
+
+def _codes(x: np.ndarray, s_eff: np.ndarray) -> np.ndarray:
+    c = np.clip(np.rint(x / s_eff), -QMAX, QMAX)
+    return c.astype(np.int8)
+
+
+def write_int8_cache(k_f32: np.ndarray, v_f32: np.ndarray, seq_lens, k_group: int,
+                     residual_len: int, T_cap: int, g: np.random.Generator):
+    """Quantize per request: tokens ``[0, n_q)`` to int8 codes, the rest to bf16.
+
+    K: one scale per (group of ``k_group`` quantized tokens, channel), taken over
+    the tokens of the group that are quantized (a partial last group uses only
+    its own rows).  V: one scale per token over its channels.
+    Slots that hold no visible data are filled with garbage (codes) or NaN
+    (scales, residual rows).
+    """
+    B, _, H_kv, D = k_f32.shape
+    R, G = residual_len, k_group
+    n_groups = (T_cap + G - 1) // G
+    kc = g.integers(-128, 128, size=(B, T_cap, H_kv, D), dtype=np.int8)
+    vc = g.integers(-128, 128, size=(B, T_cap, H_kv, D), dtype=np.int8)
+    ks = np.full((B, n_groups, H_kv, D), np.nan, dtype=np.float16)
+    vs = np.full((B, T_cap, H_kv), np.nan, dtype=np.float16)
+    kr = np.full((B, max(R, 1), H_kv, D), 0x7FC0, dtype=np.uint16)
+    vr = np.full((B, max(R, 1), H_kv, D), 0x7FC0, dtype=np.uint16)
+    for b in range(B):
+        T = int(seq_lens[b])
+        n_res = min(T, R)
+        n_q = T - n_res
+        if n_q > 0:
+            kq = k_f32[b, :n_q].astype(np.float64)      # [n_q, H, D]
+            for j in range((n_q + G - 1) // G):
+                blk = kq[j * G:min((j + 1) * G, n_q)]    # [<=G, H, D]
+                s = _store_scale_f16(np.abs(blk).max(axis=0))        # [H, D]
+                ks[b, j] = s
+                kc[b, j * G:j * G + blk.shape[0]] = _codes(blk, s.astype(np.float64)[None])
+            vq = v_f32[b, :n_q].astype(np.float64)      # [n_q, H, D]
+            s = _store_scale_f16(np.abs(vq).max(axis=2))              # [n_q, H]
+            vs[b, :n_q] = s
+            vc[b, :n_q] = _codes(vq, s.astype(np.float64)[..., None])
+        if n_res > 0:
+            kr[b, :n_res] = bf16_bits(k_f32[b, n_q:T])
+            vr[b, :n_res] = bf16_bits(v_f32[b, n_q:T])
+    return dict(k=kc, v=vc, k_scale=ks, v_scale=vs, k_resid=kr, v_resid=vr)
+
+
+def make_int8(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
+              k_group: int = 128, residual_len: int = 128,
+              kv_capacity: int | None = None, mask_kind: str = "causal",
+              n_sink: int = 0, window: int = 0, num_splits: int = 0,
+              outlier_channels: int = 3, outlier_mult: float = 20.0,
+              values=None) -> Workload:
+    """int8 K (per channel per group) / int8 V (per token) / bf16 residual.
+
+    ``outlier_channels`` channels per (batch, K/V head), drawn once from the
+    seed independently for K and for V, are multiplied by ``outlier_mult``
+    after the N(0,1) draw and before quantization.  ``values`` may supply the
+    float32 K and V tensors directly (used for exact-quantization cases).
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
+    T_cap = int(kv_capacity if kv_capacity is not None else max(1, int(seq_lens.max(initial=0))))
+    g = rng(seed)
+    q = bf16_bits(g.standard_normal(size=(B, H_q, D), dtype=np.float32))
+    if values is None:
+        kf = g.standard_normal(size=(B, T_cap, H_kv, D), dtype=np.float32)
+        vf = g.standard_normal(size=(B, T_cap, H_kv, D), dtype=np.float32)
+        for arr in (kf, vf):
+            for b in range(B):
+                for h in range(H_kv):
+                    ch = g.choice(D, size=outlier_channels, replace=False)
+                    arr[b, :, h, ch] *= np.float32(outlier_mult)
+    else:
+        kf, vf = (np.asarray(a, dtype=np.float32) for a in values)
+    bufs = write_int8_cache(kf, vf, seq_lens, k_group, residual_len, T_cap, g)
+    bufs.update(q=q, seq_lens=seq_lens)
+    prob = Problem(batch=B, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
+                   q_dtype="bf16", kv_format="i8", layout="contig",
+                   kv_capacity=T_cap, max_seq_len=int(seq_lens.max(initial=0)),
+                   mask_kind=mask_kind, n_sink=n_sink, window=window,
+                   num_splits=num_splits, k_group=k_group, residual_len=residual_len)
+    w = Workload(prob, bufs)
+    w.float_kv = (kf, vf)
+    return w
+
+
+# --------------------------------------------------------------------------
+# the five decode workloads at their full sizes
+# --------------------------------------------------------------------------
+CONFIG_NAMES = {
+    1: "tiny: B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous causal S=4",
+    2: "llama3-8b-layer: B=8 H_q=32 H_kv=8 d=128 T=4096 bf16 contiguous causal",
+    3: "paged-ragged: B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768]",
+    4: "long-context: B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal",
+    5: "int8-sink-window: B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, 4 sinks + window 4096",
+}
+
+
+def ragged_lengths(seed: int, B: int, lo: int = 1, hi: int = 32768) -> np.ndarray:
+    return rng(seed + 1_000_003).integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def config(i: int, seed: int = 0, num_splits: int = 0, **over) -> Workload:
+    """Full-size workload i (1..5)."""
+    if i == 1:
+        w = make_contiguous(seed, 1, 4, 4, 64, [256], dtype="f32",
+                            num_splits=num_splits or 4)
+    elif i == 2:
+        w = make_contiguous(seed, 8, 32, 8, 128, [4096] * 8, num_splits=num_splits)
+    elif i == 3:
+        w = make_paged(seed, 32, 32, 8, 128, ragged_lengths(seed, 32),
+                       page_size=16, max_pages_per_seq=2048, num_splits=num_splits)
+    elif i == 4:
+        T = over.pop("T", 131072)
+        lens = over.pop("seq_lens", [T])
+        w = make_contiguous(seed, len(lens), 32, 8, 128, lens,
+                            kv_capacity=max(max(lens), 1), num_splits=num_splits)
+    elif i == 5:
+        w = make_int8(seed, 16, 32, 8, 128, [16384] * 16, mask_kind="sink_window",
+                      n_sink=4, window=4096, num_splits=num_splits)
+    else:
+        raise ValueError(i)
+    w.name = f"cfg{i}"
+    w.note = CONFIG_NAMES[i]
+    return w

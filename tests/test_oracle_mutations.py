@@ -1,0 +1,128 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by the pins.
+
+Each case patches one plausible mistake into the oracle and re-runs the pin
+tests that should catch it; at least one must fail."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import importlib
+
+attend_mod = importlib.import_module("oracle.attend")
+state_mod = importlib.import_module("oracle.state")
+vis_mod = importlib.import_module("oracle.visibility")
+from tests import test_int8_format as t8
+from tests import test_oracle_math as tm
+from tests import test_oracle_pins as tp
+
+
+def _fails(fns):
+    for fn in fns:
+        try:
+            fn()
+        except AssertionError:
+            return True
+    return False
+
+
+def _bf_all():
+    for c in tm.TINY:
+        tm.test_brute_force_tiny(c, 0)
+
+
+def test_mutation_missing_softmax_scale(monkeypatch):
+    monkeypatch.setattr(attend_mod, "_scale", lambda prob: 1.0)
+    assert _fails([_bf_all])
+
+
+def test_mutation_wrong_gqa_map(monkeypatch):
+    orig = attend_mod.gather_rows
+
+    def bad(prob, buf, b, h_kv, positions):
+        # query group i of head h reads head (h+1) mod H_kv
+        return orig(prob, buf, b, (h_kv + 1) % prob.num_kv_heads, positions)
+    monkeypatch.setattr(attend_mod, "gather_rows", bad)
+    assert _fails([_bf_all])
+
+
+def test_mutation_window_off_by_one(monkeypatch):
+    orig = vis_mod.visible_positions
+
+    def bad(T, mask_kind="causal", n_sink=0, window=0):
+        if mask_kind == "sink_window":
+            return orig(T, mask_kind, n_sink, window + 1)
+        return orig(T, mask_kind, n_sink, window)
+    monkeypatch.setattr(vis_mod, "visible_positions", bad)
+    monkeypatch.setattr(oracle, "visible_positions", bad)
+    monkeypatch.setattr(attend_mod, "visible_positions", bad)
+    assert _fails([tp.test_window_and_sink_sets, _bf_all])
+
+
+def test_mutation_paged_row_swapped(monkeypatch):
+    monkeypatch.setattr(attend_mod, "paged_nhd_offset",
+                        lambda page, r, h, x, P, H, D: ((page * P + (P - 1 - r)) * H + h) * D + x)
+    assert _fails([_bf_all])
+
+
+def test_mutation_merge_wrong_frame(monkeypatch):
+    def bad(a, b):
+        if not a.valid:
+            return b
+        if not b.valid:
+            return a
+        m = max(a.m, b.m)
+        return state_mod.State(True, m, a.l + b.l, a.u + b.u)   # forgot alpha/beta
+    monkeypatch.setattr(state_mod, "merge_state", bad)
+    monkeypatch.setattr(oracle, "merge_state", bad)
+    monkeypatch.setattr(attend_mod, "merge_state", bad)
+    assert _fails([tp.test_worked_three_split_trace_bit_exact,
+                   lambda: tm.test_partition_invariance(0)])
+
+
+def test_mutation_empty_split_not_identity(monkeypatch):
+    def bad(scores, values, allowed=None):
+        scores = np.asarray(scores, dtype=np.float64)
+        values = np.asarray(values, dtype=np.float64)
+        if values.ndim == 1:
+            values = values[:, None]
+        if allowed is not None:
+            scores, values = scores[np.asarray(allowed)], values[np.asarray(allowed)]
+        if scores.size == 0:
+            return state_mod.State(True, 0.0, 1.0, np.zeros(values.shape[1]))  # fake mass
+        m = float(scores.max())
+        w = np.exp(scores - m)
+        return state_mod.State(True, m, float(w.sum()), w @ values)
+    monkeypatch.setattr(oracle, "summarize_allowed", bad)
+    monkeypatch.setattr(attend_mod, "summarize_allowed", bad)
+    assert _fails([tp.test_worked_three_split_trace_bit_exact,
+                   lambda: tm.test_partition_invariance(1)])
+
+
+def test_mutation_int8_scale_axis(monkeypatch):
+    """K scale indexed by token instead of by 128-token group."""
+    orig = attend_mod.gather_rows
+
+    def bad(prob, buf, b, h_kv, positions):
+        if prob.kv_format != "i8":
+            return orig(prob, buf, b, h_kv, positions)
+        K, V, offs, reg = orig(prob, buf, b, h_kv, positions)
+        pos = np.asarray(positions)
+        q = reg == 0
+        G = prob.k_group
+        gi = np.minimum(pos[q], buf["k_scale"].shape[1] - 1)
+        wrong = oracle.decode_f16(buf["k_scale"][b, gi, h_kv, :])
+        right = oracle.decode_f16(buf["k_scale"][b, pos[q] // G, h_kv, :])
+        K[q] = K[q] / right * wrong
+        return K, V, offs, reg
+    monkeypatch.setattr(attend_mod, "gather_rows", bad)
+    assert _fails([lambda: t8.test_int8_oracle_equals_decoded_reference(("causal", 0, 0))])
+
+
+def test_mutation_empty_request_reads_a_row(monkeypatch):
+    """A length-0 request that still reads position 0 (loop bound rounded up)."""
+    def bad(T, mask_kind="causal", n_sink=0, window=0):
+        return vis_mod.visible_positions(max(int(T), 1), mask_kind, n_sink, window)
+    monkeypatch.setattr(attend_mod, "visible_positions", bad)
+    assert _fails([tm.test_empty_and_all_masked_rows])
