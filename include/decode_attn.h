@@ -1,0 +1,206 @@
+/*
+ * decode_attn.h - C ABI of the MI355X (gfx950) Flash-Decoding decode-attention
+ * library (libdecode_attn.so).
+ *
+ * One call computes, for every query row (b, h_q) of a one-token decode step,
+ *
+ *     O[b, h_q, :] = softmax(q . K^T * scale over the visible keys) @ V
+ *     LSE[b, h_q]  = natural log of the softmax denominator (scaled scores)
+ *
+ * ("M4.5 - Decode Attention Kernels, Mask Programs, and Backend Boundaries",
+ * section 0x01), with the Flash-Decoding schedule of sections 0x02-0x03:
+ * decode_attn_run streams disjoint slices ("splits") of each request's
+ * visible keys and writes one exact partial softmax state (m, l, u) per
+ * (b, h_q, split) into a caller-owned workspace (section 0x02A, structure of
+ * arrays of section 0x03D); decode_attn_combine merges those states into the
+ * final row (sections 0x02B, 0x02C) and applies the all-masked policy
+ * O = +0.0, LSE = -inf.
+ *
+ * Conventions (all calls):
+ *  - Every pointer inside da_args, and the out/lse/workspace/offsets/positions
+ *    arguments, is a DEVICE pointer; problem, plan, reasons and
+ *    workspace_bytes pointers are HOST pointers.  The caller owns every
+ *    buffer; the library allocates no device memory and keeps no state
+ *    beyond a per-device cache of the architecture check.
+ *  - Calls return a da_status; nothing throws across the ABI and nothing is
+ *    printed.  decode_attn_run and decode_attn_combine are asynchronous on the
+ *    given HIP stream (hipStream_t passed as void*, NULL = default stream) and
+ *    never synchronize; run must precede combine on that stream.
+ *  - Semantic errors (DA_ERR_INVALID) are checked before capability checks and
+ *    before any metadata is dereferenced (section 0x07A).  Capability
+ *    failures (DA_ERR_UNSUPPORTED) report EVERY failed predicate as a bit in
+ *    *reasons (section 0x07B, admission as a conjunction with a complete
+ *    reason vector); there is no fallback path (section 0x07C, forced backend
+ *    fails closed).
+ */
+#ifndef DECODE_ATTN_H_
+#define DECODE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t da_status;
+#define DA_OK                 0
+#define DA_ERR_INVALID       (-1)  /* malformed call (bad GQA ratio, layout/page_size mismatch, W <= 0, ...) */
+#define DA_ERR_UNSUPPORTED   (-2)  /* well-formed but outside this library: see *reasons */
+#define DA_ERR_WORKSPACE     (-3)  /* workspace pointer missing or smaller than the plan needs */
+#define DA_ERR_PLAN_MISMATCH (-4)  /* plan fields changed after decode_attn_plan froze them */
+#define DA_ERR_HIP           (-5)  /* a HIP runtime call or kernel launch failed */
+
+/* element types */
+#define DA_F32  0
+#define DA_BF16 1
+#define DA_F16  2
+
+/* K/V storage formats */
+#define DA_KV_F32  0   /* fp32 rows */
+#define DA_KV_BF16 1   /* bf16 rows */
+#define DA_KV_I8   2   /* int8 codes + fp16 scales + bf16 residual, see da_args */
+
+/* cache layouts ("M4.5 ...", sections 0x04B and 0x04D) */
+#define DA_LAYOUT_CONTIG_NHD 0  /* [B, T_cap, H_kv, D]; element ((b*T_cap + t)*H_kv + h)*D + x */
+#define DA_LAYOUT_PAGED_NHD  1  /* pool [N_pages, P, H_kv, D]; page = block_table[b][t / P],
+                                   element ((page*P + t % P)*H_kv + h)*D + x */
+
+/* mask programs: visibility of logical key t for the decode row of request b,
+ * whose visible length is T = seq_lens[b] (the row sits at position T-1) */
+#define DA_MASK_CAUSAL      0  /* every t in [0, T)                                  */
+#define DA_MASK_SINK_WINDOW 1  /* t < min(n_sink, T)  or  t >= T - window  (window > 0)
+                                  ("M5.4 - Long-Context KV Policies: Retention,
+                                  Compression, and Budget Allocation", sections
+                                  0x04-0x05: sink and recent sets as a union)       */
+
+/* admission reason bits (DA_ERR_UNSUPPORTED) */
+#define DA_R_HEAD_DIM    (1ull << 0)   /* head_dim_qk not in {64, 128}                 */
+#define DA_R_HEAD_DIM_V  (1ull << 1)   /* head_dim_v != head_dim_qk                    */
+#define DA_R_GQA_GROUP   (1ull << 2)   /* H_q / H_kv not in {1, 2, 4, 8}              */
+#define DA_R_Q_DTYPE     (1ull << 3)   /* q dtype not paired with the K/V format      */
+#define DA_R_OUT_DTYPE   (1ull << 4)   /* output must be DA_F32                       */
+#define DA_R_KV_FORMAT   (1ull << 5)   /* unknown K/V format                          */
+#define DA_R_LAYOUT      (1ull << 6)   /* layout not available for this K/V format    */
+#define DA_R_INT8_PARAMS (1ull << 7)   /* int8: k_group must be 128, 0 <= R           */
+#define DA_R_SPLITS      (1ull << 8)   /* num_splits above DA_MAX_SPLITS              */
+#define DA_R_INDEX_RANGE (1ull << 9)   /* a tensor exceeds the 2^31-element index range */
+#define DA_R_DEVICE      (1ull << 10)  /* current device is not gfx950 or cannot be queried */
+#define DA_R_MASK_KIND   (1ull << 11)  /* unknown mask program                        */
+#define DA_NUM_REASONS   12
+
+#define DA_MAX_SPLITS 4096
+
+/* The decode coordinate of one call ("M4.5 ...", sections 0x00B and 0x07A). */
+typedef struct da_problem {
+  int32_t batch;             /* B >= 0                                              */
+  int32_t num_q_heads;       /* H_q >= 1                                            */
+  int32_t num_kv_heads;      /* H_kv >= 1, H_q % H_kv == 0; head h_q reads h_q / (H_q/H_kv) */
+  int32_t head_dim_qk;       /* D                                                   */
+  int32_t head_dim_v;        /* must equal head_dim_qk                              */
+  int32_t q_dtype;           /* DA_F32 with DA_KV_F32; DA_BF16 with DA_KV_BF16 / DA_KV_I8 */
+  int32_t out_dtype;         /* DA_F32                                              */
+  int32_t kv_format;         /* DA_KV_*                                             */
+  int32_t layout;            /* DA_LAYOUT_*                                         */
+  int32_t kv_capacity;       /* contiguous: token capacity T_cap of each batch row; paged: 0 */
+  int32_t page_size;         /* paged: P > 0; contiguous: must be 0                */
+  int32_t max_pages_per_seq; /* paged: columns of block_table                       */
+  int32_t num_pages;         /* paged: N_pages of the pool                          */
+  int32_t max_seq_len;       /* upper bound on every seq_lens[b]; sizes the splits  */
+  int32_t mask_kind;         /* DA_MASK_*                                           */
+  int32_t n_sink;            /* DA_MASK_SINK_WINDOW: sink positions >= 0            */
+  int32_t window;            /* DA_MASK_SINK_WINDOW: recent window W > 0            */
+  float   softmax_scale;     /* 0 -> 1/sqrt(head_dim_qk); must be finite and >= 0   */
+  int32_t num_splits;        /* 0 -> automatic; otherwise the requested split count */
+  int32_t k_group;           /* DA_KV_I8: tokens per K-scale group (128); else 0   */
+  int32_t residual_len;      /* DA_KV_I8: bf16 residual rows R >= 0; else 0        */
+  int32_t num_cus;           /* 0 -> query the current device; > 0: plan for this many CUs */
+} da_problem;
+
+/* A frozen plan: a plain value the caller owns and may copy; nothing to free.
+ * Run and combine recompute `key` from the other fields and refuse a plan
+ * whose fields changed after planning (section 0x07F). */
+typedef struct da_plan {
+  uint64_t   key;              /* hash of every field below                         */
+  da_problem problem;          /* normalized copy (softmax_scale resolved)          */
+  int32_t    num_splits;       /* S launched: producer grid is B*H_kv*S workgroups  */
+  int32_t    chunk;            /* visible rows per split (multiple of 16)           */
+  int32_t    max_visible;      /* bound on visible rows of one request              */
+  int32_t    num_cus;          /* CU count the split heuristic used                 */
+  uint64_t   workspace_bytes;  /* B*H_q*S*(D + 2)*4                                 */
+  uint64_t   reserved[2];
+} da_plan;
+
+/* Per-call device buffers.  Layouts (row-major, no padding):
+ *   q           [B, H_q, D]                q_dtype (the single decode row, squeezed)
+ *   k, v        contiguous: [B, T_cap, H_kv, D]; paged: [N_pages, P, H_kv, D]
+ *               DA_KV_I8: int8 codes [B, T_cap, H_kv, D] of tokens t < n_q(b)
+ *   k_scale     DA_KV_I8: fp16 [B, ceil(T_cap/k_group), H_kv, D]; group j scales
+ *               tokens [j*k_group, (j+1)*k_group), one scale per channel
+ *   v_scale     DA_KV_I8: fp16 [B, T_cap, H_kv]; one scale per token
+ *   k_resid,
+ *   v_resid     DA_KV_I8: bf16 [B, R, H_kv, D]; row t - n_q(b) holds token t for
+ *               t >= n_q(b) = seq_lens[b] - min(seq_lens[b], R)
+ *   block_table paged: int32 [B, max_pages_per_seq]; only slots < ceil(T_b/P) are read
+ *   seq_lens    int32 [B]; visible length T_b of each request, 0 <= T_b <= max_seq_len
+ *   workspace   >= plan.workspace_bytes, 256-byte aligned; contents on entry ignored
+ * q, k, v, k_resid and v_resid must be 16-byte aligned. */
+typedef struct da_args {
+  const void*    q;
+  const void*    k;
+  const void*    v;
+  const void*    k_scale;
+  const void*    v_scale;
+  const void*    k_resid;
+  const void*    v_resid;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void*          workspace;
+  uint64_t       workspace_bytes;
+} da_args;
+
+/* Validate the problem (semantic checks first, then every capability
+ * predicate), choose the split count, size the workspace and freeze the plan.
+ * Host only: touches the device only to read its CU count and architecture
+ * when problem->num_cus == 0.  plan, workspace_bytes and reasons may each be
+ * NULL; *reasons receives the complete bit vector of failed predicates. */
+da_status decode_attn_plan(const da_problem* problem, da_plan* plan,
+                           uint64_t* workspace_bytes, uint64_t* reasons);
+
+/* Launch the split kernel: grid B*H_kv*S workgroups; workgroup (b, h_kv, s)
+ * owns visible rows [s*chunk, min((s+1)*chunk, N_b)) of request b and the
+ * H_q/H_kv query heads sharing h_kv, reads each of its K/V rows once, and
+ * writes one (m, l, u) state per query head into the workspace: u fp32
+ * [B, H_q, S, D], then m fp32 [B, H_q, S] (natural-log units of the scaled
+ * scores), then l fp32 [B, H_q, S].  An empty split writes the identity
+ * (m = -inf, l = 0, u = 0); l > 0 marks a valid state. */
+da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream);
+
+/* Launch the combine kernel: for each (b, h_q), fold its S states in
+ * ascending split order and write out fp32 [B, H_q, D] = u/l and, when lse is
+ * not NULL, lse fp32 [B, H_q] = m + ln(l); an all-masked row gets O = +0.0
+ * and LSE = -inf. */
+da_status decode_attn_combine(const da_plan* plan, const void* workspace,
+                              uint64_t workspace_bytes, float* out, float* lse,
+                              void* stream);
+
+/* Debug entry point, never used on the timed path: walks exactly the rows the
+ * split kernel loads, through the same device address and mask code, and
+ * writes for workgroup (b, h_kv, s) and its k-th row (k < chunk):
+ *   offsets  [B, H_kv, S, chunk] int64: element offset of the row's first
+ *            element in the buffer it is read from (k/v, or k_resid/v_resid
+ *            when positions >= n_q(b) for DA_KV_I8);
+ *   positions[B, H_kv, S, chunk] int32: logical key position t.
+ * Entries with no row are left untouched (callers pre-fill them with -1). */
+da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args,
+                                    int64_t* offsets, int32_t* positions, void* stream);
+
+/* Static text for one reason bit index (0 .. DA_NUM_REASONS-1) or status. */
+const char* decode_attn_reason(int bit);
+const char* decode_attn_status_string(da_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H_ */

@@ -1,0 +1,179 @@
+"""Thin ctypes binding of libdecode_attn.so (MI355X decode attention).
+
+Argument marshalling only: every computation happens in the library's HIP
+kernels.  Tensors are passed as device pointers (``tensor.data_ptr()``) and
+the stream as ``torch.cuda.current_stream().cuda_stream``; PyTorch is used by
+callers only for device memory and streams.  Importing this module does not
+need a GPU; loading the library needs the built ``libdecode_attn.so`` and
+fails loudly when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "DA_OK", "DA_ERR_INVALID", "DA_ERR_UNSUPPORTED", "DA_ERR_WORKSPACE",
+    "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
+    "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
+    "decode_attn_run", "decode_attn_combine", "decode_attn_trace_indices",
+    "decode_attn_reason", "decode_attn_status_string", "reason_names",
+]
+
+DA_OK, DA_ERR_INVALID, DA_ERR_UNSUPPORTED = 0, -1, -2
+DA_ERR_WORKSPACE, DA_ERR_PLAN_MISMATCH, DA_ERR_HIP = -3, -4, -5
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+KV_FORMATS = {"f32": 0, "bf16": 1, "i8": 2}
+LAYOUTS = {"contig": 0, "paged": 1}
+MASKS = {"causal": 0, "sink_window": 1}
+NUM_REASONS = 12
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim_qk", "head_dim_v", "q_dtype",
+        "out_dtype", "kv_format", "layout", "kv_capacity", "page_size", "max_pages_per_seq",
+        "num_pages", "max_seq_len", "mask_kind", "n_sink", "window")] + [
+        ("softmax_scale", ctypes.c_float)] + [(n, ctypes.c_int32) for n in (
+            "num_splits", "k_group", "residual_len", "num_cus")]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("key", ctypes.c_uint64), ("problem", Problem), ("num_splits", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("max_visible", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+                ("reserved", ctypes.c_uint64 * 2)]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "block_table", "seq_lens",
+        "workspace")] + [("workspace_bytes", ctypes.c_uint64)]
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, what: str, reasons: int = 0):
+        self.status = status
+        self.reasons = reasons
+        text = decode_attn_status_string(status)
+        if reasons:
+            text += ": " + "; ".join(reason_names(reasons))
+        super().__init__(f"{what}: {text} (status {status}, reasons 0x{reasons:x})")
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecode_attn.so")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(path)
+        L.decode_attn_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Plan),
+                                       ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
+        L.decode_attn_plan.restype = ctypes.c_int32
+        L.decode_attn_run.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p]
+        L.decode_attn_run.restype = ctypes.c_int32
+        L.decode_attn_combine.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_uint64,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_attn_combine.restype = ctypes.c_int32
+        L.decode_attn_trace_indices.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_attn_trace_indices.restype = ctypes.c_int32
+        L.decode_attn_reason.argtypes = [ctypes.c_int]
+        L.decode_attn_reason.restype = ctypes.c_char_p
+        L.decode_attn_status_string.argtypes = [ctypes.c_int32]
+        L.decode_attn_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def decode_attn_reason(bit: int) -> str:
+    return lib().decode_attn_reason(bit).decode()
+
+
+def decode_attn_status_string(status: int) -> str:
+    return lib().decode_attn_status_string(status).decode()
+
+
+def reason_names(reasons: int):
+    return [decode_attn_reason(i) for i in range(NUM_REASONS) if reasons >> i & 1]
+
+
+def problem_from(p, num_cus: int = 0) -> Problem:
+    """Build the C struct from any object with the field names of
+    ``da_problem`` (strings allowed for the enum fields)."""
+    def enum(v, table):
+        return table[v] if isinstance(v, str) else int(v)
+    d = getattr(p, "head_dim", None)
+    return Problem(
+        batch=p.batch, num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads,
+        head_dim_qk=getattr(p, "head_dim_qk", d), head_dim_v=getattr(p, "head_dim_v", d),
+        q_dtype=enum(p.q_dtype, DTYPES), out_dtype=enum(getattr(p, "out_dtype", "f32"), DTYPES),
+        kv_format=enum(p.kv_format, KV_FORMATS), layout=enum(p.layout, LAYOUTS),
+        kv_capacity=p.kv_capacity if enum(p.layout, LAYOUTS) == 0 else 0,
+        page_size=p.page_size, max_pages_per_seq=p.max_pages_per_seq, num_pages=p.num_pages,
+        max_seq_len=p.max_seq_len, mask_kind=enum(p.mask_kind, MASKS), n_sink=p.n_sink,
+        window=p.window, softmax_scale=p.softmax_scale, num_splits=p.num_splits,
+        k_group=p.k_group, residual_len=p.residual_len, num_cus=num_cus)
+
+
+def decode_attn_plan(problem: Problem, check: bool = True):
+    """Returns ``(status, plan, workspace_bytes, reasons)``; raises
+    DecodeAttnError on failure when ``check``."""
+    plan = Plan()
+    ws = ctypes.c_uint64(0)
+    rs = ctypes.c_uint64(0)
+    st = lib().decode_attn_plan(ctypes.byref(problem), ctypes.byref(plan), ctypes.byref(ws),
+                                ctypes.byref(rs))
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_plan", rs.value)
+    return st, plan, ws.value, rs.value
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def make_args(q, k, v, seq_lens, workspace, workspace_bytes, k_scale=None, v_scale=None,
+              k_resid=None, v_resid=None, block_table=None) -> Args:
+    return Args(q=_ptr(q), k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
+                k_resid=_ptr(k_resid), v_resid=_ptr(v_resid), block_table=_ptr(block_table),
+                seq_lens=_ptr(seq_lens), workspace=_ptr(workspace),
+                workspace_bytes=int(workspace_bytes))
+
+
+def decode_attn_run(plan: Plan, args: Args, stream: int = 0, check: bool = True) -> int:
+    st = lib().decode_attn_run(ctypes.byref(plan), ctypes.byref(args), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_run")
+    return st
+
+
+def decode_attn_combine(plan: Plan, workspace, workspace_bytes: int, out, lse=None,
+                        stream: int = 0, check: bool = True) -> int:
+    st = lib().decode_attn_combine(ctypes.byref(plan), _ptr(workspace), int(workspace_bytes),
+                                   _ptr(out), _ptr(lse), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_combine")
+    return st
+
+
+def decode_attn_trace_indices(plan: Plan, args: Args, offsets, positions, stream: int = 0,
+                              check: bool = True) -> int:
+    st = lib().decode_attn_trace_indices(ctypes.byref(plan), ctypes.byref(args), _ptr(offsets),
+                                         _ptr(positions), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_trace_indices")
+    return st

@@ -1,0 +1,249 @@
+// C-ABI launch entry points: decode_attn_run, decode_attn_combine,
+// decode_attn_trace_indices.  Argument and plan checks happen on the host
+// before any launch; the launches are asynchronous on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "combine_kernel.hpp"
+#include "device_common.hpp"
+#include "plan_internal.hpp"
+#include "split_kernel.hpp"
+#include "split_kernel_mfma.hpp"
+
+namespace {
+
+// Launch shape of the split kernel: waves per workgroup and rows per row slot
+// per tile (see split_kernel.hpp).
+#ifndef DA_WAVES
+#define DA_WAVES 4
+#endif
+#ifndef DA_UNROLL
+#define DA_UNROLL 4
+#endif
+#ifndef DA_UNROLL_I8
+#define DA_UNROLL_I8 2
+#endif
+// bf16 K/V with D = 128 take the matrix-core score kernel.
+#ifndef DA_MFMA_QK
+#define DA_MFMA_QK 1
+#endif
+constexpr int kWaves = DA_WAVES;
+
+template <int FMT> struct Unroll { static constexpr int value = DA_UNROLL; };
+template <> struct Unroll<DA_KV_I8> { static constexpr int value = DA_UNROLL_I8; };
+
+template <int FMT, int D>
+constexpr bool use_mfma() { return DA_MFMA_QK && FMT == DA_KV_BF16 && D == 128; }
+
+// Rows per wave tile of the kernel that serves (FMT, D); the trace walk uses
+// the same value.
+template <int FMT, int D>
+constexpr int tile_rows() {
+  return use_mfma<FMT, D>() ? 16 : (64 / (D / da::KvTraits<FMT>::EPL)) * Unroll<FMT>::value;
+}
+
+int log2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+da_status check_args(const da_plan* plan, const da_args* a) {
+  if (!plan || !a) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!a->q || !a->k || !a->v || !a->seq_lens) return DA_ERR_INVALID;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return DA_ERR_INVALID;
+  if (p.layout == DA_LAYOUT_PAGED_NHD && !a->block_table) return DA_ERR_INVALID;
+  if (p.kv_format == DA_KV_I8) {
+    if (!a->k_scale || !a->v_scale) return DA_ERR_INVALID;
+    if (p.residual_len > 0 && (!a->k_resid || !a->v_resid)) return DA_ERR_INVALID;
+    if ((a->k_resid && !aligned16(a->k_resid)) || (a->v_resid && !aligned16(a->v_resid)))
+      return DA_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(a->k_scale) & 15u) != 0) return DA_ERR_INVALID;
+  }
+  return DA_OK;
+}
+
+da::SplitParams make_params(const da_plan* plan, const da_args* a) {
+  const da_problem& p = plan->problem;
+  da::SplitParams sp;
+  sp.q = a->q;
+  sp.k = a->k;
+  sp.v = a->v;
+  sp.k_scale = static_cast<const uint16_t*>(a->k_scale);
+  sp.v_scale = static_cast<const uint16_t*>(a->v_scale);
+  sp.k_resid = a->k_resid;
+  sp.v_resid = a->v_resid;
+  sp.block_table = a->block_table;
+  sp.seq_lens = a->seq_lens;
+  const uint64_t n_states = (uint64_t)p.batch * p.num_q_heads * plan->num_splits;
+  float* ws = static_cast<float*>(a->workspace);
+  sp.ws_u = ws;
+  sp.ws_m = ws ? ws + n_states * p.head_dim_v : nullptr;
+  sp.ws_l = ws ? sp.ws_m + n_states : nullptr;
+  sp.num_q_heads = p.num_q_heads;
+  sp.num_kv_heads = p.num_kv_heads;
+  sp.num_splits = plan->num_splits;
+  sp.chunk = plan->chunk;
+  sp.kv_capacity = p.kv_capacity;
+  sp.page_size = p.page_size;
+  sp.page_shift = log2_exact(p.page_size);
+  sp.max_pages = p.max_pages_per_seq;
+  sp.mask_kind = p.mask_kind;
+  sp.n_sink = p.n_sink;
+  sp.window = p.window;
+  sp.k_group_shift = p.kv_format == DA_KV_I8 ? log2_exact(p.k_group) : 0;
+  sp.residual_len = p.residual_len;
+  sp.max_seq_len = p.max_seq_len;
+  sp.num_pages = p.num_pages;
+  sp.qscale = p.softmax_scale * 1.4426950408889634f;
+  return sp;
+}
+
+template <int FMT, int D, int G, bool PAGED>
+void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
+  if constexpr (use_mfma<FMT, D>())
+    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves>), dim3(grid), dim3(kWaves * 64), 0,
+                       st, sp);
+  else
+    hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value>), dim3(grid),
+                       dim3(kWaves * 64), 0, st, sp);
+}
+
+template <int FMT, int D, bool PAGED>
+void launch_trace(const da::SplitParams& sp, unsigned grid, int64_t* off, int32_t* pos,
+                  hipStream_t st) {
+  hipLaunchKernelGGL((da::trace_kernel<FMT == DA_KV_I8, D, PAGED, kWaves, tile_rows<FMT, D>()>),
+                     dim3(grid), dim3(kWaves * 64), 0, st, sp, off, pos);
+}
+
+template <int FMT, int D, bool PAGED>
+bool dispatch_g(int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
+  switch (g) {
+    case 1: launch_split<FMT, D, 1, PAGED>(sp, grid, st); return true;
+    case 2: launch_split<FMT, D, 2, PAGED>(sp, grid, st); return true;
+    case 4: launch_split<FMT, D, 4, PAGED>(sp, grid, st); return true;
+    case 8: launch_split<FMT, D, 8, PAGED>(sp, grid, st); return true;
+    default: return false;
+  }
+}
+
+template <int FMT, bool PAGED>
+bool dispatch_d(int d, int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
+  if (d == 64) return dispatch_g<FMT, 64, PAGED>(g, sp, grid, st);
+  if (d == 128) return dispatch_g<FMT, 128, PAGED>(g, sp, grid, st);
+  return false;
+}
+
+template <int FMT, bool PAGED>
+bool dispatch_trace_d(int d, const da::SplitParams& sp, unsigned grid, int64_t* off, int32_t* pos,
+                      hipStream_t st) {
+  if (d == 64) { launch_trace<FMT, 64, PAGED>(sp, grid, off, pos, st); return true; }
+  if (d == 128) { launch_trace<FMT, 128, PAGED>(sp, grid, off, pos, st); return true; }
+  return false;
+}
+
+}  // namespace
+
+extern "C" da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream) {
+  const da_status chk = check_args(plan, args);
+  if (chk != DA_OK) return chk;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!args->workspace || args->workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(args->workspace) & 15u) != 0) return DA_ERR_WORKSPACE;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  const da::SplitParams sp = make_params(plan, args);
+  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
+  const int g = p.num_q_heads / p.num_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  bool ok = false;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
+  switch (p.kv_format) {
+    case DA_KV_F32:
+      ok = paged ? dispatch_d<DA_KV_F32, true>(p.head_dim_qk, g, sp, grid, st)
+                 : dispatch_d<DA_KV_F32, false>(p.head_dim_qk, g, sp, grid, st);
+      break;
+    case DA_KV_BF16:
+      ok = paged ? dispatch_d<DA_KV_BF16, true>(p.head_dim_qk, g, sp, grid, st)
+                 : dispatch_d<DA_KV_BF16, false>(p.head_dim_qk, g, sp, grid, st);
+      break;
+    case DA_KV_I8:
+      ok = !paged && dispatch_d<DA_KV_I8, false>(p.head_dim_qk, g, sp, grid, st);
+      break;
+    default:
+      ok = false;
+  }
+  if (!ok) return DA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+extern "C" da_status decode_attn_combine(const da_plan* plan, const void* workspace,
+                                         uint64_t workspace_bytes, float* out, float* lse,
+                                         void* stream) {
+  if (!plan) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!out) return DA_ERR_INVALID;
+  if (!workspace || workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  const uint64_t n_states = (uint64_t)p.batch * p.num_q_heads * plan->num_splits;
+  const float* ws_u = static_cast<const float*>(workspace);
+  const float* ws_m = ws_u + n_states * p.head_dim_v;
+  const float* ws_l = ws_m + n_states;
+  const unsigned rows = (unsigned)(p.batch * p.num_q_heads);
+  const size_t lds = (size_t)plan->num_splits * sizeof(float);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p.head_dim_v == 64)
+    hipLaunchKernelGGL(da::combine_kernel<64>, dim3(rows), dim3(da::kCombineThreads), lds, st, ws_u,
+                       ws_m, ws_l, out, lse, plan->num_splits);
+  else if (p.head_dim_v == 128)
+    hipLaunchKernelGGL(da::combine_kernel<128>, dim3(rows), dim3(da::kCombineThreads), lds, st, ws_u,
+                       ws_m, ws_l, out, lse, plan->num_splits);
+  else
+    return DA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+extern "C" da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args,
+                                               int64_t* offsets, int32_t* positions,
+                                               void* stream) {
+  const da_status chk = check_args(plan, args);
+  if (chk != DA_OK) return chk;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!offsets || !positions) return DA_ERR_INVALID;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  const da::SplitParams sp = make_params(plan, args);
+  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  bool ok = false;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
+  switch (p.kv_format) {
+    case DA_KV_F32:
+      ok = paged ? dispatch_trace_d<DA_KV_F32, true>(p.head_dim_qk, sp, grid, offsets, positions, st)
+                 : dispatch_trace_d<DA_KV_F32, false>(p.head_dim_qk, sp, grid, offsets, positions, st);
+      break;
+    case DA_KV_BF16:
+      ok = paged ? dispatch_trace_d<DA_KV_BF16, true>(p.head_dim_qk, sp, grid, offsets, positions, st)
+                 : dispatch_trace_d<DA_KV_BF16, false>(p.head_dim_qk, sp, grid, offsets, positions, st);
+      break;
+    case DA_KV_I8:
+      ok = !paged && dispatch_trace_d<DA_KV_I8, false>(p.head_dim_qk, sp, grid, offsets, positions, st);
+      break;
+    default:
+      ok = false;
+  }
+  if (!ok) return DA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}

@@ -1,0 +1,182 @@
+// Device-side address and mask code shared by the split kernel and the index
+// trace kernel (one source of truth for which K/V rows a workgroup reads).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_attn.h"
+
+namespace da {
+
+// Kernel arguments of the split and trace kernels (passed by value).
+struct SplitParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint16_t* k_scale;   // fp16 bits
+  const uint16_t* v_scale;   // fp16 bits
+  const void* k_resid;
+  const void* v_resid;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_u;
+  float* ws_m;
+  float* ws_l;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_splits;
+  int32_t chunk;
+  int32_t kv_capacity;
+  int32_t page_size;
+  int32_t page_shift;        // log2(page_size) when a power of two, else -1
+  int32_t max_pages;
+  int32_t mask_kind;
+  int32_t n_sink;
+  int32_t window;
+  int32_t k_group_shift;     // log2(k_group)
+  int32_t residual_len;
+  int32_t max_seq_len;       // plan bound: seq_lens are clamped to [0, max_seq_len]
+  int32_t num_pages;         // paged: page ids are clamped to [0, num_pages)
+  float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
+};
+
+// ---------------------------------------------------------------------------
+// Mask program.  The visible set of the decode row of a request with visible
+// length T is at most two intervals ("M5.4 - Long-Context KV Policies:
+// Retention, Compression, and Budget Allocation", sections 0x04-0x05):
+// causal [0, T); sink+window [0, min(n_sink, T)) U [max(0, T - W), T).  It is
+// compiled into (ns, gap): the o-th visible row (o = 0, 1, ...) sits at
+// position o for o < ns and o + gap after, and N = T - gap rows are visible.
+// Splits partition the ordinals [0, N), so a workgroup never enumerates a
+// hidden row: every SKIP tile of "M4.5 - Decode Attention Kernels, Mask
+// Programs, and Backend Boundaries" section 0x05C is dropped before any
+// address work (section 0x05D), and the only PARTIAL tiles are ragged tails,
+// whose out-of-range rows get score -inf before the max (section 0x05C).
+// ---------------------------------------------------------------------------
+struct VisProgram {
+  int n_vis;
+  int ns;
+  int gap;
+};
+
+__device__ __forceinline__ VisProgram make_vis(int T, int kind, int n_sink, int window) {
+  VisProgram v;
+  if (kind == DA_MASK_SINK_WINDOW) {
+    const int ns = min(n_sink, T);
+    const int ws = max(0, T - window);
+    v.ns = ns;
+    v.gap = max(0, ws - ns);
+    v.n_vis = T - v.gap;
+  } else {
+    v.ns = T;
+    v.gap = 0;
+    v.n_vis = T;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int vis_pos(const VisProgram& v, int o) {
+  return o < v.ns ? o : o + v.gap;
+}
+
+// Visible length of request b, clamped to the plan's bound so that no load
+// can leave the buffers the plan was sized for.
+__device__ __forceinline__ int request_len(const SplitParams& p, int b) {
+  return min(max(p.seq_lens[b], 0), p.max_seq_len);
+}
+
+// Split s of a request with N visible rows owns ordinals [s*chunk, min(.., N)):
+// a fixed-width chunk policy ("M4.5 ...", section 0x03B) whose width is a
+// multiple of 16 rows; splits past the tail own nothing and write the empty
+// identity (section 0x03G).
+__device__ __forceinline__ void split_range(int n_vis, int s, int chunk, int* begin, int* end) {
+  const long long b = (long long)s * chunk;
+  const long long e = b + chunk;
+  *begin = (int)min<long long>(b, n_vis);
+  *end = (int)min<long long>(e, n_vis);
+}
+
+// ---------------------------------------------------------------------------
+// Address translation ("M4.5 ...", sections 0x04B, 0x04D): element offset of
+// the first element of row (b, t, h) in the buffer it lives in.
+// ---------------------------------------------------------------------------
+// Split into a part that is uniform over a workgroup (the element offset of
+// head h in row 0 of request b, or of page 0) and the row index of token t
+// (t itself, or page*P + t%P); the element offset is
+// base + row_index * H_kv * D.
+template <bool PAGED>
+__device__ __forceinline__ int64_t head_base_offset(const SplitParams& p, int b, int h, int D) {
+  if (PAGED) return (int64_t)h * D;
+  return ((int64_t)b * p.kv_capacity * p.num_kv_heads + h) * (int64_t)D;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ uint32_t kv_row_index(const SplitParams& p, int b, int t) {
+  if (PAGED) {
+    int j, r;
+    if (p.page_shift >= 0) {
+      j = t >> p.page_shift;
+      r = t & (p.page_size - 1);
+    } else {
+      j = t / p.page_size;
+      r = t - j * p.page_size;
+    }
+    // A visible slot must hold a pool page; clamping keeps a corrupt table
+    // from addressing memory outside the pool.
+    const int page = min(max(p.block_table[(int64_t)b * p.max_pages + j], 0), p.num_pages - 1);
+    return (uint32_t)page * (uint32_t)p.page_size + (uint32_t)r;
+  }
+  return (uint32_t)t;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_row_offset(const SplitParams& p, int b, int t, int h, int D) {
+  return head_base_offset<PAGED>(p, b, h, D) +
+         (int64_t)((uint64_t)kv_row_index<PAGED>(p, b, t) * (uint32_t)(p.num_kv_heads * D));
+}
+
+// int8 format: tokens t < n_q come from the code buffers, the newest
+// min(T, R) tokens from the bf16 residual, row t - n_q ("M8.6 - Live-Data
+// Quantization: Activations and KV Cache", section 0x06B).
+__device__ __forceinline__ int64_t resid_row_offset(const SplitParams& p, int b, int tr, int h, int D) {
+  return (((int64_t)b * p.residual_len + tr) * p.num_kv_heads + h) * (int64_t)D;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (64-wide wavefronts)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of LANES adjacent lanes (LANES in {4, 8, 16, 32, 64}); every
+// lane of a group receives the group total.  Within a 16-lane DPP row:
+// quad_perm [1,0,3,2] and [2,3,0,1] give the quad sum, row_half_mirror pairs
+// each quad with the other quad of its half row, row_mirror pairs the two
+// halves.  Wider groups use ds_swizzle-free xor shuffles.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64, "");
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  if (LANES >= 8) x += dpp_f32<0x141>(x);   // row_half_mirror
+  if (LANES >= 16) x += dpp_f32<0x140>(x);  // row_mirror
+  if (LANES >= 32) x += __shfl_xor(x, 16);
+  if (LANES >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float i8_at(uint32_t w, int byte) {
+  return (float)(int32_t)((int32_t)(w << (24 - 8 * byte)) >> 24);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+
+}  // namespace da

@@ -1,0 +1,202 @@
+// decode_attn_plan: validation, admission reasons, split choice, workspace
+// sizing and the frozen plan key.  Host code only.
+//
+// Follows "M4.5 - Decode Attention Kernels, Mask Programs, and Backend
+// Boundaries": semantic checks before capability checks (section 0x07A),
+// admission as a conjunction whose failures are all reported (0x07B), a plan
+// whose static projection is frozen and re-checked at run (0x07F), split count
+// as a tuning decision that trades producer parallelism against workspace
+// round trip and reducer fan-in (0x03I, 0x03F).
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "plan_internal.hpp"
+
+namespace da {
+
+bool current_device_info(int* device, int* num_cus, bool* is_gfx950) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+  if (device) *device = dev;
+  if (num_cus) *num_cus = prop.multiProcessorCount;
+  if (is_gfx950) *is_gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  return true;
+}
+
+bool current_device_is_gfx950() {
+  static std::atomic<int8_t> cache[64];   // 0 unknown, 1 gfx950, 2 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (dev >= 0 && dev < 64) {
+    int8_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c) return c == 1;
+  }
+  bool ok = false;
+  if (!current_device_info(nullptr, nullptr, &ok)) return false;
+  if (dev >= 0 && dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok;
+}
+
+}  // namespace da
+
+namespace {
+
+// Automatic split choice.  A K/V head of one request is an independent
+// stream; B*H_kv of them rarely fill 256 CUs, so the visible rows are cut into
+// splits until about kWgPerCu workgroups per CU exist, but never into splits
+// shorter than kMinChunk rows: each extra split adds one (m, l, u) state per
+// query head to the workspace round trip and to the reducer fan-in.
+constexpr int kWgPerCu = 3;
+constexpr int kMinChunk = 256;
+constexpr int kRowAlign = 16;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace
+
+extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_out,
+                                      uint64_t* workspace_bytes, uint64_t* reasons_out) {
+  uint64_t reasons = 0;
+  if (reasons_out) *reasons_out = 0;
+  if (!problem) return DA_ERR_INVALID;
+  da_problem p = *problem;
+
+  // ---- semantic checks: malformed calls are not "unsupported" -------------
+  if (p.batch < 0 || p.num_q_heads < 1 || p.num_kv_heads < 1) return DA_ERR_INVALID;
+  if (p.num_q_heads % p.num_kv_heads != 0) return DA_ERR_INVALID;
+  if (p.head_dim_qk < 1 || p.head_dim_v < 1) return DA_ERR_INVALID;
+  if (p.max_seq_len < 0 || p.num_splits < 0 || p.num_cus < 0) return DA_ERR_INVALID;
+  if (!std::isfinite(p.softmax_scale) || p.softmax_scale < 0.f) return DA_ERR_INVALID;
+  if (p.layout == DA_LAYOUT_PAGED_NHD) {
+    if (p.page_size <= 0 || p.num_pages < 1 || p.max_pages_per_seq < 1) return DA_ERR_INVALID;
+    if (p.kv_capacity != 0) return DA_ERR_INVALID;
+    if (ceil_div(p.max_seq_len, p.page_size) > p.max_pages_per_seq) return DA_ERR_INVALID;
+  } else if (p.layout == DA_LAYOUT_CONTIG_NHD) {
+    if (p.page_size != 0 || p.max_pages_per_seq != 0 || p.num_pages != 0) return DA_ERR_INVALID;
+    if (p.kv_capacity < 0) return DA_ERR_INVALID;
+  }
+  if (p.mask_kind == DA_MASK_SINK_WINDOW) {
+    if (p.window <= 0 || p.n_sink < 0) return DA_ERR_INVALID;
+  } else if (p.mask_kind == DA_MASK_CAUSAL) {
+    if (p.window != 0 || p.n_sink != 0) return DA_ERR_INVALID;
+  }
+  if (p.kv_format == DA_KV_I8) {
+    if (p.k_group <= 0 || p.residual_len < 0) return DA_ERR_INVALID;
+    if (p.layout == DA_LAYOUT_CONTIG_NHD) {
+      const int64_t nq_max = p.max_seq_len - std::min(p.max_seq_len, p.residual_len);
+      if (p.kv_capacity < nq_max) return DA_ERR_INVALID;
+    }
+  } else {
+    if (p.k_group != 0 || p.residual_len != 0) return DA_ERR_INVALID;
+    if (p.layout == DA_LAYOUT_CONTIG_NHD && p.kv_capacity < p.max_seq_len) return DA_ERR_INVALID;
+  }
+
+  // ---- capability predicates: collect every failure ------------------------
+  const int g = p.num_q_heads / p.num_kv_heads;
+  if (p.head_dim_qk != 64 && p.head_dim_qk != 128) reasons |= DA_R_HEAD_DIM;
+  if (p.head_dim_v != p.head_dim_qk) reasons |= DA_R_HEAD_DIM_V;
+  if (g != 1 && g != 2 && g != 4 && g != 8) reasons |= DA_R_GQA_GROUP;
+  const bool fmt_ok = p.kv_format == DA_KV_F32 || p.kv_format == DA_KV_BF16 || p.kv_format == DA_KV_I8;
+  if (!fmt_ok) reasons |= DA_R_KV_FORMAT;
+  if (fmt_ok) {
+    const bool q_ok = (p.kv_format == DA_KV_F32) ? p.q_dtype == DA_F32 : p.q_dtype == DA_BF16;
+    if (!q_ok) reasons |= DA_R_Q_DTYPE;
+  }
+  if (p.out_dtype != DA_F32) reasons |= DA_R_OUT_DTYPE;
+  if (p.layout != DA_LAYOUT_CONTIG_NHD && p.layout != DA_LAYOUT_PAGED_NHD) reasons |= DA_R_LAYOUT;
+  if (p.kv_format == DA_KV_I8 && p.layout != DA_LAYOUT_CONTIG_NHD) reasons |= DA_R_LAYOUT;
+  if (p.kv_format == DA_KV_I8 &&
+      !(p.k_group >= 16 && p.k_group <= 1024 && (p.k_group & (p.k_group - 1)) == 0))
+    reasons |= DA_R_INT8_PARAMS;
+  if (p.mask_kind != DA_MASK_CAUSAL && p.mask_kind != DA_MASK_SINK_WINDOW) reasons |= DA_R_MASK_KIND;
+  if (p.num_splits > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;
+
+  int num_cus = p.num_cus;
+  if (num_cus == 0) {
+    int dev = 0, cus = 0;
+    bool gfx950 = false;
+    if (!da::current_device_info(&dev, &cus, &gfx950) || !gfx950 || cus <= 0) {
+      reasons |= DA_R_DEVICE;
+      cus = 256;
+    }
+    num_cus = cus;
+  }
+
+  // ---- split plan ----------------------------------------------------------
+  int64_t max_vis = p.max_seq_len;
+  if (p.mask_kind == DA_MASK_SINK_WINDOW)
+    max_vis = std::min<int64_t>(max_vis, (int64_t)p.n_sink + (int64_t)p.window);
+  int64_t chunk;
+  if (max_vis == 0) {
+    chunk = kRowAlign;
+  } else if (p.num_splits > 0) {
+    chunk = round_up(ceil_div(max_vis, p.num_splits), kRowAlign);
+  } else {
+    const int64_t units = std::max<int64_t>(1, (int64_t)p.batch * p.num_kv_heads);
+    const int64_t s0 = std::max<int64_t>(1, ceil_div((int64_t)kWgPerCu * num_cus, units));
+    chunk = round_up(ceil_div(max_vis, s0), kRowAlign);
+    chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinChunk, round_up(max_vis, kRowAlign)));
+  }
+  int64_t S = max_vis == 0 ? 1 : ceil_div(max_vis, chunk);
+  if (S > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;
+
+  const int64_t grid = (int64_t)p.batch * p.num_kv_heads * S;
+  if (grid > 0x7fffffffLL) reasons |= DA_R_INDEX_RANGE;
+  if ((int64_t)p.batch * p.num_kv_heads * S * chunk > (1LL << 40)) reasons |= DA_R_INDEX_RANGE;
+
+  if (reasons_out) *reasons_out = reasons;
+  if (reasons) return DA_ERR_UNSUPPORTED;
+
+  if (p.softmax_scale == 0.f) p.softmax_scale = 1.0f / std::sqrt((float)p.head_dim_qk);
+  const uint64_t ws = (uint64_t)p.batch * p.num_q_heads * (uint64_t)S * (uint64_t)(p.head_dim_v + 2) * 4u;
+
+  da_plan plan;
+  std::memset(&plan, 0, sizeof(plan));
+  plan.problem = p;
+  plan.num_splits = (int32_t)S;
+  plan.chunk = (int32_t)chunk;
+  plan.max_visible = (int32_t)max_vis;
+  plan.num_cus = num_cus;
+  plan.workspace_bytes = ws;
+  plan.key = da::plan_hash(plan);
+  if (plan_out) *plan_out = plan;
+  if (workspace_bytes) *workspace_bytes = ws;
+  return DA_OK;
+}
+
+extern "C" const char* decode_attn_reason(int bit) {
+  static const char* const text[DA_NUM_REASONS] = {
+      "head_dim_qk must be 64 or 128",
+      "head_dim_v must equal head_dim_qk",
+      "query heads per K/V head must be 1, 2, 4 or 8",
+      "q dtype must be f32 with f32 K/V and bf16 with bf16 or int8 K/V",
+      "output dtype must be f32",
+      "unknown K/V storage format",
+      "layout not available for this K/V format (int8 is contiguous only)",
+      "int8 k_group must be a power of two in [16, 1024]",
+      "split count above the library maximum",
+      "grid or trace size exceeds the index range",
+      "current device is not gfx950 or cannot be queried",
+      "unknown mask program",
+  };
+  if (bit < 0 || bit >= DA_NUM_REASONS) return "unknown reason bit";
+  return text[bit];
+}
+
+extern "C" const char* decode_attn_status_string(da_status s) {
+  switch (s) {
+    case DA_OK: return "ok";
+    case DA_ERR_INVALID: return "invalid call";
+    case DA_ERR_UNSUPPORTED: return "unsupported (see reason bits)";
+    case DA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DA_ERR_PLAN_MISMATCH: return "plan changed after planning";
+    case DA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}

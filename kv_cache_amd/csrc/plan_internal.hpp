@@ -1,0 +1,40 @@
+// Host helpers shared by the planner and the launch code.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+
+#include "decode_attn.h"
+
+namespace da {
+
+// FNV-1a over the plan bytes that follow the key field.  The plan is a
+// padding-free POD (int32/float fields, then 8-byte aligned uint64 fields).
+inline uint64_t plan_hash(const da_plan& p) {
+  const unsigned char* b = reinterpret_cast<const unsigned char*>(&p);
+  const size_t begin = offsetof(da_plan, problem);
+  const size_t end = offsetof(da_plan, reserved);
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = begin; i < end; ++i) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+inline bool plan_intact(const da_plan* p) { return p && p->key == plan_hash(*p); }
+
+// Element size in bytes of one K/V row element as stored in k/v.
+inline int kv_elem_bytes(int kv_format) {
+  return kv_format == DA_KV_F32 ? 4 : kv_format == DA_KV_BF16 ? 2 : 1;
+}
+
+// Queries the current device: CU count and whether it is gfx950.  Returns
+// false if the HIP runtime cannot answer.
+bool current_device_info(int* device, int* num_cus, bool* is_gfx950);
+
+// Per-device cached gfx950 check used by the launch entry points.
+bool current_device_is_gfx950();
+
+}  // namespace da

@@ -1,0 +1,216 @@
+// Split kernel for bf16 K/V with D = 128: QK^T on the matrix cores, PV on
+// the vector ALUs.
+//
+// Same ownership and output as split_kernel (workgroup (b, h_kv, s), G query
+// heads, one exact (m, l, u) state per head, "M4.5 - Decode Attention Kernels,
+// Mask Programs, and Backend Boundaries", sections 0x02A and 0x03A).  Each wave
+// consumes tiles of 16 visible rows:
+//
+//  * Scores.  v_mfma_f32_16x16x32_bf16 with A = the 16 K rows of the tile
+//    (M = rows, K = 32 channels per instruction, 4 instructions for D = 128)
+//    and B = the q rows of the group (N = 16 columns, the first G used, the
+//    rest zero).  Lane l loads 16 bytes of row l%16 for channel group l/16 of
+//    each 32-channel slice, i.e. exactly the A operand; q is loaded once in
+//    the B operand layout.  The result gives lane l the scores of rows
+//    4*(l/16) .. 4*(l/16)+3 for head l%16.  The products of the bf16 inputs
+//    are exact and accumulate in fp32, so this is a small dense tile of the
+//    GQA group rather than a reshaped memory-bound product.
+//  * Softmax.  Per head: tile maximum across the 4 lanes that hold the head,
+//    online rescale of the running state, p = 2^(s - m) (scores in base 2).
+//  * PV.  Row slot r = l/16 owns rows 4r .. 4r+3 of the tile; lane l holds
+//    channels 8*(l%16) .. +7 of those V rows and accumulates u for the G heads.
+//    The weight p(row 4r+j, head i) sits in lane 16r+i of the same 16-lane
+//    DPP row, so it is fetched with row_newbcast:i.
+#pragma once
+
+#include "split_common.hpp"
+
+namespace da {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Broadcast lane I of each 16-lane row to the whole row.
+template <int I>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xF, 0xF, false));
+}
+
+template <int G, int I = 0>
+struct HeadLoop {
+  // u[i][:] = u[i][:] * row_bcast<i>(scale)
+  __device__ __forceinline__ static void rescale(float (&u)[G][8], float scale) {
+    const float a = row_bcast<I>(scale);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[I][e] *= a;
+    HeadLoop<G, I + 1>::rescale(u, scale);
+  }
+  // u[i][:] += row_bcast<i>(w) * v[:]
+  __device__ __forceinline__ static void accumulate(float (&u)[G][8], float w, const float (&v)[8]) {
+    const float a = row_bcast<I>(w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[I][e] = fmaf(a, v[e], u[I][e]);
+    HeadLoop<G, I + 1>::accumulate(u, w, v);
+  }
+};
+template <int G>
+struct HeadLoop<G, G> {
+  __device__ __forceinline__ static void rescale(float (&)[G][8], float) {}
+  __device__ __forceinline__ static void accumulate(float (&)[G][8], float, const float (&)[8]) {}
+};
+
+struct MfmaTile {
+  uint4 k[4];   // A operand, one per 32-channel slice
+  uint4 v[4];   // V rows 4r + j, channels 8*(l%16) .. +7
+};
+
+// Waves per SIMD the register budget must allow: 4 (<= 128 VGPRs) for up to
+// 4 heads per group, so that four 4-wave workgroups are resident on every CU
+// and a grid of 4 x CU workgroups runs in one round; 8 heads need 64
+// accumulators per lane and get 3.
+template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 : 3; };
+
+template <int G, bool PAGED, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
+  constexpr int D = 128;
+  constexpr int TW = 16;
+  static_assert(G >= 1 && G <= 16, "");
+
+  const int wg = blockIdx.x;
+  const int s = wg % p.num_splits;
+  const int bh = wg / p.num_splits;
+  const int h = bh % p.num_kv_heads;
+  const int b = bh / p.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;     // K row of the tile / score column (head)
+  const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
+
+  const int T = request_len(p, b);
+  const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
+  int begin, end;
+  split_range(vis.n_vis, s, p.chunk, &begin, &end);
+  const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
+  if (begin >= end) {
+    write_identity<G, D, NWAVES>(p, st0);
+    return;
+  }
+
+  // B operand: q[head n][32c + 8kg .. +7], zero for columns n >= G.
+  uint4 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qop[c] = make_uint4(0u, 0u, 0u, 0u);
+    if (n < G)
+      qop[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
+                                               ((int64_t)b * p.num_q_heads + h * G + n) * D + 32 * c + 8 * kg);
+  }
+
+  // Row r of the tile is ordinal tile + r; rows past the split end are
+  // clamped to its last row, which is visible and finite, and then get weight
+  // 0 (score -inf), so the loads need no branches.
+  const int64_t hb = head_base_offset<PAGED>(p, b, h, D);
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k) + hb + 8 * kg;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v) + hb + 8 * n;
+  const uint32_t row_stride = (uint32_t)(p.num_kv_heads * D);
+  // Lane l resolves the row index of tile row l%16 (one page-table lookup
+  // per row); the V rows 4kg+j take theirs from lane 4kg+j.
+  auto row_index = [&](int tile) {
+    return kv_row_index<PAGED>(p, b, vis_pos(vis, min(tile + n, end - 1)));
+  };
+  auto issue_k = [&](uint32_t ri, uint4 (&k)[4]) {
+    const uint16_t* row = kb + (uint64_t)ri * row_stride;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
+  };
+  auto issue_v = [&](uint32_t ri, uint4 (&v)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t rj = (uint32_t)__shfl((int)ri, 4 * kg + j);
+      v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)rj * row_stride));
+    }
+  };
+
+  float m_run = -INFINITY;   // running max of head n (base 2), equal in the 4 lanes of the head
+  float l_run = 0.f;         // partial denominator over rows 4kg .. 4kg+3 of every tile
+  float u[G][8];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[i][e] = 0.f;
+
+  // One tile of registers: the next tile's K rows are requested as soon as
+  // the score instructions have read the current ones, its V rows as soon as
+  // PV has read the current ones.  The requests after the last tile repeat
+  // row end-1 (already cached) and keep the loop free of branches.
+  MfmaTile t;
+  int tile = begin + wave * TW;
+  uint32_t ri = 0;
+  if (tile < end) {
+    ri = row_index(tile);
+    issue_k(ri, t.k);
+    issue_v(ri, t.v);
+  }
+  for (; tile < end; tile += NWAVES * TW) {
+    const int next_tile = tile + NWAVES * TW;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[c]),
+                                                    __builtin_bit_cast(bf16x8_t, qop[c]), acc, 0, 0, 0);
+    ri = row_index(next_tile);
+    issue_k(ri, t.k);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < end) ? acc[i] * p.qscale : -INFINITY;
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m_run, mt);
+    const float mz = mn == -INFINITY ? 0.f : mn;     // no -inf - -inf
+    const float alpha = fast_exp2(m_run - mz);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - mz);
+    l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = mn;
+
+    HeadLoop<G>::rescale(u, alpha);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w[4] = {t.v[j].x, t.v[j].y, t.v[j].z, t.v[j].w};
+      float vx[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { vx[2 * e] = bf16_lo(w[e]); vx[2 * e + 1] = bf16_hi(w[e]); }
+      HeadLoop<G>::accumulate(u, pr[j], vx);
+    }
+    issue_v(ri, t.v);
+  }
+
+  // ---- wave state: all rows of a head share m, so l and u just add ---------
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u[i][e] += __shfl_xor(u[i][e], 16);
+      u[i][e] += __shfl_xor(u[i][e], 32);
+    }
+
+  __shared__ WaveStates<G, D, NWAVES> sh;
+  if (kg == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh.u[wave][i][8 * n + e] = u[i][e];
+    if (n < G) {
+      sh.m[wave][n] = m_run;
+      sh.l[wave][n] = l_run;
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<G, D, NWAVES>(p, st0, sh);
+}
+
+}  // namespace da

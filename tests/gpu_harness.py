@@ -1,0 +1,127 @@
+"""Moves synthetic workloads to the GPU and calls the library through the C
+ABI (kv_cache_amd binding).  Torch provides device memory and the stream."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import kv_cache_amd as ka
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def to_dev(arr: np.ndarray):
+    t = torch()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16 or a.dtype == np.float16:
+        a = a.view(np.int16)
+    return t.from_numpy(a).to("cuda")
+
+
+def announce(*what):
+    print("[gpu-case]", *what, file=sys.stderr, flush=True)
+
+
+class DeviceWorkload:
+    """Device copies of a synth.Workload's buffers."""
+
+    def __init__(self, w):
+        self.w = w
+        self.dev = {k: to_dev(v) for k, v in w.buffers.items()}
+
+    def args(self, ws, ws_bytes):
+        d = self.dev
+        return ka.make_args(d["q"], d["k"], d["v"], d["seq_lens"], ws, ws_bytes,
+                            k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
+                            k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
+                            block_table=d.get("block_table"))
+
+
+def plan_for(w, num_splits=None):
+    p = w.problem
+    if num_splits is not None:
+        p.num_splits = num_splits
+    _, plan, ws, _ = ka.decode_attn_plan(ka.problem_from(p))
+    return plan, ws
+
+
+def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None):
+    """Plan, run, combine.  Returns (O, LSE, plan[, workspace numpy])."""
+    t = torch()
+    dw = dw or DeviceWorkload(w)
+    plan, ws_bytes = plan_for(w, num_splits)
+    ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+    if poison_ws:
+        ws.fill_(0xFF)                  # NaN everywhere: unwritten slots would show
+    B, Hq, D = w.problem.batch, w.problem.num_q_heads, w.problem.head_dim
+    out = t.full((B, Hq, D), float("nan"), dtype=t.float32, device="cuda")
+    lse = t.full((B, Hq), float("nan"), dtype=t.float32, device="cuda")
+    s = stream if stream is not None else t.cuda.current_stream().cuda_stream
+    ka.decode_attn_run(plan, dw.args(ws, ws_bytes), s)
+    ka.decode_attn_combine(plan, ws, ws_bytes, out, lse, s)
+    t.cuda.synchronize()
+    res = (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), plan)
+    if want_ws:
+        res = res + (ws.cpu().numpy(),)
+    return res
+
+
+def split_workspace(ws_bytes: np.ndarray, plan):
+    p = plan.problem
+    n = p.batch * p.num_q_heads * plan.num_splits
+    f = ws_bytes[: n * (p.head_dim_v + 2) * 4].view(np.float32)
+    u = f[: n * p.head_dim_v].reshape(p.batch, p.num_q_heads, plan.num_splits, p.head_dim_v)
+    m = f[n * p.head_dim_v: n * p.head_dim_v + n].reshape(p.batch, p.num_q_heads, plan.num_splits)
+    l = f[n * p.head_dim_v + n:].reshape(p.batch, p.num_q_heads, plan.num_splits)
+    return u, m, l
+
+
+def trace(w, num_splits=None, dw=None):
+    t = torch()
+    dw = dw or DeviceWorkload(w)
+    plan, ws_bytes = plan_for(w, num_splits)
+    ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+    p = w.problem
+    n = p.batch * p.num_kv_heads * plan.num_splits * plan.chunk
+    offs = t.full((max(n, 1),), -1, dtype=t.int64, device="cuda")
+    pos = t.full((max(n, 1),), -1, dtype=t.int32, device="cuda")
+    ka.decode_attn_trace_indices(plan, dw.args(ws, ws_bytes), offs, pos,
+                                 t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    shape = (p.batch, p.num_kv_heads, plan.num_splits, plan.chunk)
+    return offs.cpu().numpy()[:n].reshape(shape), pos.cpu().numpy()[:n].reshape(shape), plan
+
+
+def max_abs(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def check_rows(O, L, Or, Lr, atol, rtol=0.0, rows=None):
+    """Field-aware comparison ("M4.5 ...", section 0x07G): same finite/all-
+    masked policy, max|O - O_ref| <= atol + rtol * max|O_ref|, LSE exact for
+    -inf and within tolerance otherwise."""
+    if rows is not None:
+        O = np.stack([O[b, h] for b, h in rows])
+        Or = np.stack([Or[b, h] for b, h in rows])
+        L = np.array([L[b, h] for b, h in rows])
+        Lr = np.array([Lr[b, h] for b, h in rows])
+    assert O.shape == Or.shape
+    masked = np.isneginf(Lr)
+    assert np.array_equal(np.isneginf(L), masked), "all-masked policy differs"
+    if masked.any():
+        assert np.all(O[masked] == 0) and not np.signbit(O[masked]).any()
+    assert np.all(np.isfinite(O)), "non-finite output"
+    bound = atol + rtol * float(np.max(np.abs(Or))) if Or.size else atol
+    err = max_abs(O, Or)
+    assert err <= bound, f"max|dO| = {err:.3e} > {bound:.3e}"
+    fin = ~masked
+    if fin.any():
+        lerr = float(np.max(np.abs(L[fin] - Lr[fin])))
+        assert lerr <= max(atol, 1e-6 * float(np.max(np.abs(Lr[fin])))), f"max|dLSE| = {lerr:.3e}"
+    return err

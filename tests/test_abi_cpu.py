@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+the header declares, and the planner validates, admits and sizes calls
+(no GPU needed: problems carry an explicit CU count)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import kv_cache_amd as ka
+import synth
+from tests.conftest import ROOT
+
+
+def header_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+char\s*\*|da_status)\s+(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ka.lib()
+    names = header_functions()
+    assert set(names) >= {"decode_attn_plan", "decode_attn_run", "decode_attn_combine",
+                          "decode_attn_trace_indices", "decode_attn_reason",
+                          "decode_attn_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(ka.Problem) == 22 * 4
+    assert ctypes.sizeof(ka.Plan) == 8 + 88 + 16 + 8 + 16
+    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8
+
+
+def P(**kw):
+    base = dict(batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                kv_format="bf16", layout="contig", kv_capacity=4096, max_seq_len=4096)
+    base.update(kw)
+    return synth.Problem(**base)
+
+
+def plan(p, cus=256):
+    return ka.decode_attn_plan(ka.problem_from(p, num_cus=cus), check=False)
+
+
+def test_workspace_and_auto_splits_llama_shape():
+    st, pl, ws, rs = plan(P())
+    assert st == ka.DA_OK and rs == 0
+    S = pl.num_splits
+    assert ws == 8 * 32 * S * (128 + 2) * 4 == pl.workspace_bytes
+    assert pl.chunk % 16 == 0 and S * pl.chunk >= 4096 and (S - 1) * pl.chunk < 4096
+    assert 8 * 8 * S >= 256          # at least one workgroup per CU
+    assert abs(pl.problem.softmax_scale - 1 / math.sqrt(128)) < 1e-8
+
+
+@pytest.mark.parametrize("S", [1, 8, 32, 128])
+def test_explicit_split_counts_long_context(S):
+    st, pl, ws, _ = plan(P(batch=1, kv_capacity=131072, max_seq_len=131072, num_splits=S))
+    assert st == ka.DA_OK
+    assert pl.num_splits == S and pl.chunk == 131072 // S
+
+
+def test_uneven_splits_have_partial_tail():
+    st, pl, _, _ = plan(P(batch=1, kv_capacity=131072, max_seq_len=131071, num_splits=128))
+    assert st == ka.DA_OK and pl.num_splits == 128
+    assert pl.chunk * 127 < 131071 < pl.chunk * 128
+
+
+def test_sink_window_bounds_visible_rows():
+    st, pl, _, _ = plan(P(batch=16, kv_format="i8", kv_capacity=16384, max_seq_len=16384,
+                          mask_kind="sink_window", n_sink=4, window=4096, k_group=128,
+                          residual_len=128))
+    assert st == ka.DA_OK
+    assert pl.max_visible == 4100
+    assert pl.num_splits * pl.chunk >= 4100
+
+
+def test_zero_length_plan():
+    st, pl, ws, _ = plan(P(batch=1, kv_capacity=1, max_seq_len=0))
+    assert st == ka.DA_OK and pl.num_splits == 1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(num_q_heads=30),                               # H_q % H_kv != 0
+    dict(num_kv_heads=0),
+    dict(batch=-1),
+    dict(layout="paged", page_size=0, num_pages=10, max_pages_per_seq=300, kv_capacity=0),
+    dict(page_size=16),                                 # page size on a contiguous layout
+    dict(mask_kind="sink_window", n_sink=4, window=0),  # W must be > 0
+    dict(mask_kind="sink_window", n_sink=-1, window=8),
+    dict(num_splits=-1),
+    dict(softmax_scale=-1.0),
+    dict(softmax_scale=float("nan")),
+    dict(kv_capacity=100),                              # capacity below max_seq_len
+    dict(layout="paged", page_size=16, num_pages=10, max_pages_per_seq=10, kv_capacity=0),
+    dict(kv_format="i8", k_group=0, residual_len=128),
+    dict(n_sink=3),                                     # sink count on a causal mask
+])
+def test_malformed_calls_are_invalid_not_unsupported(kw):
+    st, _, _, rs = plan(P(**kw))
+    assert st == ka.DA_ERR_INVALID and rs == 0
+
+
+def test_unsupported_reports_every_failed_predicate():
+    p = P(head_dim=96, num_q_heads=48, num_kv_heads=3, q_dtype="f32", num_splits=100000)
+    st, _, _, rs = plan(p)
+    assert st == ka.DA_ERR_UNSUPPORTED
+    want = (1 << 0) | (1 << 2) | (1 << 3) | (1 << 8)    # head dim, group 16, q dtype, splits
+    assert rs & want == want
+    names = ka.reason_names(rs)
+    assert any("head_dim_qk" in n for n in names)
+
+
+def test_unsupported_int8_paged_and_out_dtype():
+    p = P(kv_format="i8", layout="paged", page_size=16, num_pages=4096, max_pages_per_seq=256,
+          kv_capacity=0, k_group=100, residual_len=128)
+    pr = ka.problem_from(p, num_cus=256)
+    pr.out_dtype = 1
+    st, _, _, rs = ka.decode_attn_plan(pr, check=False)
+    assert st == ka.DA_ERR_UNSUPPORTED
+    assert rs & (1 << 6) and rs & (1 << 7) and rs & (1 << 4)
+
+
+def test_plan_mismatch_detected_without_gpu():
+    st, pl, ws, _ = plan(P())
+    assert st == ka.DA_OK
+    pl.num_splits += 1                      # caller edits a frozen field
+    args = ka.Args()
+    assert ka.decode_attn_run(pl, args, check=False) == ka.DA_ERR_PLAN_MISMATCH
+    assert ka.decode_attn_combine(pl, 16, ws, 16, check=False) == ka.DA_ERR_PLAN_MISMATCH
+
+
+def test_run_rejects_null_pointers_and_small_workspace_without_gpu():
+    st, pl, ws, _ = plan(P())
+    args = ka.Args()
+    assert ka.decode_attn_run(pl, args, check=False) == ka.DA_ERR_INVALID
+    args = ka.make_args(16, 16, 16, 16, 256, ws - 4)
+    assert ka.decode_attn_run(pl, args, check=False) == ka.DA_ERR_WORKSPACE
+    args = ka.make_args(8, 16, 16, 16, 256, ws)          # misaligned q
+    assert ka.decode_attn_run(pl, args, check=False) == ka.DA_ERR_INVALID
+    assert ka.decode_attn_combine(pl, 256, ws - 1, 16, check=False) == ka.DA_ERR_WORKSPACE
+
+
+def test_reason_and_status_text():
+    for i in range(ka.NUM_REASONS):
+        assert ka.decode_attn_reason(i)
+    assert ka.decode_attn_reason(99) == "unknown reason bit"
+    assert ka.decode_attn_status_string(0) == "ok"

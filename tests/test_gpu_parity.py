@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: max-abs 1e-5 for fp32 inputs, 2e-3 for bf16 inputs (fp32
+accumulation), 1e-2 relative (max|dO| <= 1e-2 max|O_ref|) for int8 K/V against
+the decoded-input oracle.  Indices are compared exactly."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    H.announce(request.node.nodeid)
+
+
+# ---------------------------------------------------------------- config 1
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cfg1_tiny_fp32(seed):
+    w = synth.config(1, seed)
+    O, L, plan = H.run(w)
+    assert plan.num_splits == 4
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    H.check_rows(O, L, Or, Lr, TOL["f32"])
+
+
+# ---------------------------------------------------------------- config 2
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cfg2_llama_shape_auto_splits(seed):
+    w = synth.config(2, seed)
+    O, L, plan = H.run(w)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+def test_cfg2_split_sweep_and_repeatability():
+    w = synth.config(2, 0)
+    dw = H.DeviceWorkload(w)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    for S in (1, 2, 3, 5, 8, 16, 32, 64):
+        O, L, plan = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, TOL["bf16"])
+    O1, L1, _ = H.run(w, num_splits=16, dw=dw)
+    O2, L2, _ = H.run(w, num_splits=16, dw=dw)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)     # fixed plan: bitwise repeatable
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 4, 4), (128, 8, 4), (128, 32, 8), (64, 16, 2), (128, 8, 1)])
+def test_small_contiguous_ragged(dtype, D, Hq, Hkv):
+    lens = [1, 17, 250, 0, 1000, 63]
+    w = synth.make_contiguous(3, len(lens), Hq, Hkv, D, lens, dtype=dtype, kv_capacity=1030)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (0, 1, 7, 16):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, TOL[dtype])
+
+
+def test_peaky_scores_stress():
+    """q scaled by sqrt(d): score std ~ 11, exercising the online rescale."""
+    w = synth.make_contiguous(4, 4, 32, 8, 128, [4096, 3000, 17, 2049], q_scale=math.sqrt(128))
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    for S in (1, 16):
+        O, L, _ = H.run(w, num_splits=S)
+        H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+def test_workspace_states_match_oracle_split_reference():
+    """Each written (m, l, u) equals the oracle summary of the same split
+    (chunk policy over the visible rows), or the identity when empty."""
+    lens = [300, 40, 0]
+    w = synth.make_contiguous(5, 3, 8, 2, 128, lens, kv_capacity=300)
+    O, L, plan, wsb = H.run(w, num_splits=4, want_ws=True)
+    u, m, l = H.split_workspace(wsb, plan)
+    S, C = plan.num_splits, plan.chunk
+    for b, T in enumerate(lens):
+        n = T
+        bounds = [(min(s * C, n), min((s + 1) * C, n)) for s in range(S)]
+        for hq in range(8):
+            states, _, _ = oracle.split_attend(w.problem, w.buffers, b, hq, bounds)
+            for s, st in enumerate(states):
+                if not st.valid:
+                    assert m[b, hq, s] == -np.inf and l[b, hq, s] == 0 and not u[b, hq, s].any()
+                else:
+                    assert abs(m[b, hq, s] - st.m) <= 2e-5 * max(1, abs(st.m))
+                    scale = math.exp(st.m - m[b, hq, s])   # GPU frame differs from the oracle's by rounding of m
+                    assert abs(l[b, hq, s] - st.l * scale) <= 1e-4 * st.l
+                    assert H.max_abs(u[b, hq, s], st.u * scale) <= 2e-3 * max(1.0, np.abs(st.u).max())
+
+
+# ---------------------------------------------------------------- config 4
+@pytest.fixture(scope="module")
+def cfg4():
+    w = synth.config(4, 0)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    return w, H.DeviceWorkload(w), Or, Lr
+
+
+@pytest.mark.parametrize("S", [1, 8, 32, 128, 0])
+def test_cfg4_long_context_split_sweep(cfg4, S):
+    w, dw, Or, Lr = cfg4
+    O, L, plan = H.run(w, num_splits=S, dw=dw)
+    if S:
+        assert plan.num_splits == S
+    H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+def test_cfg4_uneven_and_empty_variants():
+    # T = 131071 (every S > 1 has a partial split), then [131071, 0] in one batch
+    w = synth.config(4, 1, T=131071)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (8, 128, 0):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, TOL["bf16"])
+    w2 = synth.config(4, 1, seq_lens=[131071, 0])
+    O2, L2, _ = H.run(w2, num_splits=32)
+    Or2, Lr2 = oracle.attend(w2.problem, w2.buffers)
+    H.check_rows(O2, L2, Or2, Lr2, TOL["bf16"])
+    assert np.all(O2[1] == 0) and np.all(np.isneginf(L2[1]))
+    # the non-empty row is unchanged by the empty neighbour (same data, same plan width)
+    w3 = synth.make_contiguous(9, 1, 32, 8, 128, [0], kv_capacity=16)
+    O3, L3, _ = H.run(w3, num_splits=4)
+    assert np.all(O3 == 0) and not np.signbit(O3).any() and np.all(np.isneginf(L3))
+
+
+# ---------------------------------------------------------------- config 3
+def test_paged_small_ragged_with_poison():
+    lens = [1, 15, 16, 17, 300, 0, 2000, 33]
+    w = synth.make_paged(6, len(lens), 32, 8, 128, lens, page_size=16, max_pages_per_seq=130)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (0, 1, 5, 64):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+@pytest.mark.parametrize("P", [1, 3, 8, 32])
+def test_paged_other_page_sizes(P):
+    lens = [40, 7, 100]
+    w = synth.make_paged(7, 3, 8, 2, 64, lens, page_size=P, max_pages_per_seq=100 // P + 2)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.run(w, num_splits=3)
+    H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+def test_cfg3_full_sampled_rows():
+    w = synth.config(3, 0)
+    O, L, plan = H.run(w)
+    g = synth.rng(77)
+    rows = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 24), g.integers(0, 32, 24))]
+    rows += [(int(np.argmax(w.buffers["seq_lens"])), 0), (int(np.argmin(w.buffers["seq_lens"])), 31)]
+    Or, Lr = oracle.attend(w.problem, w.buffers, heads=rows)
+    H.check_rows(O, L, Or, Lr, TOL["bf16"], rows=rows)
+    assert np.all(np.isfinite(O))      # poisoned tails and spare pages never reached
+
+
+# ---------------------------------------------------------------- masks
+MASK_CASES = [
+    # (lens, n_sink, window): window >= T, sinks overlapping the window, S > T
+    ([5, 40, 300, 1, 0], 4, 16),
+    ([100, 33], 0, 200),
+    ([64, 65, 200], 70, 10),
+    ([16384], 4, 4096),
+]
+
+
+@pytest.mark.parametrize("lens,ns,W", MASK_CASES)
+def test_sink_window_contiguous(lens, ns, W):
+    w = synth.make_contiguous(8, len(lens), 16, 4, 128, lens, mask_kind="sink_window",
+                              n_sink=ns, window=W, kv_capacity=max(lens) + 5)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (0, 1, 3, 64):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+def test_sink_window_paged():
+    lens = [1000, 3, 77]
+    w = synth.make_paged(9, 3, 8, 8, 64, lens, page_size=16, mask_kind="sink_window", n_sink=2,
+                         window=50, max_pages_per_seq=64)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.run(w, num_splits=4)
+    H.check_rows(O, L, Or, Lr, TOL["bf16"])
+
+
+# ---------------------------------------------------------------- int8 (config 5)
+def test_int8_small_with_residual_and_mask():
+    w = synth.make_int8(10, 3, 16, 4, 128, [1000, 100, 250], mask_kind="sink_window",
+                        n_sink=4, window=300, kv_capacity=1000)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (0, 1, 4):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+
+
+def test_int8_causal_small():
+    w = synth.make_int8(11, 2, 8, 2, 64, [700, 50], k_group=64, residual_len=32, kv_capacity=700)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.run(w, num_splits=3)
+    H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_cfg5_full(seed):
+    w = synth.config(5, seed)
+    O, L, plan = H.run(w)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    err = H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+    H.announce(f"cfg5 seed {seed}: max|dO| = {err:.3e}, S = {plan.num_splits}")
+
+
+# ---------------------------------------------------------------- exact indices
+def _trace_rows(w, S):
+    offs, pos, plan = H.trace(w, num_splits=S)
+    _, _, tr = oracle.attend(w.problem, w.buffers, with_trace=True)
+    for (b, h), (p_ref, o_ref, _) in tr.items():
+        got_p = pos[b, h].reshape(-1)
+        got_o = offs[b, h].reshape(-1)
+        sel = got_p >= 0
+        gp, go = got_p[sel], got_o[sel]
+        order = np.argsort(gp, kind="stable")
+        assert np.array_equal(gp[order], p_ref), (b, h)          # no missing / extra / duplicate
+        assert np.array_equal(go[order], o_ref), (b, h)
+        assert np.all(got_o[~sel] == -1)
+
+
+def test_trace_indices_contiguous_and_mask():
+    _trace_rows(synth.make_contiguous(12, 3, 8, 4, 128, [500, 0, 77], mask_kind="sink_window",
+                                      n_sink=3, window=64, kv_capacity=500), 5)
+    _trace_rows(synth.make_contiguous(13, 2, 4, 4, 64, [33, 257], dtype="f32", kv_capacity=260), 3)
+
+
+def test_trace_indices_paged_cfg3_shape():
+    lens = [1, 16, 17, 4099, 0, 250]
+    _trace_rows(synth.make_paged(14, len(lens), 32, 8, 128, lens, page_size=16,
+                                 max_pages_per_seq=260), 8)
+
+
+def test_trace_indices_int8():
+    _trace_rows(synth.make_int8(15, 2, 16, 4, 128, [1000, 60], mask_kind="sink_window", n_sink=4,
+                                window=300, kv_capacity=1000), 4)
+
+
+def test_trace_indices_cfg5_full_sampled():
+    w = synth.config(5, 0)
+    offs, pos, plan = H.trace(w)
+    _, _, tr = oracle.attend(w.problem, w.buffers, heads=[(0, 0), (7, 13), (15, 31)], with_trace=True)
+    for (b, h), (p_ref, o_ref, _) in tr.items():
+        gp, go = pos[b, h].reshape(-1), offs[b, h].reshape(-1)
+        sel = gp >= 0
+        order = np.argsort(gp[sel], kind="stable")
+        assert np.array_equal(gp[sel][order], p_ref)
+        assert np.array_equal(go[sel][order], o_ref)
+        assert len(p_ref) == 4100
