@@ -4,7 +4,7 @@
 One step = one decode-attention call of the hot path: decode_attn_run (the
 split kernel: bounds, mask program, address translation, K/V streaming,
 scores, online softmax, PV, state write) followed by decode_attn_combine (the
-log-sum-exp reduction), on the workload
+log-sum-exp reduction).  The headline workload is
 
     B=8, S_q=1, H_q=32, H_kv=8 (4 query heads per K/V head), d_h=128,
     S_k=4096 for every sequence, bf16 q/k/v ~ N(0,1), contiguous
@@ -12,11 +12,13 @@ log-sum-exp reduction), on the workload
 
 Inputs are resident in HBM before timing.  Several disjoint input sets
 (> 512 MiB in total) are rotated so the 256 MB last-level cache cannot serve
-repeated K/V.  The printed JSON line reports algorithmic GB/s per call as
-`value`, the per-call time, the split kernel's roofline against the 8 TB/s
-HBM peak (its duration measured with HIP events on the launch stream), HBM
-traffic from the committed profiler counters when they were taken on the
-current kernel sources, and the CPU oracle's throughput on the same workload.
+repeated K/V.  The JSON line reports algorithmic GB/s per call as `value`,
+the per-call time, the split kernel's roofline against the 8 TB/s HBM peak
+(its duration measured with HIP events on the launch stream), HBM traffic
+from the committed profiler counters when they were taken on the current
+kernel sources, the other decode workloads (128k context, paged ragged batch,
+int8 cache with sink+window mask, tiny fp32), and the CPU oracle's
+throughput on the headline workload.
 """
 from __future__ import annotations
 
@@ -31,8 +33,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
-WORKLOAD = dict(batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_len=4096)
-LONG = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_len=131072)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_llama3_8b_layer_traffic.json")
 KERNEL_SOURCES = ["kv_cache_amd/csrc/split_kernel_mfma.hpp", "kv_cache_amd/csrc/split_common.hpp",
                   "kv_cache_amd/csrc/device_common.hpp", "kv_cache_amd/csrc/decode_attn.hip"]
@@ -46,47 +46,109 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, Hq, Hkv, D, T, S):
-    kv = 2 * B * T * Hkv * D * 2                      # visible K and V rows, once per K/V head
-    q = B * Hq * D * 2
-    ws = B * Hq * S * (D + 2) * 4                      # (m, l, u) states
-    out = B * Hq * D * 4 + B * Hq * 4                  # O and LSE
-    meta = B * 4                                       # seq_lens
-    split = kv + q + ws + meta                         # split kernel: reads K/V/q, writes states
-    combine = ws + out                                 # combine kernel: reads states, writes O, LSE
-    return kv, split, split + combine
+def visible(T, mask):
+    """Visible positions of a request of length T (plain set arithmetic)."""
+    if mask is None:
+        return range(T)
+    ns, W = mask
+    return sorted(set(range(min(ns, T))) | set(range(max(0, T - W), T)))
 
 
-class Case:
-    """Device buffers and a plan for one contiguous bf16 decode shape."""
+class GpuWorkload:
+    """Device buffers, a plan and the algorithmic byte count of one workload.
 
-    def __init__(self, torch, ka, shape, num_splits, min_bytes, seed):
-        self.torch, self.ka = torch, ka
-        B, Hq, Hkv, D, T = (shape[k] for k in ("batch", "num_q_heads", "num_kv_heads", "head_dim",
-                                                "seq_len"))
-        self.shape = (B, Hq, Hkv, D, T)
+    kinds: "contig" (bf16 or fp32), "paged" (bf16, P=16, ragged), "i8"
+    (int8 codes + fp16 scales + bf16 residual, sink+window mask)."""
+
+    def __init__(self, torch, ka, kind, B, Hq, Hkv, D, lens, num_splits=0, min_bytes=0, seed=0,
+                 dtype="bf16", mask=None, page_size=16, k_group=128, residual=128):
+        import numpy as np
         import synth
-        prob = synth.Problem(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype="bf16",
-                             kv_format="bf16", layout="contig", kv_capacity=T, max_seq_len=T,
-                             num_splits=num_splits)
-        _, self.plan, self.ws_bytes, _ = ka.decode_attn_plan(ka.problem_from(prob))
-        per_set = 2 * B * T * Hkv * D * 2
-        self.nsets = max(2, -(-min_bytes // per_set))
+        self.torch, self.ka, self.kind = torch, ka, kind
+        self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
+        self.lens = [int(t) for t in lens]
+        T = max(self.lens)
         g = torch.Generator(device="cuda")
         g.manual_seed(seed)
+        eb = 4 if dtype == "f32" else 2
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        mk = dict(mask_kind="sink_window", n_sink=mask[0], window=mask[1]) if mask else {}
+        if kind == "contig":
+            prob = synth.Problem(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=dtype,
+                                 kv_format=dtype, kv_capacity=T, max_seq_len=T, num_splits=num_splits, **mk)
+            per_set = 2 * B * T * Hkv * D * eb
+        elif kind == "paged":
+            pages = [(t + page_size - 1) // page_size for t in self.lens]
+            n_pages = int(sum(pages) * 1.1) + 1
+            maxp = max(pages)
+            prob = synth.Problem(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, layout="paged",
+                                 page_size=page_size, max_pages_per_seq=maxp, num_pages=n_pages,
+                                 max_seq_len=T, num_splits=num_splits, **mk)
+            per_set = 2 * n_pages * page_size * Hkv * D * 2
+        elif kind == "i8":
+            prob = synth.Problem(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_format="i8",
+                                 kv_capacity=T, max_seq_len=T, num_splits=num_splits, k_group=k_group,
+                                 residual_len=residual, **mk)
+            per_set = 2 * B * T * Hkv * D
+        else:
+            raise ValueError(kind)
+        _, self.plan, self.ws_bytes, _ = ka.decode_attn_plan(ka.problem_from(prob))
+        self.S = self.plan.num_splits
+        self.nsets = max(1, -(-min_bytes // per_set)) if min_bytes else 1
+        self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
         self.sets = []
         for _ in range(self.nsets):
-            k = torch.randn((B, T, Hkv, D), device="cuda", dtype=torch.bfloat16, generator=g)
-            v = torch.randn((B, T, Hkv, D), device="cuda", dtype=torch.bfloat16, generator=g)
-            q = torch.randn((B, Hq, D), device="cuda", dtype=torch.bfloat16, generator=g)
-            self.sets.append((q, k, v))
-        self.seq_lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+            d = {"q": torch.randn((B, Hq, D), device="cuda", dtype=tdt, generator=g)}
+            if kind == "contig":
+                d["k"] = torch.randn((B, T, Hkv, D), device="cuda", dtype=tdt, generator=g)
+                d["v"] = torch.randn((B, T, Hkv, D), device="cuda", dtype=tdt, generator=g)
+            elif kind == "paged":
+                d["k"] = torch.randn((n_pages, page_size, Hkv, D), device="cuda", dtype=tdt, generator=g)
+                d["v"] = torch.randn((n_pages, page_size, Hkv, D), device="cuda", dtype=tdt, generator=g)
+                perm = torch.randperm(n_pages, device="cuda", generator=g).to(torch.int32)
+                table = torch.full((B, maxp), -1, dtype=torch.int32, device="cuda")
+                cur = 0
+                for b, n in enumerate(pages):
+                    table[b, :n] = perm[cur:cur + n]
+                    cur += n
+                d["block_table"] = table
+            else:
+                n_groups = (T + k_group - 1) // k_group
+                d["k"] = torch.randint(-127, 128, (B, T, Hkv, D), device="cuda", dtype=torch.int8, generator=g)
+                d["v"] = torch.randint(-127, 128, (B, T, Hkv, D), device="cuda", dtype=torch.int8, generator=g)
+                d["k_scale"] = (torch.rand((B, n_groups, Hkv, D), device="cuda", generator=g) * 0.04 + 0.005).half()
+                d["v_scale"] = (torch.rand((B, T, Hkv), device="cuda", generator=g) * 0.04 + 0.005).half()
+                d["k_resid"] = torch.randn((B, residual, Hkv, D), device="cuda", dtype=tdt, generator=g)
+                d["v_resid"] = torch.randn((B, residual, Hkv, D), device="cuda", dtype=tdt, generator=g)
+            self.sets.append(d)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-        self.args = [ka.make_args(q, k, v, self.seq_lens, self.ws, self.ws_bytes)
-                     for (q, k, v) in self.sets]
+        self.args = [ka.make_args(d["q"], d["k"], d["v"], self.seq_lens, self.ws, self.ws_bytes,
+                                  k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
+                                  k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
+                                  block_table=d.get("block_table")) for d in self.sets]
         self.stream = torch.cuda.current_stream().cuda_stream
+        # ---- algorithmic bytes: what the method must move once ----
+        kvb = 0
+        meta = B * 4
+        for t in self.lens:
+            vis = visible(t, mask)
+            if kind == "i8":
+                n_q = t - min(t, residual)
+                quant = [p for p in vis if p < n_q]
+                kvb += Hkv * (len(quant) * (2 * D + 2) + (len(vis) - len(quant)) * 2 * D * 2
+                              + len({p // k_group for p in quant}) * D * 2)
+            else:
+                kvb += Hkv * len(vis) * 2 * D * eb
+            if kind == "paged":
+                meta += ((t + page_size - 1) // page_size) * 4
+        q = B * Hq * D * eb
+        ws = B * Hq * self.S * (D + 2) * 4
+        out = B * Hq * (D + 1) * 4
+        self.kv_bytes = kvb
+        self.split_bytes = kvb + q + ws + meta
+        self.call_bytes = self.split_bytes + ws + out
 
     def run(self, i):
         self.ka.decode_attn_run(self.plan, self.args[i % self.nsets], self.stream)
@@ -110,7 +172,7 @@ class Case:
         return e0.elapsed_time(e1) / steps      # ms per launch sequence
 
     def samples(self, fn, n, warmup):
-        """Per-call event pairs (each call's own interval) for the sample log."""
+        """Per-call event pairs for the sample statistics."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
@@ -122,14 +184,52 @@ class Case:
             fn(warmup + i)
             b.record()
         torch.cuda.synchronize()
-        return [a.elapsed_time(b) * 1000.0 for a, b in evs]
+        return sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+
+    def graph_time(self, calls_per_graph=20, replays=10):
+        """Declared hipGraph replay of `calls_per_graph` run+combine pairs
+        (rotating input sets): the GPU-side time per call without host
+        launch costs."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            st = torch.cuda.current_stream().cuda_stream
+            for i in range(3):
+                self.ka.decode_attn_run(self.plan, self.args[i % self.nsets], st)
+                self.ka.decode_attn_combine(self.plan, self.ws, self.ws_bytes, self.out, self.lse, st)
+            side.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                st = torch.cuda.current_stream().cuda_stream
+                for i in range(calls_per_graph):
+                    self.ka.decode_attn_run(self.plan, self.args[i % self.nsets], st)
+                    self.ka.decode_attn_combine(self.plan, self.ws, self.ws_bytes, self.out, self.lse, st)
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (replays * calls_per_graph)
+
+    def report(self, name, config, steps=30, warmup=5):
+        ms = self.time(self.call, steps, warmup)
+        gbs = self.call_bytes / (ms * 1e-3) / 1e9
+        return {"config": config, "num_splits": self.S, "us_per_call": round(ms * 1000, 2),
+                "GBs": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
+                "algorithmic_bytes": self.call_bytes}
 
 
 def hbm_probe(torch, nbytes=512 << 20):
-    """Practical read ceiling of the box: a plain streaming-read kernel."""
+    """Practical read ceiling of the box: a plain streaming-read kernel; then
+    one copy of known size, the reference for the profiler's byte counters."""
     import ctypes
-    path = os.path.join(ROOT, "kv_cache_amd", "libhbm_probe.so")
-    L = ctypes.CDLL(path)
+    L = ctypes.CDLL(os.path.join(ROOT, "kv_cache_amd", "libhbm_probe.so"))
     L.hbm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_void_p]
     L.hbm_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
@@ -148,21 +248,18 @@ def hbm_probe(torch, nbytes=512 << 20):
     e1.record()
     torch.cuda.synchronize()
     read_gbs = nbytes / (e0.elapsed_time(e1) / n * 1e-3) / 1e9
-    # one copy of known size: the reference for the profiler's byte counters
     L.hbm_probe_copy(bufs[0].data_ptr(), bufs[1].data_ptr(), 256 << 20, 2048, st)
     torch.cuda.synchronize()
     del bufs
     return read_gbs
 
 
-def cpu_baseline(seconds: float = 10.0):
-    """The fp64 NumPy oracle on the same workload shape and seeded data,
-    repeated until about `seconds` of wall clock have passed."""
-    import numpy as np  # noqa: F401
+def cpu_baseline(call_bytes, seconds: float = 10.0):
+    """The fp64 NumPy oracle on the headline workload shape (seeded synth
+    data), repeated until about `seconds` of wall clock have passed."""
     import oracle
     import synth
-    w = synth.make_contiguous(0, WORKLOAD["batch"], WORKLOAD["num_q_heads"], WORKLOAD["num_kv_heads"],
-                              WORKLOAD["head_dim"], [WORKLOAD["seq_len"]] * WORKLOAD["batch"])
+    w = synth.make_contiguous(0, 8, 32, 8, 128, [4096] * 8)
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -171,17 +268,16 @@ def cpu_baseline(seconds: float = 10.0):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    B, Hq, Hkv, D, T = (WORKLOAD[k] for k in ("batch", "num_q_heads", "num_kv_heads", "head_dim", "seq_len"))
-    _, _, alg = algorithmic_bytes(B, Hq, Hkv, D, T, 1)
     threads = 1
     try:
         import threadpoolctl
         threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     except Exception:
         pass
-    return {"value": round(alg * calls / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+    return {"value": round(call_bytes * calls / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "s_per_call": round(dt / calls, 4),
-            "sample": f"{calls} full calls of the workload (fp64 NumPy oracle, seed 0), {dt:.1f} s wall"}
+            "sample": f"{calls} full calls of the headline workload (fp64 NumPy oracle, seed 0), "
+                      f"{dt:.1f} s wall"}
 
 
 def main():
@@ -191,7 +287,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-long", action="store_true", help="skip the 128k-context figure")
+    ap.add_argument("--no-long", action="store_true", help="skip the other workloads")
     ap.add_argument("--samples-out", default=None, help="write raw per-call samples (JSON)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,41 +302,24 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     ceiling = hbm_probe(torch)
-    case = Case(torch, ka, WORKLOAD, a.num_splits, 600 << 20, seed=0)
-    B, Hq, Hkv, D, T = case.shape
-    S = case.plan.num_splits
-    kv_bytes, split_bytes, call_bytes = algorithmic_bytes(B, Hq, Hkv, D, T, S)
-
+    w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, num_splits=a.num_splits,
+                    min_bytes=600 << 20, seed=0)
     torch.cuda.synchronize()
-    ms_call = case.time(case.call, a.steps, a.warmup)     # timed region: K steps
-    ms_split = case.time(case.run, a.steps, a.warmup)      # split kernel alone, same stream
-    samples = case.samples(case.call, 100, 10)
-    us_call = ms_call * 1000.0
-    value = call_bytes / (ms_call * 1e-3) / 1e9
-
-    achieved = split_bytes / (ms_split * 1e-3) / 1e9
+    ms_call = w.time(w.call, a.steps, a.warmup)        # timed region: K steps
+    ms_split = w.time(w.run, a.steps, a.warmup)         # split kernel alone, same stream
+    samples = w.samples(w.call, 100, 10)
+    ms_graph = w.graph_time()
+    value = w.call_bytes / (ms_call * 1e-3) / 1e9
+    achieved = w.split_bytes / (ms_split * 1e-3) / 1e9
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("num_splits") == S:
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("num_splits") == w.S:
             traffic = tr.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         traffic = None
 
-    extra = {}
-    if not a.no_long:
-        long_case = Case(torch, ka, LONG, 0, 600 << 20, seed=1)
-        ms_long = long_case.time(long_case.call, 30, 5)
-        _, _, long_bytes = algorithmic_bytes(*long_case.shape, long_case.plan.num_splits)
-        extra["long_context_128k"] = {
-            "config": "B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal",
-            "num_splits": long_case.plan.num_splits, "us_per_call": round(ms_long * 1000, 2),
-            "GBs": round(long_bytes / (ms_long * 1e-3) / 1e9, 1),
-            "pct_of_peak": round(100 * long_bytes / (ms_long * 1e-3) / 1e9 / PEAK_GBS, 1)}
-        del long_case
-
-    samples.sort()
     line = {
         "metric": "decode-attn us/call + achieved HBM GB/s (% of peak), GQA 32q/8kv d128",
         "value": round(value, 1),
@@ -249,7 +328,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_call, 5),
-        "us_per_call": round(us_call, 2),
+        "us_per_call": round(ms_call * 1000, 2),
         "pct_of_peak": round(100 * value / PEAK_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",
@@ -258,25 +337,48 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16, rotated input sets > 512 MiB)",
         "config": {"workload": "llama3-8b-layer decode: B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16 "
                                "contiguous causal, fp32 out",
-                   "num_splits": S, "chunk": case.plan.chunk, "input_sets": case.nsets},
+                   "num_splits": w.S, "chunk": w.plan.chunk, "input_sets": w.nsets,
+                   "algorithmic_bytes_per_call": w.call_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "split_kernel_mfma", "us_per_launch": round(ms_split * 1000, 2),
-                     "algorithmic_bytes_per_launch": split_bytes},
+                     "algorithmic_bytes_per_launch": w.split_bytes},
         "samples_us": {"count": len(samples), "min": round(samples[0], 2),
                        "median": round(samples[len(samples) // 2], 2),
                        "p95": round(samples[int(len(samples) * 0.95)], 2), "max": round(samples[-1], 2)},
+        "graph_replay_us_per_call": round(ms_graph * 1000, 2),
         "hbm_read_probe_GBs": round(ceiling, 1),
         "kernel_source_hash": kernel_source_hash(),
     }
-    line.update(extra)
     if a.samples_out:
         with open(a.samples_out, "w") as f:
             json.dump({"per_call_us": samples}, f)
-    del case
+    call_bytes = w.call_bytes
+    del w
+    if not a.no_long:
+        import synth
+        others = {}
+        wl = GpuWorkload(torch, ka, "contig", 1, 32, 8, 128, [131072], min_bytes=600 << 20, seed=1)
+        others["long_context_128k"] = wl.report(
+            "long", "B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal, auto splits")
+        del wl
+        lens = synth.ragged_lengths(0, 32).tolist()
+        wp = GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, lens, seed=2)
+        others["paged_ragged"] = wp.report(
+            "paged", "B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768] (seed 0), permuted pool")
+        del wp
+        wi = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
+                         mask=(4, 4096))
+        others["int8_sink_window"] = wi.report(
+            "int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, 4 sinks + window 4096")
+        del wi
+        wt = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
+        others["tiny_fp32"] = wt.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4")
+        del wt
+        line["other_workloads"] = others
     torch.cuda.synchronize()
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"] = cpu_baseline(call_bytes)
     print(json.dumps(line), flush=True)
 
 

@@ -13,7 +13,7 @@
 // state is valid.
 //
 // Work split: thread t owns column t % D of the split class t / D (mod NG =
-// threads / D).  The u values of the first 8 states of each class are
+// threads / D).  The u values of the first 16 states of each class are
 // requested before the weights are known, so the state loads and the weight
 // computation overlap; the NG partial sums are then added in fixed order.
 // Every reduction has a fixed shape, so the result is bitwise repeatable for a
@@ -25,7 +25,7 @@
 
 namespace da {
 
-constexpr int kCombineThreads = 512;
+constexpr int kCombineThreads = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ ws_u,
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   constexpr int NT = kCombineThreads;
   constexpr int NG = NT / D;
   constexpr int NW = NT / 64;
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;

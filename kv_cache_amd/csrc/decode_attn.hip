@@ -10,6 +10,7 @@
 #include "plan_internal.hpp"
 #include "split_kernel.hpp"
 #include "split_kernel_mfma.hpp"
+#include "split_kernel_mfma_i8.hpp"
 
 namespace {
 
@@ -24,7 +25,7 @@ namespace {
 #ifndef DA_UNROLL_I8
 #define DA_UNROLL_I8 2
 #endif
-// bf16 K/V with D = 128 take the matrix-core score kernel.
+// bf16 and int8 K/V with D = 128 take the matrix-core score kernels.
 #ifndef DA_MFMA_QK
 #define DA_MFMA_QK 1
 #endif
@@ -34,7 +35,7 @@ template <int FMT> struct Unroll { static constexpr int value = DA_UNROLL; };
 template <> struct Unroll<DA_KV_I8> { static constexpr int value = DA_UNROLL_I8; };
 
 template <int FMT, int D>
-constexpr bool use_mfma() { return DA_MFMA_QK && FMT == DA_KV_BF16 && D == 128; }
+constexpr bool use_mfma() { return DA_MFMA_QK && (FMT == DA_KV_BF16 || FMT == DA_KV_I8) && D == 128; }
 
 // Rows per wave tile of the kernel that serves (FMT, D); the trace walk uses
 // the same value.
@@ -108,7 +109,9 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
 
 template <int FMT, int D, int G, bool PAGED>
 void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
-  if constexpr (use_mfma<FMT, D>())
+  if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8)
+    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves>), dim3(grid), dim3(kWaves * 64), 0, st, sp);
+  else if constexpr (use_mfma<FMT, D>())
     hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
   else

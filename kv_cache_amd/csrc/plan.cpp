@@ -50,9 +50,13 @@ namespace {
 // stream; B*H_kv of them rarely fill 256 CUs, so the visible rows are cut into
 // splits until about kWgPerCu workgroups per CU exist, but never into splits
 // shorter than kMinChunk rows: each extra split adds one (m, l, u) state per
-// query head to the workspace round trip and to the reducer fan-in.
+// query head to the workspace round trip and to the reducer fan-in.  Splits
+// are also never longer than kMaxChunk rows: the plan knows only the longest
+// request, and with ragged lengths short splits let the hardware dispatcher
+// balance the work (splits past a short request's end exit at once).
 constexpr int kWgPerCu = 3;
 constexpr int kMinChunk = 256;
+constexpr int kMaxChunk = 1024;
 constexpr int kRowAlign = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -141,6 +145,7 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
     const int64_t units = std::max<int64_t>(1, (int64_t)p.batch * p.num_kv_heads);
     const int64_t s0 = std::max<int64_t>(1, ceil_div((int64_t)kWgPerCu * num_cus, units));
     chunk = round_up(ceil_div(max_vis, s0), kRowAlign);
+    chunk = std::min<int64_t>(chunk, kMaxChunk);
     chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinChunk, round_up(max_vis, kRowAlign)));
   }
   int64_t S = max_vis == 0 ? 1 : ceil_div(max_vis, chunk);

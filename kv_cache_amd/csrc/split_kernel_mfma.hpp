@@ -86,6 +86,17 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   const int n = lane & 15;     // K row of the tile / score column (head)
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
 
+  // B operand: q[head n][32c + 8kg .. +7], zero for columns n >= G; requested
+  // before the request length is known.
+  uint4 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qop[c] = make_uint4(0u, 0u, 0u, 0u);
+    if (n < G)
+      qop[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
+                                               ((int64_t)b * p.num_q_heads + h * G + n) * D + 32 * c + 8 * kg);
+  }
+
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
@@ -94,16 +105,6 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   if (begin >= end) {
     write_identity<G, D, NWAVES>(p, st0);
     return;
-  }
-
-  // B operand: q[head n][32c + 8kg .. +7], zero for columns n >= G.
-  uint4 qop[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    qop[c] = make_uint4(0u, 0u, 0u, 0u);
-    if (n < G)
-      qop[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
-                                               ((int64_t)b * p.num_q_heads + h * G + n) * D + 32 * c + 8 * kg);
   }
 
   // Row r of the tile is ordinal tile + r; rows past the split end are
@@ -145,11 +146,14 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   // row end-1 (already cached) and keep the loop free of branches.
   MfmaTile t;
   int tile = begin + wave * TW;
-  uint32_t ri = 0;
+  // Row indices run one tile ahead of the loads that use them, so a paged
+  // cache's block-table lookup is off the load path.
+  uint32_t ri = 0, ri_ahead = 0;
   if (tile < end) {
     ri = row_index(tile);
     issue_k(ri, t.k);
     issue_v(ri, t.v);
+    ri_ahead = row_index(tile + NWAVES * TW);
   }
   for (; tile < end; tile += NWAVES * TW) {
     const int next_tile = tile + NWAVES * TW;
@@ -158,7 +162,8 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
     for (int c = 0; c < 4; ++c)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[c]),
                                                     __builtin_bit_cast(bf16x8_t, qop[c]), acc, 0, 0, 0);
-    ri = row_index(next_tile);
+    ri = ri_ahead;
+    ri_ahead = row_index(next_tile + NWAVES * TW);
     issue_k(ri, t.k);
     float sc[4];
 #pragma unroll
