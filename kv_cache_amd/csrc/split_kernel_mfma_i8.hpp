@@ -12,14 +12,14 @@
 // tile loop of split_kernel_mfma with the same running state:
 //
 //  * int8 part.  A per-channel K scale cannot leave the dot product (section
-//    0x03B), so it is folded into q once per 128-token group:
-//    q'_d = q_d * sigma_K[group, d], split into bf16 hi + lo parts (hi =
-//    bf16(q'), lo = bf16(q' - hi)); the codes are exact in bf16.  Scores are
-//    two MFMA chains, A = codes, B = hi and lo.  A tile whose rows span
-//    several groups is scored once per group and each row keeps its own
-//    group's result.  The V scale of a row multiplies that row's softmax
-//    weight (section 0x03C) before PV; the denominator uses the unscaled
-//    weight.
+//    0x03B), so each K element is dequantized inside the reduction: the code
+//    becomes an exact fp16 value (bias 1024+128 trick: the byte c^0x80 is the
+//    mantissa of 1024 + (c + 128)), is multiplied by its fp16 channel scale in
+//    packed fp16 arithmetic as an unevaluated sum hi + lo (exact to 2^-22),
+//    and both parts feed v_mfma_f32_16x16x32_f16 with q in fp16 (B operand).  Each row reads its
+//    own 128-token group's scales, so groups never need special handling.
+//    The V scale of a row multiplies that row's softmax weight (section
+//    0x03C) before PV; the denominator uses the unscaled weight.
 //  * residual part: exactly the bf16 kernel's tile (A = bf16 K rows, B = q).
 #pragma once
 
@@ -28,26 +28,38 @@
 namespace da {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
-// Round two floats to bf16 (nearest even) and pack them, first in the low half.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+// Round two floats to fp16 (nearest even) and pack them, first in the low half.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
-// Eight int8 codes (two dwords) -> eight bf16 values (exact: |code| <= 127).
-__device__ __forceinline__ uint4 codes_to_bf16(uint2 c) {
-  uint32_t o[4];
+// Eight int8 codes times their eight fp16 scales as fp16 pairs hi + lo with
+// hi = fp16(c * sigma) and lo = fp16(c * sigma - hi) (the fused multiply-add
+// forms c * sigma - hi exactly, and c * sigma has at most 18 significant bits,
+// so hi + lo represents the product to 2^-22).  Codes: the byte c ^ 0x80 =
+// c + 128 placed under the exponent of 1024 gives the fp16 value
+// 1024 + c + 128 exactly; subtracting 1152 leaves c exactly.
+__device__ __forceinline__ void dequant_f16(uint2 codes, uint4 scales, uint4& hi, uint4& lo) {
+  const uint32_t w[2] = {codes.x ^ 0x80808080u, codes.y ^ 0x80808080u};
+  const uint32_t sc[4] = {scales.x, scales.y, scales.z, scales.w};
+  uint32_t oh[4], ol[4];
+  const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t w = i < 2 ? c.x : c.y;
-    const int sh = 16 * (i & 1);
-    const float a = (float)(int32_t)((int32_t)(w << (24 - sh)) >> 24);
-    const float b = (float)(int32_t)((int32_t)(w << (16 - sh)) >> 24);
-    o[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    const uint32_t x = w[i >> 1] >> (16 * (i & 1));            // two code bytes in the low half
+    const uint32_t bits = (x & 0xffu) | ((x & 0xff00u) << 8) | 0x64006400u;
+    const f16x2_t c = __builtin_bit_cast(f16x2_t, bits) - bias;
+    const f16x2_t sg = __builtin_bit_cast(f16x2_t, sc[i]);
+    const f16x2_t h = c * sg;
+    oh[i] = __builtin_bit_cast(uint32_t, h);
+    ol[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, sg, -h));
   }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+  lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
 }
 
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
@@ -138,113 +150,55 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 
   // ================= int8 part: ordinals [begin, mid) =================
   if (begin < mid) {
-    auto pos = [&](int o) { return vis_pos(vis, min(o, mid - 1)); };
-    auto group_of = [&](int o) { return pos(o) >> p.k_group_shift; };
-    // B operand (hi, lo) of q' = q * sigma_K[group], kept per wave in LDS,
-    // and the group it holds
-    __shared__ uint4 b_lds[NWAVES][2][4][64];
-    int cur_group = -1;
-    auto load_sigma = [&](int grp, uint4 (&sg)[4]) {
-      const uint16_t* row = ks + (int64_t)grp * row_stride;
+    // B operand in fp16: q[head n][32c + 8kg .. +7] (bf16 values are exact in
+    // fp16 over the normal range of N(0,1)-scale queries).
+    uint4 qh[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sg[c] = *reinterpret_cast<const uint4*>(row + 32 * c);
-    };
-    auto make_b = [&](const uint4 (&sg)[4]) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 qv = q_lds[c][lane];
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-        const uint32_t sw[4] = {sg[c].x, sg[c].y, sg[c].z, sg[c].w};
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float q0 = bf16_lo(qw[e]) * f16_bits_to_f32(sw[e] & 0xffffu);
-          const float q1 = bf16_hi(qw[e]) * f16_bits_to_f32(sw[e] >> 16);
-          hw[e] = pack_bf16(q0, q1);
-          lw[e] = pack_bf16(q0 - bf16_lo(hw[e]), q1 - bf16_hi(hw[e]));
-        }
-        b_lds[wave][0][c][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        b_lds[wave][1][c][lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
-    };
-    auto score = [&](const uint2 (&k)[4]) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) {
+      const uint4 x = q_lds[c][lane];
+      qh[c] = make_uint4(pack_f16(bf16_lo(x.x), bf16_hi(x.x)), pack_f16(bf16_lo(x.y), bf16_hi(x.y)),
+                         pack_f16(bf16_lo(x.z), bf16_hi(x.z)), pack_f16(bf16_lo(x.w), bf16_hi(x.w)));
+    }
+    auto pos = [&](int o) { return (uint32_t)vis_pos(vis, min(o, mid - 1)); };
+    auto issue_k = [&](int tile, uint2 (&k)[4], uint4 (&sk)[4]) {
+      const uint32_t t = pos(tile + n);
+      const int8_t* row = kc + (uint64_t)t * row_stride;
+      const uint16_t* srow = ks + (uint64_t)(t >> p.k_group_shift) * row_stride;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, codes_to_bf16(k[c]));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b_lds[wave][0][c][lane]),
-                                                      acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b_lds[wave][1][c][lane]),
-                                                      acc, 0, 0, 0);
+        k[c] = stream_load(reinterpret_cast<const uint2*>(row + 32 * c));
+        sk[c] = *reinterpret_cast<const uint4*>(srow + 32 * c);
       }
-      return acc;
-    };
-    auto issue_k = [&](int tile, uint2 (&k)[4]) {
-      const int8_t* row = kc + (uint64_t)(uint32_t)pos(tile + n) * row_stride;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint2*>(row + 32 * c));
     };
     auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t t = (uint32_t)pos(tile + 4 * kg + j);
+        const uint32_t t = pos(tile + 4 * kg + j);
         v[j] = stream_load(reinterpret_cast<const uint2*>(vc + (uint64_t)t * row_stride));
         sv[j] = vs[(int64_t)t * p.num_kv_heads];
       }
     };
-
     uint2 kt[4], vt[4];
+    uint4 skt[4];
     uint32_t svt[4];
-    uint4 sig[4];
-    int sig_group = -1;
     int tile = begin + wave * TW;
     if (tile < mid) {
-      issue_k(tile, kt);
+      issue_k(tile, kt, skt);
       issue_v(tile, vt, svt);
-      sig_group = group_of(tile);
-      load_sigma(sig_group, sig);
     }
     for (; tile < mid; tile += STEP) {
       const int next_tile = tile + STEP;
-      const int g0 = group_of(tile), g1 = group_of(tile + TW - 1);
-      f32x4_t acc;
-      if (g0 == g1) {
-        if (g0 != cur_group) {
-          if (g0 != sig_group) { sig_group = g0; load_sigma(g0, sig); }
-          make_b(sig);
-          cur_group = g0;
-        }
-        acc = score(kt);
-      } else {
-        // rows of several 128-token groups: score once per group
-        int rg[4];
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rg[i] = group_of(tile + 4 * kg + i);
-        const int my = group_of(tile + n);
-        acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        int grp = g0;
-        while (true) {
-          if (grp != cur_group) {
-            if (grp != sig_group) { sig_group = grp; load_sigma(grp, sig); }
-            make_b(sig);
-            cur_group = grp;
-          }
-          const f32x4_t a = score(kt);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = rg[i] == grp ? a[i] : acc[i];
-          if (grp == g1) break;
-          int cand = my > grp ? my : 0x7fffffff;     // smallest group above grp in the tile
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) cand = min(cand, __shfl_xor(cand, off));
-          grp = cand;
-        }
+      for (int c = 0; c < 4; ++c) {
+        uint4 hi, lo;
+        dequant_f16(kt[c], skt[c], hi, lo);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hi),
+                                                     __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, lo),
+                                                     __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
       }
-      issue_k(next_tile, kt);
-      const int ng = group_of(next_tile);
-      if (next_tile < mid && ng != cur_group && ng != sig_group) {   // prefetch the next group's scales
-        sig_group = ng;
-        load_sigma(ng, sig);
-      }
+      issue_k(next_tile, kt, skt);
       float pr[4];
       softmax(acc, tile, mid, pr);
 #pragma unroll
