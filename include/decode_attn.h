@@ -127,7 +127,8 @@ typedef struct da_plan {
   int32_t    chunk;            /* visible rows per split (multiple of 16)           */
   int32_t    max_visible;      /* bound on visible rows of one request              */
   int32_t    num_cus;          /* CU count the split heuristic used                 */
-  uint64_t   workspace_bytes;  /* B*H_q*S*(D + 2)*4                                 */
+  uint64_t   workspace_bytes;  /* states round_up(B*H_q*S*(D + 2)*4, 256), then     */
+                               /* counters round_up(B*H_kv*4, 256)                  */
   uint64_t   reserved[2];
 } da_plan;
 
@@ -143,7 +144,11 @@ typedef struct da_plan {
  *               t >= n_q(b) = seq_lens[b] - min(seq_lens[b], R)
  *   block_table paged: int32 [B, max_pages_per_seq]; only slots < ceil(T_b/P) are read
  *   seq_lens    int32 [B]; visible length T_b of each request, 0 <= T_b <= max_seq_len
- *   workspace   >= plan.workspace_bytes, 256-byte aligned; contents on entry ignored
+ *   workspace   >= plan.workspace_bytes, 256-byte aligned.  The state region
+ *               (first round_up(B*H_q*S*(D+2)*4, 256) bytes) is ignored on
+ *               entry.  The B*H_kv uint32 arrival counters after it are used
+ *               only by decode_attn_forward: they must be zero when it starts
+ *               (decode_attn_workspace_init) and it leaves them zero.
  * q, k, v, k_resid and v_resid must be 16-byte aligned. */
 typedef struct da_args {
   const void*    q;
@@ -183,6 +188,27 @@ da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream
 da_status decode_attn_combine(const da_plan* plan, const void* workspace,
                               uint64_t workspace_bytes, float* out, float* lse,
                               void* stream);
+
+/* Single-launch form of run + combine: the same split kernel, with the
+ * reduction of section 0x02B folded into it.  Each workgroup stores its
+ * states, makes them visible device-wide, and increments the arrival counter
+ * of its (b, h_kv); the workgroup that arrives last (the S-th) reads the S
+ * states of its H_q/H_kv rows, folds them in ascending split order exactly as
+ * the combine kernel defines, writes out fp32 [B, H_q, D] and (when lse is not
+ * NULL) lse fp32 [B, H_q], and resets the counter to zero.  No workgroup waits
+ * for another, so the launch completes whatever the scheduling order.
+ * Requirements: the workspace counters are zero on entry (see
+ * decode_attn_workspace_init; every completed forward leaves them zero), and
+ * calls that share a workspace are ordered on one stream.  Results match
+ * run + combine up to the order of the final fp32 sums. */
+da_status decode_attn_forward(const da_plan* plan, const da_args* args, float* out, float* lse,
+                              void* stream);
+
+/* Zero the arrival counters of a workspace sized for `plan` (a fill kernel on
+ * `stream`, so it may be captured into a graph).  Needed once per workspace
+ * before its first decode_attn_forward. */
+da_status decode_attn_workspace_init(const da_plan* plan, void* workspace,
+                                     uint64_t workspace_bytes, void* stream);
 
 /* Debug entry point, never used on the timed path: walks exactly the rows the
  * split kernel loads, through the same device address and mask code, and

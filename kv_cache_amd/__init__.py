@@ -16,7 +16,8 @@ __all__ = [
     "DA_OK", "DA_ERR_INVALID", "DA_ERR_UNSUPPORTED", "DA_ERR_WORKSPACE",
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
     "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
-    "decode_attn_run", "decode_attn_combine", "decode_attn_trace_indices",
+    "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
+    "decode_attn_workspace_init", "decode_attn_trace_indices",
     "decode_attn_reason", "decode_attn_status_string", "reason_names",
 ]
 
@@ -84,6 +85,12 @@ def lib() -> ctypes.CDLL:
         L.decode_attn_combine.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_uint64,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.decode_attn_combine.restype = ctypes.c_int32
+        L.decode_attn_forward.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_attn_forward.restype = ctypes.c_int32
+        L.decode_attn_workspace_init.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p,
+                                                 ctypes.c_uint64, ctypes.c_void_p]
+        L.decode_attn_workspace_init.restype = ctypes.c_int32
         L.decode_attn_trace_indices.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.decode_attn_trace_indices.restype = ctypes.c_int32
@@ -167,6 +174,24 @@ def decode_attn_combine(plan: Plan, workspace, workspace_bytes: int, out, lse=No
                                    _ptr(out), _ptr(lse), stream)
     if check and st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_combine")
+    return st
+
+
+def decode_attn_forward(plan: Plan, args: Args, out, lse=None, stream: int = 0,
+                        check: bool = True) -> int:
+    st = lib().decode_attn_forward(ctypes.byref(plan), ctypes.byref(args), _ptr(out), _ptr(lse),
+                                   stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_forward")
+    return st
+
+
+def decode_attn_workspace_init(plan: Plan, workspace, workspace_bytes: int, stream: int = 0,
+                               check: bool = True) -> int:
+    st = lib().decode_attn_workspace_init(ctypes.byref(plan), _ptr(workspace),
+                                          int(workspace_bytes), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_workspace_init")
     return st
 
 

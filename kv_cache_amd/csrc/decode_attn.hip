@@ -88,6 +88,10 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.ws_u = ws;
   sp.ws_m = ws ? ws + n_states * p.head_dim_v : nullptr;
   sp.ws_l = ws ? sp.ws_m + n_states : nullptr;
+  sp.counters = ws ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + da::states_bytes(*plan))
+                   : nullptr;
+  sp.out = nullptr;
+  sp.lse = nullptr;
   sp.num_q_heads = p.num_q_heads;
   sp.num_kv_heads = p.num_kv_heads;
   sp.num_splits = plan->num_splits;
@@ -107,16 +111,17 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   return sp;
 }
 
-template <int FMT, int D, int G, bool PAGED>
+template <int FMT, int D, int G, bool PAGED, bool FUSED>
 void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8)
-    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves>), dim3(grid), dim3(kWaves * 64), 0, st, sp);
-  else if constexpr (use_mfma<FMT, D>())
-    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves>), dim3(grid), dim3(kWaves * 64), 0,
+    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
-  else
-    hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value>), dim3(grid),
+  else if constexpr (use_mfma<FMT, D>())
+    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED>), dim3(grid),
                        dim3(kWaves * 64), 0, st, sp);
+  else
+    hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value, FUSED>),
+                       dim3(grid), dim3(kWaves * 64), 0, st, sp);
 }
 
 template <int FMT, int D, bool PAGED>
@@ -126,22 +131,45 @@ void launch_trace(const da::SplitParams& sp, unsigned grid, int64_t* off, int32_
                      dim3(grid), dim3(kWaves * 64), 0, st, sp, off, pos);
 }
 
-template <int FMT, int D, bool PAGED>
+template <int FMT, int D, bool PAGED, bool FUSED>
 bool dispatch_g(int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   switch (g) {
-    case 1: launch_split<FMT, D, 1, PAGED>(sp, grid, st); return true;
-    case 2: launch_split<FMT, D, 2, PAGED>(sp, grid, st); return true;
-    case 4: launch_split<FMT, D, 4, PAGED>(sp, grid, st); return true;
-    case 8: launch_split<FMT, D, 8, PAGED>(sp, grid, st); return true;
+    case 1: launch_split<FMT, D, 1, PAGED, FUSED>(sp, grid, st); return true;
+    case 2: launch_split<FMT, D, 2, PAGED, FUSED>(sp, grid, st); return true;
+    case 4: launch_split<FMT, D, 4, PAGED, FUSED>(sp, grid, st); return true;
+    case 8: launch_split<FMT, D, 8, PAGED, FUSED>(sp, grid, st); return true;
     default: return false;
   }
 }
 
-template <int FMT, bool PAGED>
+template <int FMT, bool PAGED, bool FUSED>
 bool dispatch_d(int d, int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
-  if (d == 64) return dispatch_g<FMT, 64, PAGED>(g, sp, grid, st);
-  if (d == 128) return dispatch_g<FMT, 128, PAGED>(g, sp, grid, st);
+  if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED>(g, sp, grid, st);
+  if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED>(g, sp, grid, st);
   return false;
+}
+
+template <bool FUSED>
+bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
+  const int g = p.num_q_heads / p.num_kv_heads;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
+  switch (p.kv_format) {
+    case DA_KV_F32:
+      return paged ? dispatch_d<DA_KV_F32, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
+                   : dispatch_d<DA_KV_F32, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
+    case DA_KV_BF16:
+      return paged ? dispatch_d<DA_KV_BF16, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
+                   : dispatch_d<DA_KV_BF16, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
+    case DA_KV_I8:
+      return !paged && dispatch_d<DA_KV_I8, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
+    default:
+      return false;
+  }
+}
+
+__global__ void zero_words(uint32_t* w, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) w[i] = 0u;
 }
 
 template <int FMT, bool PAGED>
@@ -164,27 +192,44 @@ extern "C" da_status decode_attn_run(const da_plan* plan, const da_args* args, v
   if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
   const da::SplitParams sp = make_params(plan, args);
   const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
-  const int g = p.num_q_heads / p.num_kv_heads;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  bool ok = false;
-  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
-  switch (p.kv_format) {
-    case DA_KV_F32:
-      ok = paged ? dispatch_d<DA_KV_F32, true>(p.head_dim_qk, g, sp, grid, st)
-                 : dispatch_d<DA_KV_F32, false>(p.head_dim_qk, g, sp, grid, st);
-      break;
-    case DA_KV_BF16:
-      ok = paged ? dispatch_d<DA_KV_BF16, true>(p.head_dim_qk, g, sp, grid, st)
-                 : dispatch_d<DA_KV_BF16, false>(p.head_dim_qk, g, sp, grid, st);
-      break;
-    case DA_KV_I8:
-      ok = !paged && dispatch_d<DA_KV_I8, false>(p.head_dim_qk, g, sp, grid, st);
-      break;
-    default:
-      ok = false;
-  }
-  if (!ok) return DA_ERR_UNSUPPORTED;
+  if (!dispatch_split<false>(p, sp, grid, static_cast<hipStream_t>(stream))) return DA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+extern "C" da_status decode_attn_forward(const da_plan* plan, const da_args* args, float* out,
+                                         float* lse, void* stream) {
+  const da_status chk = check_args(plan, args);
+  if (chk != DA_OK) return chk;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!out) return DA_ERR_INVALID;
+  if (!args->workspace || args->workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(args->workspace) & 15u) != 0) return DA_ERR_WORKSPACE;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  da::SplitParams sp = make_params(plan, args);
+  sp.out = out;
+  sp.lse = lse;
+  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
+  (void)hipGetLastError();
+  if (!dispatch_split<true>(p, sp, grid, static_cast<hipStream_t>(stream))) return DA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+extern "C" da_status decode_attn_workspace_init(const da_plan* plan, void* workspace,
+                                                uint64_t workspace_bytes, void* stream) {
+  if (!plan) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!workspace || workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  const int n = p.batch * p.num_kv_heads;
+  uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                   da::states_bytes(*plan));
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     counters, n);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -23,6 +23,9 @@ struct SplitParams {
   float* ws_u;
   float* ws_m;
   float* ws_l;
+  uint32_t* counters;        // one arrival counter per (b, h_kv) (single-launch mode)
+  float* out;                // single-launch mode: O [B, H_q, D]
+  float* lse;                // single-launch mode: LSE [B, H_q] or null
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t num_splits;

@@ -159,7 +159,7 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (reasons) return DA_ERR_UNSUPPORTED;
 
   if (p.softmax_scale == 0.f) p.softmax_scale = 1.0f / std::sqrt((float)p.head_dim_qk);
-  const uint64_t ws = (uint64_t)p.batch * p.num_q_heads * (uint64_t)S * (uint64_t)(p.head_dim_v + 2) * 4u;
+  const uint64_t ws = da::workspace_bytes_for(p.batch, p.num_q_heads, p.num_kv_heads, S, p.head_dim_v);
 
   da_plan plan;
   std::memset(&plan, 0, sizeof(plan));

@@ -25,6 +25,20 @@ inline uint64_t plan_hash(const da_plan& p) {
 
 inline bool plan_intact(const da_plan* p) { return p && p->key == plan_hash(*p); }
 
+// Workspace layout: u [B,H_q,S,D] f32, m [B,H_q,S] f32, l [B,H_q,S] f32, then
+// (at a 256-byte boundary) one uint32 arrival counter per (b, h_kv).
+inline uint64_t states_bytes_raw(int64_t B, int64_t Hq, int64_t S, int64_t Dv) {
+  return (uint64_t)(B * Hq * S * (Dv + 2) * 4);
+}
+inline uint64_t round_up_256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+inline uint64_t states_bytes(const da_plan& p) {
+  return round_up_256(states_bytes_raw(p.problem.batch, p.problem.num_q_heads, p.num_splits,
+                                       p.problem.head_dim_v));
+}
+inline uint64_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t Dv) {
+  return round_up_256(states_bytes_raw(B, Hq, S, Dv)) + round_up_256((uint64_t)(B * Hkv * 4));
+}
+
 // Element size in bytes of one K/V row element as stored in k/v.
 inline int kv_elem_bytes(int kv_format) {
   return kv_format == DA_KV_F32 ? 4 : kv_format == DA_KV_BF16 ? 2 : 1;

@@ -37,15 +37,32 @@ __device__ __forceinline__ uint2 stream_load(const uint2* p) {
 // empty split ("M4.5 - Decode Attention Kernels, Mask Programs, and Backend
 // Boundaries", section 0x02C): every slot the reducer reads is defined
 // (section 0x03G).
-template <int G, int D, int NWAVES>
+// State stores and loads.  In single-launch mode a split's states are read by
+// another workgroup, possibly on another XCD, whose L2 is not coherent with
+// ours for ordinary accesses.  There the states are written and read as
+// device-scope relaxed atomics (plain stores and loads with the device
+// coherence bit): each such access is performed at the device coherence point,
+// so no L2 write-back or invalidate is needed to publish or observe them.
+template <bool SHARED>
+__device__ __forceinline__ void put_state(float* a, float v) {
+  if constexpr (SHARED)
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *a = v;
+}
+__device__ __forceinline__ float get_shared_state(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int G, int D, int NWAVES, bool SHARED>
 __device__ __forceinline__ void write_identity(const SplitParams& p, int64_t st0) {
   for (int idx = threadIdx.x; idx < G * D; idx += NWAVES * 64) {
     const int i = idx / D, c = idx % D;
-    p.ws_u[(st0 + (int64_t)i * p.num_splits) * D + c] = 0.f;
+    put_state<SHARED>(p.ws_u + (st0 + (int64_t)i * p.num_splits) * D + c, 0.f);
   }
   if (threadIdx.x < G) {
-    p.ws_m[st0 + (int64_t)threadIdx.x * p.num_splits] = -INFINITY;
-    p.ws_l[st0 + (int64_t)threadIdx.x * p.num_splits] = 0.f;
+    put_state<SHARED>(p.ws_m + st0 + (int64_t)threadIdx.x * p.num_splits, -INFINITY);
+    put_state<SHARED>(p.ws_l + st0 + (int64_t)threadIdx.x * p.num_splits, 0.f);
   }
 }
 
@@ -60,7 +77,7 @@ struct WaveStates {
 // Merge the NWAVES wave states of each head (binary merge of section 0x02B
 // folded over the waves, with the empty branch taken by weight 0) and store
 // (m, l, u) of the split; m is converted to natural-log units.
-template <int G, int D, int NWAVES>
+template <int G, int D, int NWAVES, bool SHARED>
 __device__ __forceinline__ void merge_waves_and_store(const SplitParams& p, int64_t st0,
                                                       const WaveStates<G, D, NWAVES>& sh) {
   constexpr float kLn2 = 0.69314718055994530942f;
@@ -78,11 +95,123 @@ __device__ __forceinline__ void merge_waves_and_store(const SplitParams& p, int6
       L = fmaf(f, sh.l[w][i], L);
     }
     const int64_t st = st0 + (int64_t)i * p.num_splits;
-    p.ws_u[st * D + c] = acc;
+    put_state<SHARED>(p.ws_u + st * D + c, acc);
     if (c == 0) {
-      p.ws_m[st] = M == -INFINITY ? -INFINITY : M * kLn2;
-      p.ws_l[st] = L;
+      put_state<SHARED>(p.ws_m + st, M == -INFINITY ? -INFINITY : M * kLn2);
+      put_state<SHARED>(p.ws_l + st, L);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Single-launch mode: the last of the S workgroups of a (b, h_kv) to store its
+// states folds the S states of each of its G query-head rows, with the same
+// two-pass arithmetic as the combine kernel (maximum over valid states, then
+// weights e^(m_s - M) summed in ascending split order, O = u / l, LSE = M +
+// ln l, all-masked rows O = +0.0 and LSE = -inf; "M4.5 - Decode Attention
+// Kernels, Mask Programs, and Backend Boundaries", sections 0x02B-0x02C and
+// 0x03C, which lists a fused reduction among the legal launch shapes).
+//
+// Arrival protocol.  Every wave waits until its device-coherent state stores
+// have completed (s_waitcnt 0), the workgroup synchronises, and one thread
+// increments the (b, h_kv) counter (a device-scope atomic).  The workgroup that
+// reads S-1 is the last: every other workgroup's stores completed before its
+// increment, which precedes ours in the counter's order, and our state loads
+// are issued after the increment returned and are themselves device-coherent,
+// so they observe those stores.  The last workgroup resets the counter to 0 for
+// the next call.  No workgroup ever waits for another.
+//
+// The fold is latency-bound (it runs after the streaming is over), so it
+// issues the u loads of a batch of kFoldBatch states before the weights are
+// known and broadcasts each weight with a lane read instead of a shuffle.
+// ---------------------------------------------------------------------------
+constexpr int kFoldBatch = 16;
+
+template <int D>
+__device__ __forceinline__ void fold_row(const SplitParams& p, int64_t row) {
+  constexpr int CPL = D / 64;              // columns per lane
+  constexpr int NB = kFoldBatch;
+  const int lane = threadIdx.x & 63;
+  const int S = p.num_splits;
+  const float* m = p.ws_m + row * S;
+  const float* l = p.ws_l + row * S;
+  const float* u = p.ws_u + row * S * D + lane;
+  float x[NB][CPL];
+#pragma unroll
+  for (int jj = 0; jj < NB; ++jj) {
+    const int j = min(jj, S - 1);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) x[jj][k] = get_shared_state(u + (int64_t)j * D + 64 * k);
+  }
+  const float l0 = lane < S ? get_shared_state(l + lane) : 0.f;
+  const float m0 = lane < S ? get_shared_state(m + lane) : 0.f;
+  float M = l0 > 0.f ? m0 : -INFINITY;
+  for (int s = lane + 64; s < S; s += 64)
+    if (get_shared_state(l + s) > 0.f) M = fmaxf(M, get_shared_state(m + s));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  float Lp = 0.f;
+  for (int c0 = 0; c0 < S; c0 += 64) {
+    float ls = l0, ms = m0;
+    if (c0 > 0) {
+      ls = c0 + lane < S ? get_shared_state(l + c0 + lane) : 0.f;
+      ms = c0 + lane < S ? get_shared_state(m + c0 + lane) : 0.f;
+    }
+    const float w = ls > 0.f ? __expf(ms - M) : 0.f;     // lanes past S hold 0
+    Lp = fmaf(w, ls, Lp);
+    const int n = min(64, S - c0);
+    for (int j0 = 0; j0 < n; j0 += NB) {
+      float y[NB][CPL];
+      const int nxt = c0 + j0 + NB;
+      if (nxt < S) {
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) {
+          const int j = min(nxt + jj, S - 1);
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) y[jj][k] = get_shared_state(u + (int64_t)j * D + 64 * k);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < NB; ++jj) {
+        const float wj = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + jj));
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[k] = fmaf(wj, wj > 0.f ? x[jj][k] : 0.f, acc[k]);
+      }
+      if (nxt < S) {
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) x[jj][k] = y[jj][k];
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
+  const bool valid = Lp > 0.f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) p.out[row * D + lane + 64 * k] = valid ? acc[k] / Lp : 0.f;
+  if (p.lse && lane == 0) p.lse[row] = valid ? M + logf(Lp) : -INFINITY;
+}
+
+template <int G, int D, int NWAVES, bool FUSED>
+__device__ __forceinline__ void finish_split(const SplitParams& p, int b, int h) {
+  if constexpr (FUSED) {
+    __shared__ int is_last;
+    uint32_t* cnt = p.counters + (int64_t)b * p.num_kv_heads + h;
+    __builtin_amdgcn_s_waitcnt(0);       // this wave's state stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      is_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(p.num_splits - 1);
+    __syncthreads();
+    if (!is_last) return;
+    const int wave = threadIdx.x >> 6;
+    for (int i = wave; i < G; i += NWAVES) fold_row<D>(p, (int64_t)b * p.num_q_heads + (int64_t)h * G + i);
+    if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -115,7 +115,7 @@ __device__ __forceinline__ float decode_v(const RawRow& raw, float* x) {
   }
 }
 
-template <int FMT, int D, int G, bool PAGED, int NWAVES, int U>
+template <int FMT, int D, int G, bool PAGED, int NWAVES, int U, bool FUSED>
 __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   constexpr int EPL = KvTraits<FMT>::EPL;
   constexpr int LPR = D / EPL;           // lanes per row
@@ -142,7 +142,8 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
 
   const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
   if (begin >= end) {   // empty split: the identity state, written before any arithmetic
-    write_identity<G, D, NWAVES>(p, st0);
+    write_identity<G, D, NWAVES, FUSED>(p, st0);
+    finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
 
@@ -280,7 +281,8 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
     }
   }
   __syncthreads();
-  merge_waves_and_store<G, D, NWAVES>(p, st0, sh);
+  merge_waves_and_store<G, D, NWAVES, FUSED>(p, st0, sh);
+  finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 
 }  // namespace da

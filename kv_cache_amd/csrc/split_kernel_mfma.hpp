@@ -70,7 +70,7 @@ struct MfmaTile {
 // accumulators per lane and get 3.
 template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 : 3; };
 
-template <int G, bool PAGED, int NWAVES>
+template <int G, bool PAGED, int NWAVES, bool FUSED>
 __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
   if (begin >= end) {
-    write_identity<G, D, NWAVES>(p, st0);
+    write_identity<G, D, NWAVES, FUSED>(p, st0);
+    finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
 
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
     }
   }
   __syncthreads();
-  merge_waves_and_store<G, D, NWAVES>(p, st0, sh);
+  merge_waves_and_store<G, D, NWAVES, FUSED>(p, st0, sh);
+  finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 
 }  // namespace da

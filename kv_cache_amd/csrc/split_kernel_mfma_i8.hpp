@@ -63,7 +63,7 @@ __device__ __forceinline__ void dequant_f16(uint2 codes, uint4 scales, uint4& hi
 }
 
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
-template <int G, int NWAVES>
+template <int G, int NWAVES, bool FUSED>
 __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma_i8(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
   if (begin >= end) {
-    write_identity<G, D, NWAVES>(p, st0);
+    write_identity<G, D, NWAVES, FUSED>(p, st0);
+    finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
   const int n_q = T - min(T, p.residual_len);
@@ -275,7 +276,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     }
   }
   __syncthreads();
-  merge_waves_and_store<G, D, NWAVES>(p, st0, sh);
+  merge_waves_and_store<G, D, NWAVES, FUSED>(p, st0, sh);
+  finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 
 }  // namespace da

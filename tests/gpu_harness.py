@@ -70,6 +70,43 @@ def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None)
     return res
 
 
+def states_bytes(plan):
+    p = plan.problem
+    raw = p.batch * p.num_q_heads * plan.num_splits * (p.head_dim_v + 2) * 4
+    return (raw + 255) // 256 * 256
+
+
+def forward(w, num_splits=None, dw=None, ws=None, want_ws=False, init=True):
+    """Plan and run the single-launch path (split kernel with the fused
+    reduction).  A fresh workspace is filled with 0xFF (NaN states, counters
+    garbage) and then initialised through decode_attn_workspace_init."""
+    t = torch()
+    dw = dw or DeviceWorkload(w)
+    plan, ws_bytes = plan_for(w, num_splits)
+    if ws is None:
+        ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+        ws.fill_(0xFF)
+    B, Hq, D = w.problem.batch, w.problem.num_q_heads, w.problem.head_dim
+    out = t.full((B, Hq, D), float("nan"), dtype=t.float32, device="cuda")
+    lse = t.full((B, Hq), float("nan"), dtype=t.float32, device="cuda")
+    s = t.cuda.current_stream().cuda_stream
+    if init:
+        ka.decode_attn_workspace_init(plan, ws, ws_bytes, s)
+    ka.decode_attn_forward(plan, dw.args(ws, ws_bytes), out, lse, s)
+    t.cuda.synchronize()
+    res = (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), plan)
+    if want_ws:
+        res = res + (ws,)
+    return res
+
+
+def counters(ws, plan):
+    p = plan.problem
+    off = states_bytes(plan)
+    n = p.batch * p.num_kv_heads
+    return ws[off: off + 4 * n].cpu().numpy().view(np.uint32)
+
+
 def split_workspace(ws_bytes: np.ndarray, plan):
     p = plan.problem
     n = p.batch * p.num_q_heads * plan.num_splits

@@ -27,6 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     L = ka.lib()
     names = header_functions()
     assert set(names) >= {"decode_attn_plan", "decode_attn_run", "decode_attn_combine",
+                          "decode_attn_forward", "decode_attn_workspace_init",
                           "decode_attn_trace_indices", "decode_attn_reason",
                           "decode_attn_status_string"}
     for n in names:
@@ -54,7 +55,10 @@ def test_workspace_and_auto_splits_llama_shape():
     st, pl, ws, rs = plan(P())
     assert st == ka.DA_OK and rs == 0
     S = pl.num_splits
-    assert ws == 8 * 32 * S * (128 + 2) * 4 == pl.workspace_bytes
+    states = 8 * 32 * S * (128 + 2) * 4
+    counters = 8 * 8 * 4
+    rup = lambda x: (x + 255) // 256 * 256
+    assert ws == rup(states) + rup(counters) == pl.workspace_bytes
     assert pl.chunk % 16 == 0 and S * pl.chunk >= 4096 and (S - 1) * pl.chunk < 4096
     assert 8 * 8 * S >= 256          # at least one workgroup per CU
     assert abs(pl.problem.softmax_scale - 1 / math.sqrt(128)) < 1e-8
@@ -135,6 +139,8 @@ def test_plan_mismatch_detected_without_gpu():
     args = ka.Args()
     assert ka.decode_attn_run(pl, args, check=False) == ka.DA_ERR_PLAN_MISMATCH
     assert ka.decode_attn_combine(pl, 16, ws, 16, check=False) == ka.DA_ERR_PLAN_MISMATCH
+    assert ka.decode_attn_forward(pl, args, 16, check=False) == ka.DA_ERR_PLAN_MISMATCH
+    assert ka.decode_attn_workspace_init(pl, 256, ws, check=False) == ka.DA_ERR_PLAN_MISMATCH
 
 
 def test_run_rejects_null_pointers_and_small_workspace_without_gpu():
@@ -146,6 +152,12 @@ def test_run_rejects_null_pointers_and_small_workspace_without_gpu():
     args = ka.make_args(8, 16, 16, 16, 256, ws)          # misaligned q
     assert ka.decode_attn_run(pl, args, check=False) == ka.DA_ERR_INVALID
     assert ka.decode_attn_combine(pl, 256, ws - 1, 16, check=False) == ka.DA_ERR_WORKSPACE
+    args = ka.make_args(16, 16, 16, 16, 256, ws)
+    assert ka.decode_attn_forward(pl, args, None, check=False) == ka.DA_ERR_INVALID
+    args = ka.make_args(16, 16, 16, 16, 256, ws - 4)
+    assert ka.decode_attn_forward(pl, args, 16, check=False) == ka.DA_ERR_WORKSPACE
+    assert ka.decode_attn_workspace_init(pl, 256, ws - 1, check=False) == ka.DA_ERR_WORKSPACE
+    assert ka.decode_attn_workspace_init(pl, None, ws, check=False) == ka.DA_ERR_WORKSPACE
 
 
 def test_reason_and_status_text():
