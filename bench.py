@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_llama3_8b_layer_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_fused_llama3_8b_layer_traffic.json")
 KERNEL_SOURCES = ["kv_cache_amd/csrc/split_kernel_mfma.hpp", "kv_cache_amd/csrc/split_common.hpp",
                   "kv_cache_amd/csrc/device_common.hpp", "kv_cache_amd/csrc/decode_attn.hip"]
 

@@ -199,8 +199,9 @@ da_status decode_attn_combine(const da_plan* plan, const void* workspace,
  * for another, so the launch completes whatever the scheduling order.
  * Requirements: the workspace counters are zero on entry (see
  * decode_attn_workspace_init; every completed forward leaves them zero), and
- * calls that share a workspace are ordered on one stream.  Results match
- * run + combine up to the order of the final fp32 sums. */
+ * calls that share a workspace are ordered on one stream.  out must be
+ * 16-byte aligned (DA_ERR_INVALID otherwise).  Results match run + combine up
+ * to the order of the final fp32 sums. */
 da_status decode_attn_forward(const da_plan* plan, const da_args* args, float* out, float* lse,
                               void* stream);
 

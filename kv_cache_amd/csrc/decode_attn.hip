@@ -167,6 +167,13 @@ bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned gri
   }
 }
 
+// Largest split count for which decode_attn_forward folds inside the split
+// kernel (measured: at S = 12 on the 8 x 4096 GQA shape the single launch is
+// slightly faster than split + combine, at S = 32 and S = 128 slower).  Must
+// not exceed da::kFoldMaxSplits, the fold's own limit.
+constexpr int kFusedMaxSplits = 16;
+static_assert(kFusedMaxSplits <= da::kFoldMaxSplits, "fold handles at most 64 states per row");
+
 __global__ void zero_words(uint32_t* w, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) w[i] = 0u;
@@ -203,16 +210,25 @@ extern "C" da_status decode_attn_forward(const da_plan* plan, const da_args* arg
   if (chk != DA_OK) return chk;
   const da_problem& p = plan->problem;
   if (p.batch == 0) return DA_OK;
-  if (!out) return DA_ERR_INVALID;
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return DA_ERR_INVALID;
   if (!args->workspace || args->workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(args->workspace) & 15u) != 0) return DA_ERR_WORKSPACE;
   if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (plan->num_splits > kFusedMaxSplits) {
+    // Many splits per row: the separate combine kernel folds them with far
+    // more threads than the last-arriving workgroup has, and the arrival
+    // round trip of every extra workgroup costs more than the launch it saves.
+    if (!dispatch_split<false>(p, make_params(plan, args), grid, st)) return DA_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
+    return decode_attn_combine(plan, args->workspace, args->workspace_bytes, out, lse, stream);
+  }
   da::SplitParams sp = make_params(plan, args);
   sp.out = out;
   sp.lse = lse;
-  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
-  (void)hipGetLastError();
-  if (!dispatch_split<true>(p, sp, grid, static_cast<hipStream_t>(stream))) return DA_ERR_UNSUPPORTED;
+  if (!dispatch_split<true>(p, sp, grid, st)) return DA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

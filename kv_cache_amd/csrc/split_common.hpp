@@ -121,80 +121,92 @@ __device__ __forceinline__ void merge_waves_and_store(const SplitParams& p, int6
 // so they observe those stores.  The last workgroup resets the counter to 0 for
 // the next call.  No workgroup ever waits for another.
 //
-// The fold is latency-bound (it runs after the streaming is over), so it
-// issues the u loads of a batch of kFoldBatch states before the weights are
-// known and broadcasts each weight with a lane read instead of a shuffle.
+// The fold runs after the streaming is over, so it is pure latency: it issues
+// the u loads of a batch of states (16-byte column quads, several states per
+// wave-wide load) together with the m and l loads, keeps its code short (it
+// runs once per (b, h_kv), from a cold instruction cache), and reduces across
+// lanes with DPP instead of LDS shuffles where it can.
 // ---------------------------------------------------------------------------
-constexpr int kFoldBatch = 16;
+__device__ __forceinline__ float lane_read(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+// Wave-wide max / sum: DPP inside each 16-lane row, then the four row results.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
+}
+// Four consecutive device-coherent floats (two 8-byte relaxed atomic loads).
+__device__ __forceinline__ float4 get_shared_state4(const float* a) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(a);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
+// Single-launch mode is used for S <= kFoldMaxSplits: lane s holds the m and
+// l of state s.
+constexpr int kFoldMaxSplits = 64;
 
 template <int D>
 __device__ __forceinline__ void fold_row(const SplitParams& p, int64_t row) {
-  constexpr int CPL = D / 64;              // columns per lane
-  constexpr int NB = kFoldBatch;
+  constexpr int QPS = D / 4;               // column quads per state row
+  constexpr int SPI = 64 / QPS;            // states per wave-wide quad load
+  constexpr int NI = 8;                    // quad loads in flight per lane
+  constexpr int NB = NI * SPI;             // states per batch (divides 64)
   const int lane = threadIdx.x & 63;
+  const int sub = lane / QPS;
   const int S = p.num_splits;
-  const float* m = p.ws_m + row * S;
-  const float* l = p.ws_l + row * S;
-  const float* u = p.ws_u + row * S * D + lane;
-  float x[NB][CPL];
+  const float* u = p.ws_u + row * S * D + (lane % QPS) * 4;
+  // m and l are requested first, so waiting for them does not wait for the
+  // u loads queued behind them.
+  const int sl = min(lane, S - 1);
+  float ls = get_shared_state(p.ws_l + row * S + sl);
+  const float ms = get_shared_state(p.ws_m + row * S + sl);
+  float4 x[NI];
 #pragma unroll
-  for (int jj = 0; jj < NB; ++jj) {
-    const int j = min(jj, S - 1);
+  for (int k = 0; k < NI; ++k) x[k] = get_shared_state4(u + (int64_t)min(k * SPI + sub, S - 1) * D);
+  if (lane >= S) ls = 0.f;
+  const float M = wave_max(ls > 0.f ? ms : -INFINITY);
+  const float w = ls > 0.f ? __expf(ms - M) : 0.f;        // 0 for invalid and absent states
+  const float L = wave_sum(w * ls);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0;;) {
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) x[jj][k] = get_shared_state(u + (int64_t)j * D + 64 * k);
-  }
-  const float l0 = lane < S ? get_shared_state(l + lane) : 0.f;
-  const float m0 = lane < S ? get_shared_state(m + lane) : 0.f;
-  float M = l0 > 0.f ? m0 : -INFINITY;
-  for (int s = lane + 64; s < S; s += 64)
-    if (get_shared_state(l + s) > 0.f) M = fmaxf(M, get_shared_state(m + s));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float acc[CPL];
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  float Lp = 0.f;
-  for (int c0 = 0; c0 < S; c0 += 64) {
-    float ls = l0, ms = m0;
-    if (c0 > 0) {
-      ls = c0 + lane < S ? get_shared_state(l + c0 + lane) : 0.f;
-      ms = c0 + lane < S ? get_shared_state(m + c0 + lane) : 0.f;
+    for (int k = 0; k < NI; ++k) {
+      const float wj = __shfl(w, j0 + k * SPI + sub);
+      const bool on = wj > 0.f;            // invalid or absent states never touch acc
+      acc.x = fmaf(wj, on ? x[k].x : 0.f, acc.x);
+      acc.y = fmaf(wj, on ? x[k].y : 0.f, acc.y);
+      acc.z = fmaf(wj, on ? x[k].z : 0.f, acc.z);
+      acc.w = fmaf(wj, on ? x[k].w : 0.f, acc.w);
     }
-    const float w = ls > 0.f ? __expf(ms - M) : 0.f;     // lanes past S hold 0
-    Lp = fmaf(w, ls, Lp);
-    const int n = min(64, S - c0);
-    for (int j0 = 0; j0 < n; j0 += NB) {
-      float y[NB][CPL];
-      const int nxt = c0 + j0 + NB;
-      if (nxt < S) {
+    j0 += NB;
+    if (j0 >= S) break;
 #pragma unroll
-        for (int jj = 0; jj < NB; ++jj) {
-          const int j = min(nxt + jj, S - 1);
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) y[jj][k] = get_shared_state(u + (int64_t)j * D + 64 * k);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        const float wj = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + jj));
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) acc[k] = fmaf(wj, wj > 0.f ? x[jj][k] : 0.f, acc[k]);
-      }
-      if (nxt < S) {
-#pragma unroll
-        for (int jj = 0; jj < NB; ++jj)
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) x[jj][k] = y[jj][k];
-      }
-    }
+    for (int k = 0; k < NI; ++k)
+      x[k] = get_shared_state4(u + (int64_t)min(j0 + k * SPI + sub, S - 1) * D);
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
-  const bool valid = Lp > 0.f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) p.out[row * D + lane + 64 * k] = valid ? acc[k] / Lp : 0.f;
-  if (p.lse && lane == 0) p.lse[row] = valid ? M + logf(Lp) : -INFINITY;
+  for (int off = QPS; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  const bool valid = L > 0.f;
+  const float r = valid ? __builtin_amdgcn_rcpf(L) : 0.f;
+  if (sub == 0)
+    reinterpret_cast<float4*>(p.out + row * D)[lane] =
+        make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
+  if (p.lse && lane == 0) p.lse[row] = valid ? M + __logf(L) : -INFINITY;
 }
 
 template <int G, int D, int NWAVES, bool FUSED>
