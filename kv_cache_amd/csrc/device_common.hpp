@@ -93,6 +93,21 @@ __device__ __forceinline__ int request_len(const SplitParams& p, int b) {
 // a fixed-width chunk policy ("M4.5 ...", section 0x03B) whose width is a
 // multiple of 16 rows; splits past the tail own nothing and write the empty
 // identity (section 0x03G).
+// Workgroup -> (b, h_kv, s).  Workgroups are dealt to the 8 XCDs round-robin
+// by index, so with s = index mod S every split s of every (b, h_kv) would land
+// on XCD s mod 8 whenever S is a multiple of 8, and a ragged batch (short
+// requests own only their low splits) would load the XCDs unevenly.  Rotating
+// the split index by the (b, h_kv) index sends split 0 of consecutive
+// (b, h_kv) to different XCDs, which evens the per-XCD rows for any length mix.
+__device__ __forceinline__ void decode_workgroup(const SplitParams& p, int* b, int* h, int* s) {
+  const int wg = blockIdx.x;
+  const int bh = wg / p.num_splits;
+  const int r = wg - bh * p.num_splits;
+  *s = (int)(((long long)r + bh) % p.num_splits);
+  *h = bh % p.num_kv_heads;
+  *b = bh / p.num_kv_heads;
+}
+
 __device__ __forceinline__ void split_range(int n_vis, int s, int chunk, int* begin, int* end) {
   const long long b = (long long)s * chunk;
   const long long e = b + chunk;

@@ -233,11 +233,8 @@ __device__ __forceinline__ void finish_split(const SplitParams& p, int b, int h)
 template <bool I8, int D, bool PAGED, int NWAVES, int TW>
 __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64_t* offsets,
                                                             int32_t* positions) {
-  const int wg = blockIdx.x;
-  const int s = wg % p.num_splits;
-  const int bh = wg / p.num_splits;
-  const int h = bh % p.num_kv_heads;
-  const int b = bh / p.num_kv_heads;
+  int b, h, s;
+  decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int T = request_len(p, b);
@@ -245,7 +242,7 @@ __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64
   int begin, end;
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int n_q = I8 ? T - min(T, p.residual_len) : T;
-  const int64_t base = (int64_t)wg * p.chunk;
+  const int64_t base = (((int64_t)b * p.num_kv_heads + h) * p.num_splits + s) * p.chunk;
   for (int tile = begin + wave * TW; tile < end; tile += NWAVES * TW) {
     for (int j = lane; j < TW; j += 64) {
       const int o = tile + j;

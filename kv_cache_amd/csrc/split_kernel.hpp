@@ -123,11 +123,8 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   constexpr int TW = RPW * U;            // rows per wave tile
   static_assert(LPR >= 4 && LPR <= 64 && (64 % LPR) == 0, "row must span 4..64 lanes");
 
-  const int wg = blockIdx.x;
-  const int s = wg % p.num_splits;
-  const int bh = wg / p.num_splits;
-  const int h = bh % p.num_kv_heads;
-  const int b = bh / p.num_kv_heads;
+  int b, h, s;
+  decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane / LPR;              // row slot

@@ -76,11 +76,8 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   constexpr int TW = 16;
   static_assert(G >= 1 && G <= 16, "");
 
-  const int wg = blockIdx.x;
-  const int s = wg % p.num_splits;
-  const int bh = wg / p.num_splits;
-  const int h = bh % p.num_kv_heads;
-  const int b = bh / p.num_kv_heads;
+  int b, h, s;
+  decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;     // K row of the tile / score column (head)
@@ -181,7 +178,7 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
     l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = mn;
 
-    HeadLoop<G>::rescale(u, alpha);
+    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w[4] = {t.v[j].x, t.v[j].y, t.v[j].z, t.v[j].w};

@@ -62,6 +62,43 @@ __device__ __forceinline__ void dequant_f16(uint2 codes, uint4 scales, uint4& hi
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
 }
 
+// V codes of two rows a, b as exact fp16 pairs, one 32-bit word per channel
+// e = 0..7 holding (c_a[e], c_b[e]): v_perm places the two code bytes under
+// zero bytes, the xor turns them into fp16 1024 + c + 128, the packed subtract
+// removes the bias.
+__device__ __forceinline__ void v_pairs(uint2 a, uint2 b, uint32_t (&out)[8]) {
+  const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t wa = e < 4 ? a.x : a.y, wb = e < 4 ? b.x : b.y;
+    const uint32_t sel = (uint32_t)(e & 3) | 0x0C00u | ((uint32_t)(4 + (e & 3)) << 16) | 0x0C000000u;
+    const uint32_t bits = __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
+    out[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
+  }
+}
+
+template <int I>
+__device__ __forceinline__ uint32_t row_bcast_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + I, 0xF, 0xF, false);
+}
+
+// u[i][e] += w_i(row a) * v_a[e] + w_i(row b) * v_b[e] for each head i, with the
+// fp16 weight pair of head i broadcast from lane i of the 16-lane row and the
+// two products summed in fp32 by v_dot2.
+template <int G, int I = 0>
+struct PairLoop {
+  __device__ __forceinline__ static void accumulate(float (&u)[G][8], uint32_t wp, const uint32_t (&vp)[8]) {
+    const f16x2_t w = __builtin_bit_cast(f16x2_t, row_bcast_u32<I>(wp));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[I][e] = __builtin_amdgcn_fdot2(w, __builtin_bit_cast(f16x2_t, vp[e]), u[I][e], false);
+    PairLoop<G, I + 1>::accumulate(u, wp, vp);
+  }
+};
+template <int G>
+struct PairLoop<G, G> {
+  __device__ __forceinline__ static void accumulate(float (&)[G][8], uint32_t, const uint32_t (&)[8]) {}
+};
+
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
 template <int G, int NWAVES, bool FUSED>
 __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma_i8(SplitParams p) {
@@ -70,11 +107,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   constexpr int STEP = NWAVES * TW;
   static_assert(G >= 1 && G <= 16, "");
 
-  const int wg = blockIdx.x;
-  const int s = wg % p.num_splits;
-  const int bh = wg / p.num_splits;
-  const int h = bh % p.num_kv_heads;
-  const int b = bh / p.num_kv_heads;
+  int b, h, s;
+  decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;     // K row of the tile / score column (head)
@@ -146,7 +180,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - mz);
     l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = mn;
-    HeadLoop<G>::rescale(u, alpha);
+    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
   };
 
   // ================= int8 part: ordinals [begin, mid) =================
@@ -202,12 +236,14 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
       issue_k(next_tile, kt, skt);
       float pr[4];
       softmax(acc, tile, mid, pr);
+      // PV: weight p * sigma_V of each row in fp16 (relative error 2^-11,
+      // far inside the int8 format's own error), rows paired for v_dot2.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float vx[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vx[e] = i8_at(e < 4 ? vt[j].x : vt[j].y, e & 3);
-        HeadLoop<G>::accumulate(u, pr[j] * f16_bits_to_f32(svt[j]), vx);
+      for (int j = 0; j < 4; j += 2) {
+        uint32_t vp[8];
+        v_pairs(vt[j], vt[j + 1], vp);
+        const uint32_t wp = pack_f16(pr[j] * f16_bits_to_f32(svt[j]), pr[j + 1] * f16_bits_to_f32(svt[j + 1]));
+        PairLoop<G>::accumulate(u, wp, vp);
       }
       issue_v(next_tile, vt, svt);
     }
