@@ -124,10 +124,8 @@ class GpuWorkload:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-        self.args = [ka.make_args(d["q"], d["k"], d["v"], self.seq_lens, self.ws, self.ws_bytes,
-                                  k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
-                                  k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
-                                  block_table=d.get("block_table")) for d in self.sets]
+        self.order = None
+        self.make_all_args()
         self.stream = torch.cuda.current_stream().cuda_stream
         ka.decode_attn_workspace_init(self.plan, self.ws, self.ws_bytes, self.stream)
         # ---- algorithmic bytes: what the method must move once ----
@@ -150,6 +148,21 @@ class GpuWorkload:
         self.kv_bytes = kvb
         self.split_bytes = kvb + q + ws + meta
         self.call_bytes = self.split_bytes + ws + out
+
+    def make_all_args(self):
+        ka = self.ka
+        self.args = [ka.make_args(d["q"], d["k"], d["v"], self.seq_lens, self.ws, self.ws_bytes,
+                                  k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
+                                  k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
+                                  block_table=d.get("block_table"), work_order=self.order)
+                     for d in self.sets]
+
+    def use_schedule(self, on=True):
+        """Largest-first work order from the host lengths (decode_attn_schedule)."""
+        torch = self.torch
+        self.order = (torch.from_numpy(self.ka.decode_attn_schedule(self.plan, self.lens)).to("cuda")
+                      if on else None)
+        self.make_all_args()
 
     def run(self, i):
         self.ka.decode_attn_run(self.plan, self.args[i % self.nsets], self.stream)
@@ -386,8 +399,12 @@ def main():
         del wl
         lens = synth.ragged_lengths(0, 32).tolist()
         wp = GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, lens, seed=2)
+        builtin_order = wp.time(wp.fwd, 30, 5)
+        wp.use_schedule()
         others["paged_ragged"] = wp.report(
-            "paged", "B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768] (seed 0), permuted pool")
+            "paged", "B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768] (seed 0), permuted pool, "
+                     "largest-first work order from decode_attn_schedule")
+        others["paged_ragged"]["builtin_order_us_per_call"] = round(builtin_order * 1000, 2)
         del wp
         wi = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
                          mask=(4, 4096))

@@ -144,6 +144,10 @@ typedef struct da_plan {
  *               t >= n_q(b) = seq_lens[b] - min(seq_lens[b], R)
  *   block_table paged: int32 [B, max_pages_per_seq]; only slots < ceil(T_b/P) are read
  *   seq_lens    int32 [B]; visible length T_b of each request, 0 <= T_b <= max_seq_len
+ *   work_order  optional int32 [B*H_kv*S]: workgroup i runs work item work_order[i] =
+ *               (b*H_kv + h_kv)*S + s.  It must be a permutation of 0 .. B*H_kv*S-1 (as
+ *               written by decode_attn_schedule); any permutation gives the same result
+ *               bit for bit, only the schedule changes.  NULL: the built-in order.
  *   workspace   >= plan.workspace_bytes, 256-byte aligned.  The state region
  *               (first round_up(B*H_q*S*(D+2)*4, 256) bytes) is ignored on
  *               entry.  The B*H_kv uint32 arrival counters after it are used
@@ -162,6 +166,7 @@ typedef struct da_args {
   const int32_t* seq_lens;
   void*          workspace;
   uint64_t       workspace_bytes;
+  const int32_t* work_order;   /* NULL, or B*H_kv*S work items from decode_attn_schedule */
 } da_args;
 
 /* Validate the problem (semantic checks first, then every capability
@@ -171,6 +176,21 @@ typedef struct da_args {
  * NULL; *reasons receives the complete bit vector of failed predicates. */
 da_status decode_attn_plan(const da_problem* problem, da_plan* plan,
                            uint64_t* workspace_bytes, uint64_t* reasons);
+
+/* Host-side work ordering for ragged batches ("M4.5 ...", sections 0x09E and
+ * 0x09G: a plan built on the host from the batch's lengths balances uneven
+ * requests).  Only the order in which workgroups take work items changes; the
+ * split boundaries, and so the arithmetic, stay those of the plan.  Given the
+ * requests' lengths on the host, writes into order[0 .. B*H_kv*S) the work
+ * items largest first: every full split (chunk visible rows), then each
+ * request's partial last split by decreasing size, then the empty splits;
+ * within a class the items of one request are spread over consecutive
+ * positions so that they reach different XCDs.  Copy the result to the device
+ * and pass it as da_args.work_order.  Errors: DA_ERR_INVALID for a NULL
+ * pointer, order_len < B*H_kv*S, or a length outside [0, max_seq_len];
+ * DA_ERR_PLAN_MISMATCH for an altered plan. */
+da_status decode_attn_schedule(const da_plan* plan, const int32_t* seq_lens_host, int32_t* order,
+                               uint64_t order_len);
 
 /* Launch the split kernel: grid B*H_kv*S workgroups; workgroup (b, h_kv, s)
  * owns visible rows [s*chunk, min((s+1)*chunk, N_b)) of request b and the

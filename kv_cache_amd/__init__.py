@@ -16,7 +16,7 @@ __all__ = [
     "DA_OK", "DA_ERR_INVALID", "DA_ERR_UNSUPPORTED", "DA_ERR_WORKSPACE",
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
     "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
-    "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
+    "decode_attn_schedule", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
     "decode_attn_workspace_init", "decode_attn_trace_indices",
     "decode_attn_reason", "decode_attn_status_string", "reason_names",
 ]
@@ -50,7 +50,7 @@ class Plan(ctypes.Structure):
 class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "block_table", "seq_lens",
-        "workspace")] + [("workspace_bytes", ctypes.c_uint64)]
+        "workspace")] + [("workspace_bytes", ctypes.c_uint64), ("work_order", ctypes.c_void_p)]
 
 
 class DecodeAttnError(RuntimeError):
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.decode_attn_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Plan),
                                        ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
         L.decode_attn_plan.restype = ctypes.c_int32
+        L.decode_attn_schedule.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_uint64]
+        L.decode_attn_schedule.restype = ctypes.c_int32
         L.decode_attn_run.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p]
         L.decode_attn_run.restype = ctypes.c_int32
         L.decode_attn_combine.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_uint64,
@@ -154,11 +157,25 @@ def _ptr(x):
 
 
 def make_args(q, k, v, seq_lens, workspace, workspace_bytes, k_scale=None, v_scale=None,
-              k_resid=None, v_resid=None, block_table=None) -> Args:
+              k_resid=None, v_resid=None, block_table=None, work_order=None) -> Args:
     return Args(q=_ptr(q), k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
                 k_resid=_ptr(k_resid), v_resid=_ptr(v_resid), block_table=_ptr(block_table),
                 seq_lens=_ptr(seq_lens), workspace=_ptr(workspace),
-                workspace_bytes=int(workspace_bytes))
+                workspace_bytes=int(workspace_bytes), work_order=_ptr(work_order))
+
+
+def decode_attn_schedule(plan: Plan, seq_lens_host, check: bool = True):
+    """Largest-first work order for the plan's grid from host lengths (a list
+    or int32 array); returns an int32 NumPy array of B*H_kv*S work items."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    p = plan.problem
+    n = p.batch * p.num_kv_heads * plan.num_splits
+    order = np.empty(max(n, 1), dtype=np.int32)
+    st = lib().decode_attn_schedule(ctypes.byref(plan), lens.ctypes.data, order.ctypes.data, n)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_schedule")
+    return order[:n]
 
 
 def decode_attn_run(plan: Plan, args: Args, stream: int = 0, check: bool = True) -> int:

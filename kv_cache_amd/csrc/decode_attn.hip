@@ -83,6 +83,7 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.v_resid = a->v_resid;
   sp.block_table = a->block_table;
   sp.seq_lens = a->seq_lens;
+  sp.work_order = a->work_order;
   const uint64_t n_states = (uint64_t)p.batch * p.num_q_heads * plan->num_splits;
   float* ws = static_cast<float*>(a->workspace);
   sp.ws_u = ws;

@@ -20,6 +20,7 @@ struct SplitParams {
   const void* v_resid;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const int32_t* work_order;
   float* ws_u;
   float* ws_m;
   float* ws_l;
@@ -99,11 +100,22 @@ __device__ __forceinline__ int request_len(const SplitParams& p, int b) {
 // requests own only their low splits) would load the XCDs unevenly.  Rotating
 // the split index by the (b, h_kv) index sends split 0 of consecutive
 // (b, h_kv) to different XCDs, which evens the per-XCD rows for any length mix.
+// A caller-supplied work order (a permutation of the work items, largest
+// first for ragged batches) replaces this mapping.
 __device__ __forceinline__ void decode_workgroup(const SplitParams& p, int* b, int* h, int* s) {
   const int wg = blockIdx.x;
-  const int bh = wg / p.num_splits;
-  const int r = wg - bh * p.num_splits;
-  *s = (int)(((long long)r + bh) % p.num_splits);
+  int bh;
+  if (p.work_order) {
+    int item = p.work_order[wg];
+    if ((unsigned)item >= gridDim.x) item = wg;   // never index outside the grid's work
+
+    bh = item / p.num_splits;
+    *s = item - bh * p.num_splits;
+  } else {
+    bh = wg / p.num_splits;
+    const int r = wg - bh * p.num_splits;
+    *s = (int)(((long long)r + bh) % p.num_splits);
+  }
   *h = bh % p.num_kv_heads;
   *b = bh / p.num_kv_heads;
 }

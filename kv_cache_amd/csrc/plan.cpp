@@ -12,6 +12,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <vector>
+#include <algorithm>
 
 #include "plan_internal.hpp"
 
@@ -204,4 +206,43 @@ extern "C" const char* decode_attn_status_string(da_status s) {
     case DA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+extern "C" da_status decode_attn_schedule(const da_plan* plan, const int32_t* seq_lens_host,
+                                          int32_t* order, uint64_t order_len) {
+  if (!plan || !seq_lens_host || !order) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  const int64_t S = plan->num_splits, H = p.num_kv_heads, B = p.batch, chunk = plan->chunk;
+  if (order_len < (uint64_t)(B * H * S)) return DA_ERR_INVALID;
+  std::vector<int64_t> full(B), part(B);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t T = seq_lens_host[b];
+    if (T < 0 || T > p.max_seq_len) return DA_ERR_INVALID;
+    int64_t n_vis = T;
+    if (p.mask_kind == DA_MASK_SINK_WINDOW)
+      n_vis = std::min<int64_t>(T, (int64_t)p.n_sink + (int64_t)p.window);
+    full[b] = std::min<int64_t>(S, n_vis / chunk);
+    part[b] = full[b] < S ? n_vis - full[b] * chunk : 0;   // rows of split full[b] (0: empty)
+  }
+  int64_t pos = 0;
+  auto put = [&](int64_t b, int64_t h, int64_t s) { order[pos++] = (int32_t)((b * H + h) * S + s); };
+  // full splits: split-major, then request, then head
+  for (int64_t s = 0; s < S; ++s)
+    for (int64_t b = 0; b < B; ++b)
+      if (s < full[b])
+        for (int64_t h = 0; h < H; ++h) put(b, h, s);
+  // partial last splits, largest first (ties by request index)
+  std::vector<int64_t> idx;
+  for (int64_t b = 0; b < B; ++b)
+    if (part[b] > 0) idx.push_back(b);
+  std::stable_sort(idx.begin(), idx.end(), [&](int64_t x, int64_t y) { return part[x] > part[y]; });
+  for (int64_t b : idx)
+    for (int64_t h = 0; h < H; ++h) put(b, h, full[b]);
+  // empty splits
+  for (int64_t s = 0; s < S; ++s)
+    for (int64_t b = 0; b < B; ++b)
+      if (s > full[b] || (s == full[b] && part[b] == 0))
+        for (int64_t h = 0; h < H; ++h) put(b, h, s);
+  return DA_OK;
 }

@@ -27,18 +27,24 @@ def announce(*what):
 
 
 class DeviceWorkload:
-    """Device copies of a synth.Workload's buffers."""
+    """Device copies of a synth.Workload's buffers (and an optional work order)."""
 
     def __init__(self, w):
         self.w = w
         self.dev = {k: to_dev(v) for k, v in w.buffers.items()}
+        self.order = None
+
+    def schedule(self, plan):
+        """Use the library's largest-first work order for this plan."""
+        lens = self.w.buffers["seq_lens"]
+        self.order = to_dev(ka.decode_attn_schedule(plan, lens))
 
     def args(self, ws, ws_bytes):
         d = self.dev
         return ka.make_args(d["q"], d["k"], d["v"], d["seq_lens"], ws, ws_bytes,
                             k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
                             k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
-                            block_table=d.get("block_table"))
+                            block_table=d.get("block_table"), work_order=self.order)
 
 
 def plan_for(w, num_splits=None):

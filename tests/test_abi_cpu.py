@@ -6,6 +6,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import kv_cache_amd as ka
@@ -28,6 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) >= {"decode_attn_plan", "decode_attn_run", "decode_attn_combine",
                           "decode_attn_forward", "decode_attn_workspace_init",
+                          "decode_attn_schedule",
                           "decode_attn_trace_indices", "decode_attn_reason",
                           "decode_attn_status_string"}
     for n in names:
@@ -37,7 +39,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(ka.Problem) == 22 * 4
     assert ctypes.sizeof(ka.Plan) == 8 + 88 + 16 + 8 + 16
-    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8
+    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 8
 
 
 def P(**kw):
@@ -165,3 +167,52 @@ def test_reason_and_status_text():
         assert ka.decode_attn_reason(i)
     assert ka.decode_attn_reason(99) == "unknown reason bit"
     assert ka.decode_attn_status_string(0) == "ok"
+
+
+def _work_rows(pl, lens):
+    """Rows of each work item (b*H_kv + h)*S + s under the plan's chunking."""
+    p = pl.problem
+    S, H, chunk = pl.num_splits, p.num_kv_heads, pl.chunk
+    rows = {}
+    for b, T in enumerate(lens):
+        n_vis = T if p.mask_kind == 0 else min(T, p.n_sink + p.window)
+        for h in range(H):
+            for s in range(S):
+                rows[(b * H + h) * S + s] = max(0, min(n_vis, (s + 1) * chunk) - s * chunk)
+    return rows
+
+
+@pytest.mark.parametrize("mask", [None, (4, 300)])
+def test_schedule_is_a_largest_first_permutation(mask):
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 4096, size=13).tolist() + [0, 4096, 1]
+    kw = dict(batch=len(lens), max_seq_len=4096, kv_capacity=4096)
+    if mask:
+        kw.update(mask_kind="sink_window", n_sink=mask[0], window=mask[1])
+    st, pl, ws, _ = plan(P(**kw))
+    assert st == ka.DA_OK
+    order = ka.decode_attn_schedule(pl, lens)
+    n = pl.problem.batch * pl.problem.num_kv_heads * pl.num_splits
+    assert sorted(order.tolist()) == list(range(n))
+    rows = _work_rows(pl, lens)
+    sizes = [rows[i] for i in order.tolist()]
+    assert all(a >= b for a, b in zip(sizes, sizes[1:])), "not largest first"
+    # the H_kv heads of one (request, split) sit at consecutive positions, so
+    # they go to different XCDs
+    H, S = pl.problem.num_kv_heads, pl.num_splits
+    for i in range(0, n, H):
+        it = order[i:i + H]
+        b, h, s = it // (S * H), (it // S) % H, it % S
+        assert len(set(b.tolist())) == 1 and len(set(s.tolist())) == 1
+        assert sorted(h.tolist()) == list(range(H))
+
+
+def test_schedule_rejects_bad_arguments():
+    st, pl, ws, _ = plan(P(batch=2, max_seq_len=100, kv_capacity=100))
+    with pytest.raises(ka.DecodeAttnError):
+        ka.decode_attn_schedule(pl, [50, 101])
+    with pytest.raises(ka.DecodeAttnError):
+        ka.decode_attn_schedule(pl, [50, -1])
+    pl.num_splits += 1
+    with pytest.raises(ka.DecodeAttnError):
+        ka.decode_attn_schedule(pl, [50, 50])
