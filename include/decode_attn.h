@@ -61,6 +61,14 @@ typedef int32_t da_status;
 #define DA_KV_BF16 1   /* bf16 rows */
 #define DA_KV_I8   2   /* int8 codes + fp16 scales + bf16 residual, see da_args */
 
+/* DA_KV_I8 residual policies: which of a request's T tokens are int8 codes
+ * (the oldest n_q) and which are bf16 residual rows (row t - n_q holds token t)
+ * ("M8.6 - Live-Data Quantization: Activations and KV Cache", section 0x06B) */
+#define DA_RESIDUAL_WINDOW 0  /* n_q = T - min(T, R): the newest min(T, R) tokens are bf16     */
+#define DA_RESIDUAL_GROUPS 1  /* n_q = G * max(0, ceil((T - R) / G)): whole K groups close as
+                                 soon as more than R tokens are unclosed (the streaming rule
+                                 decode_attn_append maintains; requires R == G there)       */
+
 /* cache layouts ("M4.5 ...", sections 0x04B and 0x04D) */
 #define DA_LAYOUT_CONTIG_NHD 0  /* [B, T_cap, H_kv, D]; element ((b*T_cap + t)*H_kv + h)*D + x */
 #define DA_LAYOUT_PAGED_NHD  1  /* pool [N_pages, P, H_kv, D]; page = block_table[b][t / P],
@@ -115,6 +123,8 @@ typedef struct da_problem {
   int32_t k_group;           /* DA_KV_I8: tokens per K-scale group (128); else 0   */
   int32_t residual_len;      /* DA_KV_I8: bf16 residual rows R >= 0; else 0        */
   int32_t num_cus;           /* 0 -> query the current device; > 0: plan for this many CUs */
+  int32_t residual_policy;   /* DA_KV_I8: DA_RESIDUAL_*; else 0                     */
+  int32_t reserved0;         /* must be 0                                           */
 } da_problem;
 
 /* A frozen plan: a plain value the caller owns and may copy; nothing to free.
@@ -241,6 +251,42 @@ da_status decode_attn_workspace_init(const da_plan* plan, void* workspace,
  * Entries with no row are left untouched (callers pre-fill them with -1). */
 da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args,
                                     int64_t* offsets, int32_t* positions, void* stream);
+
+/* ---- streaming append for DA_KV_I8 with DA_RESIDUAL_GROUPS ------------------ */
+
+/* per-request error bits written (OR-ed) into da_append_args.status[b] */
+#define DA_APPEND_NO_ROOM   1  /* seq_lens[b] < 0 or seq_lens[b] + 1 > max_seq_len: nothing written */
+#define DA_APPEND_BAD_SCALE 2  /* a closing group had a non-finite value or a non-finite or
+                                  subnormal fp16 scale: nothing written for that (b, h_kv)      */
+
+typedef struct da_append_args {
+  const void*    k_new;     /* bf16 [B, H_kv, D]: K row of the token appended to request b      */
+  const void*    v_new;     /* bf16 [B, H_kv, D]                                                 */
+  void*          k;         /* int8 codes [B, T_cap, H_kv, D] (the da_args k of the same cache)   */
+  void*          v;
+  void*          k_scale;   /* fp16 [B, ceil(T_cap/G), H_kv, D]                                  */
+  void*          v_scale;   /* fp16 [B, T_cap, H_kv]                                             */
+  void*          k_resid;   /* bf16 [B, R, H_kv, D]                                              */
+  void*          v_resid;
+  const int32_t* seq_lens;  /* int32 [B]: lengths before the append; the caller adds 1 after    */
+  int32_t*       status;    /* int32 [B] or NULL: error bits are OR-ed in (caller zeroes it)     */
+} da_append_args;
+
+/* Append one token to every request of an int8 cache that follows
+ * DA_RESIDUAL_GROUPS with residual_len == k_group ("M8.6 ...", sections 0x05B
+ * and 0x06B).  For request b of length T = seq_lens[b]: if its residual holds
+ * R rows, they are closed first -- K quantized per channel over the R = G rows
+ * into scale group n_q/G, V quantized per row (scale per token), codes at
+ * positions n_q .. n_q+G-1 -- then the new rows go to residual row T - n_q(T+1).
+ * The quantizer is that of the int8 format (section 0x02A).  One workgroup per
+ * (b, h_kv), asynchronous on `stream`; nothing is written for a request whose
+ * status gets an error bit (the heads of one request may then disagree, so
+ * the request must be dropped).  The same plan serves attention over the
+ * cache after seq_lens has been advanced.  Errors: DA_ERR_INVALID (NULL
+ * buffer, altered key -> DA_ERR_PLAN_MISMATCH), DA_ERR_UNSUPPORTED (not
+ * int8 + contiguous + DA_RESIDUAL_GROUPS with residual_len == k_group <= 256,
+ * or head_dim not 64/128), DA_ERR_HIP. */
+da_status decode_attn_append(const da_plan* plan, const da_append_args* args, void* stream);
 
 /* Static text for one reason bit index (0 .. DA_NUM_REASONS-1) or status. */
 const char* decode_attn_reason(int bit);

@@ -16,7 +16,7 @@ __all__ = [
     "DA_OK", "DA_ERR_INVALID", "DA_ERR_UNSUPPORTED", "DA_ERR_WORKSPACE",
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
     "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
-    "decode_attn_schedule", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
+    "decode_attn_schedule", "decode_attn_append", "AppendArgs", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
     "decode_attn_workspace_init", "decode_attn_trace_indices",
     "decode_attn_reason", "decode_attn_status_string", "reason_names",
 ]
@@ -28,6 +28,7 @@ DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 KV_FORMATS = {"f32": 0, "bf16": 1, "i8": 2}
 LAYOUTS = {"contig": 0, "paged": 1}
 MASKS = {"causal": 0, "sink_window": 1}
+RESIDUAL_POLICIES = {"window": 0, "groups": 1}
 NUM_REASONS = 12
 
 
@@ -37,7 +38,7 @@ class Problem(ctypes.Structure):
         "out_dtype", "kv_format", "layout", "kv_capacity", "page_size", "max_pages_per_seq",
         "num_pages", "max_seq_len", "mask_kind", "n_sink", "window")] + [
         ("softmax_scale", ctypes.c_float)] + [(n, ctypes.c_int32) for n in (
-            "num_splits", "k_group", "residual_len", "num_cus")]
+            "num_splits", "k_group", "residual_len", "num_cus", "residual_policy", "reserved0")]
 
 
 class Plan(ctypes.Structure):
@@ -51,6 +52,15 @@ class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "block_table", "seq_lens",
         "workspace")] + [("workspace_bytes", ctypes.c_uint64), ("work_order", ctypes.c_void_p)]
+
+
+class AppendArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_new", "v_new", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "seq_lens",
+        "status")]
+
+
+DA_APPEND_NO_ROOM, DA_APPEND_BAD_SCALE = 1, 2
 
 
 class DecodeAttnError(RuntimeError):
@@ -76,6 +86,14 @@ def lib() -> ctypes.CDLL:
         path = library_path()
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+        # One HIP runtime per process: torch ships its own libamdhip64 with the
+        # same soname as ROCm's, and whichever loads first serves both.  Load
+        # torch's first (the caller's tensors and streams live there); torch
+        # then fails to initialise if this library's runtime came first.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(path)
         L.decode_attn_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Plan),
                                        ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
@@ -83,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.decode_attn_schedule.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_uint64]
         L.decode_attn_schedule.restype = ctypes.c_int32
+        L.decode_attn_append.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(AppendArgs),
+                                         ctypes.c_void_p]
+        L.decode_attn_append.restype = ctypes.c_int32
         L.decode_attn_run.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p]
         L.decode_attn_run.restype = ctypes.c_int32
         L.decode_attn_combine.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_uint64,
@@ -132,7 +153,8 @@ def problem_from(p, num_cus: int = 0) -> Problem:
         page_size=p.page_size, max_pages_per_seq=p.max_pages_per_seq, num_pages=p.num_pages,
         max_seq_len=p.max_seq_len, mask_kind=enum(p.mask_kind, MASKS), n_sink=p.n_sink,
         window=p.window, softmax_scale=p.softmax_scale, num_splits=p.num_splits,
-        k_group=p.k_group, residual_len=p.residual_len, num_cus=num_cus)
+        k_group=p.k_group, residual_len=p.residual_len, num_cus=num_cus,
+        residual_policy=enum(getattr(p, "residual_policy", 0), RESIDUAL_POLICIES))
 
 
 def decode_attn_plan(problem: Problem, check: bool = True):
@@ -209,6 +231,17 @@ def decode_attn_workspace_init(plan: Plan, workspace, workspace_bytes: int, stre
                                           int(workspace_bytes), stream)
     if check and st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_workspace_init")
+    return st
+
+
+def decode_attn_append(plan: Plan, k_new, v_new, k, v, k_scale, v_scale, k_resid, v_resid,
+                       seq_lens, status=None, stream: int = 0, check: bool = True) -> int:
+    a = AppendArgs(k_new=_ptr(k_new), v_new=_ptr(v_new), k=_ptr(k), v=_ptr(v),
+                   k_scale=_ptr(k_scale), v_scale=_ptr(v_scale), k_resid=_ptr(k_resid),
+                   v_resid=_ptr(v_resid), seq_lens=_ptr(seq_lens), status=_ptr(status))
+    st = lib().decode_attn_append(ctypes.byref(plan), ctypes.byref(a), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_append")
     return st
 
 

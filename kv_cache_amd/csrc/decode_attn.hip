@@ -6,6 +6,7 @@
 #include <cmath>
 
 #include "combine_kernel.hpp"
+#include "append_kernel.hpp"
 #include "device_common.hpp"
 #include "plan_internal.hpp"
 #include "split_kernel.hpp"
@@ -106,6 +107,7 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.window = p.window;
   sp.k_group_shift = p.kv_format == DA_KV_I8 ? log2_exact(p.k_group) : 0;
   sp.residual_len = p.residual_len;
+  sp.residual_policy = p.residual_policy;
   sp.max_seq_len = p.max_seq_len;
   sp.num_pages = p.num_pages;
   sp.qscale = p.softmax_scale * 1.4426950408889634f;
@@ -230,6 +232,45 @@ extern "C" da_status decode_attn_forward(const da_plan* plan, const da_args* arg
   sp.out = out;
   sp.lse = lse;
   if (!dispatch_split<true>(p, sp, grid, st)) return DA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+extern "C" da_status decode_attn_append(const da_plan* plan, const da_append_args* a, void* stream) {
+  if (!plan || !a) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  if (p.kv_format != DA_KV_I8 || p.layout != DA_LAYOUT_CONTIG_NHD ||
+      p.residual_policy != DA_RESIDUAL_GROUPS || p.residual_len != p.k_group ||
+      p.k_group > da::kAppendThreads || (p.head_dim_qk != 64 && p.head_dim_qk != 128))
+    return DA_ERR_UNSUPPORTED;
+  if (p.batch == 0) return DA_OK;
+  if (!a->k_new || !a->v_new || !a->k || !a->v || !a->k_scale || !a->v_scale || !a->k_resid ||
+      !a->v_resid || !a->seq_lens)
+    return DA_ERR_INVALID;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  da::AppendParams ap;
+  ap.k_new = static_cast<const uint16_t*>(a->k_new);
+  ap.v_new = static_cast<const uint16_t*>(a->v_new);
+  ap.k = static_cast<int8_t*>(a->k);
+  ap.v = static_cast<int8_t*>(a->v);
+  ap.k_scale = static_cast<uint16_t*>(a->k_scale);
+  ap.v_scale = static_cast<uint16_t*>(a->v_scale);
+  ap.k_resid = static_cast<uint16_t*>(a->k_resid);
+  ap.v_resid = static_cast<uint16_t*>(a->v_resid);
+  ap.seq_lens = a->seq_lens;
+  ap.status = a->status;
+  ap.num_kv_heads = p.num_kv_heads;
+  ap.kv_capacity = p.kv_capacity;
+  ap.max_seq_len = p.max_seq_len;
+  ap.group = p.k_group;
+  ap.n_groups = (p.kv_capacity + p.k_group - 1) / p.k_group;
+  const dim3 grid((unsigned)(p.batch * p.num_kv_heads));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p.head_dim_qk == 128)
+    hipLaunchKernelGGL(da::append_kernel<128>, grid, dim3(da::kAppendThreads), 0, st, ap);
+  else
+    hipLaunchKernelGGL(da::append_kernel<64>, grid, dim3(da::kAppendThreads), 0, st, ap);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

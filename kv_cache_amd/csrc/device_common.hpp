@@ -40,6 +40,7 @@ struct SplitParams {
   int32_t window;
   int32_t k_group_shift;     // log2(k_group)
   int32_t residual_len;
+  int32_t residual_policy;   // DA_RESIDUAL_*
   int32_t max_seq_len;       // plan bound: seq_lens are clamped to [0, max_seq_len]
   int32_t num_pages;         // paged: page ids are clamped to [0, num_pages)
   float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
@@ -118,6 +119,18 @@ __device__ __forceinline__ void decode_workgroup(const SplitParams& p, int* b, i
   }
   *h = bh % p.num_kv_heads;
   *b = bh / p.num_kv_heads;
+}
+
+// Tokens of a request of length T held as int8 codes (the oldest n_q); the
+// rest are bf16 residual rows t - n_q (DA_RESIDUAL_* in the header).
+__device__ __forceinline__ int quantized_len(const SplitParams& p, int T) {
+  const int R = p.residual_len;
+  if (p.residual_policy == DA_RESIDUAL_GROUPS) {
+    const int excess = T - R;
+    const int G = 1 << p.k_group_shift;
+    return excess > 0 ? ((excess + G - 1) >> p.k_group_shift) << p.k_group_shift : 0;
+  }
+  return T - min(T, R);
 }
 
 __device__ __forceinline__ void split_range(int n_vis, int s, int chunk, int* begin, int* end) {

@@ -62,6 +62,8 @@ constexpr int kMaxChunk = 1024;
 constexpr int kRowAlign = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for b > 0 and any sign of a
+int64_t ceil_div_i64(int64_t a, int64_t b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace
@@ -92,14 +94,23 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   } else if (p.mask_kind == DA_MASK_CAUSAL) {
     if (p.window != 0 || p.n_sink != 0) return DA_ERR_INVALID;
   }
+  if (p.reserved0 != 0) return DA_ERR_INVALID;
   if (p.kv_format == DA_KV_I8) {
     if (p.k_group <= 0 || p.residual_len < 0) return DA_ERR_INVALID;
+    if (p.residual_policy != DA_RESIDUAL_WINDOW && p.residual_policy != DA_RESIDUAL_GROUPS)
+      return DA_ERR_INVALID;
+    // closing G rows must leave a row in the residual
+    if (p.residual_policy == DA_RESIDUAL_GROUPS && p.k_group > p.residual_len) return DA_ERR_INVALID;
     if (p.layout == DA_LAYOUT_CONTIG_NHD) {
-      const int64_t nq_max = p.max_seq_len - std::min(p.max_seq_len, p.residual_len);
+      // n_q grows with T, so its largest value is at T = max_seq_len
+      const int64_t excess = (int64_t)p.max_seq_len - p.residual_len;
+      const int64_t nq_max = p.residual_policy == DA_RESIDUAL_GROUPS
+                                 ? p.k_group * std::max<int64_t>(0, ceil_div_i64(excess, p.k_group))
+                                 : std::max<int64_t>(0, excess);
       if (p.kv_capacity < nq_max) return DA_ERR_INVALID;
     }
   } else {
-    if (p.k_group != 0 || p.residual_len != 0) return DA_ERR_INVALID;
+    if (p.k_group != 0 || p.residual_len != 0 || p.residual_policy != 0) return DA_ERR_INVALID;
     if (p.layout == DA_LAYOUT_CONTIG_NHD && p.kv_capacity < p.max_seq_len) return DA_ERR_INVALID;
   }
 

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
-  const int n_q = I8 ? T - min(T, p.residual_len) : T;
+  const int n_q = I8 ? quantized_len(p, T) : T;
   const int64_t base = (((int64_t)b * p.num_kv_heads + h) * p.num_splits + s) * p.chunk;
   for (int tile = begin + wave * TW; tile < end; tile += NWAVES * TW) {
     for (int j = lane; j < TW; j += 64) {

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
-  const int n_q = FMT == DA_KV_I8 ? T - min(T, p.residual_len) : T;
+  const int n_q = FMT == DA_KV_I8 ? quantized_len(p, T) : T;
 
   const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
   if (begin >= end) {   // empty split: the identity state, written before any arithmetic

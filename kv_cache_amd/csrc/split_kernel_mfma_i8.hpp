@@ -140,7 +140,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
-  const int n_q = T - min(T, p.residual_len);
+  const int n_q = quantized_len(p, T);
   // first ordinal whose position is >= n_q
   const int o_res = n_q <= vis.ns ? n_q : max(vis.ns, n_q - vis.gap);
   const int mid = min(max(o_res, begin), end);

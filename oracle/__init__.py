@@ -34,4 +34,7 @@ from .state import (  # noqa: F401
     lse_merge, workspace_bytes_mlu, workspace_bytes_lse_o,
 )
 from .attend import attend, gather_rows, split_attend  # noqa: F401
-from .quant import quantize_symmetric_rows, write_int8_cache_oracle  # noqa: F401
+from .quant import (  # noqa: F401
+    quantize_symmetric_rows, write_int8_cache_oracle, quantized_count, kivi_empty_state,
+    kivi_append, kivi_state_parts, kivi_state_from_parts,
+)

@@ -12,9 +12,10 @@ and for an empty A_b (length 0 or everything masked): ``O = 0``, ``LSE = -inf``
 rows are located through ``address`` with the oracle's own translation and
 decoded from the stored bytes (``numerics``); int8 rows are ``code * scale``
 with the K scale of the token's 128-token group and channel and the V scale
-of the token (M8.6 §0x03B, §0x03C), and the newest ``min(T_b, R)`` tokens
-come from the bf16 residual (M8.6 §0x06B/§0x06C: one shared softmax over
-both regions).
+of the token (M8.6 §0x03B, §0x03C), and the tokens from n_q on (the newest
+``min(T_b, R)`` under the window policy, the unclosed tail under the group
+policy; ``quant.quantized_count``) come from the bf16 residual, row t - n_q
+(M8.6 §0x06B/§0x06C: one shared softmax over both regions).
 
 ``split_attend`` is the Flash-Decoding reference: it summarizes each
 physical split of the visible positions (M4.5 §0x02A, §0x03I), merges the
@@ -29,6 +30,7 @@ import numpy as np
 
 from .address import nhd_offset, paged_nhd_offset
 from .numerics import decode, decode_bf16, decode_f16
+from .quant import quantized_count
 from .state import EMPTY, finalize, merge_state, summarize_allowed
 from .visibility import visible_positions
 
@@ -70,7 +72,7 @@ def gather_rows(prob, buf, b: int, h_kv: int, positions):
         T = int(buf["seq_lens"][b])
         R = prob.residual_len
         G = prob.k_group
-        n_q = T - min(T, R)
+        n_q = quantized_count(T, getattr(prob, "residual_policy", "window"), G, R)
         K = np.empty((n, D), dtype=np.float64)
         V = np.empty((n, D), dtype=np.float64)
         offs = np.empty(n, dtype=np.int64)

@@ -66,6 +66,7 @@ class Problem:
     num_splits: int = 0            # 0 -> auto
     k_group: int = 0               # int8 only: tokens per K scale group
     residual_len: int = 0          # int8 only: bf16 residual rows
+    residual_policy: str = "window"  # int8 only: "window" | "groups" (which tokens are bf16)
 
     @property
     def group(self) -> int:
@@ -253,16 +254,34 @@ def _codes(x: np.ndarray, s_eff: np.ndarray) -> np.ndarray:
     return c.astype(np.int8)
 
 
+def quantized_tokens(T: int, k_group: int, residual_len: int, policy: str) -> int:
+    """Tokens stored as int8 at length T: "window" keeps the newest
+    min(T, R) as bf16; "groups" closes whole groups of k_group tokens as soon
+    as more than R tokens are unclosed."""
+    if policy == "window":
+        return T - min(T, residual_len)
+    closed = 0
+    while T - closed > residual_len:
+        closed += k_group
+    return closed
+
+
 def write_int8_cache(k_f32: np.ndarray, v_f32: np.ndarray, seq_lens, k_group: int,
-                     residual_len: int, T_cap: int, g: np.random.Generator):
+                     residual_len: int, T_cap: int, g: np.random.Generator,
+                     policy: str = "window"):
     """Quantize per request: tokens ``[0, n_q)`` to int8 codes, the rest to bf16.
 
     K: one scale per (group of ``k_group`` quantized tokens, channel), taken over
     the tokens of the group that are quantized (a partial last group uses only
-    its own rows).  V: one scale per token over its channels.
+    its own rows).  V: one scale per token over its channels.  Under the
+    "groups" policy every token was appended as a bf16 row, so the values are
+    rounded to bf16 before quantization.
     Slots that hold no visible data are filled with garbage (codes) or NaN
     (scales, residual rows).
     """
+    if policy == "groups":
+        k_f32 = (bf16_bits(k_f32).astype(np.uint32) << 16).view(np.float32)
+        v_f32 = (bf16_bits(v_f32).astype(np.uint32) << 16).view(np.float32)
     B, _, H_kv, D = k_f32.shape
     R, G = residual_len, k_group
     n_groups = (T_cap + G - 1) // G
@@ -274,8 +293,8 @@ def write_int8_cache(k_f32: np.ndarray, v_f32: np.ndarray, seq_lens, k_group: in
     vr = np.full((B, max(R, 1), H_kv, D), 0x7FC0, dtype=np.uint16)
     for b in range(B):
         T = int(seq_lens[b])
-        n_res = min(T, R)
-        n_q = T - n_res
+        n_q = quantized_tokens(T, G, R, policy)
+        n_res = T - n_q
         if n_q > 0:
             kq = k_f32[b, :n_q].astype(np.float64)      # [n_q, H, D]
             for j in range((n_q + G - 1) // G):
@@ -298,7 +317,7 @@ def make_int8(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
               kv_capacity: int | None = None, mask_kind: str = "causal",
               n_sink: int = 0, window: int = 0, num_splits: int = 0,
               outlier_channels: int = 3, outlier_mult: float = 20.0,
-              values=None) -> Workload:
+              values=None, residual_policy: str = "window") -> Workload:
     """int8 K (per channel per group) / int8 V (per token) / bf16 residual.
 
     ``outlier_channels`` channels per (batch, K/V head), drawn once from the
@@ -320,13 +339,14 @@ def make_int8(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
                     arr[b, :, h, ch] *= np.float32(outlier_mult)
     else:
         kf, vf = (np.asarray(a, dtype=np.float32) for a in values)
-    bufs = write_int8_cache(kf, vf, seq_lens, k_group, residual_len, T_cap, g)
+    bufs = write_int8_cache(kf, vf, seq_lens, k_group, residual_len, T_cap, g, residual_policy)
     bufs.update(q=q, seq_lens=seq_lens)
     prob = Problem(batch=B, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
                    q_dtype="bf16", kv_format="i8", layout="contig",
                    kv_capacity=T_cap, max_seq_len=int(seq_lens.max(initial=0)),
                    mask_kind=mask_kind, n_sink=n_sink, window=window,
-                   num_splits=num_splits, k_group=k_group, residual_len=residual_len)
+                   num_splits=num_splits, k_group=k_group, residual_len=residual_len,
+                   residual_policy=residual_policy)
     w = Workload(prob, bufs)
     w.float_kv = (kf, vf)
     return w
@@ -371,3 +391,18 @@ def config(i: int, seed: int = 0, num_splits: int = 0, **over) -> Workload:
     w.name = f"cfg{i}"
     w.note = CONFIG_NAMES[i]
     return w
+
+
+def append_rows(seed: int, B: int, H_kv: int, D: int, outlier_channels: int = 3,
+                outlier_mult: float = 20.0):
+    """One new token per request for an append: bf16 bit patterns of K and V,
+    ``[B, H_kv, D]`` each, N(0,1) with the outlier channels scaled."""
+    g = rng(seed + 7919)
+    kf = g.standard_normal(size=(B, H_kv, D), dtype=np.float32)
+    vf = g.standard_normal(size=(B, H_kv, D), dtype=np.float32)
+    for arr in (kf, vf):
+        for b in range(B):
+            for h in range(H_kv):
+                ch = g.choice(D, size=outlier_channels, replace=False)
+                arr[b, h, ch] *= np.float32(outlier_mult)
+    return bf16_bits(kf), bf16_bits(vf)

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) >= {"decode_attn_plan", "decode_attn_run", "decode_attn_combine",
                           "decode_attn_forward", "decode_attn_workspace_init",
-                          "decode_attn_schedule",
+                          "decode_attn_schedule", "decode_attn_append",
                           "decode_attn_trace_indices", "decode_attn_reason",
                           "decode_attn_status_string"}
     for n in names:
@@ -37,8 +37,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(ka.Problem) == 22 * 4
-    assert ctypes.sizeof(ka.Plan) == 8 + 88 + 16 + 8 + 16
+    assert ctypes.sizeof(ka.Problem) == 24 * 4
+    assert ctypes.sizeof(ka.Plan) == 8 + 96 + 16 + 8 + 16
     assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 8
 
 
@@ -216,3 +216,27 @@ def test_schedule_rejects_bad_arguments():
     pl.num_splits += 1
     with pytest.raises(ka.DecodeAttnError):
         ka.decode_attn_schedule(pl, [50, 50])
+
+
+def test_append_rejects_unsupported_plans_and_null_buffers_without_gpu():
+    st, pl, ws, _ = plan(P(kv_format="i8", k_group=128, residual_len=128, residual_policy="window"))
+    assert st == ka.DA_OK
+    assert ka.decode_attn_append(pl, *([16] * 9), check=False) == ka.DA_ERR_UNSUPPORTED
+    st, pl, ws, _ = plan(P(kv_format="i8", k_group=128, residual_len=128, residual_policy="groups"))
+    assert st == ka.DA_OK
+    assert ka.decode_attn_append(pl, *([16] * 8), None, check=False) == ka.DA_ERR_INVALID
+    pl.chunk += 16
+    assert ka.decode_attn_append(pl, *([16] * 9), check=False) == ka.DA_ERR_PLAN_MISMATCH
+
+
+def test_groups_policy_plan_checks():
+    # closing G rows must leave a residual row: G <= R
+    st, _, _, _ = plan(P(kv_format="i8", k_group=128, residual_len=64, residual_policy="groups"))
+    assert st == ka.DA_ERR_INVALID
+    # capacity must hold G * ceil((max_seq_len - R) / G) quantized rows
+    st, _, _, _ = plan(P(kv_format="i8", k_group=128, residual_len=128, residual_policy="groups",
+                         max_seq_len=4097, kv_capacity=4000))
+    assert st == ka.DA_ERR_INVALID
+    st, _, _, _ = plan(P(kv_format="i8", k_group=128, residual_len=128, residual_policy="groups",
+                         max_seq_len=4097, kv_capacity=4096))
+    assert st == ka.DA_OK

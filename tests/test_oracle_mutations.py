@@ -126,3 +126,44 @@ def test_mutation_empty_request_reads_a_row(monkeypatch):
         return vis_mod.visible_positions(max(int(T), 1), mask_kind, n_sink, window)
     monkeypatch.setattr(attend_mod, "visible_positions", bad)
     assert _fails([tm.test_empty_and_all_masked_rows])
+
+
+quant_mod = importlib.import_module("oracle.quant")
+
+
+def _kivi_pins():
+    from tests import test_kivi_append as tk
+    fns = [lambda c=c: tk.test_closure_counts_follow_the_pages_rule(c) for c in tk._golden()["cases"]]
+    fns += [lambda: tk.test_sequential_appends_equal_the_static_writer(128, 128, 300),
+            lambda: tk.test_sequential_appends_equal_the_static_writer(32, 128, 300)]
+    return fns
+
+
+def test_mutation_kivi_closes_at_residual_instead_of_above(monkeypatch):
+    orig = quant_mod.quantized_count
+
+    def bad(T, policy, k_group, residual_len):
+        if policy == "groups":
+            return k_group * max(0, -(-(int(T) - residual_len + 1) // k_group))
+        return orig(T, policy, k_group, residual_len)
+    monkeypatch.setattr(quant_mod, "quantized_count", bad)
+    from tests import test_kivi_append as tk
+    monkeypatch.setattr(tk, "quantized_count", bad)
+    assert _fails(_kivi_pins())
+
+
+def test_mutation_kivi_append_v_scale_per_channel(monkeypatch):
+    orig = quant_mod.quantize_symmetric_rows
+    calls = {"n": 0}
+
+    def bad(x, *a, **k):
+        # every second call (the V call of each head) quantizes the transposed
+        # block: one scale per channel instead of per token
+        calls["n"] += 1
+        if calls["n"] % 2 == 0 and x.shape[0] != x.shape[1]:
+            c, s = orig(np.asarray(x).T, *a, **k)
+            return c.T, np.resize(s, x.shape[0]).astype(s.dtype)
+        return orig(x, *a, **k)
+    monkeypatch.setattr(quant_mod, "quantize_symmetric_rows", bad)
+    from tests import test_kivi_append as tk
+    assert _fails([lambda: tk.test_sequential_appends_equal_the_static_writer(32, 128, 300)])
