@@ -251,6 +251,49 @@ class GpuWorkload:
                 "algorithmic_bytes": self.call_bytes}
 
 
+def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, steps=50):
+    """decode_attn_append on the int8 cache shape of the sink+window workload
+    (group-closing residual, R = G = 128): one call where no request closes a
+    group and one where every request closes one (all of its residual)."""
+    import synth
+    cap = T + G
+    prob = synth.Problem(batch=B, num_q_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=D, kv_format="i8",
+                         kv_capacity=cap, max_seq_len=cap, k_group=G, residual_len=G,
+                         residual_policy="groups")
+    _, plan, _, _ = ka.decode_attn_plan(ka.problem_from(prob))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    k = torch.randint(-127, 128, (B, cap, Hkv, D), device="cuda", dtype=torch.int8, generator=g)
+    v = torch.randint(-127, 128, (B, cap, Hkv, D), device="cuda", dtype=torch.int8, generator=g)
+    ks = (torch.rand((B, cap // G + 1, Hkv, D), device="cuda", generator=g) * 0.04 + 0.005).half()
+    vs = (torch.rand((B, cap, Hkv), device="cuda", generator=g) * 0.04 + 0.005).half()
+    kr = torch.randn((B, G, Hkv, D), device="cuda", generator=g).bfloat16()
+    vr = torch.randn((B, G, Hkv, D), device="cuda", generator=g).bfloat16()
+    kn = torch.randn((B, Hkv, D), device="cuda", generator=g).bfloat16()
+    vn = torch.randn((B, Hkv, D), device="cuda", generator=g).bfloat16()
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    out = {}
+    # lengths before the append: residual 100 rows (no closure) / 128 rows (closure)
+    for name, t in (("no_closure", T - 28), ("closure", T)):
+        sl = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        call = lambda: ka.decode_attn_append(plan, kn, vn, k, v, ks, vs, kr, vr, sl, status, st)
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(e0.elapsed_time(e1) / steps * 1000, 2)
+    assert int(status.max()) == 0
+    out["config"] = (f"B={B} H_kv={Hkv} d={D} int8 cache T={T}, R=G={G}; closure = quantize "
+                     f"{G} residual rows per (b, h_kv): K per channel, V per row")
+    return out
+
+
 def hbm_probe(torch, nbytes=512 << 20):
     """Practical read ceiling of the box: a plain streaming-read kernel; then
     one copy of known size, the reference for the profiler's byte counters."""
@@ -411,6 +454,7 @@ def main():
         others["int8_sink_window"] = wi.report(
             "int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, 4 sinks + window 4096")
         del wi
+        others["int8_append"] = append_timing(torch, ka)
         wt = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
         others["tiny_fp32"] = wt.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4")
         del wt
