@@ -95,7 +95,9 @@ typedef int32_t da_status;
 #define DA_R_INDEX_RANGE (1ull << 9)   /* a tensor exceeds the 2^31-element index range */
 #define DA_R_DEVICE      (1ull << 10)  /* current device is not gfx950 or cannot be queried */
 #define DA_R_MASK_KIND   (1ull << 11)  /* unknown mask program                        */
-#define DA_NUM_REASONS   12
+#define DA_R_QUERY_ROWS  (1ull << 12)  /* num_queries C: (H_q/H_kv)*C not in {1,2,4,8}, or
+                                          C > 1 with a mask other than causal        */
+#define DA_NUM_REASONS   13
 
 #define DA_MAX_SPLITS 4096
 
@@ -124,7 +126,7 @@ typedef struct da_problem {
   int32_t residual_len;      /* DA_KV_I8: bf16 residual rows R >= 0; else 0        */
   int32_t num_cus;           /* 0 -> query the current device; > 0: plan for this many CUs */
   int32_t residual_policy;   /* DA_KV_I8: DA_RESIDUAL_*; else 0                     */
-  int32_t reserved0;         /* must be 0                                           */
+  int32_t num_queries;       /* C query rows per request (0 -> 1); see da_args q     */
 } da_problem;
 
 /* A frozen plan: a plain value the caller owns and may copy; nothing to free.
@@ -143,7 +145,11 @@ typedef struct da_plan {
 } da_plan;
 
 /* Per-call device buffers.  Layouts (row-major, no padding):
- *   q           [B, H_q, D]                q_dtype (the single decode row, squeezed)
+ *   q           [B, C, H_q, D]             q_dtype; C = num_queries (C = 1: the decode row).
+ *               Query row i of request b sits at position T_b - C + i and sees keys
+ *               [0, T_b - C + i + 1): bottom-right causal alignment ("M4.5 ...",
+ *               sections 0x08B-0x08C: the C new rows are already in the cache, so
+ *               T_b counts them and a one-token decode is C = 1)
  *   k, v        contiguous: [B, T_cap, H_kv, D]; paged: [N_pages, P, H_kv, D]
  *               DA_KV_I8: int8 codes [B, T_cap, H_kv, D] of tokens t < n_q(b)
  *   k_scale     DA_KV_I8: fp16 [B, ceil(T_cap/k_group), H_kv, D]; group j scales
@@ -211,10 +217,11 @@ da_status decode_attn_schedule(const da_plan* plan, const int32_t* seq_lens_host
  * (m = -inf, l = 0, u = 0); l > 0 marks a valid state. */
 da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream);
 
-/* Launch the combine kernel: for each (b, h_q), fold its S states in
- * ascending split order and write out fp32 [B, H_q, D] = u/l and, when lse is
- * not NULL, lse fp32 [B, H_q] = m + ln(l); an all-masked row gets O = +0.0
- * and LSE = -inf. */
+/* Launch the combine kernel: for each (b, i, h_q), fold its S states in
+ * ascending split order and write out fp32 [B, C, H_q, D] = u/l and, when lse
+ * is not NULL, lse fp32 [B, C, H_q] = m + ln(l); an all-masked row gets
+ * O = +0.0 and LSE = -inf.  (State rows, out and lse rows are ordered
+ * (b, i, h_q); with C = 1 this is [B, H_q].) */
 da_status decode_attn_combine(const da_plan* plan, const void* workspace,
                               uint64_t workspace_bytes, float* out, float* lse,
                               void* stream);

@@ -29,7 +29,7 @@ KV_FORMATS = {"f32": 0, "bf16": 1, "i8": 2}
 LAYOUTS = {"contig": 0, "paged": 1}
 MASKS = {"causal": 0, "sink_window": 1}
 RESIDUAL_POLICIES = {"window": 0, "groups": 1}
-NUM_REASONS = 12
+NUM_REASONS = 13
 
 
 class Problem(ctypes.Structure):
@@ -38,7 +38,7 @@ class Problem(ctypes.Structure):
         "out_dtype", "kv_format", "layout", "kv_capacity", "page_size", "max_pages_per_seq",
         "num_pages", "max_seq_len", "mask_kind", "n_sink", "window")] + [
         ("softmax_scale", ctypes.c_float)] + [(n, ctypes.c_int32) for n in (
-            "num_splits", "k_group", "residual_len", "num_cus", "residual_policy", "reserved0")]
+            "num_splits", "k_group", "residual_len", "num_cus", "residual_policy", "num_queries")]
 
 
 class Plan(ctypes.Structure):
@@ -154,7 +154,8 @@ def problem_from(p, num_cus: int = 0) -> Problem:
         max_seq_len=p.max_seq_len, mask_kind=enum(p.mask_kind, MASKS), n_sink=p.n_sink,
         window=p.window, softmax_scale=p.softmax_scale, num_splits=p.num_splits,
         k_group=p.k_group, residual_len=p.residual_len, num_cus=num_cus,
-        residual_policy=enum(getattr(p, "residual_policy", 0), RESIDUAL_POLICIES))
+        residual_policy=enum(getattr(p, "residual_policy", 0), RESIDUAL_POLICIES),
+        num_queries=int(getattr(p, "num_queries", 1) or 1))
 
 
 def decode_attn_plan(problem: Problem, check: bool = True):

@@ -85,7 +85,7 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.block_table = a->block_table;
   sp.seq_lens = a->seq_lens;
   sp.work_order = a->work_order;
-  const uint64_t n_states = (uint64_t)p.batch * p.num_q_heads * plan->num_splits;
+  const uint64_t n_states = (uint64_t)da::output_rows(p) * plan->num_splits;
   float* ws = static_cast<float*>(a->workspace);
   sp.ws_u = ws;
   sp.ws_m = ws ? ws + n_states * p.head_dim_v : nullptr;
@@ -96,6 +96,8 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.lse = nullptr;
   sp.num_q_heads = p.num_q_heads;
   sp.num_kv_heads = p.num_kv_heads;
+  sp.num_queries = p.num_queries;
+  sp.q_group_shift = log2_exact(p.num_q_heads / p.num_kv_heads);
   sp.num_splits = plan->num_splits;
   sp.chunk = plan->chunk;
   sp.kv_capacity = p.kv_capacity;
@@ -154,7 +156,9 @@ bool dispatch_d(int d, int g, const da::SplitParams& sp, unsigned grid, hipStrea
 
 template <bool FUSED>
 bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
-  const int g = p.num_q_heads / p.num_kv_heads;
+  // A workgroup serves the C query rows of each of its H_q/H_kv heads: C*g
+  // "virtual heads" sharing one K/V head.
+  const int g = p.num_q_heads / p.num_kv_heads * p.num_queries;
   const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
   switch (p.kv_format) {
     case DA_KV_F32:
@@ -301,11 +305,11 @@ extern "C" da_status decode_attn_combine(const da_plan* plan, const void* worksp
   if (!out) return DA_ERR_INVALID;
   if (!workspace || workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
   if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
-  const uint64_t n_states = (uint64_t)p.batch * p.num_q_heads * plan->num_splits;
+  const uint64_t n_states = (uint64_t)da::output_rows(p) * plan->num_splits;
   const float* ws_u = static_cast<const float*>(workspace);
   const float* ws_m = ws_u + n_states * p.head_dim_v;
   const float* ws_l = ws_m + n_states;
-  const unsigned rows = (unsigned)(p.batch * p.num_q_heads);
+  const unsigned rows = (unsigned)da::output_rows(p);
   const size_t lds = (size_t)plan->num_splits * sizeof(float);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();

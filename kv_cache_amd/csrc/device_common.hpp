@@ -28,6 +28,8 @@ struct SplitParams {
   float* out;                // single-launch mode: O [B, H_q, D]
   float* lse;                // single-launch mode: LSE [B, H_q] or null
   int32_t num_q_heads;
+  int32_t num_queries;       // C query rows per request (bottom-right causal)
+  int32_t q_group_shift;     // log2(H_q / H_kv)
   int32_t num_kv_heads;
   int32_t num_splits;
   int32_t chunk;
@@ -119,6 +121,22 @@ __device__ __forceinline__ void decode_workgroup(const SplitParams& p, int* b, i
   }
   *h = bh % p.num_kv_heads;
   *b = bh / p.num_kv_heads;
+}
+
+// A workgroup of K/V head h serves "virtual heads" j = 0 .. C*g-1: query row
+// i = j / g of request b, query head h*g + j % g (g = H_q/H_kv).  Its row of
+// q, of the split states and of O/LSE, ordered (b, i, h_q):
+__device__ __forceinline__ int64_t out_row(const SplitParams& p, int b, int h, int j) {
+  const int i = j >> p.q_group_shift;
+  const int gi = j - (i << p.q_group_shift);
+  return ((int64_t)b * p.num_queries + i) * p.num_q_heads + ((int64_t)h << p.q_group_shift) + gi;
+}
+// Visible ordinals of virtual head j: query row i sits C-1-i positions before
+// the last one and sees keys up to its own (bottom-right causal alignment,
+// "M4.5 ...", section 0x08B).  Multi-row calls use the causal mask only, where
+// ordinals are positions.
+__device__ __forceinline__ int row_limit(const SplitParams& p, int n_vis, int j) {
+  return n_vis - (p.num_queries - 1 - (j >> p.q_group_shift));
 }
 
 // Tokens of a request of length T held as int8 codes (the oldest n_q); the

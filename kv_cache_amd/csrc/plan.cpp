@@ -94,7 +94,8 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   } else if (p.mask_kind == DA_MASK_CAUSAL) {
     if (p.window != 0 || p.n_sink != 0) return DA_ERR_INVALID;
   }
-  if (p.reserved0 != 0) return DA_ERR_INVALID;
+  if (p.num_queries < 0) return DA_ERR_INVALID;
+  if (p.num_queries == 0) p.num_queries = 1;
   if (p.kv_format == DA_KV_I8) {
     if (p.k_group <= 0 || p.residual_len < 0) return DA_ERR_INVALID;
     if (p.residual_policy != DA_RESIDUAL_WINDOW && p.residual_policy != DA_RESIDUAL_GROUPS)
@@ -119,6 +120,12 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (p.head_dim_qk != 64 && p.head_dim_qk != 128) reasons |= DA_R_HEAD_DIM;
   if (p.head_dim_v != p.head_dim_qk) reasons |= DA_R_HEAD_DIM_V;
   if (g != 1 && g != 2 && g != 4 && g != 8) reasons |= DA_R_GQA_GROUP;
+  {
+    const int64_t gc = (int64_t)g * p.num_queries;
+    if ((gc != 1 && gc != 2 && gc != 4 && gc != 8) ||
+        (p.num_queries > 1 && p.mask_kind != DA_MASK_CAUSAL))
+      reasons |= DA_R_QUERY_ROWS;
+  }
   const bool fmt_ok = p.kv_format == DA_KV_F32 || p.kv_format == DA_KV_BF16 || p.kv_format == DA_KV_I8;
   if (!fmt_ok) reasons |= DA_R_KV_FORMAT;
   if (fmt_ok) {
@@ -172,7 +179,8 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (reasons) return DA_ERR_UNSUPPORTED;
 
   if (p.softmax_scale == 0.f) p.softmax_scale = 1.0f / std::sqrt((float)p.head_dim_qk);
-  const uint64_t ws = da::workspace_bytes_for(p.batch, p.num_q_heads, p.num_kv_heads, S, p.head_dim_v);
+  const uint64_t ws = da::workspace_bytes_for((int64_t)p.batch * p.num_queries * p.num_q_heads,
+                                              (int64_t)p.batch * p.num_kv_heads, S, p.head_dim_v);
 
   da_plan plan;
   std::memset(&plan, 0, sizeof(plan));
@@ -202,6 +210,7 @@ extern "C" const char* decode_attn_reason(int bit) {
       "grid or trace size exceeds the index range",
       "current device is not gfx950 or cannot be queried",
       "unknown mask program",
+      "(H_q/H_kv) * num_queries must be 1, 2, 4 or 8, and num_queries > 1 needs the causal mask",
   };
   if (bit < 0 || bit >= DA_NUM_REASONS) return "unknown reason bit";
   return text[bit];

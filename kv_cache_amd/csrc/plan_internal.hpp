@@ -25,18 +25,21 @@ inline uint64_t plan_hash(const da_plan& p) {
 
 inline bool plan_intact(const da_plan* p) { return p && p->key == plan_hash(*p); }
 
-// Workspace layout: u [B,H_q,S,D] f32, m [B,H_q,S] f32, l [B,H_q,S] f32, then
-// (at a 256-byte boundary) one uint32 arrival counter per (b, h_kv).
-inline uint64_t states_bytes_raw(int64_t B, int64_t Hq, int64_t S, int64_t Dv) {
-  return (uint64_t)(B * Hq * S * (Dv + 2) * 4);
+// Workspace layout: u [rows,S,D] f32, m [rows,S] f32, l [rows,S] f32 with
+// rows = B*C*H_q ordered (b, i, h_q), then (at a 256-byte boundary) one uint32
+// arrival counter per (b, h_kv).
+inline uint64_t states_bytes_raw(int64_t rows, int64_t S, int64_t Dv) {
+  return (uint64_t)(rows * S * (Dv + 2) * 4);
 }
 inline uint64_t round_up_256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
-inline uint64_t states_bytes(const da_plan& p) {
-  return round_up_256(states_bytes_raw(p.problem.batch, p.problem.num_q_heads, p.num_splits,
-                                       p.problem.head_dim_v));
+inline int64_t output_rows(const da_problem& p) {
+  return (int64_t)p.batch * p.num_queries * p.num_q_heads;
 }
-inline uint64_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t Dv) {
-  return round_up_256(states_bytes_raw(B, Hq, S, Dv)) + round_up_256((uint64_t)(B * Hkv * 4));
+inline uint64_t states_bytes(const da_plan& p) {
+  return round_up_256(states_bytes_raw(output_rows(p.problem), p.num_splits, p.problem.head_dim_v));
+}
+inline uint64_t workspace_bytes_for(int64_t rows, int64_t groups, int64_t S, int64_t Dv) {
+  return round_up_256(states_bytes_raw(rows, S, Dv)) + round_up_256((uint64_t)(groups * 4));
 }
 
 // Element size in bytes of one K/V row element as stored in k/v.

@@ -55,14 +55,15 @@ __device__ __forceinline__ float get_shared_state(const float* a) {
 }
 
 template <int G, int D, int NWAVES, bool SHARED>
-__device__ __forceinline__ void write_identity(const SplitParams& p, int64_t st0) {
+__device__ __forceinline__ void write_identity(const SplitParams& p, int b, int h, int s) {
   for (int idx = threadIdx.x; idx < G * D; idx += NWAVES * 64) {
     const int i = idx / D, c = idx % D;
-    put_state<SHARED>(p.ws_u + (st0 + (int64_t)i * p.num_splits) * D + c, 0.f);
+    put_state<SHARED>(p.ws_u + (out_row(p, b, h, i) * p.num_splits + s) * D + c, 0.f);
   }
   if (threadIdx.x < G) {
-    put_state<SHARED>(p.ws_m + st0 + (int64_t)threadIdx.x * p.num_splits, -INFINITY);
-    put_state<SHARED>(p.ws_l + st0 + (int64_t)threadIdx.x * p.num_splits, 0.f);
+    const int64_t st = out_row(p, b, h, threadIdx.x) * p.num_splits + s;
+    put_state<SHARED>(p.ws_m + st, -INFINITY);
+    put_state<SHARED>(p.ws_l + st, 0.f);
   }
 }
 
@@ -78,7 +79,7 @@ struct WaveStates {
 // folded over the waves, with the empty branch taken by weight 0) and store
 // (m, l, u) of the split; m is converted to natural-log units.
 template <int G, int D, int NWAVES, bool SHARED>
-__device__ __forceinline__ void merge_waves_and_store(const SplitParams& p, int64_t st0,
+__device__ __forceinline__ void merge_waves_and_store(const SplitParams& p, int b, int h, int s,
                                                       const WaveStates<G, D, NWAVES>& sh) {
   constexpr float kLn2 = 0.69314718055994530942f;
   for (int idx = threadIdx.x; idx < G * D; idx += NWAVES * 64) {
@@ -94,7 +95,7 @@ __device__ __forceinline__ void merge_waves_and_store(const SplitParams& p, int6
       acc = fmaf(f, sh.u[w][i][c], acc);
       L = fmaf(f, sh.l[w][i], L);
     }
-    const int64_t st = st0 + (int64_t)i * p.num_splits;
+    const int64_t st = out_row(p, b, h, i) * p.num_splits + s;
     put_state<SHARED>(p.ws_u + st * D + c, acc);
     if (c == 0) {
       put_state<SHARED>(p.ws_m + st, M == -INFINITY ? -INFINITY : M * kLn2);
@@ -222,7 +223,7 @@ __device__ __forceinline__ void finish_split(const SplitParams& p, int b, int h)
     __syncthreads();
     if (!is_last) return;
     const int wave = threadIdx.x >> 6;
-    for (int i = wave; i < G; i += NWAVES) fold_row<D>(p, (int64_t)b * p.num_q_heads + (int64_t)h * G + i);
+    for (int i = wave; i < G; i += NWAVES) fold_row<D>(p, out_row(p, b, h, i));
     if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

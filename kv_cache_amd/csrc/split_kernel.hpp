@@ -137,9 +137,8 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int n_q = FMT == DA_KV_I8 ? quantized_len(p, T) : T;
 
-  const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
   if (begin >= end) {   // empty split: the identity state, written before any arithmetic
-    write_identity<G, D, NWAVES, FUSED>(p, st0);
+    write_identity<G, D, NWAVES, FUSED>(p, b, h, s);
     finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   float qf[G][EPL];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int64_t qoff = ((int64_t)b * p.num_q_heads + h * G + i) * D + col0;
+    const int64_t qoff = out_row(p, b, h, i) * D + col0;
     if (FMT == DA_KV_F32) {
       const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff);
       qf[i][0] = x.x * p.qscale; qf[i][1] = x.y * p.qscale;
@@ -163,6 +162,10 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
       }
     }
   }
+
+  int lim[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) lim[i] = row_limit(p, vis.n_vis, i);
 
   float m[G], l[G], u[G][EPL];
 #pragma unroll
@@ -208,7 +211,8 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) part = fmaf(qf[i][e], kx[e], part);
         part = group_sum<LPR>(part);
-        sc[j][i] = cur[j].valid ? part : -INFINITY;
+        // virtual head i sees ordinals below its own limit (C > 1 rows)
+        sc[j][i] = (cur[j].valid && tile + j * RPW + r < lim[i]) ? part : -INFINITY;
       }
     }
     float pw[U][G];
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
     }
   }
   __syncthreads();
-  merge_waves_and_store<G, D, NWAVES, FUSED>(p, st0, sh);
+  merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
   finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 

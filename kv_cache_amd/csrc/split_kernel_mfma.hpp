@@ -91,16 +91,17 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
     qop[c] = make_uint4(0u, 0u, 0u, 0u);
     if (n < G)
       qop[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
-                                               ((int64_t)b * p.num_q_heads + h * G + n) * D + 32 * c + 8 * kg);
+                                               out_row(p, b, h, n) * D + 32 * c + 8 * kg);
   }
 
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
-  const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
+  // Score column n is virtual head n, with its own visible end (C > 1 rows).
+  const int end_n = min(end, row_limit(p, vis.n_vis, n));
   if (begin >= end) {
-    write_identity<G, D, NWAVES, FUSED>(p, st0);
+    write_identity<G, D, NWAVES, FUSED>(p, b, h, s);
     finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
     issue_k(ri, t.k);
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < end) ? acc[i] * p.qscale : -INFINITY;
+    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < end_n) ? acc[i] * p.qscale : -INFINITY;
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
     }
   }
   __syncthreads();
-  merge_waves_and_store<G, D, NWAVES, FUSED>(p, st0, sh);
+  merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
   finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 

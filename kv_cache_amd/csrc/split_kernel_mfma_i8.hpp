@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
       uint4 x = make_uint4(0u, 0u, 0u, 0u);
       if (n < G)
         x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
-                                            ((int64_t)b * p.num_q_heads + h * G + n) * D + 32 * c + 8 * kg);
+                                            out_row(p, b, h, n) * D + 32 * c + 8 * kg);
       q_lds[c][lane] = x;
     }
   }
@@ -134,9 +134,10 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
-  const int64_t st0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * p.num_splits + s;
+  // Score column n is virtual head n, with its own visible end (C > 1 rows).
+  const int lim_n = row_limit(p, vis.n_vis, n);
   if (begin >= end) {
-    write_identity<G, D, NWAVES, FUSED>(p, st0);
+    write_identity<G, D, NWAVES, FUSED>(p, b, h, s);
     finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   auto softmax = [&](const f32x4_t& acc, int tile, int lim, float (&pr)[4]) {
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < lim) ? acc[i] * p.qscale : -INFINITY;
+    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < min(lim, lim_n)) ? acc[i] * p.qscale : -INFINITY;
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     }
   }
   __syncthreads();
-  merge_waves_and_store<G, D, NWAVES, FUSED>(p, st0, sh);
+  merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
   finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 

@@ -25,7 +25,7 @@ values the pages print, closed forms, invariants or brute force, except the
 auto split heuristic, which lives in the GPU library and affects only speed.
 """
 from .numerics import decode_bf16, decode_f16, decode_f32  # noqa: F401
-from .visibility import visible_positions, visible_count  # noqa: F401
+from .visibility import visible_positions, visible_count, query_row_length  # noqa: F401
 from .address import (  # noqa: F401
     nhd_offset, hnd_offset, paged_nhd_offset, paged_hnd_offset, paged_segments,
 )

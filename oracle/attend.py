@@ -32,7 +32,7 @@ from .address import nhd_offset, paged_nhd_offset
 from .numerics import decode, decode_bf16, decode_f16
 from .quant import quantized_count
 from .state import EMPTY, finalize, merge_state, summarize_allowed
-from .visibility import visible_positions
+from .visibility import query_row_length, visible_positions
 
 
 def _scale(prob) -> float:
@@ -106,13 +106,21 @@ def attend(prob, buf, heads=None, with_trace: bool = False):
     Returns ``(O [B, H_q, D], LSE [B, H_q])`` in fp64, and with ``with_trace``
     also ``{(b, h_kv): (positions, offsets, regions)}`` of every row read.
     ``heads`` optionally restricts the work to a list of ``(b, h_q)`` rows
-    (the other rows are returned as NaN)."""
+    (the other rows are returned as NaN).
+
+    With ``prob.num_queries = C > 1`` (few-query decode / append, M4.5
+    §0x08B-§0x08C) q is ``[B, C, H_q, D]``, the results are ``[B, C, H_q, D]``
+    and ``[B, C, H_q]``, and query row i of request b sees the keys visible to
+    a decode at length ``T_b - C + 1 + i`` (``visibility.query_row_length``):
+    bottom-right causal alignment, the C new rows being the last C of the
+    cache.  The trace then lists the rows of the last query row (the union)."""
     B, Hq, Hkv, D = prob.batch, prob.num_q_heads, prob.num_kv_heads, prob.head_dim
+    C = int(getattr(prob, "num_queries", 1) or 1)
     g = Hq // Hkv
     scale = _scale(prob)
-    q = decode(buf["q"], prob.q_dtype).reshape(B, Hq, D)
-    O = np.full((B, Hq, D), np.nan)
-    LSE = np.full((B, Hq), np.nan)
+    q = decode(buf["q"], prob.q_dtype).reshape(B, C, Hq, D)
+    O = np.full((B, C, Hq, D), np.nan)
+    LSE = np.full((B, C, Hq), np.nan)
     trace = {}
     want = None
     if heads is not None:
@@ -121,28 +129,32 @@ def attend(prob, buf, heads=None, with_trace: bool = False):
             want.setdefault((int(b), int(hq) // g), []).append(int(hq) % g)
     for b in range(B):
         T = int(buf["seq_lens"][b])
-        A = visible_positions(T, prob.mask_kind, prob.n_sink, prob.window)
-        for h in range(Hkv):
-            if want is not None and (b, h) not in want:
-                continue
-            rows = range(g) if want is None else sorted(set(want[(b, h)]))
-            if A.size == 0:
+        for qi in range(C):
+            A = visible_positions(query_row_length(T, C, qi), prob.mask_kind, prob.n_sink, prob.window)
+            last = qi == C - 1
+            for h in range(Hkv):
+                if want is not None and (b, h) not in want:
+                    continue
+                rows = range(g) if want is None else sorted(set(want[(b, h)]))
+                if A.size == 0:
+                    for i in rows:
+                        O[b, qi, h * g + i] = 0.0
+                        LSE[b, qi, h * g + i] = -math.inf
+                    if with_trace and last:
+                        trace[(b, h)] = (A, np.zeros(0, np.int64), np.zeros(0, np.int8))
+                    continue
+                K, V, offs, region = gather_rows(prob, buf, b, h, A)
+                if with_trace and last:
+                    trace[(b, h)] = (A, offs, region)
                 for i in rows:
-                    O[b, h * g + i] = 0.0
-                    LSE[b, h * g + i] = -math.inf
-                if with_trace:
-                    trace[(b, h)] = (A, np.zeros(0, np.int64), np.zeros(0, np.int8))
-                continue
-            K, V, offs, region = gather_rows(prob, buf, b, h, A)
-            if with_trace:
-                trace[(b, h)] = (A, offs, region)
-            for i in rows:
-                s = (K @ q[b, h * g + i]) * scale
-                m = np.max(s)
-                w = np.exp(s - m)
-                l = np.sum(w)
-                O[b, h * g + i] = (w @ V) / l
-                LSE[b, h * g + i] = m + math.log(l)
+                    s = (K @ q[b, qi, h * g + i]) * scale
+                    m = np.max(s)
+                    w = np.exp(s - m)
+                    l = np.sum(w)
+                    O[b, qi, h * g + i] = (w @ V) / l
+                    LSE[b, qi, h * g + i] = m + math.log(l)
+    if C == 1:
+        O, LSE = O[:, 0], LSE[:, 0]
     if with_trace:
         return O, LSE, trace
     return O, LSE

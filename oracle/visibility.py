@@ -45,3 +45,12 @@ def visible_count(T: int, mask_kind: str = "causal", n_sink: int = 0,
     ks = min(n_sink, T)
     overlap = max(0, ks - max(0, T - window))
     return ks + min(window, T) - overlap
+
+
+def query_row_length(T_total: int, C: int, i: int) -> int:
+    """Few-query decode (M4.5 §0x08B): with T committed rows and C new rows,
+    new row i sits at absolute position T + i and may read positions
+    [0, T + i + 1).  The cache holds T_total = T + C rows (the new rows are
+    staged in it), so row i sees what a one-row decode of visible length
+    T_total - C + 1 + i sees (negative lengths see nothing)."""
+    return max(0, int(T_total) - int(C) + 1 + int(i))

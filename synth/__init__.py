@@ -67,6 +67,7 @@ class Problem:
     k_group: int = 0               # int8 only: tokens per K scale group
     residual_len: int = 0          # int8 only: bf16 residual rows
     residual_policy: str = "window"  # int8 only: "window" | "groups" (which tokens are bf16)
+    num_queries: int = 1           # C query rows per request (q is [B, C, H_q, D] when C > 1)
 
     @property
     def group(self) -> int:
@@ -132,7 +133,7 @@ def make_contiguous(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
                     dtype: str = "bf16", kv_capacity: int | None = None,
                     mask_kind: str = "causal", n_sink: int = 0, window: int = 0,
                     num_splits: int = 0, q_scale: float = 1.0,
-                    poison_tail: bool = True) -> Workload:
+                    poison_tail: bool = True, num_queries: int = 1) -> Workload:
     """q, K, V ~ N(0,1) (q optionally multiplied by ``q_scale`` before rounding).
 
     Token slots at or beyond ``seq_lens[b]`` (allocated, never visible) are
@@ -141,7 +142,8 @@ def make_contiguous(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
     seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
     T_cap = int(kv_capacity if kv_capacity is not None else max(1, int(seq_lens.max(initial=0))))
     g = rng(seed)
-    qf = g.standard_normal(size=(B, H_q, D), dtype=np.float32) * np.float32(q_scale)
+    qshape = (B, H_q, D) if num_queries == 1 else (B, num_queries, H_q, D)
+    qf = g.standard_normal(size=qshape, dtype=np.float32) * np.float32(q_scale)
     q = qf if dtype == "f32" else bf16_bits(qf)
     k = _draw(g, (B, T_cap, H_kv, D), dtype)
     v = _draw(g, (B, T_cap, H_kv, D), dtype)
@@ -155,7 +157,7 @@ def make_contiguous(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
                    q_dtype=dtype, kv_format=dtype, layout="contig",
                    kv_capacity=T_cap, max_seq_len=int(seq_lens.max(initial=0)),
                    mask_kind=mask_kind, n_sink=n_sink, window=window,
-                   num_splits=num_splits)
+                   num_splits=num_splits, num_queries=num_queries)
     return Workload(prob, dict(q=q, k=k, v=v, seq_lens=seq_lens))
 
 
@@ -166,7 +168,7 @@ def make_paged(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
                page_size: int = 16, dtype: str = "bf16",
                max_pages_per_seq: int | None = None, spare_frac: float = 0.10,
                mask_kind: str = "causal", n_sink: int = 0, window: int = 0,
-               num_splits: int = 0) -> Workload:
+               num_splits: int = 0, num_queries: int = 1) -> Workload:
     """Paged pool.  Every visible logical page maps to a seeded random
     permutation of the pool; everything that is allocated but not visible holds
     garbage:
@@ -185,7 +187,8 @@ def make_paged(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
     N_pages = max(1, used + spare)
     maxp = int(max_pages_per_seq if max_pages_per_seq is not None
                else max(1, max(pages_needed, default=1)))
-    qf = g.standard_normal(size=(B, H_q, D), dtype=np.float32)
+    qshape = (B, H_q, D) if num_queries == 1 else (B, num_queries, H_q, D)
+    qf = g.standard_normal(size=qshape, dtype=np.float32)
     q = qf if dtype == "f32" else bf16_bits(qf)
     perm = g.permutation(N_pages).astype(np.int32)
     table = np.empty((B, maxp), dtype=np.int32)
@@ -227,7 +230,7 @@ def make_paged(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
                    q_dtype=dtype, kv_format=dtype, layout="paged",
                    page_size=P, max_pages_per_seq=maxp, num_pages=N_pages,
                    max_seq_len=int(seq_lens.max(initial=0)), mask_kind=mask_kind,
-                   n_sink=n_sink, window=window, num_splits=num_splits)
+                   n_sink=n_sink, window=window, num_splits=num_splits, num_queries=num_queries)
     return Workload(prob, dict(q=q, k=k, v=v, block_table=table, seq_lens=seq_lens))
 
 
@@ -317,7 +320,7 @@ def make_int8(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
               kv_capacity: int | None = None, mask_kind: str = "causal",
               n_sink: int = 0, window: int = 0, num_splits: int = 0,
               outlier_channels: int = 3, outlier_mult: float = 20.0,
-              values=None, residual_policy: str = "window") -> Workload:
+              values=None, residual_policy: str = "window", num_queries: int = 1) -> Workload:
     """int8 K (per channel per group) / int8 V (per token) / bf16 residual.
 
     ``outlier_channels`` channels per (batch, K/V head), drawn once from the
@@ -328,7 +331,8 @@ def make_int8(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
     seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
     T_cap = int(kv_capacity if kv_capacity is not None else max(1, int(seq_lens.max(initial=0))))
     g = rng(seed)
-    q = bf16_bits(g.standard_normal(size=(B, H_q, D), dtype=np.float32))
+    qshape = (B, H_q, D) if num_queries == 1 else (B, num_queries, H_q, D)
+    q = bf16_bits(g.standard_normal(size=qshape, dtype=np.float32))
     if values is None:
         kf = g.standard_normal(size=(B, T_cap, H_kv, D), dtype=np.float32)
         vf = g.standard_normal(size=(B, T_cap, H_kv, D), dtype=np.float32)
@@ -346,7 +350,7 @@ def make_int8(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
                    kv_capacity=T_cap, max_seq_len=int(seq_lens.max(initial=0)),
                    mask_kind=mask_kind, n_sink=n_sink, window=window,
                    num_splits=num_splits, k_group=k_group, residual_len=residual_len,
-                   residual_policy=residual_policy)
+                   residual_policy=residual_policy, num_queries=num_queries)
     w = Workload(prob, bufs)
     w.float_kv = (kf, vf)
     return w

@@ -47,6 +47,18 @@ class DeviceWorkload:
                             block_table=d.get("block_table"), work_order=self.order)
 
 
+def _outputs(w):
+    """NaN-filled O and LSE, [B, H_q, D] / [B, H_q] or with a query-row axis
+    after B when the problem has C > 1 query rows."""
+    t = torch()
+    p = w.problem
+    C = getattr(p, "num_queries", 1)
+    lead = (p.batch,) if C == 1 else (p.batch, C)
+    out = t.full(lead + (p.num_q_heads, p.head_dim), float("nan"), dtype=t.float32, device="cuda")
+    lse = t.full(lead + (p.num_q_heads,), float("nan"), dtype=t.float32, device="cuda")
+    return out, lse
+
+
 def plan_for(w, num_splits=None):
     p = w.problem
     if num_splits is not None:
@@ -63,9 +75,7 @@ def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None)
     ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
     if poison_ws:
         ws.fill_(0xFF)                  # NaN everywhere: unwritten slots would show
-    B, Hq, D = w.problem.batch, w.problem.num_q_heads, w.problem.head_dim
-    out = t.full((B, Hq, D), float("nan"), dtype=t.float32, device="cuda")
-    lse = t.full((B, Hq), float("nan"), dtype=t.float32, device="cuda")
+    out, lse = _outputs(w)
     s = stream if stream is not None else t.cuda.current_stream().cuda_stream
     ka.decode_attn_run(plan, dw.args(ws, ws_bytes), s)
     ka.decode_attn_combine(plan, ws, ws_bytes, out, lse, s)
@@ -78,7 +88,7 @@ def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None)
 
 def states_bytes(plan):
     p = plan.problem
-    raw = p.batch * p.num_q_heads * plan.num_splits * (p.head_dim_v + 2) * 4
+    raw = p.batch * p.num_queries * p.num_q_heads * plan.num_splits * (p.head_dim_v + 2) * 4
     return (raw + 255) // 256 * 256
 
 
@@ -92,9 +102,7 @@ def forward(w, num_splits=None, dw=None, ws=None, want_ws=False, init=True):
     if ws is None:
         ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
         ws.fill_(0xFF)
-    B, Hq, D = w.problem.batch, w.problem.num_q_heads, w.problem.head_dim
-    out = t.full((B, Hq, D), float("nan"), dtype=t.float32, device="cuda")
-    lse = t.full((B, Hq), float("nan"), dtype=t.float32, device="cuda")
+    out, lse = _outputs(w)
     s = t.cuda.current_stream().cuda_stream
     if init:
         ka.decode_attn_workspace_init(plan, ws, ws_bytes, s)

@@ -240,3 +240,21 @@ def test_groups_policy_plan_checks():
     st, _, _, _ = plan(P(kv_format="i8", k_group=128, residual_len=128, residual_policy="groups",
                          max_seq_len=4097, kv_capacity=4096))
     assert st == ka.DA_OK
+
+
+def test_query_rows_plan_checks_and_workspace():
+    # C query rows per request: (H_q/H_kv) * C virtual heads per K/V head
+    st, pl, ws, rs = plan(P(num_queries=2))
+    assert st == ka.DA_OK and pl.problem.num_queries == 2
+    S = pl.num_splits
+    rup = lambda x: (x + 255) // 256 * 256
+    assert ws == rup(8 * 2 * 32 * S * 130 * 4) + rup(8 * 8 * 4)
+    st, pl, ws, rs = plan(P(num_queries=0))
+    assert st == ka.DA_OK and pl.problem.num_queries == 1
+    st, _, _, rs = plan(P(num_queries=4))              # 4 * 4 = 16 virtual heads
+    assert st == ka.DA_ERR_UNSUPPORTED and rs == 1 << 12
+    st, _, _, rs = plan(P(num_queries=2, mask_kind="sink_window", n_sink=4, window=64))
+    assert st == ka.DA_ERR_UNSUPPORTED and rs == 1 << 12
+    st, _, _, rs = plan(P(num_queries=8, num_q_heads=8, num_kv_heads=8))
+    assert st == ka.DA_OK
+    assert ka.decode_attn_reason(12)

@@ -255,3 +255,31 @@ def test_trace_lists_each_visible_row_once():
         for t, o in zip(pos, offs):
             page = w.buffers["block_table"][b, t // 4]
             assert o == ((page * 4 + t % 4) * 2 + h) * 8
+
+
+@pytest.mark.parametrize("C,T_list", [(3, [8, 3, 0]), (2, [5, 1]), (4, [6, 9])])
+def test_few_query_rows_brute_force(C, T_list):
+    """C > 1 against a pure-Python loop over the C x T score rectangle with the
+    bottom-right causal predicate j <= T - C + i (M4.5 §0x08B)."""
+    B, Hq, Hkv, D = len(T_list), 4, 2, 8
+    w = synth.make_contiguous(11, B, Hq, Hkv, D, T_list, dtype="f32", kv_capacity=12, num_queries=C)
+    O, L = oracle.attend(w.problem, w.buffers)
+    q = w.buffers["q"].astype(np.float64)
+    k = w.buffers["k"].astype(np.float64)
+    v = w.buffers["v"].astype(np.float64)
+    for b, T in enumerate(T_list):
+        for i in range(C):
+            for hq in range(Hq):
+                h = hq // (Hq // Hkv)
+                keys = [j for j in range(T) if j <= T - C + i]
+                if not keys:
+                    assert np.all(O[b, i, hq] == 0) and L[b, i, hq] == -math.inf
+                    continue
+                s = [math.fsum(q[b, i, hq, x] * k[b, j, h, x] for x in range(D)) / math.sqrt(D) for j in keys]
+                m = max(s)
+                e = [math.exp(t - m) for t in s]
+                den = math.fsum(e)
+                for x in range(D):
+                    ref = math.fsum(e[n] * v[b, keys[n], h, x] for n in range(len(keys))) / den
+                    assert abs(O[b, i, hq, x] - ref) < 1e-12
+                assert abs(L[b, i, hq] - (m + math.log(den))) < 1e-12

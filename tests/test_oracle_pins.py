@@ -245,3 +245,13 @@ def test_decode_phase_row():
         assert C * (T + C) == r["rect"]
         assert r["rect"] - vis == r["masked"]
         assert T + C == r["post"]
+        # the oracle's row rule: the cache holds T + C rows, row i sees a decode
+        # of length T_total - C + 1 + i
+        rows = [oracle.visible_positions(oracle.query_row_length(T + C, C, i)) for i in range(C)]
+        assert sum(len(a) for a in rows) == r["visible"]
+    tr = fx["append_row_trace"]
+    names = tr["old_cache"] + tr["staged"]
+    C = len(tr["staged"])
+    for i, row in enumerate(tr["rows"]):
+        got = [names[t] for t in oracle.visible_positions(oracle.query_row_length(len(names), C, i))]
+        assert got == row["visible"] and row["position"] == len(tr["old_cache"]) + i
