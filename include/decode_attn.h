@@ -70,9 +70,19 @@ typedef int32_t da_status;
                                  decode_attn_append maintains; requires R == G there)       */
 
 /* cache layouts ("M4.5 ...", sections 0x04B and 0x04D) */
-#define DA_LAYOUT_CONTIG_NHD 0  /* [B, T_cap, H_kv, D]; element ((b*T_cap + t)*H_kv + h)*D + x */
-#define DA_LAYOUT_PAGED_NHD  1  /* pool [N_pages, P, H_kv, D]; page = block_table[b][t / P],
-                                   element ((page*P + t % P)*H_kv + h)*D + x */
+#define DA_LAYOUT_CONTIG_NHD 0  /* [B_c, T_cap, H_kv, D]; element ((c*T_cap + t)*H_kv + h)*D + x  */
+#define DA_LAYOUT_PAGED_NHD  1  /* pool [N_pages, P, H_kv, D]; element ((pi*P + t%P)*H_kv + h)*D + x */
+#define DA_LAYOUT_CONTIG_HND 2  /* [B_c, H_kv, T_cap, D]; element ((c*H_kv + h)*T_cap + t)*D + x  */
+#define DA_LAYOUT_PAGED_HND  3  /* pool [N_pages, H_kv, P, D]; element ((pi*H_kv + h)*P + t%P)*D + x */
+#define DA_LAYOUT_RAGGED_NHD 4  /* packed [N_rows, H_kv, D]; request b's token t is packed row
+                                   indptr[b] + t: element ((indptr[b] + t)*H_kv + h)*D + x
+                                   ("M4.5 ...", section 0x04C)                             */
+/* Contiguous layouts: cache row c = cache_batch_idx[b] when given, else b
+ * (section 0x04B).  Paged layouts: the physical page pi of logical block
+ * j = t / P of request b comes from the page table (section 0x04D): */
+#define DA_PAGE_TABLE_DENSE 0   /* pi = block_table[b * max_pages_per_seq + j]              */
+#define DA_PAGE_TABLE_CSR   1   /* pi = block_table[indptr[b] + j]  (kv_page_indices with
+                                   kv_page_indptr; num_page_entries entries)               */
 
 /* mask programs: visibility of logical key t for the decode row of request b,
  * whose visible length is T = seq_lens[b] (the row sits at position T-1) */
@@ -127,6 +137,11 @@ typedef struct da_problem {
   int32_t num_cus;           /* 0 -> query the current device; > 0: plan for this many CUs */
   int32_t residual_policy;   /* DA_KV_I8: DA_RESIDUAL_*; else 0                     */
   int32_t num_queries;       /* C query rows per request (0 -> 1); see da_args q     */
+  int32_t page_table;        /* paged: DA_PAGE_TABLE_*; else 0                      */
+  int32_t cache_rows;        /* contiguous: rows B_c of the cache (0 -> B; > 0 needs
+                                cache_batch_idx); ragged: packed rows N_rows           */
+  int32_t num_page_entries;  /* DA_PAGE_TABLE_CSR: entries of block_table; else 0  */
+  int32_t reserved1;         /* must be 0                                           */
 } da_problem;
 
 /* A frozen plan: a plain value the caller owns and may copy; nothing to free.
@@ -150,15 +165,24 @@ typedef struct da_plan {
  *               [0, T_b - C + i + 1): bottom-right causal alignment ("M4.5 ...",
  *               sections 0x08B-0x08C: the C new rows are already in the cache, so
  *               T_b counts them and a one-token decode is C = 1)
- *   k, v        contiguous: [B, T_cap, H_kv, D]; paged: [N_pages, P, H_kv, D]
- *               DA_KV_I8: int8 codes [B, T_cap, H_kv, D] of tokens t < n_q(b)
+ *   k, v        per DA_LAYOUT_* (B_c = cache_rows or B): contiguous NHD [B_c, T_cap, H_kv, D],
+ *               contiguous HND [B_c, H_kv, T_cap, D], paged NHD [N_pages, P, H_kv, D],
+ *               paged HND [N_pages, H_kv, P, D], ragged NHD [N_rows, H_kv, D]
+ *               DA_KV_I8: int8 codes [B, T_cap, H_kv, D] of tokens t < n_q(b) (contiguous NHD)
  *   k_scale     DA_KV_I8: fp16 [B, ceil(T_cap/k_group), H_kv, D]; group j scales
  *               tokens [j*k_group, (j+1)*k_group), one scale per channel
  *   v_scale     DA_KV_I8: fp16 [B, T_cap, H_kv]; one scale per token
  *   k_resid,
  *   v_resid     DA_KV_I8: bf16 [B, R, H_kv, D]; row t - n_q(b) holds token t for
  *               t >= n_q(b) = seq_lens[b] - min(seq_lens[b], R)
- *   block_table paged: int32 [B, max_pages_per_seq]; only slots < ceil(T_b/P) are read
+ *   block_table paged, dense: int32 [B, max_pages_per_seq]; CSR: int32 [num_page_entries];
+ *               only the entries of blocks < ceil(T_b/P) are read
+ *   indptr      int32 [B + 1]: ragged layout: packed row of each request's token 0;
+ *               CSR page table: first table entry of each request.  Else NULL.
+ *   cache_batch_idx optional int32 [B] (contiguous layouts): cache row of request b
+ *               (cache_rows > 0).  Out-of-range entries and table values are clamped into
+ *               the buffers they index, so corrupt metadata can never address memory
+ *               outside them.
  *   seq_lens    int32 [B]; visible length T_b of each request, 0 <= T_b <= max_seq_len
  *   work_order  optional int32 [B*H_kv*S]: workgroup i runs work item work_order[i] =
  *               (b*H_kv + h_kv)*S + s.  It must be a permutation of 0 .. B*H_kv*S-1 (as
@@ -183,6 +207,8 @@ typedef struct da_args {
   void*          workspace;
   uint64_t       workspace_bytes;
   const int32_t* work_order;   /* NULL, or B*H_kv*S work items from decode_attn_schedule */
+  const int32_t* indptr;       /* ragged layout / CSR page table: [B + 1]; else NULL     */
+  const int32_t* cache_batch_idx; /* contiguous layouts with cache_rows > 0: [B]; else NULL */
 } da_args;
 
 /* Validate the problem (semantic checks first, then every capability

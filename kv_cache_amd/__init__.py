@@ -26,7 +26,8 @@ DA_ERR_WORKSPACE, DA_ERR_PLAN_MISMATCH, DA_ERR_HIP = -3, -4, -5
 
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 KV_FORMATS = {"f32": 0, "bf16": 1, "i8": 2}
-LAYOUTS = {"contig": 0, "paged": 1}
+LAYOUTS = {"contig": 0, "paged": 1, "contig_hnd": 2, "paged_hnd": 3, "ragged": 4}
+PAGE_TABLES = {"dense": 0, "csr": 1}
 MASKS = {"causal": 0, "sink_window": 1}
 RESIDUAL_POLICIES = {"window": 0, "groups": 1}
 NUM_REASONS = 13
@@ -38,7 +39,8 @@ class Problem(ctypes.Structure):
         "out_dtype", "kv_format", "layout", "kv_capacity", "page_size", "max_pages_per_seq",
         "num_pages", "max_seq_len", "mask_kind", "n_sink", "window")] + [
         ("softmax_scale", ctypes.c_float)] + [(n, ctypes.c_int32) for n in (
-            "num_splits", "k_group", "residual_len", "num_cus", "residual_policy", "num_queries")]
+            "num_splits", "k_group", "residual_len", "num_cus", "residual_policy", "num_queries",
+            "page_table", "cache_rows", "num_page_entries", "reserved1")]
 
 
 class Plan(ctypes.Structure):
@@ -51,7 +53,8 @@ class Plan(ctypes.Structure):
 class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "block_table", "seq_lens",
-        "workspace")] + [("workspace_bytes", ctypes.c_uint64), ("work_order", ctypes.c_void_p)]
+        "workspace")] + [("workspace_bytes", ctypes.c_uint64), ("work_order", ctypes.c_void_p),
+                         ("indptr", ctypes.c_void_p), ("cache_batch_idx", ctypes.c_void_p)]
 
 
 class AppendArgs(ctypes.Structure):
@@ -149,13 +152,16 @@ def problem_from(p, num_cus: int = 0) -> Problem:
         head_dim_qk=getattr(p, "head_dim_qk", d), head_dim_v=getattr(p, "head_dim_v", d),
         q_dtype=enum(p.q_dtype, DTYPES), out_dtype=enum(getattr(p, "out_dtype", "f32"), DTYPES),
         kv_format=enum(p.kv_format, KV_FORMATS), layout=enum(p.layout, LAYOUTS),
-        kv_capacity=p.kv_capacity if enum(p.layout, LAYOUTS) == 0 else 0,
+        kv_capacity=p.kv_capacity if enum(p.layout, LAYOUTS) in (0, 2) else 0,
         page_size=p.page_size, max_pages_per_seq=p.max_pages_per_seq, num_pages=p.num_pages,
         max_seq_len=p.max_seq_len, mask_kind=enum(p.mask_kind, MASKS), n_sink=p.n_sink,
         window=p.window, softmax_scale=p.softmax_scale, num_splits=p.num_splits,
         k_group=p.k_group, residual_len=p.residual_len, num_cus=num_cus,
         residual_policy=enum(getattr(p, "residual_policy", 0), RESIDUAL_POLICIES),
-        num_queries=int(getattr(p, "num_queries", 1) or 1))
+        num_queries=int(getattr(p, "num_queries", 1) or 1),
+        page_table=enum(getattr(p, "page_table", 0), PAGE_TABLES),
+        cache_rows=int(getattr(p, "cache_rows", 0)),
+        num_page_entries=int(getattr(p, "num_page_entries", 0)))
 
 
 def decode_attn_plan(problem: Problem, check: bool = True):
@@ -180,11 +186,13 @@ def _ptr(x):
 
 
 def make_args(q, k, v, seq_lens, workspace, workspace_bytes, k_scale=None, v_scale=None,
-              k_resid=None, v_resid=None, block_table=None, work_order=None) -> Args:
+              k_resid=None, v_resid=None, block_table=None, work_order=None, indptr=None,
+              cache_batch_idx=None) -> Args:
     return Args(q=_ptr(q), k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
                 k_resid=_ptr(k_resid), v_resid=_ptr(v_resid), block_table=_ptr(block_table),
                 seq_lens=_ptr(seq_lens), workspace=_ptr(workspace),
-                workspace_bytes=int(workspace_bytes), work_order=_ptr(work_order))
+                workspace_bytes=int(workspace_bytes), work_order=_ptr(work_order),
+                indptr=_ptr(indptr), cache_batch_idx=_ptr(cache_batch_idx))
 
 
 def decode_attn_schedule(plan: Plan, seq_lens_host, check: bool = True):

@@ -61,7 +61,13 @@ da_status check_args(const da_plan* plan, const da_args* a) {
   if (p.batch == 0) return DA_OK;
   if (!a->q || !a->k || !a->v || !a->seq_lens) return DA_ERR_INVALID;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return DA_ERR_INVALID;
-  if (p.layout == DA_LAYOUT_PAGED_NHD && !a->block_table) return DA_ERR_INVALID;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
+  if (paged && !a->block_table) return DA_ERR_INVALID;
+  if (((paged && p.page_table == DA_PAGE_TABLE_CSR) || p.layout == DA_LAYOUT_RAGGED_NHD) && !a->indptr)
+    return DA_ERR_INVALID;
+  if (p.cache_rows > 0 && (p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND) &&
+      !a->cache_batch_idx)
+    return DA_ERR_INVALID;
   if (p.kv_format == DA_KV_I8) {
     if (!a->k_scale || !a->v_scale) return DA_ERR_INVALID;
     if (p.residual_len > 0 && (!a->k_resid || !a->v_resid)) return DA_ERR_INVALID;
@@ -85,6 +91,16 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.block_table = a->block_table;
   sp.seq_lens = a->seq_lens;
   sp.work_order = a->work_order;
+  sp.indptr = a->indptr;
+  const bool contig = p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND;
+  sp.cache_batch_idx = contig && p.cache_rows > 0 ? a->cache_batch_idx : nullptr;
+  sp.layout = p.layout;
+  sp.page_csr = p.page_table == DA_PAGE_TABLE_CSR;
+  sp.cache_rows = p.cache_rows;
+  sp.num_page_entries = p.num_page_entries;
+  const bool hnd = p.layout == DA_LAYOUT_CONTIG_HND || p.layout == DA_LAYOUT_PAGED_HND;
+  sp.row_stride = (uint32_t)(hnd ? p.head_dim_qk : p.num_kv_heads * p.head_dim_qk);
+  sp.page_rows = (uint32_t)(p.layout == DA_LAYOUT_PAGED_HND ? p.num_kv_heads * p.page_size : p.page_size);
   const uint64_t n_states = (uint64_t)da::output_rows(p) * plan->num_splits;
   float* ws = static_cast<float*>(a->workspace);
   sp.ws_u = ws;
@@ -159,7 +175,7 @@ bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned gri
   // A workgroup serves the C query rows of each of its H_q/H_kv heads: C*g
   // "virtual heads" sharing one K/V head.
   const int g = p.num_q_heads / p.num_kv_heads * p.num_queries;
-  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
   switch (p.kv_format) {
     case DA_KV_F32:
       return paged ? dispatch_d<DA_KV_F32, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
@@ -243,7 +259,7 @@ extern "C" da_status decode_attn_append(const da_plan* plan, const da_append_arg
   if (!plan || !a) return DA_ERR_INVALID;
   if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
   const da_problem& p = plan->problem;
-  if (p.kv_format != DA_KV_I8 || p.layout != DA_LAYOUT_CONTIG_NHD ||
+  if (p.kv_format != DA_KV_I8 || p.layout != DA_LAYOUT_CONTIG_NHD || p.cache_rows != 0 ||
       p.residual_policy != DA_RESIDUAL_GROUPS || p.residual_len != p.k_group ||
       p.k_group > da::kAppendThreads || (p.head_dim_qk != 64 && p.head_dim_qk != 128))
     return DA_ERR_UNSUPPORTED;
@@ -338,7 +354,7 @@ extern "C" da_status decode_attn_trace_indices(const da_plan* plan, const da_arg
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   bool ok = false;
-  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
   switch (p.kv_format) {
     case DA_KV_F32:
       ok = paged ? dispatch_trace_d<DA_KV_F32, true>(p.head_dim_qk, sp, grid, offsets, positions, st)

@@ -21,6 +21,8 @@ struct SplitParams {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* work_order;
+  const int32_t* indptr;           // ragged rows / CSR table entries, [B + 1]
+  const int32_t* cache_batch_idx;  // contiguous: cache row of each request, or null
   float* ws_u;
   float* ws_m;
   float* ws_l;
@@ -44,7 +46,13 @@ struct SplitParams {
   int32_t residual_len;
   int32_t residual_policy;   // DA_RESIDUAL_*
   int32_t max_seq_len;       // plan bound: seq_lens are clamped to [0, max_seq_len]
-  int32_t num_pages;         // paged: page ids are clamped to [0, num_pages)
+  int32_t num_pages;
+  int32_t layout;            // DA_LAYOUT_*
+  int32_t page_csr;          // paged: 1 for DA_PAGE_TABLE_CSR
+  int32_t cache_rows;        // contiguous: B_c (0: B); ragged: packed rows
+  int32_t num_page_entries;  // CSR table entries
+  uint32_t row_stride;       // elements between consecutive row indices
+  uint32_t page_rows;        // paged: row indices per page (P for NHD, H_kv*P for HND)         // paged: page ids are clamped to [0, num_pages)
   float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
 };
 
@@ -162,18 +170,48 @@ __device__ __forceinline__ void split_range(int n_vis, int s, int chunk, int* be
 // Address translation ("M4.5 ...", sections 0x04B, 0x04D): element offset of
 // the first element of row (b, t, h) in the buffer it lives in.
 // ---------------------------------------------------------------------------
-// Split into a part that is uniform over a workgroup (the element offset of
-// head h in row 0 of request b, or of page 0) and the row index of token t
-// (t itself, or page*P + t%P); the element offset is
-// base + row_index * H_kv * D.
+// Split into a part that is uniform over a workgroup (RowAddr: the element
+// offset of head h's first row, and what the row lookup needs) and a row index
+// per token; the element offset of row (b, t, h) is base + row_index *
+// row_stride:
+//   contiguous NHD  base ((c*T_cap)*H + h)*D,  row t,              stride H*D
+//   contiguous HND  base ((c*H + h)*T_cap)*D,  row t,              stride D
+//   ragged NHD      base ((indptr[b])*H + h)*D, row t,             stride H*D
+//   paged NHD       base h*D,                  row pi*P + t%P,     stride H*D
+//   paged HND       base h*P*D,                row pi*H*P + t%P,   stride D
+// with c = cache_batch_idx[b] (or b) and pi the table's page for block t/P.
+// Metadata read from memory is clamped into the buffers it indexes.
+struct RowAddr {
+  int64_t base;
+  int32_t row_cap;    // non-paged: rows addressable from base
+  int32_t tbase;      // paged: index of the request's first table entry
+};
+
 template <bool PAGED>
-__device__ __forceinline__ int64_t head_base_offset(const SplitParams& p, int b, int h, int D) {
-  if (PAGED) return (int64_t)h * D;
-  return ((int64_t)b * p.kv_capacity * p.num_kv_heads + h) * (int64_t)D;
+__device__ __forceinline__ RowAddr row_addr(const SplitParams& p, int b, int h, int D) {
+  RowAddr a;
+  const int64_t H = p.num_kv_heads;
+  if (PAGED) {
+    a.base = p.layout == DA_LAYOUT_PAGED_HND ? (int64_t)h * p.page_size * D : (int64_t)h * D;
+    a.tbase = p.page_csr ? min(max(p.indptr[b], 0), p.num_page_entries - 1) : b * p.max_pages;
+    a.row_cap = 0;
+  } else if (p.layout == DA_LAYOUT_RAGGED_NHD) {
+    const int r0 = min(max(p.indptr[b], 0), p.cache_rows - 1);
+    a.base = ((int64_t)r0 * H + h) * D;
+    a.row_cap = p.cache_rows - r0;
+    a.tbase = 0;
+  } else {
+    const int c = p.cache_batch_idx ? min(max(p.cache_batch_idx[b], 0), p.cache_rows - 1) : b;
+    a.base = p.layout == DA_LAYOUT_CONTIG_HND ? (((int64_t)c * H + h) * p.kv_capacity) * D
+                                              : (((int64_t)c * p.kv_capacity) * H + h) * D;
+    a.row_cap = p.kv_capacity;
+    a.tbase = 0;
+  }
+  return a;
 }
 
 template <bool PAGED>
-__device__ __forceinline__ uint32_t kv_row_index(const SplitParams& p, int b, int t) {
+__device__ __forceinline__ uint32_t kv_row_index(const SplitParams& p, const RowAddr& a, int t) {
   if (PAGED) {
     int j, r;
     if (p.page_shift >= 0) {
@@ -183,18 +221,19 @@ __device__ __forceinline__ uint32_t kv_row_index(const SplitParams& p, int b, in
       j = t / p.page_size;
       r = t - j * p.page_size;
     }
-    // A visible slot must hold a pool page; clamping keeps a corrupt table
+    int e = a.tbase + j;
+    if (p.page_csr) e = min(e, p.num_page_entries - 1);
+    // A visible block must map to a pool page; clamping keeps a corrupt table
     // from addressing memory outside the pool.
-    const int page = min(max(p.block_table[(int64_t)b * p.max_pages + j], 0), p.num_pages - 1);
-    return (uint32_t)page * (uint32_t)p.page_size + (uint32_t)r;
+    const int page = min(max(p.block_table[e], 0), p.num_pages - 1);
+    return (uint32_t)page * p.page_rows + (uint32_t)r;
   }
-  return (uint32_t)t;
+  return (uint32_t)min(t, a.row_cap - 1);
 }
 
 template <bool PAGED>
-__device__ __forceinline__ int64_t kv_row_offset(const SplitParams& p, int b, int t, int h, int D) {
-  return head_base_offset<PAGED>(p, b, h, D) +
-         (int64_t)((uint64_t)kv_row_index<PAGED>(p, b, t) * (uint32_t)(p.num_kv_heads * D));
+__device__ __forceinline__ int64_t kv_row_offset(const SplitParams& p, const RowAddr& a, int t) {
+  return a.base + (int64_t)((uint64_t)kv_row_index<PAGED>(p, a, t) * p.row_stride);
 }
 
 // int8 format: tokens t < n_q come from the code buffers, the newest

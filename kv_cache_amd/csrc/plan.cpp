@@ -81,13 +81,29 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (p.head_dim_qk < 1 || p.head_dim_v < 1) return DA_ERR_INVALID;
   if (p.max_seq_len < 0 || p.num_splits < 0 || p.num_cus < 0) return DA_ERR_INVALID;
   if (!std::isfinite(p.softmax_scale) || p.softmax_scale < 0.f) return DA_ERR_INVALID;
-  if (p.layout == DA_LAYOUT_PAGED_NHD) {
-    if (p.page_size <= 0 || p.num_pages < 1 || p.max_pages_per_seq < 1) return DA_ERR_INVALID;
-    if (p.kv_capacity != 0) return DA_ERR_INVALID;
-    if (ceil_div(p.max_seq_len, p.page_size) > p.max_pages_per_seq) return DA_ERR_INVALID;
-  } else if (p.layout == DA_LAYOUT_CONTIG_NHD) {
+  if (p.reserved1 != 0) return DA_ERR_INVALID;
+  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
+  const bool contig = p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND;
+  if (paged) {
+    if (p.page_size <= 0 || p.num_pages < 1) return DA_ERR_INVALID;
+    if (p.kv_capacity != 0 || p.cache_rows != 0) return DA_ERR_INVALID;
+    if (p.page_table == DA_PAGE_TABLE_DENSE) {
+      if (p.max_pages_per_seq < 1 || p.num_page_entries != 0) return DA_ERR_INVALID;
+      if (ceil_div(p.max_seq_len, p.page_size) > p.max_pages_per_seq) return DA_ERR_INVALID;
+    } else if (p.page_table == DA_PAGE_TABLE_CSR) {
+      if (p.max_pages_per_seq != 0 || p.num_page_entries < 1) return DA_ERR_INVALID;
+    } else {
+      return DA_ERR_INVALID;
+    }
+  } else if (contig) {
     if (p.page_size != 0 || p.max_pages_per_seq != 0 || p.num_pages != 0) return DA_ERR_INVALID;
-    if (p.kv_capacity < 0) return DA_ERR_INVALID;
+    if (p.kv_capacity < 0 || p.cache_rows < 0 || p.page_table != 0 || p.num_page_entries != 0)
+      return DA_ERR_INVALID;
+  } else if (p.layout == DA_LAYOUT_RAGGED_NHD) {
+    if (p.page_size != 0 || p.max_pages_per_seq != 0 || p.num_pages != 0 || p.kv_capacity != 0 ||
+        p.page_table != 0 || p.num_page_entries != 0)
+      return DA_ERR_INVALID;
+    if (p.cache_rows < 1 && p.batch > 0 && p.max_seq_len > 0) return DA_ERR_INVALID;
   }
   if (p.mask_kind == DA_MASK_SINK_WINDOW) {
     if (p.window <= 0 || p.n_sink < 0) return DA_ERR_INVALID;
@@ -112,7 +128,7 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
     }
   } else {
     if (p.k_group != 0 || p.residual_len != 0 || p.residual_policy != 0) return DA_ERR_INVALID;
-    if (p.layout == DA_LAYOUT_CONTIG_NHD && p.kv_capacity < p.max_seq_len) return DA_ERR_INVALID;
+    if (contig && p.kv_capacity < p.max_seq_len) return DA_ERR_INVALID;
   }
 
   // ---- capability predicates: collect every failure ------------------------
@@ -133,8 +149,9 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
     if (!q_ok) reasons |= DA_R_Q_DTYPE;
   }
   if (p.out_dtype != DA_F32) reasons |= DA_R_OUT_DTYPE;
-  if (p.layout != DA_LAYOUT_CONTIG_NHD && p.layout != DA_LAYOUT_PAGED_NHD) reasons |= DA_R_LAYOUT;
-  if (p.kv_format == DA_KV_I8 && p.layout != DA_LAYOUT_CONTIG_NHD) reasons |= DA_R_LAYOUT;
+  if (!paged && !contig && p.layout != DA_LAYOUT_RAGGED_NHD) reasons |= DA_R_LAYOUT;
+  if (p.kv_format == DA_KV_I8 && (p.layout != DA_LAYOUT_CONTIG_NHD || p.cache_rows != 0))
+    reasons |= DA_R_LAYOUT;
   if (p.kv_format == DA_KV_I8 &&
       !(p.k_group >= 16 && p.k_group <= 1024 && (p.k_group & (p.k_group - 1)) == 0))
     reasons |= DA_R_INT8_PARAMS;
@@ -204,7 +221,7 @@ extern "C" const char* decode_attn_reason(int bit) {
       "q dtype must be f32 with f32 K/V and bf16 with bf16 or int8 K/V",
       "output dtype must be f32",
       "unknown K/V storage format",
-      "layout not available for this K/V format (int8 is contiguous only)",
+      "layout not available for this K/V format (int8 is contiguous NHD without a batch index)",
       "int8 k_group must be a power of two in [16, 1024]",
       "split count above the library maximum",
       "grid or trace size exceeds the index range",

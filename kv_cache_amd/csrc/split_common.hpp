@@ -244,6 +244,7 @@ __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64
   split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int n_q = I8 ? quantized_len(p, T) : T;
   const int64_t base = (((int64_t)b * p.num_kv_heads + h) * p.num_splits + s) * p.chunk;
+  const RowAddr ra = row_addr<PAGED && !I8>(p, b, h, D);
   for (int tile = begin + wave * TW; tile < end; tile += NWAVES * TW) {
     for (int j = lane; j < TW; j += 64) {
       const int o = tile + j;
@@ -251,9 +252,9 @@ __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64
         const int t = vis_pos(vis, o);
         int64_t off;
         if (I8)
-          off = t < n_q ? kv_row_offset<false>(p, b, t, h, D) : resid_row_offset(p, b, t - n_q, h, D);
+          off = t < n_q ? kv_row_offset<false>(p, ra, t) : resid_row_offset(p, b, t - n_q, h, D);
         else
-          off = kv_row_offset<PAGED>(p, b, t, h, D);
+          off = kv_row_offset<PAGED>(p, ra, t);
         offsets[base + (o - begin)] = off;
         positions[base + (o - begin)] = t;
       }

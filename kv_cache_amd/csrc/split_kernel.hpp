@@ -43,17 +43,17 @@ struct RawRow {
 };
 
 template <int FMT, int D, bool PAGED>
-__device__ __forceinline__ void load_row(const SplitParams& p, int b, int h, int t, int n_q,
-                                         int col0, RawRow& raw) {
+__device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra, int b, int h, int t,
+                                         int n_q, int col0, RawRow& raw) {
   constexpr int EB = FMT == DA_KV_F32 ? 4 : FMT == DA_KV_BF16 ? 2 : 1;
   if (FMT != DA_KV_I8) {
-    const int64_t off = kv_row_offset<PAGED>(p, b, t, h, D) + col0;
+    const int64_t off = kv_row_offset<PAGED>(p, ra, t) + col0;
     raw.k = stream_load(reinterpret_cast<const uint4*>(static_cast<const char*>(p.k) + off * EB));
     raw.v = stream_load(reinterpret_cast<const uint4*>(static_cast<const char*>(p.v) + off * EB));
     raw.region = 0;
   } else {
     if (t < n_q) {
-      const int64_t off = kv_row_offset<false>(p, b, t, h, D) + col0;
+      const int64_t off = kv_row_offset<false>(p, ra, t) + col0;
       const uint2 kc = stream_load(reinterpret_cast<const uint2*>(static_cast<const int8_t*>(p.k) + off));
       const uint2 vc = stream_load(reinterpret_cast<const uint2*>(static_cast<const int8_t*>(p.v) + off));
       raw.k = make_uint4(kc.x, kc.y, 0u, 0u);
@@ -176,6 +176,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
     for (int e = 0; e < EPL; ++e) u[i][e] = 0.f;
   }
 
+  const RowAddr ra = row_addr<PAGED>(p, b, h, D);
   RawRow nxt[U];
   auto issue = [&](int tile, RawRow* rr) {
 #pragma unroll
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
       rr[j].ks = make_uint4(0u, 0u, 0u, 0u);
       rr[j].vs = 0u;
       rr[j].region = 0;
-      if (rr[j].valid) load_row<FMT, D, PAGED>(p, b, h, vis_pos(vis, o), n_q, col0, rr[j]);
+      if (rr[j].valid) load_row<FMT, D, PAGED>(p, ra, b, h, vis_pos(vis, o), n_q, col0, rr[j]);
     }
   };
 

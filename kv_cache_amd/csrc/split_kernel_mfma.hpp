@@ -109,14 +109,15 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   // Row r of the tile is ordinal tile + r; rows past the split end are
   // clamped to its last row, which is visible and finite, and then get weight
   // 0 (score -inf), so the loads need no branches.
-  const int64_t hb = head_base_offset<PAGED>(p, b, h, D);
+  const RowAddr ra = row_addr<PAGED>(p, b, h, D);
+  const int64_t hb = ra.base;
   const uint16_t* kb = static_cast<const uint16_t*>(p.k) + hb + 8 * kg;
   const uint16_t* vb = static_cast<const uint16_t*>(p.v) + hb + 8 * n;
-  const uint32_t row_stride = (uint32_t)(p.num_kv_heads * D);
+  const uint32_t row_stride = p.row_stride;
   // Lane l resolves the row index of tile row l%16 (one page-table lookup
   // per row); the V rows 4kg+j take theirs from lane 4kg+j.
   auto row_index = [&](int tile) {
-    return kv_row_index<PAGED>(p, b, vis_pos(vis, min(tile + n, end - 1)));
+    return kv_row_index<PAGED>(p, ra, vis_pos(vis, min(tile + n, end - 1)));
   };
   auto issue_k = [&](uint32_t ri, uint4 (&k)[4]) {
     const uint16_t* row = kb + (uint64_t)ri * row_stride;

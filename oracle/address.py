@@ -1,8 +1,9 @@
 """Read-side address translation (test infrastructure only).
 
 Element offsets of one K or V element, from M4.5 §0x04B (contiguous NHD/HND
-strides) and §0x04D (paged NHD/HND through a dense block table); page
-segments of a logical interval from §0x04E.  K and V have separate bases.
+strides), §0x04C (packed ragged rows through indptr) and §0x04D (paged NHD/HND
+through a dense block table or a CSR page list); page segments of a logical
+interval from §0x04E.  K and V have separate bases.
 """
 
 
@@ -24,6 +25,17 @@ def paged_nhd_offset(page: int, r: int, h_kv: int, x: int, P: int, H_kv: int, D:
 def paged_hnd_offset(page: int, r: int, h_kv: int, x: int, P: int, H_kv: int, D: int) -> int:
     """Page pool ``[N_pages, H_kv, P, D]``: ((page*H_kv + h)*P + r)*D + x."""
     return ((page * H_kv + h_kv) * P + r) * D + x
+
+
+def ragged_nhd_offset(indptr, r: int, t: int, h_kv: int, x: int, H_kv: int, D: int) -> int:
+    """Packed ragged cache ``[sum_r T_r, H_kv, D]``: request r's token t is
+    packed row indptr[r] + t; offset ((indptr[r] + t)*H_kv + h)*D + x."""
+    return ((int(indptr[r]) + t) * H_kv + h_kv) * D + x
+
+
+def csr_page(kv_page_indptr, kv_page_indices, r: int, j: int) -> int:
+    """Physical page of logical block j of request r from a CSR page list."""
+    return int(kv_page_indices[int(kv_page_indptr[r]) + j])
 
 
 def page_of(block_table_row, t: int, P: int):

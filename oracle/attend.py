@@ -28,7 +28,8 @@ import math
 
 import numpy as np
 
-from .address import nhd_offset, paged_nhd_offset
+from .address import (csr_page, hnd_offset, nhd_offset, paged_hnd_offset, paged_nhd_offset,
+                      ragged_nhd_offset)
 from .numerics import decode, decode_bf16, decode_f16
 from .quant import quantized_count
 from .state import EMPTY, finalize, merge_state, summarize_allowed
@@ -51,13 +52,23 @@ def gather_rows(prob, buf, b: int, h_kv: int, positions):
     lane = np.arange(D, dtype=np.int64)
     region = np.zeros(n, dtype=np.int8)
     if prob.kv_format in ("f32", "bf16"):
-        if prob.layout == "contig":
-            offs = nhd_offset(b, positions, h_kv, 0, prob.kv_capacity, H, D)
-        elif prob.layout == "paged":
+        layout = prob.layout
+        if layout in ("contig", "contig_hnd"):
+            bidx = buf.get("cache_batch_idx")
+            c = int(bidx[b]) if bidx is not None else b
+            fn = nhd_offset if layout == "contig" else hnd_offset
+            offs = fn(c, positions, h_kv, 0, prob.kv_capacity, H, D)
+        elif layout == "ragged":
+            offs = ragged_nhd_offset(buf["indptr"], b, positions, h_kv, 0, H, D)
+        elif layout in ("paged", "paged_hnd"):
             P = prob.page_size
-            table = buf["block_table"][b]
-            pages = table[positions // P].astype(np.int64)
-            offs = paged_nhd_offset(pages, positions % P, h_kv, 0, P, H, D)
+            if getattr(prob, "page_table", "dense") == "csr":
+                pages = np.array([csr_page(buf["indptr"], buf["block_table"], b, j)
+                                  for j in (positions // P)], dtype=np.int64)
+            else:
+                pages = buf["block_table"][b][positions // P].astype(np.int64)
+            fn = paged_nhd_offset if layout == "paged" else paged_hnd_offset
+            offs = fn(pages, positions % P, h_kv, 0, P, H, D)
         else:
             raise ValueError(prob.layout)
         idx = offs[:, None] + lane[None, :]

@@ -68,6 +68,9 @@ class Problem:
     residual_len: int = 0          # int8 only: bf16 residual rows
     residual_policy: str = "window"  # int8 only: "window" | "groups" (which tokens are bf16)
     num_queries: int = 1           # C query rows per request (q is [B, C, H_q, D] when C > 1)
+    page_table: str = "dense"      # paged: "dense" | "csr"
+    cache_rows: int = 0            # contiguous: cache rows B_c (0: B); ragged: packed rows
+    num_page_entries: int = 0      # CSR page list length
 
     @property
     def group(self) -> int:
@@ -410,3 +413,78 @@ def append_rows(seed: int, B: int, H_kv: int, D: int, outlier_channels: int = 3,
                 ch = g.choice(D, size=outlier_channels, replace=False)
                 arr[b, h, ch] *= np.float32(outlier_mult)
     return bf16_bits(kf), bf16_bits(vf)
+
+
+# --------------------------------------------------------------------------
+# the same logical cache in the other layouts of the ABI
+# --------------------------------------------------------------------------
+def relayout(w: Workload, layout: str, page_table: str = "dense", cache_rows: int = 0,
+             seed: int = 0) -> Workload:
+    """Copy of ``w`` (contiguous NHD or paged NHD, not int8) whose K/V bytes are
+    stored in another layout; the logical data (q, lengths, every visible K/V
+    row) is unchanged.
+
+    * from contiguous NHD: ``"contig"`` with ``cache_rows`` > B (request b in a
+      seeded random cache row, the other rows NaN, plus ``cache_batch_idx``),
+      ``"contig_hnd"`` (``[B_c, H_kv, T_cap, D]``, same cache rows) or
+      ``"ragged"`` (rows packed as ``[sum T_b, H_kv, D]`` with ``indptr``);
+    * from paged NHD: ``"paged"`` or ``"paged_hnd"`` (pool ``[N_pages, H_kv, P, D]``),
+      with ``page_table="csr"`` turning the dense table into ``indptr`` plus the
+      list of pages (followed by a few garbage entries).
+    """
+    p = dataclasses.replace(w.problem)
+    buf = dict(w.buffers)
+    g = rng(seed + 4242)
+    lens = [int(t) for t in buf["seq_lens"]]
+    if w.problem.layout == "contig" and layout in ("contig", "contig_hnd", "ragged"):
+        k, v = buf["k"], buf["v"]
+        B = p.batch
+        if layout == "ragged":
+            indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            rows = max(1, int(indptr[-1]))
+            kp = _poison_like(g, (rows,) + k.shape[2:], _dt_name(k))
+            vp = _poison_like(g, (rows,) + v.shape[2:], _dt_name(v))
+            for b, T in enumerate(lens):
+                kp[indptr[b]:indptr[b] + T] = k[b, :T]
+                vp[indptr[b]:indptr[b] + T] = v[b, :T]
+            buf.update(k=kp, v=vp, indptr=indptr)
+            p.layout, p.cache_rows, p.kv_capacity = "ragged", rows, 0
+            return Workload(p, buf)
+        if cache_rows:
+            if cache_rows < B:
+                raise ValueError("cache_rows < B")
+            perm = g.permutation(cache_rows)[:B].astype(np.int32)
+            kc = _poison_like(g, (cache_rows,) + k.shape[1:], _dt_name(k))
+            vc = _poison_like(g, (cache_rows,) + v.shape[1:], _dt_name(v))
+            kc[perm] = k
+            vc[perm] = v
+            k, v = kc, vc
+            buf["cache_batch_idx"] = perm
+            p.cache_rows = cache_rows
+        if layout == "contig_hnd":
+            k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+            v = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+        buf.update(k=k, v=v)
+        p.layout = layout
+        return Workload(p, buf)
+    if w.problem.layout == "paged" and layout in ("paged", "paged_hnd"):
+        if layout == "paged_hnd":
+            buf["k"] = np.ascontiguousarray(buf["k"].transpose(0, 2, 1, 3))
+            buf["v"] = np.ascontiguousarray(buf["v"].transpose(0, 2, 1, 3))
+        if page_table == "csr":
+            P = p.page_size
+            table = buf["block_table"]
+            n = [(T + P - 1) // P for T in lens]
+            indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+            garbage = np.array([-1, p.num_pages + 7, np.iinfo(np.int32).max], dtype=np.int32)
+            entries = np.concatenate([table[b, :n[b]] for b in range(p.batch)] + [garbage])
+            buf["block_table"] = entries.astype(np.int32)
+            buf["indptr"] = indptr
+            p.page_table, p.num_page_entries, p.max_pages_per_seq = "csr", int(entries.size), 0
+        p.layout = layout
+        return Workload(p, buf)
+    raise ValueError(f"cannot make {layout} from {w.problem.layout}")
+
+
+def _dt_name(a: np.ndarray) -> str:
+    return "f32" if a.dtype == np.float32 else "bf16"

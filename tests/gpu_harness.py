@@ -44,7 +44,8 @@ class DeviceWorkload:
         return ka.make_args(d["q"], d["k"], d["v"], d["seq_lens"], ws, ws_bytes,
                             k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
                             k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
-                            block_table=d.get("block_table"), work_order=self.order)
+                            block_table=d.get("block_table"), work_order=self.order,
+                            indptr=d.get("indptr"), cache_batch_idx=d.get("cache_batch_idx"))
 
 
 def _outputs(w):

@@ -37,9 +37,9 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(ka.Problem) == 24 * 4
-    assert ctypes.sizeof(ka.Plan) == 8 + 96 + 16 + 8 + 16
-    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 8
+    assert ctypes.sizeof(ka.Problem) == 28 * 4
+    assert ctypes.sizeof(ka.Plan) == 8 + 112 + 16 + 8 + 16
+    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 3 * 8
 
 
 def P(**kw):

@@ -283,3 +283,23 @@ def test_few_query_rows_brute_force(C, T_list):
                     ref = math.fsum(e[n] * v[b, keys[n], h, x] for n in range(len(keys))) / den
                     assert abs(O[b, i, hq, x] - ref) < 1e-12
                 assert abs(L[b, i, hq] - (m + math.log(den))) < 1e-12
+
+
+
+@pytest.mark.parametrize("layout,kw", [("contig_hnd", {}), ("contig", {"cache_rows": 7}),
+                                       ("contig_hnd", {"cache_rows": 6}), ("ragged", {})])
+def test_contiguous_relayouts_give_identical_results(layout, kw):
+    w = synth.make_contiguous(13, 4, 8, 2, 16, [9, 0, 33, 20], dtype="f32", kv_capacity=40)
+    O, L = oracle.attend(w.problem, w.buffers)
+    w2 = synth.relayout(w, layout, **kw)
+    O2, L2 = oracle.attend(w2.problem, w2.buffers)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+@pytest.mark.parametrize("layout,table", [("paged_hnd", "dense"), ("paged", "csr"), ("paged_hnd", "csr")])
+def test_paged_relayouts_give_identical_results(layout, table):
+    w = synth.make_paged(14, 3, 4, 2, 16, [37, 5, 64], page_size=8, dtype="f32")
+    O, L = oracle.attend(w.problem, w.buffers)
+    w2 = synth.relayout(w, layout, page_table=table)
+    O2, L2 = oracle.attend(w2.problem, w2.buffers)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)

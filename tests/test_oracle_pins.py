@@ -255,3 +255,27 @@ def test_decode_phase_row():
     for i, row in enumerate(tr["rows"]):
         got = [names[t] for t in oracle.visible_positions(oracle.query_row_length(len(names), C, i))]
         assert got == row["visible"] and row["position"] == len(tr["old_cache"]) + i
+
+
+
+def test_ragged_indptr_fixture():
+    """M4.5 §0x04C: lengths [10, 7, 5] pack with indptr [0, 10, 17, 22]; request B's
+    token 6 is packed row 16 (not cache row 0 of a padded layout)."""
+    fx = load("address_translation.json")["ragged"]
+    indptr = np.concatenate([[0], np.cumsum(fx["lengths"])])
+    assert indptr.tolist() == fx["indptr"]
+    q = fx["query"]
+    assert oracle.ragged_nhd_offset(indptr, q["request"], q["t"], 0, 0, 1, 1) == q["packed_row"]
+    # with heads and channels the packed row keeps the NHD strides
+    assert oracle.ragged_nhd_offset(indptr, 1, 6, 1, 2, 2, 4) == (16 * 2 + 1) * 4 + 2
+
+
+def test_csr_and_dense_tables_name_the_same_page():
+    """M4.5 §0x04D: both encodings must give the same physical page."""
+    dense = np.array([[7, 3, 9, -1], [2, 5, -1, -1]])
+    n = [3, 2]
+    indptr = [0, 3, 5]
+    indices = [7, 3, 9, 2, 5]
+    for r in range(2):
+        for j in range(n[r]):
+            assert oracle.csr_page(indptr, indices, r, j) == dense[r, j]
