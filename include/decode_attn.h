@@ -77,6 +77,11 @@ typedef int32_t da_status;
 #define DA_LAYOUT_RAGGED_NHD 4  /* packed [N_rows, H_kv, D]; request b's token t is packed row
                                    indptr[b] + t: element ((indptr[b] + t)*H_kv + h)*D + x
                                    ("M4.5 ...", section 0x04C)                             */
+#define DA_LAYOUT_RING_NHD   5  /* fixed-capacity sink + window cache [B_c, n_sink + W, H_kv, D]
+                                   with DA_MASK_SINK_WINDOW: position t < n_sink lives in slot t,
+                                   any other position in ring slot n_sink + t mod W ("M5.4 ...",
+                                   section 0x04: the slot is an address, the position stays t);
+                                   kv_capacity must equal n_sink + W                       */
 /* Contiguous layouts: cache row c = cache_batch_idx[b] when given, else b
  * (section 0x04B).  Paged layouts: the physical page pi of logical block
  * j = t / P of request b comes from the page table (section 0x04D): */

@@ -26,7 +26,7 @@ DA_ERR_WORKSPACE, DA_ERR_PLAN_MISMATCH, DA_ERR_HIP = -3, -4, -5
 
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 KV_FORMATS = {"f32": 0, "bf16": 1, "i8": 2}
-LAYOUTS = {"contig": 0, "paged": 1, "contig_hnd": 2, "paged_hnd": 3, "ragged": 4}
+LAYOUTS = {"contig": 0, "paged": 1, "contig_hnd": 2, "paged_hnd": 3, "ragged": 4, "ring": 5}
 PAGE_TABLES = {"dense": 0, "csr": 1}
 MASKS = {"causal": 0, "sink_window": 1}
 RESIDUAL_POLICIES = {"window": 0, "groups": 1}
@@ -152,7 +152,7 @@ def problem_from(p, num_cus: int = 0) -> Problem:
         head_dim_qk=getattr(p, "head_dim_qk", d), head_dim_v=getattr(p, "head_dim_v", d),
         q_dtype=enum(p.q_dtype, DTYPES), out_dtype=enum(getattr(p, "out_dtype", "f32"), DTYPES),
         kv_format=enum(p.kv_format, KV_FORMATS), layout=enum(p.layout, LAYOUTS),
-        kv_capacity=p.kv_capacity if enum(p.layout, LAYOUTS) in (0, 2) else 0,
+        kv_capacity=p.kv_capacity if enum(p.layout, LAYOUTS) in (0, 2, 5) else 0,
         page_size=p.page_size, max_pages_per_seq=p.max_pages_per_seq, num_pages=p.num_pages,
         max_seq_len=p.max_seq_len, mask_kind=enum(p.mask_kind, MASKS), n_sink=p.n_sink,
         window=p.window, softmax_scale=p.softmax_scale, num_splits=p.num_splits,

@@ -65,7 +65,8 @@ da_status check_args(const da_plan* plan, const da_args* a) {
   if (paged && !a->block_table) return DA_ERR_INVALID;
   if (((paged && p.page_table == DA_PAGE_TABLE_CSR) || p.layout == DA_LAYOUT_RAGGED_NHD) && !a->indptr)
     return DA_ERR_INVALID;
-  if (p.cache_rows > 0 && (p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND) &&
+  if (p.cache_rows > 0 &&
+      (p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND || p.layout == DA_LAYOUT_RING_NHD) &&
       !a->cache_batch_idx)
     return DA_ERR_INVALID;
   if (p.kv_format == DA_KV_I8) {
@@ -92,7 +93,8 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.seq_lens = a->seq_lens;
   sp.work_order = a->work_order;
   sp.indptr = a->indptr;
-  const bool contig = p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND;
+  const bool contig = p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND ||
+                      p.layout == DA_LAYOUT_RING_NHD;
   sp.cache_batch_idx = contig && p.cache_rows > 0 ? a->cache_batch_idx : nullptr;
   sp.layout = p.layout;
   sp.page_csr = p.page_table == DA_PAGE_TABLE_CSR;

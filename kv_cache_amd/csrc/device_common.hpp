@@ -176,6 +176,7 @@ __device__ __forceinline__ void split_range(int n_vis, int s, int chunk, int* be
 // row_stride:
 //   contiguous NHD  base ((c*T_cap)*H + h)*D,  row t,              stride H*D
 //   contiguous HND  base ((c*H + h)*T_cap)*D,  row t,              stride D
+//   ring NHD        as contiguous NHD (T_cap = n_sink + W), row t < n_sink ? t : n_sink + t mod W
 //   ragged NHD      base ((indptr[b])*H + h)*D, row t,             stride H*D
 //   paged NHD       base h*D,                  row pi*P + t%P,     stride H*D
 //   paged HND       base h*P*D,                row pi*H*P + t%P,   stride D
@@ -228,6 +229,8 @@ __device__ __forceinline__ uint32_t kv_row_index(const SplitParams& p, const Row
     const int page = min(max(p.block_table[e], 0), p.num_pages - 1);
     return (uint32_t)page * p.page_rows + (uint32_t)r;
   }
+  if (p.layout == DA_LAYOUT_RING_NHD)   // sinks in their own slots, the rest in a ring of W slots
+    return (uint32_t)(t < p.n_sink ? t : p.n_sink + t % p.window);
   return (uint32_t)min(t, a.row_cap - 1);
 }
 

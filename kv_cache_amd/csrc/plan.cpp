@@ -83,7 +83,11 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (!std::isfinite(p.softmax_scale) || p.softmax_scale < 0.f) return DA_ERR_INVALID;
   if (p.reserved1 != 0) return DA_ERR_INVALID;
   const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
-  const bool contig = p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND;
+  const bool contig = p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND ||
+                      p.layout == DA_LAYOUT_RING_NHD;
+  if (p.layout == DA_LAYOUT_RING_NHD &&
+      (p.mask_kind != DA_MASK_SINK_WINDOW || (int64_t)p.kv_capacity != (int64_t)p.n_sink + p.window))
+    return DA_ERR_INVALID;
   if (paged) {
     if (p.page_size <= 0 || p.num_pages < 1) return DA_ERR_INVALID;
     if (p.kv_capacity != 0 || p.cache_rows != 0) return DA_ERR_INVALID;
@@ -128,7 +132,7 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
     }
   } else {
     if (p.k_group != 0 || p.residual_len != 0 || p.residual_policy != 0) return DA_ERR_INVALID;
-    if (contig && p.kv_capacity < p.max_seq_len) return DA_ERR_INVALID;
+    if (contig && p.layout != DA_LAYOUT_RING_NHD && p.kv_capacity < p.max_seq_len) return DA_ERR_INVALID;
   }
 
   // ---- capability predicates: collect every failure ------------------------

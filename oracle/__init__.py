@@ -28,7 +28,7 @@ from .numerics import decode_bf16, decode_f16, decode_f32  # noqa: F401
 from .visibility import visible_positions, visible_count, query_row_length  # noqa: F401
 from .address import (  # noqa: F401
     nhd_offset, hnd_offset, paged_nhd_offset, paged_hnd_offset, paged_segments,
-    ragged_nhd_offset, csr_page,
+    ragged_nhd_offset, csr_page, ring_slot,
 )
 from .state import (  # noqa: F401
     State, EMPTY, merge_state, summarize_allowed, finalize, balanced_bounds,

@@ -38,6 +38,15 @@ def csr_page(kv_page_indptr, kv_page_indices, r: int, j: int) -> int:
     return int(kv_page_indices[int(kv_page_indptr[r]) + j])
 
 
+def ring_slot(t, n_sink: int, window: int):
+    """Fixed-capacity sink + window cache (M5.4 §0x04, "logical position is
+    not ring slot"): sink position t < n_sink keeps slot t; any other position
+    lives in ring slot n_sink + (t mod W).  The slot is an address only."""
+    import numpy as _np
+    t = _np.asarray(t)
+    return _np.where(t < n_sink, t, n_sink + t % window)
+
+
 def page_of(block_table_row, t: int, P: int):
     """Logical block j = t // P, row r = t mod P, physical page = table[j]."""
     j, r = divmod(int(t), int(P))

@@ -29,7 +29,7 @@ import math
 import numpy as np
 
 from .address import (csr_page, hnd_offset, nhd_offset, paged_hnd_offset, paged_nhd_offset,
-                      ragged_nhd_offset)
+                      ragged_nhd_offset, ring_slot)
 from .numerics import decode, decode_bf16, decode_f16
 from .quant import quantized_count
 from .state import EMPTY, finalize, merge_state, summarize_allowed
@@ -60,6 +60,11 @@ def gather_rows(prob, buf, b: int, h_kv: int, positions):
             offs = fn(c, positions, h_kv, 0, prob.kv_capacity, H, D)
         elif layout == "ragged":
             offs = ragged_nhd_offset(buf["indptr"], b, positions, h_kv, 0, H, D)
+        elif layout == "ring":
+            bidx = buf.get("cache_batch_idx")
+            c = int(bidx[b]) if bidx is not None else b
+            slots = ring_slot(positions, prob.n_sink, prob.window)
+            offs = nhd_offset(c, slots, h_kv, 0, prob.n_sink + prob.window, H, D)
         elif layout in ("paged", "paged_hnd"):
             P = prob.page_size
             if getattr(prob, "page_table", "dense") == "csr":

@@ -424,6 +424,9 @@ def relayout(w: Workload, layout: str, page_table: str = "dense", cache_rows: in
     stored in another layout; the logical data (q, lengths, every visible K/V
     row) is unchanged.
 
+    * from contiguous NHD with a sink + window mask: ``"ring"`` (only the
+      visible rows, sinks in slots 0 .. n_sink-1 and the window in ring slots
+      n_sink + t mod W; the other slots poisoned);
     * from contiguous NHD: ``"contig"`` with ``cache_rows`` > B (request b in a
       seeded random cache row, the other rows NaN, plus ``cache_batch_idx``),
       ``"contig_hnd"`` (``[B_c, H_kv, T_cap, D]``, same cache rows) or
@@ -436,6 +439,22 @@ def relayout(w: Workload, layout: str, page_table: str = "dense", cache_rows: in
     buf = dict(w.buffers)
     g = rng(seed + 4242)
     lens = [int(t) for t in buf["seq_lens"]]
+    if w.problem.layout == "contig" and layout == "ring":
+        if p.mask_kind != "sink_window":
+            raise ValueError("the ring layout holds a sink + window cache")
+        ns, W = p.n_sink, p.window
+        k, v = buf["k"], buf["v"]
+        kr = _poison_like(g, (p.batch, ns + W) + k.shape[2:], _dt_name(k))
+        vr = _poison_like(g, (p.batch, ns + W) + v.shape[2:], _dt_name(v))
+        for b, T in enumerate(lens):
+            keep = [t for t in range(T) if t < ns or t >= T - W]
+            for t in keep:
+                slot = t if t < ns else ns + t % W
+                kr[b, slot] = k[b, t]
+                vr[b, slot] = v[b, t]
+        buf.update(k=kr, v=vr)
+        p.layout, p.kv_capacity = "ring", ns + W
+        return Workload(p, buf)
     if w.problem.layout == "contig" and layout in ("contig", "contig_hnd", "ragged"):
         k, v = buf["k"], buf["v"]
         B = p.batch

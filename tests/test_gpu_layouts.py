@@ -72,3 +72,18 @@ def test_few_query_rows_on_hnd_and_csr():
         Or, Lr = oracle.attend(w.problem, w.buffers)
         O, L, _ = H.forward(w)
         H.check_rows(O, L, Or, Lr, 2e-3)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_ring_sink_window_layout(dtype, D):
+    lens = [5000, 3, 700, 0, 4100]
+    w = synth.make_contiguous(55, len(lens), 8, 2, D, lens, dtype=dtype, kv_capacity=5000,
+                              mask_kind="sink_window", n_sink=4, window=600)
+    w = synth.relayout(w, "ring")
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    tol = 2e-3 if dtype == "bf16" else 1e-5
+    O, L, _ = H.forward(w)
+    H.check_rows(O, L, Or, Lr, tol)
+    O, L, _ = H.run(w, num_splits=5)
+    H.check_rows(O, L, Or, Lr, tol)
+    _trace_rows(w, 3)

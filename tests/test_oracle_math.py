@@ -303,3 +303,14 @@ def test_paged_relayouts_give_identical_results(layout, table):
     w2 = synth.relayout(w, layout, page_table=table)
     O2, L2 = oracle.attend(w2.problem, w2.buffers)
     assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+
+@pytest.mark.parametrize("lens", [[9, 0, 33, 20], [2, 5, 7, 40]])
+def test_ring_layout_gives_identical_results(lens):
+    w = synth.make_contiguous(15, 4, 8, 2, 16, lens, dtype="f32", kv_capacity=40,
+                              mask_kind="sink_window", n_sink=2, window=5)
+    O, L = oracle.attend(w.problem, w.buffers)
+    w2 = synth.relayout(w, "ring")
+    O2, L2 = oracle.attend(w2.problem, w2.buffers)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)

@@ -279,3 +279,11 @@ def test_csr_and_dense_tables_name_the_same_page():
     for r in range(2):
         for j in range(n[r]):
             assert oracle.csr_page(indptr, indices, r, j) == dense[r, j]
+
+
+
+def test_ring_slot_is_an_address_not_a_position():
+    """M5.4 §0x04: with W = 3, original position 6 lives in slot 6 mod 3 = 0 and
+    keeps position 6; sinks keep their own slots."""
+    assert int(oracle.ring_slot(6, 0, 3)) == 0
+    assert oracle.ring_slot(np.arange(10), 2, 3).tolist() == [0, 1, 2 + 2 % 3, 2 + 0, 2 + 1, 2 + 2, 2, 3, 4, 2]
