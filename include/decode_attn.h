@@ -96,6 +96,11 @@ typedef int32_t da_status;
                                   ("M5.4 - Long-Context KV Policies: Retention,
                                   Compression, and Budget Allocation", sections
                                   0x04-0x05: sink and recent sets as a union)       */
+#define DA_MASK_FLASHMASK   2  /* FlashMask ("M4.5 ...", sections 0x06A-0x06D): key t < T is
+                                  hidden when q = T-1 lies in [UTS_t, UTE_t) or [LTS_t, LTE_t)
+                                  (da_args mask_intervals); 16-key tiles are classified SKIP /
+                                  FULL / PARTIAL from mask_summary and SKIP tiles are never
+                                  loaded.  bf16 K/V, head_dim 128, one query row.             */
 
 /* admission reason bits (DA_ERR_UNSUPPORTED) */
 #define DA_R_HEAD_DIM    (1ull << 0)   /* head_dim_qk not in {64, 128}                 */
@@ -109,7 +114,8 @@ typedef int32_t da_status;
 #define DA_R_SPLITS      (1ull << 8)   /* num_splits above DA_MAX_SPLITS              */
 #define DA_R_INDEX_RANGE (1ull << 9)   /* a tensor exceeds the 2^31-element index range */
 #define DA_R_DEVICE      (1ull << 10)  /* current device is not gfx950 or cannot be queried */
-#define DA_R_MASK_KIND   (1ull << 11)  /* unknown mask program                        */
+#define DA_R_MASK_KIND   (1ull << 11)  /* unknown mask program, or FlashMask outside its
+                                          domain (bf16, d=128, C=1, splits <= 1024 keys) */
 #define DA_R_QUERY_ROWS  (1ull << 12)  /* num_queries C: (H_q/H_kv)*C not in {1,2,4,8}, or
                                           C > 1 with a mask other than causal        */
 #define DA_NUM_REASONS   13
@@ -214,6 +220,8 @@ typedef struct da_args {
   const int32_t* work_order;   /* NULL, or B*H_kv*S work items from decode_attn_schedule */
   const int32_t* indptr;       /* ragged layout / CSR page table: [B + 1]; else NULL     */
   const int32_t* cache_batch_idx; /* contiguous layouts with cache_rows > 0: [B]; else NULL */
+  const int32_t* mask_intervals;  /* DA_MASK_FLASHMASK: [B, max_seq_len, 4] (UTS, UTE, LTS, LTE) */
+  const int32_t* mask_summary;    /* DA_MASK_FLASHMASK: [B, ceil(max_seq_len/16), 8]           */
 } da_args;
 
 /* Validate the problem (semantic checks first, then every capability
@@ -272,6 +280,15 @@ da_status decode_attn_combine(const da_plan* plan, const void* workspace,
  * to the order of the final fp32 sums. */
 da_status decode_attn_forward(const da_plan* plan, const da_args* args, float* out, float* lse,
                               void* stream);
+
+/* FlashMask block summaries ("M4.5 ...", section 0x06C): for each request b
+ * and block J of 16 key columns [16J, min(16J+16, max_seq_len)), write
+ * summary[b][J] = (UTS min, UTS max, UTE min, UTE max, LTS min, LTS max,
+ * LTE min, LTE max) over the block's columns of intervals [B, max_seq_len, 4].
+ * Both pointers are device pointers, 16-byte aligned.  Run it whenever the
+ * intervals change, before decode_attn_run / decode_attn_forward. */
+da_status decode_attn_flashmask_summarize(const da_plan* plan, const int32_t* intervals,
+                                          int32_t* summary, void* stream);
 
 /* Zero the arrival counters of a workspace sized for `plan` (a fill kernel on
  * `stream`, so it may be captured into a graph).  Needed once per workspace

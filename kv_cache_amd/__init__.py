@@ -16,7 +16,7 @@ __all__ = [
     "DA_OK", "DA_ERR_INVALID", "DA_ERR_UNSUPPORTED", "DA_ERR_WORKSPACE",
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
     "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
-    "decode_attn_schedule", "decode_attn_append", "AppendArgs", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
+    "decode_attn_schedule", "decode_attn_append", "decode_attn_flashmask_summarize", "AppendArgs", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
     "decode_attn_workspace_init", "decode_attn_trace_indices",
     "decode_attn_reason", "decode_attn_status_string", "reason_names",
 ]
@@ -28,7 +28,7 @@ DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 KV_FORMATS = {"f32": 0, "bf16": 1, "i8": 2}
 LAYOUTS = {"contig": 0, "paged": 1, "contig_hnd": 2, "paged_hnd": 3, "ragged": 4, "ring": 5}
 PAGE_TABLES = {"dense": 0, "csr": 1}
-MASKS = {"causal": 0, "sink_window": 1}
+MASKS = {"causal": 0, "sink_window": 1, "flashmask": 2}
 RESIDUAL_POLICIES = {"window": 0, "groups": 1}
 NUM_REASONS = 13
 
@@ -54,7 +54,8 @@ class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "block_table", "seq_lens",
         "workspace")] + [("workspace_bytes", ctypes.c_uint64), ("work_order", ctypes.c_void_p),
-                         ("indptr", ctypes.c_void_p), ("cache_batch_idx", ctypes.c_void_p)]
+                         ("indptr", ctypes.c_void_p), ("cache_batch_idx", ctypes.c_void_p),
+                         ("mask_intervals", ctypes.c_void_p), ("mask_summary", ctypes.c_void_p)]
 
 
 class AppendArgs(ctypes.Structure):
@@ -107,6 +108,9 @@ def lib() -> ctypes.CDLL:
         L.decode_attn_append.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(AppendArgs),
                                          ctypes.c_void_p]
         L.decode_attn_append.restype = ctypes.c_int32
+        L.decode_attn_flashmask_summarize.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_attn_flashmask_summarize.restype = ctypes.c_int32
         L.decode_attn_run.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p]
         L.decode_attn_run.restype = ctypes.c_int32
         L.decode_attn_combine.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_uint64,
@@ -187,12 +191,13 @@ def _ptr(x):
 
 def make_args(q, k, v, seq_lens, workspace, workspace_bytes, k_scale=None, v_scale=None,
               k_resid=None, v_resid=None, block_table=None, work_order=None, indptr=None,
-              cache_batch_idx=None) -> Args:
+              cache_batch_idx=None, mask_intervals=None, mask_summary=None) -> Args:
     return Args(q=_ptr(q), k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
                 k_resid=_ptr(k_resid), v_resid=_ptr(v_resid), block_table=_ptr(block_table),
                 seq_lens=_ptr(seq_lens), workspace=_ptr(workspace),
                 workspace_bytes=int(workspace_bytes), work_order=_ptr(work_order),
-                indptr=_ptr(indptr), cache_batch_idx=_ptr(cache_batch_idx))
+                indptr=_ptr(indptr), cache_batch_idx=_ptr(cache_batch_idx),
+                mask_intervals=_ptr(mask_intervals), mask_summary=_ptr(mask_summary))
 
 
 def decode_attn_schedule(plan: Plan, seq_lens_host, check: bool = True):
@@ -207,6 +212,15 @@ def decode_attn_schedule(plan: Plan, seq_lens_host, check: bool = True):
     if check and st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_schedule")
     return order[:n]
+
+
+def decode_attn_flashmask_summarize(plan: Plan, intervals, summary, stream: int = 0,
+                                    check: bool = True) -> int:
+    st = lib().decode_attn_flashmask_summarize(ctypes.byref(plan), _ptr(intervals), _ptr(summary),
+                                               stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_flashmask_summarize")
+    return st
 
 
 def decode_attn_run(plan: Plan, args: Args, stream: int = 0, check: bool = True) -> int:

@@ -63,6 +63,12 @@ da_status check_args(const da_plan* plan, const da_args* a) {
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return DA_ERR_INVALID;
   const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
   if (paged && !a->block_table) return DA_ERR_INVALID;
+  if (p.mask_kind == DA_MASK_FLASHMASK) {
+    if (!a->mask_intervals || !a->mask_summary) return DA_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(a->mask_intervals) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(a->mask_summary) & 15u) != 0)
+      return DA_ERR_INVALID;
+  }
   if (((paged && p.page_table == DA_PAGE_TABLE_CSR) || p.layout == DA_LAYOUT_RAGGED_NHD) && !a->indptr)
     return DA_ERR_INVALID;
   if (p.cache_rows > 0 &&
@@ -103,6 +109,10 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   const bool hnd = p.layout == DA_LAYOUT_CONTIG_HND || p.layout == DA_LAYOUT_PAGED_HND;
   sp.row_stride = (uint32_t)(hnd ? p.head_dim_qk : p.num_kv_heads * p.head_dim_qk);
   sp.page_rows = (uint32_t)(p.layout == DA_LAYOUT_PAGED_HND ? p.num_kv_heads * p.page_size : p.page_size);
+  const bool fm = p.mask_kind == DA_MASK_FLASHMASK;
+  sp.mask_iv = fm ? reinterpret_cast<const int4*>(a->mask_intervals) : nullptr;
+  sp.mask_sum = fm ? reinterpret_cast<const int4*>(a->mask_summary) : nullptr;
+  sp.n_mask_blocks = (p.max_seq_len + da::kMaskBlock - 1) / da::kMaskBlock;
   const uint64_t n_states = (uint64_t)da::output_rows(p) * plan->num_splits;
   float* ws = static_cast<float*>(a->workspace);
   sp.ws_u = ws;
@@ -134,17 +144,20 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   return sp;
 }
 
-template <int FMT, int D, int G, bool PAGED, bool FUSED>
+template <int FMT, int D, int G, bool PAGED, bool FUSED, bool FM>
 void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
-  if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8)
+  if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8) {
+    static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
     hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
-  else if constexpr (use_mfma<FMT, D>())
-    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED>), dim3(grid),
+  } else if constexpr (use_mfma<FMT, D>()) {
+    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED, FM>), dim3(grid),
                        dim3(kWaves * 64), 0, st, sp);
-  else
+  } else {
+    static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
     hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value, FUSED>),
                        dim3(grid), dim3(kWaves * 64), 0, st, sp);
+  }
 }
 
 template <int FMT, int D, bool PAGED>
@@ -154,22 +167,26 @@ void launch_trace(const da::SplitParams& sp, unsigned grid, int64_t* off, int32_
                      dim3(grid), dim3(kWaves * 64), 0, st, sp, off, pos);
 }
 
-template <int FMT, int D, bool PAGED, bool FUSED>
+template <int FMT, int D, bool PAGED, bool FUSED, bool FM>
 bool dispatch_g(int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   switch (g) {
-    case 1: launch_split<FMT, D, 1, PAGED, FUSED>(sp, grid, st); return true;
-    case 2: launch_split<FMT, D, 2, PAGED, FUSED>(sp, grid, st); return true;
-    case 4: launch_split<FMT, D, 4, PAGED, FUSED>(sp, grid, st); return true;
-    case 8: launch_split<FMT, D, 8, PAGED, FUSED>(sp, grid, st); return true;
+    case 1: launch_split<FMT, D, 1, PAGED, FUSED, FM>(sp, grid, st); return true;
+    case 2: launch_split<FMT, D, 2, PAGED, FUSED, FM>(sp, grid, st); return true;
+    case 4: launch_split<FMT, D, 4, PAGED, FUSED, FM>(sp, grid, st); return true;
+    case 8: launch_split<FMT, D, 8, PAGED, FUSED, FM>(sp, grid, st); return true;
     default: return false;
   }
 }
 
-template <int FMT, bool PAGED, bool FUSED>
+template <int FMT, bool PAGED, bool FUSED, bool FM = false>
 bool dispatch_d(int d, int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
-  if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED>(g, sp, grid, st);
-  if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED>(g, sp, grid, st);
-  return false;
+  if constexpr (FM) {
+    return d == 128 && dispatch_g<FMT, 128, PAGED, FUSED, true>(g, sp, grid, st);
+  } else {
+    if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED, false>(g, sp, grid, st);
+    if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED, false>(g, sp, grid, st);
+    return false;
+  }
 }
 
 template <bool FUSED>
@@ -180,12 +197,17 @@ bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned gri
   const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
   switch (p.kv_format) {
     case DA_KV_F32:
+      if (p.mask_kind == DA_MASK_FLASHMASK) return false;
       return paged ? dispatch_d<DA_KV_F32, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
                    : dispatch_d<DA_KV_F32, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
     case DA_KV_BF16:
+      if (p.mask_kind == DA_MASK_FLASHMASK)
+        return paged ? dispatch_d<DA_KV_BF16, true, FUSED, true>(p.head_dim_qk, g, sp, grid, st)
+                     : dispatch_d<DA_KV_BF16, false, FUSED, true>(p.head_dim_qk, g, sp, grid, st);
       return paged ? dispatch_d<DA_KV_BF16, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
                    : dispatch_d<DA_KV_BF16, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
     case DA_KV_I8:
+      if (p.mask_kind == DA_MASK_FLASHMASK) return false;
       return !paged && dispatch_d<DA_KV_I8, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
     default:
       return false;
@@ -293,6 +315,44 @@ extern "C" da_status decode_attn_append(const da_plan* plan, const da_append_arg
     hipLaunchKernelGGL(da::append_kernel<128>, grid, dim3(da::kAppendThreads), 0, st, ap);
   else
     hipLaunchKernelGGL(da::append_kernel<64>, grid, dim3(da::kAppendThreads), 0, st, ap);
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+__global__ void flashmask_summary_kernel(const int4* __restrict__ iv, int4* __restrict__ sum, int B,
+                                         int L, int nblk) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * nblk) return;
+  const int b = i / nblk, J = i - b * nblk;
+  const int j0 = J * da::kMaskBlock, j1 = min(L, j0 + da::kMaskBlock);
+  int4 mn = make_int4(INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX);
+  int4 mx = make_int4(INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN);
+  for (int j = j0; j < j1; ++j) {
+    const int4 v = iv[(int64_t)b * L + j];
+    mn = make_int4(min(mn.x, v.x), min(mn.y, v.y), min(mn.z, v.z), min(mn.w, v.w));
+    mx = make_int4(max(mx.x, v.x), max(mx.y, v.y), max(mx.z, v.z), max(mx.w, v.w));
+  }
+  // (UTS min, UTS max, UTE min, UTE max), (LTS min, LTS max, LTE min, LTE max)
+  sum[(int64_t)i * 2] = make_int4(mn.x, mx.x, mn.y, mx.y);
+  sum[(int64_t)i * 2 + 1] = make_int4(mn.z, mx.z, mn.w, mx.w);
+}
+
+extern "C" da_status decode_attn_flashmask_summarize(const da_plan* plan, const int32_t* intervals,
+                                                     int32_t* summary, void* stream) {
+  if (!plan) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  if (p.mask_kind != DA_MASK_FLASHMASK) return DA_ERR_INVALID;
+  if (p.batch == 0 || p.max_seq_len == 0) return DA_OK;
+  if (!intervals || !summary) return DA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(intervals) & 15u) != 0 || (reinterpret_cast<uintptr_t>(summary) & 15u) != 0)
+    return DA_ERR_INVALID;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  const int nblk = (p.max_seq_len + da::kMaskBlock - 1) / da::kMaskBlock;
+  const int n = p.batch * nblk;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(flashmask_summary_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<const int4*>(intervals),
+                     reinterpret_cast<int4*>(summary), p.batch, p.max_seq_len, nblk);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -23,6 +23,8 @@ struct SplitParams {
   const int32_t* work_order;
   const int32_t* indptr;           // ragged rows / CSR table entries, [B + 1]
   const int32_t* cache_batch_idx;  // contiguous: cache row of each request, or null
+  const int4* mask_iv;             // FlashMask: [B, max_seq_len] (UTS, UTE, LTS, LTE)
+  const int4* mask_sum;            // FlashMask: [B, n_mask_blocks, 2] block min/max pairs
   float* ws_u;
   float* ws_m;
   float* ws_l;
@@ -52,7 +54,8 @@ struct SplitParams {
   int32_t cache_rows;        // contiguous: B_c (0: B); ragged: packed rows
   int32_t num_page_entries;  // CSR table entries
   uint32_t row_stride;       // elements between consecutive row indices
-  uint32_t page_rows;        // paged: row indices per page (P for NHD, H_kv*P for HND)         // paged: page ids are clamped to [0, num_pages)
+  uint32_t page_rows;        // paged: row indices per page (P for NHD, H_kv*P for HND)
+  int32_t n_mask_blocks;     // FlashMask: ceil(max_seq_len / 16)         // paged: page ids are clamped to [0, num_pages)
   float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
 };
 
@@ -89,6 +92,33 @@ __device__ __forceinline__ VisProgram make_vis(int T, int kind, int n_sink, int 
     v.n_vis = T;
   }
   return v;
+}
+
+// ---------------------------------------------------------------------------
+// FlashMask ("M4.5 ...", sections 0x06A-0x06D): key t is hidden from query
+// row q when q lies in [UTS_t, UTE_t) or [LTS_t, LTE_t).  A block of 16 keys
+// is classified for the rows [q, q+1) from its eight min/max values.
+// ---------------------------------------------------------------------------
+constexpr int kMaskBlock = 16;
+enum { kTileSkip = 0, kTileFull = 1, kTilePartial = 2 };
+
+__device__ __forceinline__ bool fm_hidden(const int4& iv, int q) {
+  return (iv.x <= q && q < iv.y) || (iv.z <= q && q < iv.w);
+}
+// relation of rows [q, q+1) to one interval family: 0 covers, 1 overlaps, 2 disjoint
+__device__ __forceinline__ int fm_family(int q, int s_min, int s_max, int e_min, int e_max) {
+  if (q >= s_max && q + 1 <= e_min) return 0;
+  if (q + 1 > s_min && q < e_max) return 1;
+  return 2;
+}
+__device__ __forceinline__ int fm_tile_class(const SplitParams& p, int b, int q, int tile) {
+  const int4* sm = p.mask_sum + ((int64_t)b * p.n_mask_blocks + tile / kMaskBlock) * 2;
+  const int4 u = sm[0], l = sm[1];      // (UTS min, max, UTE min, max), (LTS ..., LTE ...)
+  const int fu = fm_family(q, u.x, u.y, u.z, u.w);
+  const int fl = fm_family(q, l.x, l.y, l.z, l.w);
+  if (fu == 0 || fl == 0) return kTileSkip;
+  if (fu == 2 && fl == 2) return kTileFull;
+  return kTilePartial;
 }
 
 __device__ __forceinline__ int vis_pos(const VisProgram& v, int o) {

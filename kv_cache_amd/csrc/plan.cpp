@@ -111,7 +111,7 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   }
   if (p.mask_kind == DA_MASK_SINK_WINDOW) {
     if (p.window <= 0 || p.n_sink < 0) return DA_ERR_INVALID;
-  } else if (p.mask_kind == DA_MASK_CAUSAL) {
+  } else if (p.mask_kind == DA_MASK_CAUSAL || p.mask_kind == DA_MASK_FLASHMASK) {
     if (p.window != 0 || p.n_sink != 0) return DA_ERR_INVALID;
   }
   if (p.num_queries < 0) return DA_ERR_INVALID;
@@ -159,7 +159,12 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (p.kv_format == DA_KV_I8 &&
       !(p.k_group >= 16 && p.k_group <= 1024 && (p.k_group & (p.k_group - 1)) == 0))
     reasons |= DA_R_INT8_PARAMS;
-  if (p.mask_kind != DA_MASK_CAUSAL && p.mask_kind != DA_MASK_SINK_WINDOW) reasons |= DA_R_MASK_KIND;
+  if (p.mask_kind != DA_MASK_CAUSAL && p.mask_kind != DA_MASK_SINK_WINDOW &&
+      p.mask_kind != DA_MASK_FLASHMASK)
+    reasons |= DA_R_MASK_KIND;
+  if (p.mask_kind == DA_MASK_FLASHMASK &&
+      (p.kv_format != DA_KV_BF16 || p.head_dim_qk != 128 || p.num_queries != 1))
+    reasons |= DA_R_MASK_KIND;
   if (p.num_splits > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;
 
   int num_cus = p.num_cus;
@@ -191,6 +196,8 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   }
   int64_t S = max_vis == 0 ? 1 : ceil_div(max_vis, chunk);
   if (S > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;
+  // FlashMask classifies at most 64 tiles of 16 keys per split
+  if (p.mask_kind == DA_MASK_FLASHMASK && chunk > 64 * 16) reasons |= DA_R_MASK_KIND;
 
   const int64_t grid = (int64_t)p.batch * p.num_kv_heads * S;
   if (grid > 0x7fffffffLL) reasons |= DA_R_INDEX_RANGE;
@@ -230,7 +237,8 @@ extern "C" const char* decode_attn_reason(int bit) {
       "split count above the library maximum",
       "grid or trace size exceeds the index range",
       "current device is not gfx950 or cannot be queried",
-      "unknown mask program",
+      "mask program unknown, or FlashMask outside bf16 / head_dim 128 / one query row / "
+      "splits of at most 1024 keys",
       "(H_q/H_kv) * num_queries must be 1, 2, 4 or 8, and num_queries > 1 needs the causal mask",
   };
   if (bit < 0 || bit >= DA_NUM_REASONS) return "unknown reason bit";

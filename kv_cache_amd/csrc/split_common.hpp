@@ -245,9 +245,21 @@ __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64
   const int n_q = I8 ? quantized_len(p, T) : T;
   const int64_t base = (((int64_t)b * p.num_kv_heads + h) * p.num_splits + s) * p.chunk;
   const RowAddr ra = row_addr<PAGED && !I8>(p, b, h, D);
+  const bool fm = !I8 && p.mask_kind == DA_MASK_FLASHMASK;
+  const int q_row = vis.n_vis - 1;
   for (int tile = begin + wave * TW; tile < end; tile += NWAVES * TW) {
+    // FlashMask: the tile walk of the split kernel (16-key tiles; SKIP tiles
+    // are not read, PARTIAL tiles drop their hidden rows)
+    int cls = kTileFull;
+    if (fm) {
+      cls = fm_tile_class(p, b, q_row, tile);
+      if (cls == kTileSkip) continue;
+    }
     for (int j = lane; j < TW; j += 64) {
       const int o = tile + j;
+      if (fm && cls == kTilePartial && o < end &&
+          fm_hidden(p.mask_iv[(int64_t)b * p.max_seq_len + o], q_row))
+        continue;
       if (o < end) {
         const int t = vis_pos(vis, o);
         int64_t off;

@@ -70,7 +70,7 @@ struct MfmaTile {
 // accumulators per lane and get 3.
 template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 : 3; };
 
-template <int G, bool PAGED, int NWAVES, bool FUSED>
+template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM>
 __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
@@ -144,30 +144,76 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   // the score instructions have read the current ones, its V rows as soon as
   // PV has read the current ones.  The requests after the last tile repeat
   // row end-1 (already cached) and keep the loop free of branches.
+  // FlashMask: lane k classifies tile k of the split (a split has at most 64
+  // tiles of 16 keys); SKIP tiles are never loaded, PARTIAL tiles bring the
+  // interval vectors of their rows with their K rows.  The wave walks its
+  // tiles (k = wave mod NWAVES) that are not SKIP.
+  const int q_row = vis.n_vis - 1;
+  uint64_t walk = 0, partial = 0;
+  if constexpr (FM) {
+    const int nt = (end - begin + TW - 1) / TW;
+    const int cls = lane < nt ? fm_tile_class(p, b, q_row, begin + TW * lane) : kTileSkip;
+    uint64_t every = 0;
+    for (int k = wave; k < 64; k += NWAVES) every |= 1ull << k;
+    walk = __ballot(cls != kTileSkip) & every;
+    partial = __ballot(cls == kTilePartial);
+  }
+  const int past = end + NWAVES * TW * 2;     // any ordinal >= end: row_index clamps it
+  auto first_tile = [&]() -> int {
+    if constexpr (!FM) return begin + wave * TW;
+    else return walk ? begin + TW * __builtin_ctzll(walk) : past;
+  };
+  auto step = [&](int tile) -> int {
+    if constexpr (!FM) {
+      return tile + NWAVES * TW;
+    } else {
+      if (tile >= end) return past;
+      const int k = (tile - begin) / TW;
+      const uint64_t rest = k >= 63 ? 0ull : walk & (~0ull << (k + 1));
+      return rest ? begin + TW * __builtin_ctzll(rest) : past;
+    }
+  };
+  int4 ivt = make_int4(0, 0, 0, 0);   // FlashMask intervals of row tile + n (PARTIAL tiles)
+  auto issue_iv = [&](int tile) {
+    if constexpr (FM) {
+      if (tile < end && ((partial >> ((tile - begin) / TW)) & 1))
+        ivt = p.mask_iv[(int64_t)b * p.max_seq_len + min(tile + n, end - 1)];
+    }
+  };
+
   MfmaTile t;
-  int tile = begin + wave * TW;
+  int tile = first_tile();
   // Row indices run one tile ahead of the loads that use them, so a paged
   // cache's block-table lookup is off the load path.
   uint32_t ri = 0, ri_ahead = 0;
   if (tile < end) {
     ri = row_index(tile);
     issue_k(ri, t.k);
+    issue_iv(tile);
     issue_v(ri, t.v);
-    ri_ahead = row_index(tile + NWAVES * TW);
+    ri_ahead = row_index(step(tile));
   }
-  for (; tile < end; tile += NWAVES * TW) {
-    const int next_tile = tile + NWAVES * TW;
+  for (; tile < end; tile = step(tile)) {
+    const int next_tile = step(tile);
+    uint32_t hidden = 0;                  // rows of this tile hidden by FlashMask (bit r)
+    if constexpr (FM) {
+      if ((partial >> ((tile - begin) / TW)) & 1)
+        hidden = (uint32_t)__ballot(fm_hidden(ivt, q_row)) & 0xFFFFu;
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[c]),
                                                     __builtin_bit_cast(bf16x8_t, qop[c]), acc, 0, 0, 0);
     ri = ri_ahead;
-    ri_ahead = row_index(next_tile + NWAVES * TW);
+    ri_ahead = row_index(step(next_tile));
     issue_k(ri, t.k);
+    issue_iv(next_tile);
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < end_n) ? acc[i] * p.qscale : -INFINITY;
+    for (int i = 0; i < 4; ++i)
+      sc[i] = (tile + 4 * kg + i < end_n && !((hidden >> (4 * kg + i)) & 1u)) ? acc[i] * p.qscale
+                                                                             : -INFINITY;
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));

@@ -39,3 +39,4 @@ from .quant import (  # noqa: F401
     quantize_symmetric_rows, write_int8_cache_oracle, quantized_count, kivi_empty_state,
     kivi_append, kivi_state_parts, kivi_state_from_parts,
 )
+from . import flashmask  # noqa: F401

@@ -31,6 +31,7 @@ import numpy as np
 from .address import (csr_page, hnd_offset, nhd_offset, paged_hnd_offset, paged_nhd_offset,
                       ragged_nhd_offset, ring_slot)
 from .numerics import decode, decode_bf16, decode_f16
+from . import flashmask
 from .quant import quantized_count
 from .state import EMPTY, finalize, merge_state, summarize_allowed
 from .visibility import query_row_length, visible_positions
@@ -146,7 +147,11 @@ def attend(prob, buf, heads=None, with_trace: bool = False):
     for b in range(B):
         T = int(buf["seq_lens"][b])
         for qi in range(C):
-            A = visible_positions(query_row_length(T, C, qi), prob.mask_kind, prob.n_sink, prob.window)
+            if prob.mask_kind == "flashmask":
+                A = flashmask.visible_columns(query_row_length(T, C, qi), buf["mask_intervals"][b])
+            else:
+                A = visible_positions(query_row_length(T, C, qi), prob.mask_kind, prob.n_sink,
+                                      prob.window)
             last = qi == C - 1
             for h in range(Hkv):
                 if want is not None and (b, h) not in want:

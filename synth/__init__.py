@@ -507,3 +507,43 @@ def relayout(w: Workload, layout: str, page_table: str = "dense", cache_rows: in
 
 def _dt_name(a: np.ndarray) -> str:
     return "f32" if a.dtype == np.float32 else "bf16"
+
+
+# --------------------------------------------------------------------------
+# FlashMask column intervals for the decode row
+# --------------------------------------------------------------------------
+FLASHMASK_OPEN = 1 << 30     # an end that no query row reaches
+
+
+def flashmask_intervals(seed: int, seq_lens, L: int, block: int = 16) -> np.ndarray:
+    """int32 [B, L, 4] (UTS, UTE, LTS, LTE) per key column, seeded, chosen so
+    that the decode row q = T_b - 1 of each request meets whole blocks that it
+    cannot see (documents closed before q: LT = [doc_end, open)), whole blocks
+    it sees (empty intervals) and blocks with scattered hidden columns (UT
+    intervals around q), in runs of a few blocks.  Columns >= T_b get random
+    intervals."""
+    g = rng(seed + 5151)
+    B = len(seq_lens)
+    iv = np.zeros((B, L, 4), dtype=np.int64)
+    iv[:, :, 2] = FLASHMASK_OPEN      # LT empty: [open, open)
+    iv[:, :, 3] = FLASHMASK_OPEN
+    for b, T in enumerate(int(t) for t in seq_lens):
+        q = T - 1
+        j = 0
+        while j < L:
+            run = int(g.integers(1, 5)) * block
+            kind = int(g.integers(0, 3))
+            hi = min(L, j + run)
+            if kind == 0 and q >= 0:          # a closed document: hidden from q on
+                iv[b, j:hi, 2] = int(g.integers(max(0, q - 3), q + 1))
+                iv[b, j:hi, 3] = FLASHMASK_OPEN
+            elif kind == 2 and q >= 0:        # scattered hidden columns around q
+                hide = g.random(hi - j) < 0.4
+                lo_ = g.integers(max(0, q - 5), q + 1, size=hi - j)
+                up_ = g.integers(q + 1, q + 6, size=hi - j)
+                iv[b, j:hi, 0] = np.where(hide, lo_, 0)
+                iv[b, j:hi, 1] = np.where(hide, up_, 0)
+            j = hi
+        if T < L:                              # never read: random garbage intervals
+            iv[b, T:, :2] = np.sort(g.integers(0, L, size=(L - T, 2)), axis=1)
+    return iv.astype(np.int32)

@@ -34,6 +34,17 @@ class DeviceWorkload:
         self.dev = {k: to_dev(v) for k, v in w.buffers.items()}
         self.order = None
 
+    def summarize_mask(self, plan):
+        """FlashMask block summaries of the device intervals, by the library."""
+        t = torch()
+        p = self.w.problem
+        nblk = (p.max_seq_len + 15) // 16
+        self.dev["mask_summary"] = t.zeros((p.batch, nblk, 8), dtype=t.int32, device="cuda")
+        ka.decode_attn_flashmask_summarize(plan, self.dev["mask_intervals"], self.dev["mask_summary"],
+                                           t.cuda.current_stream().cuda_stream)
+        t.cuda.synchronize()
+        return self.dev["mask_summary"].cpu().numpy()
+
     def schedule(self, plan):
         """Use the library's largest-first work order for this plan."""
         lens = self.w.buffers["seq_lens"]
@@ -45,7 +56,8 @@ class DeviceWorkload:
                             k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
                             k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
                             block_table=d.get("block_table"), work_order=self.order,
-                            indptr=d.get("indptr"), cache_batch_idx=d.get("cache_batch_idx"))
+                            indptr=d.get("indptr"), cache_batch_idx=d.get("cache_batch_idx"),
+                            mask_intervals=d.get("mask_intervals"), mask_summary=d.get("mask_summary"))
 
 
 def _outputs(w):

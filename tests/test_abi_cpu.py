@@ -30,6 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) >= {"decode_attn_plan", "decode_attn_run", "decode_attn_combine",
                           "decode_attn_forward", "decode_attn_workspace_init",
                           "decode_attn_schedule", "decode_attn_append",
+                          "decode_attn_flashmask_summarize",
                           "decode_attn_trace_indices", "decode_attn_reason",
                           "decode_attn_status_string"}
     for n in names:
@@ -39,7 +40,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(ka.Problem) == 28 * 4
     assert ctypes.sizeof(ka.Plan) == 8 + 112 + 16 + 8 + 16
-    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 3 * 8
+    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 5 * 8
 
 
 def P(**kw):
@@ -258,3 +259,14 @@ def test_query_rows_plan_checks_and_workspace():
     st, _, _, rs = plan(P(num_queries=8, num_q_heads=8, num_kv_heads=8))
     assert st == ka.DA_OK
     assert ka.decode_attn_reason(12)
+
+
+def test_flashmask_plan_domain():
+    st, pl, _, rs = plan(P(mask_kind="flashmask"))
+    assert st == ka.DA_OK and pl.chunk <= 1024
+    for kw in (dict(kv_format="f32", q_dtype="f32"), dict(head_dim=64), dict(num_queries=2),
+               dict(num_splits=2)):                       # 4096 / 2 keys per split > 1024
+        st, _, _, rs = plan(P(mask_kind="flashmask", **kw))
+        assert st == ka.DA_ERR_UNSUPPORTED and rs & (1 << 11), kw
+    st, _, _, _ = plan(P(mask_kind="flashmask", window=4))
+    assert st == ka.DA_ERR_INVALID

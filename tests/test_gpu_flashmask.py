@@ -1,0 +1,89 @@
+"""GPU parity for the FlashMask mask program (M4.5 §0x06A-§0x06D): library
+block summaries equal the oracle's, attention equals the oracle over the
+visible columns of the decode row, and the traced rows (SKIP tiles unread,
+hidden rows of PARTIAL tiles dropped) equal the oracle's visible set."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import flashmask as fm
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    H.announce(request.node.nodeid)
+
+
+def _masked(w, seed):
+    p = w.problem
+    L = p.max_seq_len
+    w.buffers["mask_intervals"] = synth.flashmask_intervals(seed, w.buffers["seq_lens"], L)
+    p.mask_kind = "flashmask"
+    return w
+
+
+def _ready(w, num_splits=None):
+    dw = H.DeviceWorkload(w)
+    plan, _ = H.plan_for(w, num_splits)
+    summ = dw.summarize_mask(plan)
+    ref = np.stack([fm.block_summary(w.buffers["mask_intervals"][b], 16) for b in range(w.problem.batch)])
+    assert np.array_equal(summ, ref)
+    return dw
+
+
+@pytest.mark.parametrize("S", [None, 3, 9])
+def test_flashmask_contiguous(S):
+    lens = [3000, 517, 16, 1, 0, 2222]
+    w = _masked(synth.make_contiguous(61, len(lens), 32, 8, 128, lens, kv_capacity=3008), 1)
+    dw = _ready(w, S)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.forward(w, num_splits=S, dw=dw)
+    H.check_rows(O, L, Or, Lr, 2e-3)
+    O, L, _ = H.run(w, num_splits=S, dw=dw)
+    H.check_rows(O, L, Or, Lr, 2e-3)
+
+
+def test_flashmask_paged_and_trace():
+    lens = [1500, 33, 700]
+    w = _masked(synth.make_paged(62, len(lens), 8, 2, 128, lens, page_size=16), 2)
+    dw = _ready(w)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.forward(w, dw=dw)
+    H.check_rows(O, L, Or, Lr, 2e-3)
+    _trace_rows_fm(w, dw, 4)
+
+
+def test_flashmask_trace_contiguous():
+    lens = [2000, 100, 3]
+    w = _masked(synth.make_contiguous(63, len(lens), 8, 2, 128, lens, kv_capacity=2000), 3)
+    dw = _ready(w, 3)
+    _trace_rows_fm(w, dw, 3)
+
+
+def test_flashmask_everything_hidden():
+    lens = [400, 64]
+    w = synth.make_contiguous(64, 2, 8, 2, 128, lens, kv_capacity=400)
+    iv = np.zeros((2, 400, 4), np.int32)
+    iv[:, :, 0], iv[:, :, 1] = 0, 1 << 30          # UT covers every query row
+    iv[:, :, 2], iv[:, :, 3] = 1 << 30, 1 << 30
+    w.buffers["mask_intervals"] = iv
+    w.problem.mask_kind = "flashmask"
+    dw = _ready(w)
+    O, L, _ = H.forward(w, dw=dw)
+    assert np.all(O == 0) and not np.signbit(O).any() and np.all(np.isneginf(L))
+
+
+def _trace_rows_fm(w, dw, S):
+    offs, pos, plan = H.trace(w, num_splits=S, dw=dw)
+    _, _, tr = oracle.attend(w.problem, w.buffers, with_trace=True)
+    for (b, h), (p_ref, o_ref, _) in tr.items():
+        got_p = pos[b, h].reshape(-1)
+        got_o = offs[b, h].reshape(-1)
+        sel = got_p >= 0
+        order = np.argsort(got_p[sel], kind="stable")
+        assert np.array_equal(got_p[sel][order], p_ref), (b, h)
+        assert np.array_equal(got_o[sel][order], o_ref), (b, h)
