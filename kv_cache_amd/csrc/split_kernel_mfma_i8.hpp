@@ -17,9 +17,10 @@
 //    mantissa of 1024 + (c + 128)), is multiplied by its fp16 channel scale in
 //    packed fp16 arithmetic as an unevaluated sum hi + lo (exact to 2^-22),
 //    and both parts feed v_mfma_f32_16x16x32_f16 with q in fp16 (B operand).  Each row reads its
-//    own 128-token group's scales, so groups never need special handling.
-//    The V scale of a row multiplies that row's softmax weight (section
-//    0x03C) before PV; the denominator uses the unscaled weight.
+//    own 128-token group's scales (staged in LDS per phase of the split), so
+//    groups never need special handling.  The V scale of a row multiplies
+//    that row's softmax weight (section 0x03C) before PV; the denominator
+//    uses the unscaled weight.  Each wave keeps two tiles in flight.
 //  * residual part: exactly the bf16 kernel's tile (A = bf16 K rows, B = q).
 #pragma once
 
@@ -99,6 +100,11 @@ struct PairLoop<G, G> {
   __device__ __forceinline__ static void accumulate(float (&)[G][8], uint32_t, const uint32_t (&)[8]) {}
 };
 
+// K scale rows staged in LDS per workgroup (256 B each for D = 128): enough
+// for a split of 22 full 128-token groups plus partial groups at both ends
+// of the sink and window runs.
+constexpr int kI8ScaleSlots = 24;
+
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
 template <int G, int NWAVES, bool FUSED>
 __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma_i8(SplitParams p) {
@@ -148,13 +154,13 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 
   const uint32_t row_stride = (uint32_t)(p.num_kv_heads * D);
   const int64_t code_base = ((int64_t)b * p.kv_capacity * p.num_kv_heads + h) * D;
-  const int8_t* kc = static_cast<const int8_t*>(p.k) + code_base + 8 * kg;
+  const int8_t* kc = static_cast<const int8_t*>(p.k) + code_base;
   const int8_t* vc = static_cast<const int8_t*>(p.v) + code_base + 8 * n;
   const int64_t res_base = ((int64_t)b * p.residual_len * p.num_kv_heads + h) * D;
   const uint16_t* kr = static_cast<const uint16_t*>(p.k_resid) + res_base + 8 * kg;
   const uint16_t* vr = static_cast<const uint16_t*>(p.v_resid) + res_base + 8 * n;
   const int n_groups = (p.kv_capacity + (1 << p.k_group_shift) - 1) >> p.k_group_shift;
-  const uint16_t* ks = p.k_scale + ((int64_t)b * n_groups * p.num_kv_heads + h) * D + 8 * kg;
+  const uint16_t* ks = p.k_scale + ((int64_t)b * n_groups * p.num_kv_heads + h) * D;
   const uint16_t* vs = p.v_scale + (int64_t)b * p.kv_capacity * p.num_kv_heads + h;
 
   float m_run = -INFINITY;   // running max of head n (base 2)
@@ -183,70 +189,149 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     m_run = mn;
     if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
   };
+  // Online softmax over the 8 scores of this lane for two tiles (rows
+  // 4kg+i of tiles ta and tb, head n).
+  auto softmax2 = [&](const f32x4_t& acc, const f32x4_t& acc2, int ta, int tb, int lim, float (&pr)[8]) {
+    float sc[8];
+    const int l = min(lim, lim_n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = (ta + 4 * kg + i < l) ? acc[i] * p.qscale : -INFINITY;
+      sc[4 + i] = (tb + 4 * kg + i < l) ? acc2[i] * p.qscale : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m_run, mt);
+    const float mz = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m_run - mz);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(sc[i] - mz);
+    l_run = fmaf(l_run, alpha, ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+    m_run = mn;
+    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);
+  };
 
   // ================= int8 part: ordinals [begin, mid) =================
+  // K codes.  Lane (n, kg) holds 32 codes of row n of the tile: bytes
+  // [16kg, 16kg+16) and [64+16kg, 64+16kg+16), so each of the two 16-byte
+  // requests covers 64 contiguous bytes of every row (half a cache line)
+  // instead of 32-byte quarters.  Its MFMA slice c then carries the channels
+  // kch(c) .. kch(c)+7 below; q and the scales are read in the same order,
+  // which leaves every dot product unchanged (it is a sum over channels).
+  //
+  // Scales.  The K scale rows of the 128-token groups a phase of the split
+  // touches are staged in LDS (the rows' positions form at most two runs,
+  // sinks and window); a phase is short enough for the table, so a tile in
+  // flight holds only codes and V scales and each wave keeps two tiles in
+  // flight.  Splits usually fit in one phase.
+  auto kch = [&](int c) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1); };
+  __shared__ uint4 ksc[kI8ScaleSlots][16];
   if (begin < mid) {
-    // B operand in fp16: q[head n][32c + 8kg .. +7] (bf16 values are exact in
-    // fp16 over the normal range of N(0,1)-scale queries).
     uint4 qh[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 x = q_lds[c][lane];
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (n < G)
+        x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + out_row(p, b, h, n) * D + kch(c));
+      // bf16 values of N(0,1)-scale queries are exact in fp16
       qh[c] = make_uint4(pack_f16(bf16_lo(x.x), bf16_hi(x.x)), pack_f16(bf16_lo(x.y), bf16_hi(x.y)),
                          pack_f16(bf16_lo(x.z), bf16_hi(x.z)), pack_f16(bf16_lo(x.w), bf16_hi(x.w)));
     }
-    auto pos = [&](int o) { return (uint32_t)vis_pos(vis, min(o, mid - 1)); };
-    auto issue_k = [&](int tile, uint2 (&k)[4], uint4 (&sk)[4]) {
-      const uint32_t t = pos(tile + n);
-      const int8_t* row = kc + (uint64_t)t * row_stride;
-      const uint16_t* srow = ks + (uint64_t)(t >> p.k_group_shift) * row_stride;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        k[c] = stream_load(reinterpret_cast<const uint2*>(row + 32 * c));
-        sk[c] = *reinterpret_cast<const uint4*>(srow + 32 * c);
+    const int sh = p.k_group_shift;
+    const int phase = (kI8ScaleSlots - 4) << sh;   // two runs: at most len/G + 4 groups
+    for (int pb = begin; pb < mid; pb += phase) {
+      const int pe = min(pb + phase, mid);
+      int a0 = 0, nA = 0, b0 = 0, nB = 0;
+      const int sink_end = min(pe, vis.ns);              // ordinals [pb, sink_end) sit at o
+      if (pb < sink_end) {
+        a0 = pb >> sh;
+        nA = ((sink_end - 1) >> sh) - a0 + 1;
       }
-    };
-    auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t t = pos(tile + 4 * kg + j);
-        v[j] = stream_load(reinterpret_cast<const uint2*>(vc + (uint64_t)t * row_stride));
-        sv[j] = vs[(int64_t)t * p.num_kv_heads];
+      const int wbeg = max(pb, vis.ns);                  // ordinals [wbeg, pe) sit at o + gap
+      if (wbeg < pe) {
+        b0 = (wbeg + vis.gap) >> sh;
+        nB = ((pe - 1 + vis.gap) >> sh) - b0 + 1;
       }
-    };
-    uint2 kt[4], vt[4];
-    uint4 skt[4];
-    uint32_t svt[4];
-    int tile = begin + wave * TW;
-    if (tile < mid) {
-      issue_k(tile, kt, skt);
-      issue_v(tile, vt, svt);
-    }
-    for (; tile < mid; tile += STEP) {
-      const int next_tile = tile + STEP;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint4 hi, lo;
-        dequant_f16(kt[c], skt[c], hi, lo);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hi),
-                                                     __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, lo),
-                                                     __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+      if (pb != begin) __syncthreads();                  // the previous phase has read its table
+      for (int idx = threadIdx.x; idx < (nA + nB) * 16; idx += NWAVES * 64) {
+        const int k = idx >> 4;
+        const int g = k < nA ? a0 + k : b0 + (k - nA);
+        ksc[k][idx & 15] = *reinterpret_cast<const uint4*>(ks + (uint64_t)g * row_stride + 8 * (idx & 15));
       }
-      issue_k(next_tile, kt, skt);
-      float pr[4];
-      softmax(acc, tile, mid, pr);
-      // PV: weight p * sigma_V of each row in fp16 (relative error 2^-11,
-      // far inside the int8 format's own error), rows paired for v_dot2.
+      __syncthreads();
+
+      auto pos = [&](int o) { return (uint32_t)vis_pos(vis, min(o, pe - 1)); };
+      // LDS slot of the scale row of position t (sink run first, then window run)
+      auto slot = [&](uint32_t t) {
+        const int g = (int)(t >> sh);
+        return (nA > 0 && g < a0 + nA) ? g - a0 : nA + (g - b0);
+      };
+      auto issue_k = [&](int tile, uint4 (&k)[2]) {
+        const int8_t* row = kc + (uint64_t)pos(tile + n) * row_stride;
+        k[0] = stream_load(reinterpret_cast<const uint4*>(row + 16 * kg));
+        k[1] = stream_load(reinterpret_cast<const uint4*>(row + 64 + 16 * kg));
+      };
+      auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        uint32_t vp[8];
-        v_pairs(vt[j], vt[j + 1], vp);
-        const uint32_t wp = pack_f16(pr[j] * f16_bits_to_f32(svt[j]), pr[j + 1] * f16_bits_to_f32(svt[j + 1]));
-        PairLoop<G>::accumulate(u, wp, vp);
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t t = pos(tile + 4 * kg + j);
+          v[j] = stream_load(reinterpret_cast<const uint2*>(vc + (uint64_t)t * row_stride));
+          sv[j] = vs[(int64_t)t * p.num_kv_heads];
+        }
+      };
+      auto scores = [&](int tile, const uint4 (&k)[2]) {
+        const int sl = slot(pos(tile + n));
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 w = k[c >> 1];
+          const uint2 codes = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
+          uint4 hi, lo;
+          dequant_f16(codes, ksc[sl][kch(c) >> 3], hi, lo);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hi),
+                                                       __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, lo),
+                                                       __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+        }
+        return acc;
+      };
+      // PV: weight p * sigma_V of each row in fp16 (relative error 2^-11, far
+      // inside the int8 format's own error), rows paired for v_dot2.
+      auto pv = [&](const uint2 (&v)[4], const uint32_t (&sv)[4], const float* pr) {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          uint32_t vp[8];
+          v_pairs(v[j], v[j + 1], vp);
+          const uint32_t wp = pack_f16(pr[j] * f16_bits_to_f32(sv[j]), pr[j + 1] * f16_bits_to_f32(sv[j + 1]));
+          PairLoop<G>::accumulate(u, wp, vp);
+        }
+      };
+      uint4 ka[2], kb[2];
+      uint2 va[4], vb[4];
+      uint32_t sva[4], svb[4];
+      int tile = pb + wave * TW;
+      // the loop's request order (K, K, V, V), so its waits leave newer requests in flight
+      if (tile < pe) {
+        issue_k(tile, ka);
+        issue_k(tile + STEP, kb);
+        issue_v(tile, va, sva);
+        issue_v(tile + STEP, vb, svb);
       }
-      issue_v(next_tile, vt, svt);
+      for (; tile < pe; tile += 2 * STEP) {
+        const int tb = tile + STEP;
+        const f32x4_t acc = scores(tile, ka);
+        const f32x4_t acc2 = scores(tb, kb);
+        issue_k(tile + 2 * STEP, ka);
+        issue_k(tb + 2 * STEP, kb);
+        float pr[8];
+        softmax2(acc, acc2, tile, tb, pe, pr);
+        pv(va, sva, pr);
+        pv(vb, svb, pr + 4);
+        issue_v(tile + 2 * STEP, va, sva);
+        issue_v(tb + 2 * STEP, vb, svb);
+      }
     }
   }
 

@@ -212,6 +212,26 @@ def test_int8_causal_small():
     H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
+def test_int8_scale_table_edges():
+    # many 64-token groups in one split (more than the staged scale table
+    # holds: per-tile scale reads) and a window whose first group is the
+    # sinks' last group (the two position runs share a scale row)
+    w = synth.make_int8(14, 2, 8, 2, 128, [4000, 1500], k_group=64, residual_len=64,
+                        kv_capacity=4000)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (1, 2, 0):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+    w = synth.make_int8(15, 2, 8, 2, 128, [1000, 700], mask_kind="sink_window", n_sink=100,
+                        window=890, k_group=64, residual_len=64, kv_capacity=1000)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (1, 3, 0):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_cfg5_full(seed):
     w = synth.config(5, seed)
