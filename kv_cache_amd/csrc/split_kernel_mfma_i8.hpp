@@ -78,6 +78,15 @@ __device__ __forceinline__ void v_pairs(uint2 a, uint2 b, uint32_t (&out)[8]) {
   }
 }
 
+// Channel e of two rows a, b as one fp16 pair (the word v_pairs makes for e).
+__device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
+  const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t wa = e < 4 ? a.x : a.y, wb = e < 4 ? b.x : b.y;
+  const uint32_t sel = (uint32_t)(e & 3) | 0x0C00u | ((uint32_t)(4 + (e & 3)) << 16) | 0x0C000000u;
+  const uint32_t bits = __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
+}
+
 template <int I>
 __device__ __forceinline__ uint32_t row_bcast_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + I, 0xF, 0xF, false);
@@ -165,33 +174,13 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 
   float m_run = -INFINITY;   // running max of head n (base 2)
   float l_run = 0.f;         // partial denominator over rows 4kg .. 4kg+3 of every tile
-  float u[G][8];
+  f32x4_t o[8];              // int8 part: PV accumulators in the matrix-core layout
 #pragma unroll
-  for (int i = 0; i < G; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u[i][e] = 0.f;
+  for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Online softmax over the 4 scores of this lane (rows 4kg+i, head n);
-  // returns the weights and rescales l and u.
-  auto softmax = [&](const f32x4_t& acc, int tile, int lim, float (&pr)[4]) {
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < min(lim, lim_n)) ? acc[i] * p.qscale : -INFINITY;
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m_run, mt);
-    const float mz = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fast_exp2(m_run - mz);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - mz);
-    l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = mn;
-    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
-  };
   // Online softmax over the 8 scores of this lane for two tiles (rows
   // 4kg+i of tiles ta and tb, head n).
-  auto softmax2 = [&](const f32x4_t& acc, const f32x4_t& acc2, int ta, int tb, int lim, float (&pr)[8]) {
+  auto softmax2 = [&](const f32x4_t& acc, const f32x4_t& acc2, int ta, int tb, int lim, float (&pr)[8]) -> float {
     float sc[8];
     const int l = min(lim, lim_n);
 #pragma unroll
@@ -210,7 +199,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(sc[i] - mz);
     l_run = fmaf(l_run, alpha, ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
     m_run = mn;
-    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);
+    return alpha;
   };
 
   // ================= int8 part: ordinals [begin, mid) =================
@@ -297,15 +286,38 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
         }
         return acc;
       };
-      // PV: weight p * sigma_V of each row in fp16 (relative error 2^-11, far
-      // inside the int8 format's own error), rows paired for v_dot2.
-      auto pv = [&](const uint2 (&v)[4], const uint32_t (&sv)[4], const float* pr) {
+      // PV on the matrix cores, O (heads x channels) += P (heads x rows) V
+      // (rows x channels) over the 32 rows of the two tiles: A = the weights
+      // p * sigma_V in fp16 (relative error 2^-11, far inside the int8 format's
+      // own error; lane (n, kg) already holds head n's weights of rows 4kg..4kg+3
+      // of both tiles, the A operand's k = 8kg .. 8kg+7), B = the V codes as
+      // exact fp16, whose lane (n, kg) holds the same rows at 8 channels 8n ..
+      // 8n+7: instruction c takes channel 8n + c of each row, so column n of
+      // block c is channel 8n + c and no code moves between lanes.  The
+      // accumulator o[c] of lane (n, kg) holds heads 4kg .. 4kg+3 at channel
+      // 8n + c.  The denominator uses the unscaled weights.
+      auto pv2 = [&](const uint2 (&a)[4], const uint32_t (&sa)[4], const uint2 (&bv)[4],
+                     const uint32_t (&sb)[4], const float (&pr)[8]) {
+        uint4 w;
+        w.x = pack_f16(pr[0] * f16_bits_to_f32(sa[0]), pr[1] * f16_bits_to_f32(sa[1]));
+        w.y = pack_f16(pr[2] * f16_bits_to_f32(sa[2]), pr[3] * f16_bits_to_f32(sa[3]));
+        w.z = pack_f16(pr[4] * f16_bits_to_f32(sb[0]), pr[5] * f16_bits_to_f32(sb[1]));
+        w.w = pack_f16(pr[6] * f16_bits_to_f32(sb[2]), pr[7] * f16_bits_to_f32(sb[3]));
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          uint32_t vp[8];
-          v_pairs(v[j], v[j + 1], vp);
-          const uint32_t wp = pack_f16(pr[j] * f16_bits_to_f32(sv[j]), pr[j + 1] * f16_bits_to_f32(sv[j + 1]));
-          PairLoop<G>::accumulate(u, wp, vp);
+        for (int c = 0; c < 8; ++c) {
+          const uint4 vcol = make_uint4(v_pair_word(a[0], a[1], c), v_pair_word(a[2], a[3], c),
+                                        v_pair_word(bv[0], bv[1], c), v_pair_word(bv[2], bv[3], c));
+          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, w),
+                                                        __builtin_bit_cast(f16x8_t, vcol), o[c], 0, 0, 0);
+        }
+      };
+      // running-maximum rescale of o: lane (n, kg) scales heads 4kg .. 4kg+3
+      auto rescale_o = [&](float alpha) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[c][i] *= a;
         }
       };
       uint4 ka[2], kb[2];
@@ -326,14 +338,42 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
         issue_k(tile + 2 * STEP, ka);
         issue_k(tb + 2 * STEP, kb);
         float pr[8];
-        softmax2(acc, acc2, tile, tb, pe, pr);
-        pv(va, sva, pr);
-        pv(vb, svb, pr + 4);
+        const float alpha = softmax2(acc, acc2, tile, tb, pe, pr);
+        if (__any(alpha != 1.f)) rescale_o(alpha);   // skipped while no head maximum moves
+        pv2(va, sva, vb, svb, pr);
         issue_v(tile + 2 * STEP, va, sva);
         issue_v(tb + 2 * STEP, vb, svb);
       }
     }
   }
+
+  // u in the vector-ALU layout of the residual part and the state merge: lane
+  // (n, kg) holds a partial sum of head i at channels 8n .. 8n+7 (the partials
+  // of the four kg lanes add up); head i of o sits in the kg = i/4 lanes.
+  float u[G][8];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? o[e][i & 3] : 0.f;
+
+  // Online softmax over the 4 scores of this lane (rows 4kg+i, head n);
+  // returns the weights and rescales l and u.
+  auto softmax = [&](const f32x4_t& acc, int tile, int lim, float (&pr)[4]) {
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < min(lim, lim_n)) ? acc[i] * p.qscale : -INFINITY;
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m_run, mt);
+    const float mz = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m_run - mz);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - mz);
+    l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = mn;
+    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
+  };
 
   // ============ residual part: ordinals [mid, end), bf16 rows ============
   if (mid < end) {
