@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   int b, h, s;
   decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int n = lane & 15;     // K row of the tile / score column (head)
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
 

@@ -51,8 +51,9 @@ __device__ __forceinline__ void dequant_f16(uint2 codes, uint4 scales, uint4& hi
   const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t x = w[i >> 1] >> (16 * (i & 1));            // two code bytes in the low half
-    const uint32_t bits = (x & 0xffu) | ((x & 0xff00u) << 8) | 0x64006400u;
+    // code bytes 2(i&1) and 2(i&1)+1 of word i/2 under the exponent byte 0x64
+    const uint32_t sel = (uint32_t)(2 * (i & 1)) | 0x0400u | ((uint32_t)(2 * (i & 1) + 1) << 16) | 0x04000000u;
+    const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, w[i >> 1], sel);
     const f16x2_t c = __builtin_bit_cast(f16x2_t, bits) - bias;
     const f16x2_t sg = __builtin_bit_cast(f16x2_t, sc[i]);
     const f16x2_t h = c * sg;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   int b, h, s;
   decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int n = lane & 15;     // K row of the tile / score column (head)
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
 
