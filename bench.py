@@ -154,7 +154,9 @@ class GpuWorkload:
         self.args = [ka.make_args(d["q"], d["k"], d["v"], self.seq_lens, self.ws, self.ws_bytes,
                                   k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
                                   k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
-                                  block_table=d.get("block_table"), work_order=self.order)
+                                  block_table=d.get("block_table"), work_order=self.order,
+                                  partition=getattr(self, "part", None),
+                                  partition_items=getattr(self, "part_items", 0))
                      for d in self.sets]
 
     def use_schedule(self, on=True):
@@ -163,6 +165,23 @@ class GpuWorkload:
         self.order = (torch.from_numpy(self.ka.decode_attn_schedule(self.plan, self.lens)).to("cuda")
                       if on else None)
         self.make_all_args()
+
+    def use_partition(self, items_per_head=0):
+        """Balanced partition of the batch from the host lengths (decode_attn_partition)."""
+        torch = self.torch
+        part, items = self.ka.decode_attn_partition(self.plan, self.lens, items_per_head)
+        self.part, self.part_items = torch.from_numpy(part).to("cuda"), items
+        self.make_all_args()
+        # the states a partitioned run writes (and the combine reads): one per
+        # request piece and query head, instead of B*H_q*S
+        B, L = self.B, int(part[1])
+        P = [int(x) for x in part[4:5 + B]]
+        pieces = sum((P[b + 1] - 1) // L - P[b] // L + 1 for b in range(B) if P[b + 1] > P[b])
+        ws_old = B * self.Hq * self.S * (self.D + 2) * 4
+        ws_new = pieces * self.Hq * (self.D + 2) * 4
+        self.split_bytes += ws_new - ws_old
+        self.call_bytes += 2 * (ws_new - ws_old)
+        return self
 
     def run(self, i):
         self.ka.decode_attn_run(self.plan, self.args[i % self.nsets], self.stream)
@@ -444,10 +463,15 @@ def main():
         wp = GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, lens, seed=2)
         builtin_order = wp.time(wp.fwd, 30, 5)
         wp.use_schedule()
+        scheduled = wp.time(wp.fwd, 30, 5)
+        wp.use_schedule(False)
+        wp.use_partition()
         others["paged_ragged"] = wp.report(
             "paged", "B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768] (seed 0), permuted pool, "
-                     "largest-first work order from decode_attn_schedule")
-        others["paged_ragged"]["builtin_order_us_per_call"] = round(builtin_order * 1000, 2)
+                     "balanced partition from decode_attn_partition (equal visible rows per workgroup)")
+        others["paged_ragged"]["partition_items_per_head"] = wp.part_items
+        others["paged_ragged"]["fixed_splits_us_per_call"] = round(builtin_order * 1000, 2)
+        others["paged_ragged"]["fixed_splits_largest_first_us_per_call"] = round(scheduled * 1000, 2)
         del wp
         wi = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
                          mask=(4, 4096))

@@ -166,7 +166,8 @@ typedef struct da_plan {
   int32_t    max_visible;      /* bound on visible rows of one request              */
   int32_t    num_cus;          /* CU count the split heuristic used                 */
   uint64_t   workspace_bytes;  /* states round_up(B*H_q*S*(D + 2)*4, 256), then     */
-                               /* counters round_up(B*H_kv*4, 256)                  */
+                               /* counters round_up(B*H_kv*4, 256), then the        */
+                               /* partition header round_up((B+5)*4, 256)           */
   uint64_t   reserved[2];
 } da_plan;
 
@@ -203,7 +204,13 @@ typedef struct da_plan {
  *               (first round_up(B*H_q*S*(D+2)*4, 256) bytes) is ignored on
  *               entry.  The B*H_kv uint32 arrival counters after it are used
  *               only by decode_attn_forward: they must be zero when it starts
- *               (decode_attn_workspace_init) and it leaves them zero.
+ *               (decode_attn_workspace_init) and it leaves them zero.  The
+ *               last round_up((B+5)*4, 256) bytes receive, from every run, the
+ *               partition header the combine needs (ignored on entry).
+ *   partition   optional int32 descriptor from decode_attn_partition (device copy);
+ *               NULL: the plan's fixed splits.  With a partition the producer grid is
+ *               partition_items*H_kv workgroups of equal work (see decode_attn_partition).
+ *   partition_items  the descriptor's item count W (host value; 0 without partition)
  * q, k, v, k_resid and v_resid must be 16-byte aligned. */
 typedef struct da_args {
   const void*    q;
@@ -222,6 +229,9 @@ typedef struct da_args {
   const int32_t* cache_batch_idx; /* contiguous layouts with cache_rows > 0: [B]; else NULL */
   const int32_t* mask_intervals;  /* DA_MASK_FLASHMASK: [B, max_seq_len, 4] (UTS, UTE, LTS, LTE) */
   const int32_t* mask_summary;    /* DA_MASK_FLASHMASK: [B, ceil(max_seq_len/16), 8]           */
+  const int32_t* partition;       /* NULL, or a descriptor from decode_attn_partition          */
+  int32_t        partition_items; /* W of that descriptor (0 without one)                      */
+  int32_t        reserved0;
 } da_args;
 
 /* Validate the problem (semantic checks first, then every capability
@@ -247,17 +257,49 @@ da_status decode_attn_plan(const da_problem* problem, da_plan* plan,
 da_status decode_attn_schedule(const da_plan* plan, const int32_t* seq_lens_host, int32_t* order,
                                uint64_t order_len);
 
+/* Host-side balanced partition of a ragged batch ("M4.5 ...", sections 0x09E
+ * and 0x09G: a plan built from the lengths gives every workgroup the same
+ * amount of work, as LeanAttention and FlashInfer's planner do, instead of
+ * fixed splits whose last round runs part-empty).  The visible ordinals of
+ * the requests, concatenated in request order (N = sum of N_b), are cut into W
+ * items of L consecutive ordinals (the last may be shorter); workgroup
+ * (i, h_kv) processes item i for K/V head h_kv.  Where an item crosses request
+ * boundaries it produces one state per request piece: piece j of request b
+ * is item floor(P_b / L) + j with P_b = N_0 + ... + N_{b-1}, stored in split
+ * slot j, and request b has last_item(b) - first_item(b) + 1 <= S pieces
+ * (L >= max_b N_b / (S - 1) guarantees it; S >= 2 is required).  The combine
+ * folds exactly those pieces, in ascending order; the arithmetic is the same
+ * split/merge, so the result matches the oracle to the same tolerance (but is
+ * not bitwise equal to the fixed-split result).
+ *   items_per_head  target W (0: 3 workgroups per CU of the plan / H_kv, one round)
+ *   part            host int32 [5 + B + W_max] with W_max = the target W:
+ *                   [W, L, B, 0, P_0 .. P_B, first request of item 0 .. W-1]
+ *   *items_out      W (may be 0 when every request is empty)
+ * Copy part to the device and pass it with W as da_args.partition /
+ * partition_items.  Supported by the bf16 D = 128 matrix-core kernel with the
+ * causal or sink+window mask (any layout).  Errors: DA_ERR_INVALID for a NULL
+ * pointer, a length outside [0, max_seq_len], part_len too small, or N >= 2^31;
+ * DA_ERR_UNSUPPORTED for S < 2; DA_ERR_PLAN_MISMATCH for an altered plan. */
+da_status decode_attn_partition(const da_plan* plan, const int32_t* seq_lens_host, int32_t items_per_head,
+                                int32_t* part, uint64_t part_len, int32_t* items_out);
+
 /* Launch the split kernel: grid B*H_kv*S workgroups; workgroup (b, h_kv, s)
  * owns visible rows [s*chunk, min((s+1)*chunk, N_b)) of request b and the
  * H_q/H_kv query heads sharing h_kv, reads each of its K/V rows once, and
  * writes one (m, l, u) state per query head into the workspace: u fp32
  * [B, H_q, S, D], then m fp32 [B, H_q, S] (natural-log units of the scaled
  * scores), then l fp32 [B, H_q, S].  An empty split writes the identity
- * (m = -inf, l = 0, u = 0); l > 0 marks a valid state. */
+ * (m = -inf, l = 0, u = 0); l > 0 marks a valid state.  With a partition
+ * (da_args.partition) the grid is W*H_kv workgroups and only the pieces of the
+ * partition are written (slots j >= the request's piece count are left as
+ * they were).  Every run also writes the partition header of the workspace
+ * (W = 0 without a partition), which the combine reads. */
 da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream);
 
-/* Launch the combine kernel: for each (b, i, h_q), fold its S states in
- * ascending split order and write out fp32 [B, C, H_q, D] = u/l and, when lse
+/* Launch the combine kernel: for each (b, i, h_q), fold its S states (with
+ * a partition: its pieces, as the workspace's partition header written by
+ * the preceding run says) in ascending split order and write out fp32
+ * [B, C, H_q, D] = u/l and, when lse
  * is not NULL, lse fp32 [B, C, H_q] = m + ln(l); an all-masked row gets
  * O = +0.0 and LSE = -inf.  (State rows, out and lse rows are ordered
  * (b, i, h_q); with C = 1 this is [B, H_q].) */
@@ -277,7 +319,8 @@ da_status decode_attn_combine(const da_plan* plan, const void* workspace,
  * decode_attn_workspace_init; every completed forward leaves them zero), and
  * calls that share a workspace are ordered on one stream.  out must be
  * 16-byte aligned (DA_ERR_INVALID otherwise).  Results match run + combine up
- * to the order of the final fp32 sums. */
+ * to the order of the final fp32 sums.  With a partition, or when S exceeds
+ * the in-kernel fold's limit, it launches run then combine. */
 da_status decode_attn_forward(const da_plan* plan, const da_args* args, float* out, float* lse,
                               void* stream);
 
@@ -303,7 +346,10 @@ da_status decode_attn_workspace_init(const da_plan* plan, void* workspace,
  *            element in the buffer it is read from (k/v, or k_resid/v_resid
  *            when positions >= n_q(b) for DA_KV_I8);
  *   positions[B, H_kv, S, chunk] int32: logical key position t.
- * Entries with no row are left untouched (callers pre-fill them with -1). */
+ * Entries with no row are left untouched (callers pre-fill them with -1).
+ * The walk follows the plan's fixed splits; a balanced partition reads the
+ * same rows (the same visible ordinals through the same address code), cut
+ * at other boundaries, so da_args.partition is ignored here. */
 da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args,
                                     int64_t* offsets, int32_t* positions, void* stream);
 

@@ -55,7 +55,9 @@ class Args(ctypes.Structure):
         "q", "k", "v", "k_scale", "v_scale", "k_resid", "v_resid", "block_table", "seq_lens",
         "workspace")] + [("workspace_bytes", ctypes.c_uint64), ("work_order", ctypes.c_void_p),
                          ("indptr", ctypes.c_void_p), ("cache_batch_idx", ctypes.c_void_p),
-                         ("mask_intervals", ctypes.c_void_p), ("mask_summary", ctypes.c_void_p)]
+                         ("mask_intervals", ctypes.c_void_p), ("mask_summary", ctypes.c_void_p),
+                         ("partition", ctypes.c_void_p), ("partition_items", ctypes.c_int32),
+                         ("reserved0", ctypes.c_int32)]
 
 
 class AppendArgs(ctypes.Structure):
@@ -105,6 +107,10 @@ def lib() -> ctypes.CDLL:
         L.decode_attn_schedule.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_uint64]
         L.decode_attn_schedule.restype = ctypes.c_int32
+        L.decode_attn_partition.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_uint64,
+                                            ctypes.POINTER(ctypes.c_int32)]
+        L.decode_attn_partition.restype = ctypes.c_int32
         L.decode_attn_append.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(AppendArgs),
                                          ctypes.c_void_p]
         L.decode_attn_append.restype = ctypes.c_int32
@@ -191,13 +197,32 @@ def _ptr(x):
 
 def make_args(q, k, v, seq_lens, workspace, workspace_bytes, k_scale=None, v_scale=None,
               k_resid=None, v_resid=None, block_table=None, work_order=None, indptr=None,
-              cache_batch_idx=None, mask_intervals=None, mask_summary=None) -> Args:
+              cache_batch_idx=None, mask_intervals=None, mask_summary=None, partition=None,
+              partition_items=0) -> Args:
     return Args(q=_ptr(q), k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
                 k_resid=_ptr(k_resid), v_resid=_ptr(v_resid), block_table=_ptr(block_table),
                 seq_lens=_ptr(seq_lens), workspace=_ptr(workspace),
                 workspace_bytes=int(workspace_bytes), work_order=_ptr(work_order),
                 indptr=_ptr(indptr), cache_batch_idx=_ptr(cache_batch_idx),
-                mask_intervals=_ptr(mask_intervals), mask_summary=_ptr(mask_summary))
+                mask_intervals=_ptr(mask_intervals), mask_summary=_ptr(mask_summary),
+                partition=_ptr(partition), partition_items=int(partition_items), reserved0=0)
+
+
+def decode_attn_partition(plan: Plan, seq_lens_host, items_per_head: int = 0, check: bool = True):
+    """Balanced partition of the batch from host lengths; returns (descriptor
+    int32 NumPy array, W).  Copy the descriptor to the device and pass both to
+    make_args(partition=..., partition_items=W)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    p = plan.problem
+    target = items_per_head or max(1, (3 * plan.num_cus) // max(p.num_kv_heads, 1))
+    part = np.zeros(5 + p.batch + target, dtype=np.int32)
+    items = ctypes.c_int32(0)
+    st = lib().decode_attn_partition(ctypes.byref(plan), lens.ctypes.data, int(items_per_head),
+                                     part.ctypes.data, part.size, ctypes.byref(items))
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_partition")
+    return part[:5 + p.batch + items.value], items.value
 
 
 def decode_attn_schedule(plan: Plan, seq_lens_host, check: bool = True):

@@ -32,18 +32,34 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
                                                                   const float* __restrict__ ws_m,
                                                                   const float* __restrict__ ws_l,
                                                                   float* __restrict__ out,
-                                                                  float* __restrict__ lse, int S) {
+                                                                  float* __restrict__ lse, int S_plan,
+                                                                  const int32_t* __restrict__ part_hdr,
+                                                                  int rows_per_request) {
   constexpr int NT = kCombineThreads;
   constexpr int NG = NT / D;
   constexpr int NW = NT / 64;
   constexpr int U = 16;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  // States of this row: the plan's S splits, or with a balanced partition
+  // (header W > 0, written by the run) the request's pieces: items
+  // floor(P_b / L) .. floor((P_{b+1} - 1) / L), stored as slots 0, 1, ...
+  int S = S_plan;
+  if (part_hdr[0] > 0) {
+    const int b = row / rows_per_request;
+    const int L = part_hdr[1], pb = part_hdr[4 + b], pb1 = part_hdr[5 + b];
+    S = (pb1 > pb && L > 0) ? min((pb1 - 1) / L - pb / L + 1, S_plan) : 0;
+  }
+  if (S == 0) {                     // no state: all-masked row (O = +0.0, LSE = -inf)
+    if (tid < D) out[(int64_t)row * D + tid] = 0.f;
+    if (lse && tid == 0) lse[row] = -INFINITY;
+    return;
+  }
   const int lane = tid & 63, wave = tid >> 6;
   const int c = tid % D, g = tid / D;
-  const float* m = ws_m + (int64_t)row * S;
-  const float* l = ws_l + (int64_t)row * S;
-  const float* u = ws_u + (int64_t)row * S * D;
+  const float* m = ws_m + (int64_t)row * S_plan;
+  const float* l = ws_l + (int64_t)row * S_plan;
+  const float* u = ws_u + (int64_t)row * S_plan * D;
 
   __shared__ float red_m[NW];
   __shared__ float red_l[NW];

@@ -75,6 +75,15 @@ da_status check_args(const da_plan* plan, const da_args* a) {
       (p.layout == DA_LAYOUT_CONTIG_NHD || p.layout == DA_LAYOUT_CONTIG_HND || p.layout == DA_LAYOUT_RING_NHD) &&
       !a->cache_batch_idx)
     return DA_ERR_INVALID;
+  if (a->partition) {
+    if (a->partition_items < 0) return DA_ERR_INVALID;
+    // balanced partitions run on the bf16 D = 128 matrix-core kernel, without FlashMask
+    if (p.kv_format != DA_KV_BF16 || p.head_dim_qk != 128 || p.mask_kind == DA_MASK_FLASHMASK ||
+        plan->num_splits < 2 || !DA_MFMA_QK)
+      return DA_ERR_UNSUPPORTED;
+  } else if (a->partition_items != 0) {
+    return DA_ERR_INVALID;
+  }
   if (p.kv_format == DA_KV_I8) {
     if (!a->k_scale || !a->v_scale) return DA_ERR_INVALID;
     if (p.residual_len > 0 && (!a->k_resid || !a->v_resid)) return DA_ERR_INVALID;
@@ -124,6 +133,10 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.lse = nullptr;
   sp.num_q_heads = p.num_q_heads;
   sp.num_kv_heads = p.num_kv_heads;
+  sp.batch = p.batch;
+  sp.partition = a->partition;
+  sp.ws_part = ws ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + da::partition_header_offset(*plan))
+                  : nullptr;
   sp.num_queries = p.num_queries;
   sp.q_group_shift = log2_exact(p.num_q_heads / p.num_kv_heads);
   sp.num_splits = plan->num_splits;
@@ -151,6 +164,13 @@ void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
     hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
   } else if constexpr (use_mfma<FMT, D>()) {
+    if constexpr (!FUSED && !FM) {
+      if (sp.partition) {
+        hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, false, false, true>), dim3(grid),
+                           dim3(kWaves * 64), 0, st, sp);
+        return;
+      }
+    }
     hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED, FM>), dim3(grid),
                        dim3(kWaves * 64), 0, st, sp);
   } else {
@@ -245,9 +265,14 @@ extern "C" da_status decode_attn_run(const da_plan* plan, const da_args* args, v
   if ((reinterpret_cast<uintptr_t>(args->workspace) & 15u) != 0) return DA_ERR_WORKSPACE;
   if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
   const da::SplitParams sp = make_params(plan, args);
-  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
+  // With a partition, W*H_kv workgroups (at least one: workgroup 0 writes the
+  // workspace's partition header even when every request is empty).
+  const uint64_t grid64 = args->partition
+                              ? (uint64_t)std::max(args->partition_items, 1) * p.num_kv_heads
+                              : (uint64_t)p.batch * p.num_kv_heads * plan->num_splits;
+  if (grid64 > 0x7fffffffull) return DA_ERR_INVALID;
   (void)hipGetLastError();
-  if (!dispatch_split<false>(p, sp, grid, static_cast<hipStream_t>(stream))) return DA_ERR_UNSUPPORTED;
+  if (!dispatch_split<false>(p, sp, (unsigned)grid64, static_cast<hipStream_t>(stream))) return DA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 
@@ -264,12 +289,13 @@ extern "C" da_status decode_attn_forward(const da_plan* plan, const da_args* arg
   const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (plan->num_splits > kFusedMaxSplits) {
+  if (plan->num_splits > kFusedMaxSplits || args->partition) {
     // Many splits per row: the separate combine kernel folds them with far
     // more threads than the last-arriving workgroup has, and the arrival
     // round trip of every extra workgroup costs more than the launch it saves.
-    if (!dispatch_split<false>(p, make_params(plan, args), grid, st)) return DA_ERR_UNSUPPORTED;
-    if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
+    // A partitioned run always folds in the combine kernel.
+    const da_status st_run = decode_attn_run(plan, args, stream);
+    if (st_run != DA_OK) return st_run;
     return decode_attn_combine(plan, args->workspace, args->workspace_bytes, out, lse, stream);
   }
   da::SplitParams sp = make_params(plan, args);
@@ -391,12 +417,15 @@ extern "C" da_status decode_attn_combine(const da_plan* plan, const void* worksp
   const size_t lds = (size_t)plan->num_splits * sizeof(float);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  const int32_t* part = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
+                                                        da::partition_header_offset(*plan));
+  const int rows_per_request = p.num_queries * p.num_q_heads;
   if (p.head_dim_v == 64)
     hipLaunchKernelGGL(da::combine_kernel<64>, dim3(rows), dim3(da::kCombineThreads), lds, st, ws_u,
-                       ws_m, ws_l, out, lse, plan->num_splits);
+                       ws_m, ws_l, out, lse, plan->num_splits, part, rows_per_request);
   else if (p.head_dim_v == 128)
     hipLaunchKernelGGL(da::combine_kernel<128>, dim3(rows), dim3(da::kCombineThreads), lds, st, ws_u,
-                       ws_m, ws_l, out, lse, plan->num_splits);
+                       ws_m, ws_l, out, lse, plan->num_splits, part, rows_per_request);
   else
     return DA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;

@@ -25,6 +25,8 @@ struct SplitParams {
   const int32_t* cache_batch_idx;  // contiguous: cache row of each request, or null
   const int4* mask_iv;             // FlashMask: [B, max_seq_len] (UTS, UTE, LTS, LTE)
   const int4* mask_sum;            // FlashMask: [B, n_mask_blocks, 2] block min/max pairs
+  const int32_t* partition;        // balanced partition [W, L, B, 0, P_0..P_B, first request of item i], or null
+  int32_t* ws_part;                // workspace partition header [W, L, B, 0, P_0..P_B] for the combine
   float* ws_u;
   float* ws_m;
   float* ws_l;
@@ -35,6 +37,7 @@ struct SplitParams {
   int32_t num_queries;       // C query rows per request (bottom-right causal)
   int32_t q_group_shift;     // log2(H_q / H_kv)
   int32_t num_kv_heads;
+  int32_t batch;
   int32_t num_splits;
   int32_t chunk;
   int32_t kv_capacity;
@@ -123,6 +126,16 @@ __device__ __forceinline__ int fm_tile_class(const SplitParams& p, int b, int q,
 
 __device__ __forceinline__ int vis_pos(const VisProgram& v, int o) {
   return o < v.ns ? o : o + v.gap;
+}
+
+// Every run records in the workspace how its states are laid out, so that
+// the combine (which gets no run arguments) folds the right slots: W = 0 for
+// the plan's fixed splits, else the partition header [W, L, B, 0, P_0..P_B].
+// Written by workgroup 0 before any state.
+__device__ __forceinline__ void write_partition_header(const SplitParams& p) {
+  if (blockIdx.x != 0 || !p.ws_part) return;
+  for (int i = threadIdx.x; i < p.batch + 5; i += blockDim.x)
+    p.ws_part[i] = (p.partition && i != 3) ? p.partition[i] : 0;
 }
 
 // Visible length of request b, clamped to the plan's bound so that no load

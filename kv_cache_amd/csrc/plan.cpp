@@ -60,6 +60,9 @@ constexpr int kWgPerCu = 3;
 constexpr int kMinChunk = 256;
 constexpr int kMaxChunk = 1024;
 constexpr int kRowAlign = 16;
+// Workgroups per CU a balanced partition targets by default: one round of the
+// partitioned split kernel (its launch bound allows this many per CU).
+constexpr int kPartitionWgPerCu = 3;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ceil(a / b) for b > 0 and any sign of a
@@ -208,7 +211,7 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
 
   if (p.softmax_scale == 0.f) p.softmax_scale = 1.0f / std::sqrt((float)p.head_dim_qk);
   const uint64_t ws = da::workspace_bytes_for((int64_t)p.batch * p.num_queries * p.num_q_heads,
-                                              (int64_t)p.batch * p.num_kv_heads, S, p.head_dim_v);
+                                              (int64_t)p.batch * p.num_kv_heads, p.batch, S, p.head_dim_v);
 
   da_plan plan;
   std::memset(&plan, 0, sizeof(plan));
@@ -293,5 +296,58 @@ extern "C" da_status decode_attn_schedule(const da_plan* plan, const int32_t* se
     for (int64_t b = 0; b < B; ++b)
       if (s > full[b] || (s == full[b] && part[b] == 0))
         for (int64_t h = 0; h < H; ++h) put(b, h, s);
+  return DA_OK;
+}
+
+// Balanced partition of a ragged batch: equal runs of L visible ordinals over
+// the requests concatenated in order ("M4.5 ...", sections 0x09E and 0x09G).
+extern "C" da_status decode_attn_partition(const da_plan* plan, const int32_t* seq_lens_host,
+                                           int32_t items_per_head, int32_t* part, uint64_t part_len,
+                                           int32_t* items_out) {
+  if (!plan || !seq_lens_host || !part || !items_out) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  const da_problem& p = plan->problem;
+  const int64_t B = p.batch, H = p.num_kv_heads, S = plan->num_splits;
+  if (items_per_head < 0) return DA_ERR_INVALID;
+  int64_t target = items_per_head;
+  if (target == 0) target = std::max<int64_t>(1, (kPartitionWgPerCu * (int64_t)plan->num_cus) / std::max<int64_t>(H, 1));
+  if (part_len < (uint64_t)(5 + B + target)) return DA_ERR_INVALID;
+  if (S < 2) return DA_ERR_UNSUPPORTED;
+  std::vector<int64_t> n(B);
+  int64_t N = 0, nmax = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t T = seq_lens_host[b];
+    if (T < 0 || T > p.max_seq_len) return DA_ERR_INVALID;
+    int64_t v = T;
+    if (p.mask_kind == DA_MASK_SINK_WINDOW) v = std::min<int64_t>(T, (int64_t)p.n_sink + (int64_t)p.window);
+    n[b] = v;
+    N += v;
+    nmax = std::max(nmax, v);
+  }
+  if (N >= (1LL << 31)) return DA_ERR_INVALID;
+  // L: equal work per item, and long enough that no request has more than S
+  // pieces (a request of n rows spans at most ceil(n / L) + 1 items).
+  int64_t L = std::max<int64_t>(ceil_div(std::max<int64_t>(N, 1), target), ceil_div(nmax, S - 1));
+  L = std::max<int64_t>(round_up(L, kRowAlign), kRowAlign);
+  const int64_t W = N == 0 ? 0 : ceil_div(N, L);
+  part[0] = (int32_t)W;
+  part[1] = (int32_t)L;
+  part[2] = (int32_t)B;
+  part[3] = 0;
+  int64_t P = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    part[4 + b] = (int32_t)P;
+    P += n[b];
+  }
+  part[4 + B] = (int32_t)P;
+  // first request of each item: the request holding ordinal i*L (empty
+  // requests are skipped: P_b == P_{b+1})
+  int64_t b = 0;
+  for (int64_t i = 0; i < W; ++i) {
+    const int64_t x = i * L;
+    while (b + 1 <= B && (int64_t)part[4 + b + 1] <= x) ++b;
+    part[5 + B + i] = (int32_t)b;
+  }
+  *items_out = (int32_t)W;
   return DA_OK;
 }

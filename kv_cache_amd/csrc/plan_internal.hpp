@@ -27,7 +27,8 @@ inline bool plan_intact(const da_plan* p) { return p && p->key == plan_hash(*p);
 
 // Workspace layout: u [rows,S,D] f32, m [rows,S] f32, l [rows,S] f32 with
 // rows = B*C*H_q ordered (b, i, h_q), then (at a 256-byte boundary) one uint32
-// arrival counter per (b, h_kv).
+// arrival counter per (b, h_kv), then (at a 256-byte boundary) the partition
+// header [W, L, B, 0, P_0 .. P_B] that every run writes for the combine.
 inline uint64_t states_bytes_raw(int64_t rows, int64_t S, int64_t Dv) {
   return (uint64_t)(rows * S * (Dv + 2) * 4);
 }
@@ -38,8 +39,14 @@ inline int64_t output_rows(const da_problem& p) {
 inline uint64_t states_bytes(const da_plan& p) {
   return round_up_256(states_bytes_raw(output_rows(p.problem), p.num_splits, p.problem.head_dim_v));
 }
-inline uint64_t workspace_bytes_for(int64_t rows, int64_t groups, int64_t S, int64_t Dv) {
-  return round_up_256(states_bytes_raw(rows, S, Dv)) + round_up_256((uint64_t)(groups * 4));
+inline uint64_t counters_bytes(int64_t groups) { return round_up_256((uint64_t)(groups * 4)); }
+inline uint64_t partition_header_bytes(int64_t batch) { return round_up_256((uint64_t)((batch + 5) * 4)); }
+inline uint64_t workspace_bytes_for(int64_t rows, int64_t groups, int64_t batch, int64_t S, int64_t Dv) {
+  return round_up_256(states_bytes_raw(rows, S, Dv)) + counters_bytes(groups) + partition_header_bytes(batch);
+}
+// Byte offset of the partition header in the workspace.
+inline uint64_t partition_header_offset(const da_plan& p) {
+  return states_bytes(p) + counters_bytes((int64_t)p.problem.batch * p.problem.num_kv_heads);
 }
 
 // Element size in bytes of one K/V row element as stored in k/v.

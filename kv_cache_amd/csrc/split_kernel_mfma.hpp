@@ -69,20 +69,26 @@ struct MfmaTile {
 // and a grid of 4 x CU workgroups runs in one round; 8 heads need 64
 // accumulators per lane and get 3.
 template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 : 3; };
+// A partitioned run is sized for one round of workgroups at this many per CU
+// (the host's default item count uses the same figure).
+constexpr int kPartitionWgPerCu = 3;
 
-template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM>
-__global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
+template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM, bool PART = false>
+__global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
   static_assert(G >= 1 && G <= 16, "");
 
-  int b, h, s;
-  decode_workgroup(p, &b, &h, &s);
+  write_partition_header(p);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int n = lane & 15;     // K row of the tile / score column (head)
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
+  __shared__ WaveStates<G, D, NWAVES> sh;
 
+  // One piece of work: visible ordinals [pbeg, pend) of request b for K/V
+  // head h, stored as split slot s.  pend < 0: the plan's split s.
+  auto piece = [&](int b, int h, int s, int pbeg, int pend) {
   // B operand: q[head n][32c + 8kg .. +7], zero for columns n >= G; requested
   // before the request length is known.
   uint4 qop[4];
@@ -97,7 +103,12 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
-  split_range(vis.n_vis, s, p.chunk, &begin, &end);
+  if (pend < 0) {
+    split_range(vis.n_vis, s, p.chunk, &begin, &end);
+  } else {
+    begin = min(pbeg, vis.n_vis);
+    end = min(pend, vis.n_vis);
+  }
   // Score column n is virtual head n, with its own visible end (C > 1 rows).
   const int end_n = min(end, row_limit(p, vis.n_vis, n));
   if (begin >= end) {
@@ -249,7 +260,6 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
       u[i][e] += __shfl_xor(u[i][e], 32);
     }
 
-  __shared__ WaveStates<G, D, NWAVES> sh;
   if (kg == 0) {
 #pragma unroll
     for (int i = 0; i < G; ++i)
@@ -263,6 +273,36 @@ __global__ __launch_bounds__(NWAVES * 64, MfmaOccupancy<G>::value) void split_ke
   __syncthreads();
   merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
   finish_split<G, D, NWAVES, FUSED>(p, b, h);
+  };
+
+  if constexpr (!PART) {
+    int b, h, s;
+    decode_workgroup(p, &b, &h, &s);
+    piece(b, h, s, 0, -1);
+  } else {
+    // Balanced partition: workgroup (item, h) takes ordinals [item*L,
+    // (item+1)*L) of the requests' visible ordinals laid end to end, one piece
+    // per request it meets, stored as split slot (items since the request's
+    // first).  Descriptor values are checked against the plan, so a corrupt
+    // descriptor skips work instead of addressing memory outside the buffers.
+    static_assert(!FUSED && !FM, "partitions fold in the combine kernel; FlashMask walks <= 64 tiles");
+    const int32_t* part = p.partition;
+    const int h = (int)(blockIdx.x % (unsigned)p.num_kv_heads);
+    const int item = (int)(blockIdx.x / (unsigned)p.num_kv_heads);
+    const int L = part[1];
+    if (part[2] != p.batch || L <= 0 || item >= part[0]) return;
+    int x = item * L;
+    const int xe = min(x + L, part[4 + p.batch]);
+    for (int b = part[5 + p.batch + item]; x < xe && b >= 0 && b < p.batch; ++b) {
+      const int pb = part[4 + b], pb1 = part[5 + b];
+      if (pb1 <= x) continue;                     // empty request
+      const int j = item - pb / L;
+      if (j < 0 || j >= p.num_splits || x < pb) return;
+      if (x != item * L) __syncthreads();          // the previous piece has read sh
+      piece(b, h, j, x - pb, min(xe, pb1) - pb);
+      x = min(xe, pb1);
+    }
+  }
 }
 
 }  // namespace da

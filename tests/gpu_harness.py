@@ -50,6 +50,13 @@ class DeviceWorkload:
         lens = self.w.buffers["seq_lens"]
         self.order = to_dev(ka.decode_attn_schedule(plan, lens))
 
+    def partition(self, plan, items_per_head=0):
+        """Use the library's balanced partition of this batch for this plan."""
+        lens = self.w.buffers["seq_lens"]
+        part, items = ka.decode_attn_partition(plan, lens, items_per_head)
+        self.part, self.part_items = to_dev(part), items
+        return part, items
+
     def args(self, ws, ws_bytes):
         d = self.dev
         return ka.make_args(d["q"], d["k"], d["v"], d["seq_lens"], ws, ws_bytes,
@@ -57,7 +64,9 @@ class DeviceWorkload:
                             k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
                             block_table=d.get("block_table"), work_order=self.order,
                             indptr=d.get("indptr"), cache_batch_idx=d.get("cache_batch_idx"),
-                            mask_intervals=d.get("mask_intervals"), mask_summary=d.get("mask_summary"))
+                            mask_intervals=d.get("mask_intervals"), mask_summary=d.get("mask_summary"),
+                            partition=getattr(self, "part", None),
+                            partition_items=getattr(self, "part_items", 0))
 
 
 def _outputs(w):
@@ -80,11 +89,17 @@ def plan_for(w, num_splits=None):
     return plan, ws
 
 
-def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None):
-    """Plan, run, combine.  Returns (O, LSE, plan[, workspace numpy])."""
+def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None, partition=None):
+    """Plan, run, combine.  Returns (O, LSE, plan[, workspace numpy]).
+    partition: None (fixed splits) or a target item count per K/V head for the
+    balanced partition (0: the library's default)."""
     t = torch()
     dw = dw or DeviceWorkload(w)
     plan, ws_bytes = plan_for(w, num_splits)
+    if partition is not None:
+        dw.partition(plan, partition)
+    elif getattr(dw, "part", None) is not None:
+        dw.part, dw.part_items = None, 0
     ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
     if poison_ws:
         ws.fill_(0xFF)                  # NaN everywhere: unwritten slots would show

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) >= {"decode_attn_plan", "decode_attn_run", "decode_attn_combine",
                           "decode_attn_forward", "decode_attn_workspace_init",
-                          "decode_attn_schedule", "decode_attn_append",
+                          "decode_attn_schedule", "decode_attn_partition", "decode_attn_append",
                           "decode_attn_flashmask_summarize",
                           "decode_attn_trace_indices", "decode_attn_reason",
                           "decode_attn_status_string"}
@@ -40,7 +40,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(ka.Problem) == 28 * 4
     assert ctypes.sizeof(ka.Plan) == 8 + 112 + 16 + 8 + 16
-    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 5 * 8
+    assert ctypes.sizeof(ka.Args) == 10 * 8 + 8 + 5 * 8 + 8 + 2 * 4
 
 
 def P(**kw):
@@ -60,8 +60,9 @@ def test_workspace_and_auto_splits_llama_shape():
     S = pl.num_splits
     states = 8 * 32 * S * (128 + 2) * 4
     counters = 8 * 8 * 4
+    header = (8 + 5) * 4          # partition header [W, L, B, 0, P_0..P_B]
     rup = lambda x: (x + 255) // 256 * 256
-    assert ws == rup(states) + rup(counters) == pl.workspace_bytes
+    assert ws == rup(states) + rup(counters) + rup(header) == pl.workspace_bytes
     assert pl.chunk % 16 == 0 and S * pl.chunk >= 4096 and (S - 1) * pl.chunk < 4096
     assert 8 * 8 * S >= 256          # at least one workgroup per CU
     assert abs(pl.problem.softmax_scale - 1 / math.sqrt(128)) < 1e-8
@@ -249,7 +250,7 @@ def test_query_rows_plan_checks_and_workspace():
     assert st == ka.DA_OK and pl.problem.num_queries == 2
     S = pl.num_splits
     rup = lambda x: (x + 255) // 256 * 256
-    assert ws == rup(8 * 2 * 32 * S * 130 * 4) + rup(8 * 8 * 4)
+    assert ws == rup(8 * 2 * 32 * S * 130 * 4) + rup(8 * 8 * 4) + rup((8 + 5) * 4)
     st, pl, ws, rs = plan(P(num_queries=0))
     assert st == ka.DA_OK and pl.problem.num_queries == 1
     st, _, _, rs = plan(P(num_queries=4))              # 4 * 4 = 16 virtual heads
@@ -270,3 +271,96 @@ def test_flashmask_plan_domain():
         assert st == ka.DA_ERR_UNSUPPORTED and rs & (1 << 11), kw
     st, _, _, _ = plan(P(mask_kind="flashmask", window=4))
     assert st == ka.DA_ERR_INVALID
+
+
+# ---------------------------------------------------------------- balanced partition
+def _pieces(part, B, H_unused=None):
+    """Expand a partition descriptor into per-item pieces (b, slot, lo, hi)."""
+    W, L, Bd = int(part[0]), int(part[1]), int(part[2])
+    P = [int(x) for x in part[4:5 + B]]
+    first = [int(x) for x in part[5 + B:5 + B + W]]
+    items = []
+    for i in range(W):
+        x, xe, b, got = i * L, min((i + 1) * L, P[B]), first[i], []
+        while x < xe:
+            if P[b + 1] <= x:
+                b += 1
+                continue
+            got.append((b, i - P[b] // L, x - P[b], min(xe, P[b + 1]) - P[b]))
+            x = min(xe, P[b + 1])
+            b += 1
+        items.append(got)
+    return W, L, P, items
+
+
+@pytest.mark.parametrize("mask", [None, (4, 300)])
+@pytest.mark.parametrize("target", [0, 7, 64])
+def test_partition_covers_every_visible_ordinal_once(mask, target):
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 4096, size=13).tolist() + [0, 4096, 1, 0]
+    kw = dict(batch=len(lens), max_seq_len=4096, kv_capacity=4096)
+    if mask:
+        kw.update(mask_kind="sink_window", n_sink=mask[0], window=mask[1])
+    st, pl, ws, _ = plan(P(**kw))
+    assert st == ka.DA_OK
+    part, W = ka.decode_attn_partition(pl, lens, items_per_head=target)
+    B, S = len(lens), pl.num_splits
+    n_vis = [min(t, mask[0] + mask[1]) if mask else t for t in lens]
+    W2, L, Pfx, items = _pieces(part, B)
+    assert W2 == W and part[2] == B and part[3] == 0 and L % 16 == 0
+    assert Pfx == list(np.concatenate([[0], np.cumsum(n_vis)]))
+    want = target or (3 * pl.num_cus) // pl.problem.num_kv_heads
+    assert W <= want and W == -(-sum(n_vis) // L)
+    seen = {b: [] for b in range(B)}
+    for i, got in enumerate(items):
+        assert 0 < sum(hi - lo for _, _, lo, hi in got) <= L          # equal work, last may be short
+        for b, j, lo, hi in got:
+            assert 0 <= j < S and 0 <= lo < hi <= n_vis[b]
+            seen[b].append((j, lo, hi))
+    for b in range(B):
+        pieces = sorted(seen[b])
+        assert [j for j, _, _ in pieces] == list(range(len(pieces)))   # slots 0, 1, ... in order
+        assert sum(hi - lo for _, lo, hi in pieces) == n_vis[b]
+        edges = [lo for _, lo, _ in pieces] + [n_vis[b]] if pieces else [0]
+        assert edges[0] == 0 and all(pieces[k][2] == edges[k + 1] for k in range(len(pieces)))
+        n_pieces = (Pfx[b + 1] - 1) // L - Pfx[b] // L + 1 if n_vis[b] else 0
+        assert len(pieces) == n_pieces <= S                              # the combine's count
+
+
+def test_partition_bounds_pieces_by_the_plan_and_rejects_bad_arguments():
+    st, pl, ws, _ = plan(P(batch=3, max_seq_len=4096, kv_capacity=4096, num_splits=4))
+    part, W = ka.decode_attn_partition(pl, [4096, 4096, 4096], items_per_head=1000)
+    _, L, _, _ = _pieces(part, 3)
+    assert L * (pl.num_splits - 1) >= 4096                 # no request has more than S pieces
+    part, W = ka.decode_attn_partition(pl, [0, 0, 0])
+    assert W == 0 and list(part[4:8]) == [0, 0, 0, 0]
+    with pytest.raises(ka.DecodeAttnError):
+        ka.decode_attn_partition(pl, [1, 4097, 0])
+    st, pl1, ws, _ = plan(P(batch=3, max_seq_len=4096, kv_capacity=4096, num_splits=1))
+    assert ka.decode_attn_partition(pl1, [5, 5, 5], check=False)[1] == 0
+    L_ = ka.lib()
+    buf = np.zeros(4, dtype=np.int32)
+    items = ctypes.c_int32(0)
+    assert L_.decode_attn_partition(ctypes.byref(pl), np.array([1, 2, 3], dtype=np.int32).ctypes.data, 0,
+                                    buf.ctypes.data, buf.size, ctypes.byref(items)) == ka.DA_ERR_INVALID
+    assert L_.decode_attn_partition(ctypes.byref(pl1), np.array([1, 2, 3], dtype=np.int32).ctypes.data, 0,
+                                    np.zeros(4096, dtype=np.int32).ctypes.data, 4096,
+                                    ctypes.byref(items)) == ka.DA_ERR_UNSUPPORTED
+    pl.chunk += 16
+    with pytest.raises(ka.DecodeAttnError):
+        ka.decode_attn_partition(pl, [5, 5, 5])
+
+
+def test_partition_rejected_where_unsupported_without_gpu():
+    # int8 (and fp32, FlashMask) run only on the fixed splits; a partition item
+    # count without a descriptor is malformed.  Both fail before any device work.
+    st, pl, ws, _ = plan(P(kv_format="i8", k_group=128, residual_len=128))
+    assert st == ka.DA_OK
+    a = ka.make_args(16, 16, 16, 16, 16, ws, k_scale=16, v_scale=16, k_resid=16, v_resid=16,
+                     partition=16, partition_items=1)
+    assert ka.decode_attn_run(pl, a, check=False) == ka.DA_ERR_UNSUPPORTED
+    st, pl, ws, _ = plan(P())
+    a = ka.make_args(16, 16, 16, 16, 16, ws, partition_items=3)
+    assert ka.decode_attn_run(pl, a, check=False) == ka.DA_ERR_INVALID
+    a = ka.make_args(16, 16, 16, 16, 16, ws, partition=16, partition_items=-1)
+    assert ka.decode_attn_run(pl, a, check=False) == ka.DA_ERR_INVALID
