@@ -270,6 +270,39 @@ class GpuWorkload:
                 "algorithmic_bytes": self.call_bytes}
 
 
+def other_workload(torch, ka, name, steps=30, warmup=5):
+    """Timing report of one of the non-headline workloads."""
+    import synth
+    if name == "long_context_128k":
+        w = GpuWorkload(torch, ka, "contig", 1, 32, 8, 128, [131072], min_bytes=600 << 20, seed=1)
+        return w.report("long", "B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal, auto splits",
+                        steps, warmup)
+    if name == "paged_ragged":
+        lens = synth.ragged_lengths(0, 32).tolist()
+        w = GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, lens, seed=2)
+        fixed = w.time(w.fwd, steps, warmup)
+        w.use_schedule()
+        scheduled = w.time(w.fwd, steps, warmup)
+        w.use_schedule(False)
+        w.use_partition()
+        r = w.report("paged", "B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768] (seed 0), permuted pool, "
+                              "balanced partition from decode_attn_partition (equal visible rows per "
+                              "workgroup)", steps, warmup)
+        r["partition_items_per_head"] = w.part_items
+        r["fixed_splits_us_per_call"] = round(fixed * 1000, 2)
+        r["fixed_splits_largest_first_us_per_call"] = round(scheduled * 1000, 2)
+        return r
+    if name == "int8_sink_window":
+        w = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
+                        mask=(4, 4096))
+        return w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, "
+                                "4 sinks + window 4096", steps, warmup)
+    if name == "tiny_fp32":
+        w = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
+        return w.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4", steps, warmup)
+    raise ValueError(name)
+
+
 def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, steps=50):
     """decode_attn_append on the int8 cache shape of the sink+window workload
     (group-closing residual, R = G = 128): one call where no request closes a
@@ -376,6 +409,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only", default=None,
+                    choices=["long_context_128k", "paged_ragged", "int8_sink_window", "tiny_fp32"],
+                    help="time one of the other workloads alone and print its report (for profiling)")
     ap.add_argument("--samples-out", default=None, help="write raw per-call samples (JSON)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -388,6 +424,9 @@ def main():
     import kv_cache_amd as ka
     ka.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.only:
+        print(json.dumps({a.only: other_workload(torch, ka, a.only, a.steps, a.warmup)}), flush=True)
+        return
 
     ceiling = hbm_probe(torch)
     w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, num_splits=a.num_splits,
@@ -453,35 +492,10 @@ def main():
     call_bytes = w.call_bytes
     del w
     if not a.no_long:
-        import synth
-        others = {}
-        wl = GpuWorkload(torch, ka, "contig", 1, 32, 8, 128, [131072], min_bytes=600 << 20, seed=1)
-        others["long_context_128k"] = wl.report(
-            "long", "B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal, auto splits")
-        del wl
-        lens = synth.ragged_lengths(0, 32).tolist()
-        wp = GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, lens, seed=2)
-        builtin_order = wp.time(wp.fwd, 30, 5)
-        wp.use_schedule()
-        scheduled = wp.time(wp.fwd, 30, 5)
-        wp.use_schedule(False)
-        wp.use_partition()
-        others["paged_ragged"] = wp.report(
-            "paged", "B=32 H_q=32 H_kv=8 d=128 bf16 P=16 T~U[1,32768] (seed 0), permuted pool, "
-                     "balanced partition from decode_attn_partition (equal visible rows per workgroup)")
-        others["paged_ragged"]["partition_items_per_head"] = wp.part_items
-        others["paged_ragged"]["fixed_splits_us_per_call"] = round(builtin_order * 1000, 2)
-        others["paged_ragged"]["fixed_splits_largest_first_us_per_call"] = round(scheduled * 1000, 2)
-        del wp
-        wi = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
-                         mask=(4, 4096))
-        others["int8_sink_window"] = wi.report(
-            "int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, 4 sinks + window 4096")
-        del wi
+        others = {name: other_workload(torch, ka, name)
+                  for name in ("long_context_128k", "paged_ragged", "int8_sink_window")}
         others["int8_append"] = append_timing(torch, ka)
-        wt = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
-        others["tiny_fp32"] = wt.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4")
-        del wt
+        others["tiny_fp32"] = other_workload(torch, ka, "tiny_fp32")
         line["other_workloads"] = others
     torch.cuda.synchronize()
     if not a.no_cpu_baseline:
