@@ -1,5 +1,5 @@
-// Split kernel for the int8 K/V format with D = 128: QK^T on the matrix
-// cores, PV on the vector ALUs.
+// Split kernel for the int8 K/V format with D = 128: QK^T and PV on the
+// matrix cores.
 //
 // Format ("M8.6 - Live-Data Quantization: Activations and KV Cache",
 // sections 0x06-0x06C): K codes with one fp16 scale per (128-token group,
@@ -19,7 +19,8 @@
 //    and both parts feed v_mfma_f32_16x16x32_f16 with q in fp16 (B operand).  Each row reads its
 //    own 128-token group's scales (staged in LDS per phase of the split), so
 //    groups never need special handling.  The V scale of a row multiplies
-//    that row's softmax weight (section 0x03C) before PV; the denominator
+//    that row's softmax weight (section 0x03C) before PV, which runs on
+//    v_mfma_f32_16x16x32_f16 with the V codes as exact fp16; the denominator
 //    uses the unscaled weight.  Each wave keeps two tiles in flight.
 //  * residual part: exactly the bf16 kernel's tile (A = bf16 K rows, B = q).
 #pragma once
@@ -64,22 +65,10 @@ __device__ __forceinline__ void dequant_f16(uint2 codes, uint4 scales, uint4& hi
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
 }
 
-// V codes of two rows a, b as exact fp16 pairs, one 32-bit word per channel
-// e = 0..7 holding (c_a[e], c_b[e]): v_perm places the two code bytes under
-// zero bytes, the xor turns them into fp16 1024 + c + 128, the packed subtract
-// removes the bias.
-__device__ __forceinline__ void v_pairs(uint2 a, uint2 b, uint32_t (&out)[8]) {
-  const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t wa = e < 4 ? a.x : a.y, wb = e < 4 ? b.x : b.y;
-    const uint32_t sel = (uint32_t)(e & 3) | 0x0C00u | ((uint32_t)(4 + (e & 3)) << 16) | 0x0C000000u;
-    const uint32_t bits = __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
-    out[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
-  }
-}
-
-// Channel e of two rows a, b as one fp16 pair (the word v_pairs makes for e).
+// V codes of channel e (0..7) of two rows a, b as one exact fp16 pair
+// (c_a[e], c_b[e]): v_perm places the two code bytes under zero bytes, the
+// xor turns them into fp16 1024 + c + 128, the packed subtract removes the
+// bias.
 __device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
   const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
   const uint32_t wa = e < 4 ? a.x : a.y, wb = e < 4 ? b.x : b.y;
@@ -87,28 +76,6 @@ __device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
   const uint32_t bits = __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
 }
-
-template <int I>
-__device__ __forceinline__ uint32_t row_bcast_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + I, 0xF, 0xF, false);
-}
-
-// u[i][e] += w_i(row a) * v_a[e] + w_i(row b) * v_b[e] for each head i, with the
-// fp16 weight pair of head i broadcast from lane i of the 16-lane row and the
-// two products summed in fp32 by v_dot2.
-template <int G, int I = 0>
-struct PairLoop {
-  __device__ __forceinline__ static void accumulate(float (&u)[G][8], uint32_t wp, const uint32_t (&vp)[8]) {
-    const f16x2_t w = __builtin_bit_cast(f16x2_t, row_bcast_u32<I>(wp));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u[I][e] = __builtin_amdgcn_fdot2(w, __builtin_bit_cast(f16x2_t, vp[e]), u[I][e], false);
-    PairLoop<G, I + 1>::accumulate(u, wp, vp);
-  }
-};
-template <int G>
-struct PairLoop<G, G> {
-  __device__ __forceinline__ static void accumulate(float (&)[G][8], uint32_t, const uint32_t (&)[8]) {}
-};
 
 // K scale rows staged in LDS per workgroup (256 B each for D = 128): enough
 // for a split of 22 full 128-token groups plus partial groups at both ends
@@ -132,8 +99,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
 
   // q rows in the B operand layout, q[head n][32c + 8kg .. +7] (zero for
-  // n >= G), staged in LDS: the int8 part derives its group operands from
-  // them and the residual part uses them directly.
+  // n >= G), staged in LDS for the residual part (the int8 part reads q in
+  // its own channel order).
   __shared__ uint4 q_lds[4][64];
   if (wave == 0) {
 #pragma unroll
