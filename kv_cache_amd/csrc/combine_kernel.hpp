@@ -25,17 +25,21 @@
 
 namespace da {
 
+// Threads per row: 1024 for many states, 256 when a row has at most
+// kCombineSmallS of them (two split classes of D = 128 columns, 16 states each
+// in flight), so short rows do not hold a full 1024-thread workgroup.
 constexpr int kCombineThreads = 1024;
+constexpr int kCombineThreadsSmall = 256;
+constexpr int kCombineSmallS = 32;
 
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ ws_u,
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void combine_kernel(const float* __restrict__ ws_u,
                                                                   const float* __restrict__ ws_m,
                                                                   const float* __restrict__ ws_l,
                                                                   float* __restrict__ out,
                                                                   float* __restrict__ lse, int S_plan,
                                                                   const int32_t* __restrict__ part_hdr,
                                                                   int rows_per_request) {
-  constexpr int NT = kCombineThreads;
   constexpr int NG = NT / D;
   constexpr int NW = NT / 64;
   constexpr int U = 16;

@@ -420,12 +420,22 @@ extern "C" da_status decode_attn_combine(const da_plan* plan, const void* worksp
   const int32_t* part = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
                                                         da::partition_header_offset(*plan));
   const int rows_per_request = p.num_queries * p.num_q_heads;
-  if (p.head_dim_v == 64)
-    hipLaunchKernelGGL(da::combine_kernel<64>, dim3(rows), dim3(da::kCombineThreads), lds, st, ws_u,
-                       ws_m, ws_l, out, lse, plan->num_splits, part, rows_per_request);
+  const bool small = plan->num_splits <= da::kCombineSmallS;
+  const int S = plan->num_splits;
+  if (p.head_dim_v == 64 && small)
+    hipLaunchKernelGGL((da::combine_kernel<64, da::kCombineThreadsSmall>), dim3(rows),
+                       dim3(da::kCombineThreadsSmall), lds, st, ws_u, ws_m, ws_l, out, lse, S, part,
+                       rows_per_request);
+  else if (p.head_dim_v == 64)
+    hipLaunchKernelGGL((da::combine_kernel<64, da::kCombineThreads>), dim3(rows), dim3(da::kCombineThreads),
+                       lds, st, ws_u, ws_m, ws_l, out, lse, S, part, rows_per_request);
+  else if (p.head_dim_v == 128 && small)
+    hipLaunchKernelGGL((da::combine_kernel<128, da::kCombineThreadsSmall>), dim3(rows),
+                       dim3(da::kCombineThreadsSmall), lds, st, ws_u, ws_m, ws_l, out, lse, S, part,
+                       rows_per_request);
   else if (p.head_dim_v == 128)
-    hipLaunchKernelGGL(da::combine_kernel<128>, dim3(rows), dim3(da::kCombineThreads), lds, st, ws_u,
-                       ws_m, ws_l, out, lse, plan->num_splits, part, rows_per_request);
+    hipLaunchKernelGGL((da::combine_kernel<128, da::kCombineThreads>), dim3(rows), dim3(da::kCombineThreads),
+                       lds, st, ws_u, ws_m, ws_l, out, lse, S, part, rows_per_request);
   else
     return DA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
