@@ -110,9 +110,11 @@ typedef int32_t da_status;
 #define DA_R_OUT_DTYPE   (1ull << 4)   /* output must be DA_F32                       */
 #define DA_R_KV_FORMAT   (1ull << 5)   /* unknown K/V format                          */
 #define DA_R_LAYOUT      (1ull << 6)   /* layout not available for this K/V format    */
-#define DA_R_INT8_PARAMS (1ull << 7)   /* int8: k_group must be 128, 0 <= R           */
+#define DA_R_INT8_PARAMS (1ull << 7)   /* int8: k_group not a power of two in [16, 1024] */
 #define DA_R_SPLITS      (1ull << 8)   /* num_splits above DA_MAX_SPLITS              */
-#define DA_R_INDEX_RANGE (1ull << 9)   /* a tensor exceeds the 2^31-element index range */
+#define DA_R_INDEX_RANGE (1ull << 9)   /* an index exceeds its range: grid >= 2^31
+                                          workgroups, or int8 with H_kv * d > 2^20 bytes
+                                          per position                               */
 #define DA_R_DEVICE      (1ull << 10)  /* current device is not gfx950 or cannot be queried */
 #define DA_R_MASK_KIND   (1ull << 11)  /* unknown mask program, or FlashMask outside its
                                           domain (bf16, d=128, C=1, splits <= 1024 keys) */

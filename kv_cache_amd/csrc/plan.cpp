@@ -162,6 +162,10 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   if (p.kv_format == DA_KV_I8 &&
       !(p.k_group >= 16 && p.k_group <= 1024 && (p.k_group & (p.k_group - 1)) == 0))
     reasons |= DA_R_INT8_PARAMS;
+  // the int8 kernel forms row offsets inside a phase as 24-bit products
+  // r * (num_kv_heads * head_dim) with r < 2048, kept below 2^31
+  if (p.kv_format == DA_KV_I8 && (int64_t)p.num_kv_heads * p.head_dim_qk > (1 << 20))
+    reasons |= DA_R_INDEX_RANGE;
   if (p.mask_kind != DA_MASK_CAUSAL && p.mask_kind != DA_MASK_SINK_WINDOW &&
       p.mask_kind != DA_MASK_FLASHMASK)
     reasons |= DA_R_MASK_KIND;
@@ -238,7 +242,7 @@ extern "C" const char* decode_attn_reason(int bit) {
       "layout not available for this K/V format (int8 is contiguous NHD without a batch index)",
       "int8 k_group must be a power of two in [16, 1024]",
       "split count above the library maximum",
-      "grid or trace size exceeds the index range",
+      "grid or trace size exceeds the index range, or int8 with num_kv_heads * head_dim > 2^20",
       "current device is not gfx950 or cannot be queried",
       "mask program unknown, or FlashMask outside bf16 / head_dim 128 / one query row / "
       "splits of at most 1024 keys",

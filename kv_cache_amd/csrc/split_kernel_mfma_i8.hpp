@@ -77,9 +77,13 @@ __device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
 }
 
-// K scale rows staged in LDS per workgroup (256 B each for D = 128): enough
-// for a split of 22 full 128-token groups plus partial groups at both ends
-// of the sink and window runs.
+// a * b for a, b < 2^24 with a product below 2^32 (v_mul_u32_u24), unsigned so
+// that it extends to an address offset by zero extension
+__device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) { return (uint32_t)__umul24(a, b); }
+
+// K scale rows staged in LDS per workgroup (256 B each for D = 128): a phase
+// of at most 23 groups' length starting anywhere in a group touches at most
+// 24 of them.
 constexpr int kI8ScaleSlots = 24;
 
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const uint32_t row_stride = (uint32_t)(p.num_kv_heads * D);
   const int64_t code_base = ((int64_t)b * p.kv_capacity * p.num_kv_heads + h) * D;
   const int8_t* kc = static_cast<const int8_t*>(p.k) + code_base;
-  const int8_t* vc = static_cast<const int8_t*>(p.v) + code_base + 8 * n;
+  const int8_t* vc = static_cast<const int8_t*>(p.v) + code_base;
   const int64_t res_base = ((int64_t)b * p.residual_len * p.num_kv_heads + h) * D;
   const uint16_t* kr = static_cast<const uint16_t*>(p.k_resid) + res_base + 8 * kg;
   const uint16_t* vr = static_cast<const uint16_t*>(p.v_resid) + res_base + 8 * n;
@@ -180,10 +184,9 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   // which leaves every dot product unchanged (it is a sum over channels).
   //
   // Scales.  The K scale rows of the 128-token groups a phase of the split
-  // touches are staged in LDS (the rows' positions form at most two runs,
-  // sinks and window); a phase is short enough for the table, so a tile in
-  // flight holds only codes and V scales and each wave keeps two tiles in
-  // flight.  Splits usually fit in one phase.
+  // touches are staged in LDS; a phase is short enough for the table, so a
+  // tile in flight holds only codes and V scales and each wave keeps two
+  // tiles in flight.  A split is one phase per run unless it is long.
   auto kch = [&](int c) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1); };
   __shared__ uint4 ksc[kI8ScaleSlots][16];
   if (begin < mid) {
@@ -198,120 +201,125 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
                          pack_f16(bf16_lo(x.z), bf16_hi(x.z)), pack_f16(bf16_lo(x.w), bf16_hi(x.w)));
     }
     const int sh = p.k_group_shift;
-    const int phase = (kI8ScaleSlots - 4) << sh;   // two runs: at most len/G + 4 groups
-    for (int pb = begin; pb < mid; pb += phase) {
-      const int pe = min(pb + phase, mid);
-      int a0 = 0, nA = 0, b0 = 0, nB = 0;
-      const int sink_end = min(pe, vis.ns);              // ordinals [pb, sink_end) sit at o
-      if (pb < sink_end) {
-        a0 = pb >> sh;
-        nA = ((sink_end - 1) >> sh) - a0 + 1;
-      }
-      const int wbeg = max(pb, vis.ns);                  // ordinals [wbeg, pe) sit at o + gap
-      if (wbeg < pe) {
-        b0 = (wbeg + vis.gap) >> sh;
-        nB = ((pe - 1 + vis.gap) >> sh) - b0 + 1;
-      }
-      if (pb != begin) __syncthreads();                  // the previous phase has read its table
-      for (int idx = threadIdx.x; idx < (nA + nB) * 16; idx += NWAVES * 64) {
-        const int k = idx >> 4;
-        const int g = k < nA ? a0 + k : b0 + (k - nA);
-        ksc[k][idx & 15] = *reinterpret_cast<const uint4*>(ks + (uint64_t)g * row_stride + 8 * (idx & 15));
-      }
-      __syncthreads();
+    // Ordinals map to positions by a constant shift inside each run (sinks:
+    // 0, window: gap), so a phase never spans the seam: its rows are the
+    // positions t_pb + r, r in [0, pe - pb), addressed from wave-uniform bases
+    // with lane offsets r * row_stride formed by 24-bit multiplies (r < 2048
+    // and row_stride <= 2^20 bytes keep them below 2^31).  A phase of at most
+    // (slots - 1) groups' length touches at most `slots` scale rows.
+    const int phase = min((kI8ScaleSlots - 1) << sh, 2048);
+    const uint32_t vs_stride = 2 * (uint32_t)p.num_kv_heads;   // V scale bytes per position
+    bool staged = false;
+    for (int run = 0; run < 2; ++run) {
+      const int rb = run == 0 ? begin : max(begin, vis.ns);
+      const int re = run == 0 ? min(mid, vis.ns) : mid;
+      const int shift = run == 0 ? 0 : vis.gap;
+      for (int pb = rb; pb < re; pb += phase) {
+        const int pe = min(pb + phase, re);
+        const int t_pb = pb + shift;
+        const int g0 = t_pb >> sh;
+        const int ng = ((pe - 1 + shift) >> sh) - g0 + 1;
+        if (staged) __syncthreads();                       // the previous phase has read its table
+        staged = true;
+        for (int idx = threadIdx.x; idx < ng * 16; idx += NWAVES * 64)
+          ksc[idx >> 4][idx & 15] =
+              *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
+        __syncthreads();
 
-      auto pos = [&](int o) { return (uint32_t)vis_pos(vis, min(o, pe - 1)); };
-      // LDS slot of the scale row of position t (sink run first, then window run)
-      auto slot = [&](uint32_t t) {
-        const int g = (int)(t >> sh);
-        return (nA > 0 && g < a0 + nA) ? g - a0 : nA + (g - b0);
-      };
-      auto issue_k = [&](int tile, uint4 (&k)[2]) {
-        const int8_t* row = kc + (uint64_t)pos(tile + n) * row_stride;
-        k[0] = stream_load(reinterpret_cast<const uint4*>(row + 16 * kg));
-        k[1] = stream_load(reinterpret_cast<const uint4*>(row + 64 + 16 * kg));
-      };
-      auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
+        const int8_t* kp = kc + (uint64_t)t_pb * row_stride;
+        const int8_t* vp = vc + (uint64_t)t_pb * row_stride;
+        const char* vsp = reinterpret_cast<const char*>(vs + (int64_t)t_pb * p.num_kv_heads);
+        const uint32_t last = (uint32_t)(pe - 1 - pb);
+        // row of ordinal o within the phase, clamped to its last row
+        auto rel = [&](int o) { return min((uint32_t)(o - pb), last); };
+        auto issue_k = [&](int tile, uint4 (&k)[2]) {
+          const uint32_t off = mul_u24(rel(tile + n), row_stride) + 16 * kg;
+          k[0] = stream_load(reinterpret_cast<const uint4*>(kp + off));
+          k[1] = stream_load(reinterpret_cast<const uint4*>(kp + off + 64));
+        };
+        auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t t = pos(tile + 4 * kg + j);
-          v[j] = stream_load(reinterpret_cast<const uint2*>(vc + (uint64_t)t * row_stride));
-          sv[j] = vs[(int64_t)t * p.num_kv_heads];
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t r = rel(tile + 4 * kg + j);
+            v[j] = stream_load(reinterpret_cast<const uint2*>(vp + (mul_u24(r, row_stride) + 8 * (uint32_t)n)));
+            sv[j] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
+          }
+        };
+        auto slot = [&](int tile) { return (int)((t_pb + rel(tile + n)) >> sh) - g0; };
+        auto scores = [&](int tile, const uint4 (&k)[2]) {
+          const int sl = slot(tile);
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint4 w = k[c >> 1];
+            const uint2 codes = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
+            uint4 hi, lo;
+            dequant_f16(codes, ksc[sl][kch(c) >> 3], hi, lo);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hi),
+                                                         __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, lo),
+                                                         __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+          }
+          return acc;
+        };
+        // PV on the matrix cores, O (heads x channels) += P (heads x rows) V
+        // (rows x channels) over the 32 rows of the two tiles: A = the weights
+        // p * sigma_V in fp16 (relative error 2^-11, far inside the int8 format's
+        // own error; lane (n, kg) already holds head n's weights of rows 4kg..4kg+3
+        // of both tiles, the A operand's k = 8kg .. 8kg+7), B = the V codes as
+        // exact fp16, whose lane (n, kg) holds the same rows at 8 channels 8n ..
+        // 8n+7: instruction c takes channel 8n + c of each row, so column n of
+        // block c is channel 8n + c and no code moves between lanes.  The
+        // accumulator o[c] of lane (n, kg) holds heads 4kg .. 4kg+3 at channel
+        // 8n + c.  The denominator uses the unscaled weights.
+        auto pv2 = [&](const uint2 (&a)[4], const uint32_t (&sa)[4], const uint2 (&bv)[4],
+                       const uint32_t (&sb)[4], const float (&pr)[8]) {
+          uint4 w;
+          w.x = pack_f16(pr[0] * f16_bits_to_f32(sa[0]), pr[1] * f16_bits_to_f32(sa[1]));
+          w.y = pack_f16(pr[2] * f16_bits_to_f32(sa[2]), pr[3] * f16_bits_to_f32(sa[3]));
+          w.z = pack_f16(pr[4] * f16_bits_to_f32(sb[0]), pr[5] * f16_bits_to_f32(sb[1]));
+          w.w = pack_f16(pr[6] * f16_bits_to_f32(sb[2]), pr[7] * f16_bits_to_f32(sb[3]));
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint4 vcol = make_uint4(v_pair_word(a[0], a[1], c), v_pair_word(a[2], a[3], c),
+                                          v_pair_word(bv[0], bv[1], c), v_pair_word(bv[2], bv[3], c));
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, w),
+                                                          __builtin_bit_cast(f16x8_t, vcol), o[c], 0, 0, 0);
+          }
+        };
+        // running-maximum rescale of o: lane (n, kg) scales heads 4kg .. 4kg+3
+        auto rescale_o = [&](float alpha) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[c][i] *= a;
+          }
+        };
+        uint4 ka[2], kb[2];
+        uint2 va[4], vb[4];
+        uint32_t sva[4], svb[4];
+        int tile = pb + wave * TW;
+        // the loop's request order (K, K, V, V), so its waits leave newer requests in flight
+        if (tile < pe) {
+          issue_k(tile, ka);
+          issue_k(tile + STEP, kb);
+          issue_v(tile, va, sva);
+          issue_v(tile + STEP, vb, svb);
         }
-      };
-      auto scores = [&](int tile, const uint4 (&k)[2]) {
-        const int sl = slot(pos(tile + n));
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 w = k[c >> 1];
-          const uint2 codes = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
-          uint4 hi, lo;
-          dequant_f16(codes, ksc[sl][kch(c) >> 3], hi, lo);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hi),
-                                                       __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, lo),
-                                                       __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
+        for (; tile < pe; tile += 2 * STEP) {
+          const int tb = tile + STEP;
+          const f32x4_t acc = scores(tile, ka);
+          const f32x4_t acc2 = scores(tb, kb);
+          issue_k(tile + 2 * STEP, ka);
+          issue_k(tb + 2 * STEP, kb);
+          float pr[8];
+          const float alpha = softmax2(acc, acc2, tile, tb, pe, pr);
+          if (__any(alpha != 1.f)) rescale_o(alpha);   // skipped while no head maximum moves
+          pv2(va, sva, vb, svb, pr);
+          issue_v(tile + 2 * STEP, va, sva);
+          issue_v(tb + 2 * STEP, vb, svb);
         }
-        return acc;
-      };
-      // PV on the matrix cores, O (heads x channels) += P (heads x rows) V
-      // (rows x channels) over the 32 rows of the two tiles: A = the weights
-      // p * sigma_V in fp16 (relative error 2^-11, far inside the int8 format's
-      // own error; lane (n, kg) already holds head n's weights of rows 4kg..4kg+3
-      // of both tiles, the A operand's k = 8kg .. 8kg+7), B = the V codes as
-      // exact fp16, whose lane (n, kg) holds the same rows at 8 channels 8n ..
-      // 8n+7: instruction c takes channel 8n + c of each row, so column n of
-      // block c is channel 8n + c and no code moves between lanes.  The
-      // accumulator o[c] of lane (n, kg) holds heads 4kg .. 4kg+3 at channel
-      // 8n + c.  The denominator uses the unscaled weights.
-      auto pv2 = [&](const uint2 (&a)[4], const uint32_t (&sa)[4], const uint2 (&bv)[4],
-                     const uint32_t (&sb)[4], const float (&pr)[8]) {
-        uint4 w;
-        w.x = pack_f16(pr[0] * f16_bits_to_f32(sa[0]), pr[1] * f16_bits_to_f32(sa[1]));
-        w.y = pack_f16(pr[2] * f16_bits_to_f32(sa[2]), pr[3] * f16_bits_to_f32(sa[3]));
-        w.z = pack_f16(pr[4] * f16_bits_to_f32(sb[0]), pr[5] * f16_bits_to_f32(sb[1]));
-        w.w = pack_f16(pr[6] * f16_bits_to_f32(sb[2]), pr[7] * f16_bits_to_f32(sb[3]));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint4 vcol = make_uint4(v_pair_word(a[0], a[1], c), v_pair_word(a[2], a[3], c),
-                                        v_pair_word(bv[0], bv[1], c), v_pair_word(bv[2], bv[3], c));
-          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, w),
-                                                        __builtin_bit_cast(f16x8_t, vcol), o[c], 0, 0, 0);
-        }
-      };
-      // running-maximum rescale of o: lane (n, kg) scales heads 4kg .. 4kg+3
-      auto rescale_o = [&](float alpha) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = __shfl(alpha, 4 * kg + i);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) o[c][i] *= a;
-        }
-      };
-      uint4 ka[2], kb[2];
-      uint2 va[4], vb[4];
-      uint32_t sva[4], svb[4];
-      int tile = pb + wave * TW;
-      // the loop's request order (K, K, V, V), so its waits leave newer requests in flight
-      if (tile < pe) {
-        issue_k(tile, ka);
-        issue_k(tile + STEP, kb);
-        issue_v(tile, va, sva);
-        issue_v(tile + STEP, vb, svb);
-      }
-      for (; tile < pe; tile += 2 * STEP) {
-        const int tb = tile + STEP;
-        const f32x4_t acc = scores(tile, ka);
-        const f32x4_t acc2 = scores(tb, kb);
-        issue_k(tile + 2 * STEP, ka);
-        issue_k(tb + 2 * STEP, kb);
-        float pr[8];
-        const float alpha = softmax2(acc, acc2, tile, tb, pe, pr);
-        if (__any(alpha != 1.f)) rescale_o(alpha);   // skipped while no head maximum moves
-        pv2(va, sva, vb, svb, pr);
-        issue_v(tile + 2 * STEP, va, sva);
-        issue_v(tb + 2 * STEP, vb, svb);
       }
     }
   }

@@ -136,6 +136,15 @@ def test_unsupported_int8_paged_and_out_dtype():
     assert rs & (1 << 6) and rs & (1 << 7) and rs & (1 << 4)
 
 
+def test_int8_row_stride_bound():
+    # 32-bit in-phase row offsets: H_kv * d may not exceed 2^20 bytes per position
+    kw = dict(kv_format="i8", batch=1, max_seq_len=256, kv_capacity=256, k_group=128, residual_len=128)
+    st, _, _, rs = plan(P(num_q_heads=8192, num_kv_heads=8192, **kw))
+    assert st == ka.DA_OK and rs == 0
+    st, _, _, rs = plan(P(num_q_heads=8200, num_kv_heads=8200, **kw))
+    assert st == ka.DA_ERR_UNSUPPORTED and rs == 1 << 9
+
+
 def test_plan_mismatch_detected_without_gpu():
     st, pl, ws, _ = plan(P())
     assert st == ka.DA_OK

@@ -213,9 +213,9 @@ def test_int8_causal_small():
 
 
 def test_int8_scale_table_edges():
-    # many 64-token groups in one split (more than the staged scale table
-    # holds: per-tile scale reads) and a window whose first group is the
-    # sinks' last group (the two position runs share a scale row)
+    # many 64-token groups in one split (several phases of the staged scale
+    # table) and a window whose first group is the sinks' last group (the two
+    # position runs share a scale row)
     w = synth.make_int8(14, 2, 8, 2, 128, [4000, 1500], k_group=64, residual_len=64,
                         kv_capacity=4000)
     Or, Lr = oracle.attend(w.problem, w.buffers)
@@ -230,6 +230,17 @@ def test_int8_scale_table_edges():
     for S in (1, 3, 0):
         O, L, _ = H.run(w, num_splits=S, dw=dw)
         H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+    # no sinks (one run), and sinks covering whole requests (T <= n_sink) next
+    # to a request whose sink run ends inside a tile
+    for n_sink, window in ((0, 333), (517, 200)):
+        w = synth.make_int8(16, 3, 8, 2, 128, [1200, 400, 517], mask_kind="sink_window",
+                            n_sink=n_sink, window=window, k_group=128, residual_len=128,
+                            kv_capacity=1200)
+        Or, Lr = oracle.attend(w.problem, w.buffers)
+        dw = H.DeviceWorkload(w)
+        for S in (1, 2, 0):
+            O, L, _ = H.run(w, num_splits=S, dw=dw)
+            H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
 @pytest.mark.parametrize("seed", [0, 1])
