@@ -12,10 +12,13 @@
 // Finalize: O = u / l and LSE = M + ln l, or O = +0.0 and LSE = -inf when no
 // state is valid.
 //
-// Work split: thread t owns column t % D of the split class t / D (mod NG =
-// threads / D).  The u values of the first 16 states of each class are
-// requested before the weights are known, so the state loads and the weight
-// computation overlap; the NG partial sums are then added in fixed order.
+// Work split: a workgroup owns DS columns of a row (all D, or a slice when
+// the rows are too few to spread the state reads over the chip); thread t
+// owns column t % DS of the split class t / DS (mod NG = threads / DS).  Every
+// slice derives the same weights from the row's (m, l) values.  The u values
+// of the first 16 states of each class are requested before the weights are
+// known, so the state loads and the weight computation overlap; the NG
+// partial sums are then added in fixed order.
 // Every reduction has a fixed shape, so the result is bitwise repeatable for a
 // fixed plan (section 0x02H, determinism contract).
 #pragma once
@@ -27,12 +30,16 @@ namespace da {
 
 // Threads per row: 1024 for many states, 256 when a row has at most
 // kCombineSmallS of them (two split classes of D = 128 columns, 16 states each
-// in flight), so short rows do not hold a full 1024-thread workgroup.
+// in flight), so short rows do not hold a full 1024-thread workgroup.  With
+// fewer rows than kCombineSliceRows, 256-thread workgroups of kCombineSlice
+// columns each.
 constexpr int kCombineThreads = 1024;
 constexpr int kCombineThreadsSmall = 256;
 constexpr int kCombineSmallS = 32;
+constexpr int kCombineSlice = 16;
+constexpr int kCombineSliceRows = 256;
 
-template <int D, int NT>
+template <int D, int NT, int DS = D>
 __global__ __launch_bounds__(NT) void combine_kernel(const float* __restrict__ ws_u,
                                                                   const float* __restrict__ ws_m,
                                                                   const float* __restrict__ ws_l,
@@ -40,10 +47,12 @@ __global__ __launch_bounds__(NT) void combine_kernel(const float* __restrict__ w
                                                                   float* __restrict__ lse, int S_plan,
                                                                   const int32_t* __restrict__ part_hdr,
                                                                   int rows_per_request) {
-  constexpr int NG = NT / D;
+  static_assert(D % DS == 0 && NT % DS == 0, "");
+  constexpr int NG = NT / DS;
   constexpr int NW = NT / 64;
   constexpr int U = 16;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / (D / DS);
+  const int col0 = (blockIdx.x % (D / DS)) * DS;
   const int tid = threadIdx.x;
   // States of this row: the plan's S splits, or with a balanced partition
   // (header W > 0, written by the run) the request's pieces: items
@@ -55,19 +64,19 @@ __global__ __launch_bounds__(NT) void combine_kernel(const float* __restrict__ w
     S = (pb1 > pb && L > 0) ? min((pb1 - 1) / L - pb / L + 1, S_plan) : 0;
   }
   if (S == 0) {                     // no state: all-masked row (O = +0.0, LSE = -inf)
-    if (tid < D) out[(int64_t)row * D + tid] = 0.f;
-    if (lse && tid == 0) lse[row] = -INFINITY;
+    if (tid < DS) out[(int64_t)row * D + col0 + tid] = 0.f;
+    if (lse && col0 == 0 && tid == 0) lse[row] = -INFINITY;
     return;
   }
   const int lane = tid & 63, wave = tid >> 6;
-  const int c = tid % D, g = tid / D;
+  const int c = col0 + tid % DS, g = tid / DS;
   const float* m = ws_m + (int64_t)row * S_plan;
   const float* l = ws_l + (int64_t)row * S_plan;
   const float* u = ws_u + (int64_t)row * S_plan * D;
 
   __shared__ float red_m[NW];
   __shared__ float red_l[NW];
-  __shared__ float part[NG][D];
+  __shared__ float part[NG][DS];
   extern __shared__ float w_s[];   // S weights
 
   float x[U];
@@ -124,15 +133,15 @@ __global__ __launch_bounds__(NT) void combine_kernel(const float* __restrict__ w
 #pragma unroll
     for (int j = 0; j < U; ++j) x[j] = u[(int64_t)min(s0 + U * NG + j * NG, S - 1) * D + c];
   }
-  part[g][c] = acc;
+  part[g][c - col0] = acc;
   __syncthreads();
-  if (tid < D) {
+  if (tid < DS) {
     float a = part[0][tid];
 #pragma unroll
     for (int k = 1; k < NG; ++k) a += part[k][tid];
     const bool valid = L > 0.f;
-    out[(int64_t)row * D + tid] = valid ? a / L : 0.f;
-    if (lse && tid == 0) lse[row] = valid ? M + logf(L) : -INFINITY;
+    out[(int64_t)row * D + col0 + tid] = valid ? a / L : 0.f;
+    if (lse && col0 == 0 && tid == 0) lse[row] = valid ? M + logf(L) : -INFINITY;
   }
 }
 

@@ -420,22 +420,28 @@ extern "C" da_status decode_attn_combine(const da_plan* plan, const void* worksp
   const int32_t* part = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
                                                         da::partition_header_offset(*plan));
   const int rows_per_request = p.num_queries * p.num_q_heads;
-  const bool small = plan->num_splits <= da::kCombineSmallS;
   const int S = plan->num_splits;
-  if (p.head_dim_v == 64 && small)
-    hipLaunchKernelGGL((da::combine_kernel<64, da::kCombineThreadsSmall>), dim3(rows),
-                       dim3(da::kCombineThreadsSmall), lds, st, ws_u, ws_m, ws_l, out, lse, S, part,
-                       rows_per_request);
+  const bool small = S <= da::kCombineSmallS;
+  const bool sliced = rows < (unsigned)da::kCombineSliceRows;
+  constexpr int NS = da::kCombineThreadsSmall, NL = da::kCombineThreads, DS = da::kCombineSlice;
+  if (p.head_dim_v == 64 && sliced)
+    hipLaunchKernelGGL((da::combine_kernel<64, NS, DS>), dim3(rows * (64 / DS)), dim3(NS), lds, st, ws_u,
+                       ws_m, ws_l, out, lse, S, part, rows_per_request);
+  else if (p.head_dim_v == 64 && small)
+    hipLaunchKernelGGL((da::combine_kernel<64, NS>), dim3(rows), dim3(NS), lds, st, ws_u, ws_m, ws_l, out,
+                       lse, S, part, rows_per_request);
   else if (p.head_dim_v == 64)
-    hipLaunchKernelGGL((da::combine_kernel<64, da::kCombineThreads>), dim3(rows), dim3(da::kCombineThreads),
-                       lds, st, ws_u, ws_m, ws_l, out, lse, S, part, rows_per_request);
+    hipLaunchKernelGGL((da::combine_kernel<64, NL>), dim3(rows), dim3(NL), lds, st, ws_u, ws_m, ws_l, out,
+                       lse, S, part, rows_per_request);
+  else if (p.head_dim_v == 128 && sliced)
+    hipLaunchKernelGGL((da::combine_kernel<128, NS, DS>), dim3(rows * (128 / DS)), dim3(NS), lds, st, ws_u,
+                       ws_m, ws_l, out, lse, S, part, rows_per_request);
   else if (p.head_dim_v == 128 && small)
-    hipLaunchKernelGGL((da::combine_kernel<128, da::kCombineThreadsSmall>), dim3(rows),
-                       dim3(da::kCombineThreadsSmall), lds, st, ws_u, ws_m, ws_l, out, lse, S, part,
-                       rows_per_request);
+    hipLaunchKernelGGL((da::combine_kernel<128, NS>), dim3(rows), dim3(NS), lds, st, ws_u, ws_m, ws_l, out,
+                       lse, S, part, rows_per_request);
   else if (p.head_dim_v == 128)
-    hipLaunchKernelGGL((da::combine_kernel<128, da::kCombineThreads>), dim3(rows), dim3(da::kCombineThreads),
-                       lds, st, ws_u, ws_m, ws_l, out, lse, S, part, rows_per_request);
+    hipLaunchKernelGGL((da::combine_kernel<128, NL>), dim3(rows), dim3(NL), lds, st, ws_u, ws_m, ws_l, out,
+                       lse, S, part, rows_per_request);
   else
     return DA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
