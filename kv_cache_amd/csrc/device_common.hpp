@@ -202,11 +202,32 @@ __device__ __forceinline__ int quantized_len(const SplitParams& p, int T) {
   return T - min(T, R);
 }
 
+// First visible ordinal whose position is >= n_q (positions grow with the
+// ordinal, so [o_res, n_vis) are the visible residual rows).
+__device__ __forceinline__ int residual_ordinal(const VisProgram& vis, int n_q) {
+  return n_q <= vis.ns ? n_q : max(vis.ns, n_q - vis.gap);
+}
+
 __device__ __forceinline__ void split_range(int n_vis, int s, int chunk, int* begin, int* end) {
   const long long b = (long long)s * chunk;
   const long long e = b + chunk;
   *begin = (int)min<long long>(b, n_vis);
   *end = (int)min<long long>(e, n_vis);
+}
+
+// int8 caches: the residual ordinals [o_res, n_vis) are bf16 K and V rows,
+// twice the bytes of an int8 row, so the plan's chunk counts them twice:
+// split s owns the ordinals whose weighted offsets (int8 rows 1, residual
+// rows 2) fall in [s*chunk, (s+1)*chunk) -- still a disjoint exact cover of
+// [0, n_vis), with the residual rows' cost spread over the splits.
+__device__ __forceinline__ void split_range_weighted(int n_vis, int o_res, int s, int chunk, int* begin,
+                                                     int* end) {
+  const long long n_w = (long long)n_vis + (n_vis - o_res);
+  auto ord = [&](long long x) { return (int)(x <= o_res ? x : o_res + (x - o_res + 1) / 2); };
+  const long long xb = min((long long)s * chunk, n_w);
+  const long long xe = min(xb + chunk, n_w);
+  *begin = ord(xb);
+  *end = ord(xe);
 }
 
 // ---------------------------------------------------------------------------

@@ -189,19 +189,25 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   int64_t max_vis = p.max_seq_len;
   if (p.mask_kind == DA_MASK_SINK_WINDOW)
     max_vis = std::min<int64_t>(max_vis, (int64_t)p.n_sink + (int64_t)p.window);
+  // Splits cut the visible ordinals into chunks of equal length; for int8
+  // caches by weight, a residual row (bf16 K and V) counting as two int8 rows,
+  // with no tile alignment (the int8 kernel's tiles start at the split).
+  const bool i8 = p.kv_format == DA_KV_I8;
+  const int64_t split_len = max_vis + (i8 ? std::min<int64_t>(std::max(p.residual_len, 0), max_vis) : 0);
+  const int64_t align = i8 ? 1 : kRowAlign;
   int64_t chunk;
   if (max_vis == 0) {
     chunk = kRowAlign;
   } else if (p.num_splits > 0) {
-    chunk = round_up(ceil_div(max_vis, p.num_splits), kRowAlign);
+    chunk = round_up(ceil_div(split_len, p.num_splits), align);
   } else {
     const int64_t units = std::max<int64_t>(1, (int64_t)p.batch * p.num_kv_heads);
     const int64_t s0 = std::max<int64_t>(1, ceil_div((int64_t)kWgPerCu * num_cus, units));
-    chunk = round_up(ceil_div(max_vis, s0), kRowAlign);
+    chunk = round_up(ceil_div(split_len, s0), align);
     chunk = std::min<int64_t>(chunk, kMaxChunk);
-    chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinChunk, round_up(max_vis, kRowAlign)));
+    chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinChunk, round_up(split_len, align)));
   }
-  int64_t S = max_vis == 0 ? 1 : ceil_div(max_vis, chunk);
+  int64_t S = max_vis == 0 ? 1 : ceil_div(split_len, chunk);
   if (S > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;
   // FlashMask classifies at most 64 tiles of 16 keys per split
   if (p.mask_kind == DA_MASK_FLASHMASK && chunk > 64 * 16) reasons |= DA_R_MASK_KIND;
@@ -275,11 +281,22 @@ extern "C" da_status decode_attn_schedule(const da_plan* plan, const int32_t* se
   for (int64_t b = 0; b < B; ++b) {
     const int64_t T = seq_lens_host[b];
     if (T < 0 || T > p.max_seq_len) return DA_ERR_INVALID;
-    int64_t n_vis = T;
-    if (p.mask_kind == DA_MASK_SINK_WINDOW)
-      n_vis = std::min<int64_t>(T, (int64_t)p.n_sink + (int64_t)p.window);
-    full[b] = std::min<int64_t>(S, n_vis / chunk);
-    part[b] = full[b] < S ? n_vis - full[b] * chunk : 0;   // rows of split full[b] (0: empty)
+    int64_t n_vis = T, ns = T, gap = 0;
+    if (p.mask_kind == DA_MASK_SINK_WINDOW) {
+      ns = std::min<int64_t>(p.n_sink, T);
+      gap = std::max<int64_t>(0, std::max<int64_t>(0, T - p.window) - ns);
+      n_vis = T - gap;
+    }
+    int64_t len = n_vis;   // split length: int8 residual rows count twice
+    if (p.kv_format == DA_KV_I8) {
+      int64_t n_q = T - std::min<int64_t>(T, p.residual_len);
+      if (p.residual_policy == DA_RESIDUAL_GROUPS)
+        n_q = T > p.residual_len ? ceil_div(T - p.residual_len, p.k_group) * p.k_group : 0;
+      const int64_t o_res = n_q <= ns ? n_q : std::max<int64_t>(ns, n_q - gap);
+      len += n_vis - o_res;
+    }
+    full[b] = std::min<int64_t>(S, len / chunk);
+    part[b] = full[b] < S ? len - full[b] * chunk : 0;   // length of split full[b] (0: empty)
   }
   int64_t pos = 0;
   auto put = [&](int64_t b, int64_t h, int64_t s) { order[pos++] = (int32_t)((b * H + h) * S + s); };

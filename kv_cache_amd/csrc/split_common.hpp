@@ -240,9 +240,12 @@ __global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64
   const int wave = threadIdx.x >> 6;
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
-  int begin, end;
-  split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int n_q = I8 ? quantized_len(p, T) : T;
+  int begin, end;
+  if (I8)
+    split_range_weighted(vis.n_vis, residual_ordinal(vis, n_q), s, p.chunk, &begin, &end);
+  else
+    split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int64_t base = (((int64_t)b * p.num_kv_heads + h) * p.num_splits + s) * p.chunk;
   const RowAddr ra = row_addr<PAGED && !I8>(p, b, h, D);
   const bool fm = !I8 && p.mask_kind == DA_MASK_FLASHMASK;

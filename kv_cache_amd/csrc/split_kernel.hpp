@@ -134,9 +134,12 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
 
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
-  int begin, end;
-  split_range(vis.n_vis, s, p.chunk, &begin, &end);
   const int n_q = FMT == DA_KV_I8 ? quantized_len(p, T) : T;
+  int begin, end;
+  if (FMT == DA_KV_I8)
+    split_range_weighted(vis.n_vis, residual_ordinal(vis, n_q), s, p.chunk, &begin, &end);
+  else
+    split_range(vis.n_vis, s, p.chunk, &begin, &end);
 
   if (begin >= end) {   // empty split: the identity state, written before any arithmetic
     write_identity<G, D, NWAVES, FUSED>(p, b, h, s);

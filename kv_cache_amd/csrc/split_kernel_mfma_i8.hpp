@@ -120,8 +120,10 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
+  const int n_q = quantized_len(p, T);
+  const int o_res = residual_ordinal(vis, n_q);
   int begin, end;
-  split_range(vis.n_vis, s, p.chunk, &begin, &end);
+  split_range_weighted(vis.n_vis, o_res, s, p.chunk, &begin, &end);
   // Score column n is virtual head n, with its own visible end (C > 1 rows).
   const int lim_n = row_limit(p, vis.n_vis, n);
   if (begin >= end) {
@@ -129,9 +131,6 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
-  const int n_q = quantized_len(p, T);
-  // first ordinal whose position is >= n_q
-  const int o_res = n_q <= vis.ns ? n_q : max(vis.ns, n_q - vis.gap);
   const int mid = min(max(o_res, begin), end);
 
   const uint32_t row_stride = (uint32_t)(p.num_kv_heads * D);
