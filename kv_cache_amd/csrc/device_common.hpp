@@ -131,12 +131,22 @@ __device__ __forceinline__ int vis_pos(const VisProgram& v, int o) {
 // Every run records in the workspace how its states are laid out, so that
 // the combine (which gets no run arguments) folds the right slots: W = 0 for
 // the plan's fixed splits, else the partition header [W, L, B, 0, P_0..P_B].
-// Written by workgroup 0 before any state.
+// Written by workgroup 0.
 __device__ __forceinline__ void write_partition_header(const SplitParams& p) {
   if (blockIdx.x != 0 || !p.ws_part) return;
   for (int i = threadIdx.x; i < p.batch + 5; i += blockDim.x)
     p.ws_part[i] = (p.partition && i != 3) ? p.partition[i] : 0;
 }
+
+// Writes the header when a split kernel returns, on every path.  A store at
+// the start of the kernel would keep the compiler from proving the request
+// metadata (lengths, work order) unchanged when it is read, so those reads
+// could not go through the scalar unit and their waits would also wait for
+// every vector load issued before them.
+struct PartitionHeaderAtExit {
+  const SplitParams& p;
+  __device__ ~PartitionHeaderAtExit() { write_partition_header(p); }
+};
 
 // Visible length of request b, clamped to the plan's bound so that no load
 // can leave the buffers the plan was sized for.
@@ -160,7 +170,7 @@ __device__ __forceinline__ void decode_workgroup(const SplitParams& p, int* b, i
   const int wg = blockIdx.x;
   int bh;
   if (p.work_order) {
-    int item = p.work_order[wg];
+    int item = __builtin_amdgcn_readfirstlane(p.work_order[wg]);   // one entry per workgroup
     if ((unsigned)item >= gridDim.x) item = wg;   // never index outside the grid's work
 
     bh = item / p.num_splits;

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   static_assert(LPR >= 4 && LPR <= 64 && (64 % LPR) == 0, "row must span 4..64 lanes");
 
   int b, h, s;
-  write_partition_header(p);
+  const PartitionHeaderAtExit header_at_exit{p};
   decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   constexpr int TW = 16;
   static_assert(G >= 1 && G <= 16, "");
 
-  write_partition_header(p);
+  const PartitionHeaderAtExit header_at_exit{p};
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int n = lane & 15;     // K row of the tile / score column (head)
@@ -100,23 +100,6 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
                                                out_row(p, b, h, n) * D + 32 * c + 8 * kg);
   }
 
-  const int T = request_len(p, b);
-  const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
-  int begin, end;
-  if (pend < 0) {
-    split_range(vis.n_vis, s, p.chunk, &begin, &end);
-  } else {
-    begin = min(pbeg, vis.n_vis);
-    end = min(pend, vis.n_vis);
-  }
-  // Score column n is virtual head n, with its own visible end (C > 1 rows).
-  const int end_n = min(end, row_limit(p, vis.n_vis, n));
-  if (begin >= end) {
-    write_identity<G, D, NWAVES, FUSED>(p, b, h, s);
-    finish_split<G, D, NWAVES, FUSED>(p, b, h);
-    return;
-  }
-
   // Row r of the tile is ordinal tile + r; rows past the split end are
   // clamped to its last row, which is visible and finite, and then get weight
   // 0 (score -inf), so the loads need no branches.
@@ -125,11 +108,6 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   const uint16_t* kb = static_cast<const uint16_t*>(p.k) + hb + 8 * kg;
   const uint16_t* vb = static_cast<const uint16_t*>(p.v) + hb + 8 * n;
   const uint32_t row_stride = p.row_stride;
-  // Lane l resolves the row index of tile row l%16 (one page-table lookup
-  // per row); the V rows 4kg+j take theirs from lane 4kg+j.
-  auto row_index = [&](int tile) {
-    return kv_row_index<PAGED>(p, ra, vis_pos(vis, min(tile + n, end - 1)));
-  };
   auto issue_k = [&](uint32_t ri, uint4 (&k)[4]) {
     const uint16_t* row = kb + (uint64_t)ri * row_stride;
 #pragma unroll
@@ -141,6 +119,47 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       const uint32_t rj = (uint32_t)__shfl((int)ri, 4 * kg + j);
       v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)rj * row_stride));
     }
+  };
+
+  // Speculative first tile: with a plain contiguous cache and the causal mask
+  // the first tile's rows (ordinals s*chunk + wave*16 + r, positions equal to
+  // ordinals) do not depend on the request length, so they are requested
+  // before it arrives, clamped to the capacity (in bounds); once the split end
+  // is known, rows at or past it get zero V, and their scores are masked like
+  // those of any row past the end.
+  MfmaTile t;
+  bool spec = false;
+  if constexpr (!PAGED && !FM && !PART) {
+    spec = p.mask_kind == DA_MASK_CAUSAL && p.layout == DA_LAYOUT_CONTIG_NHD && !p.cache_batch_idx &&
+           p.kv_capacity > 0;
+    if (spec) {
+      const int t0 = s * p.chunk + wave * TW;
+      const int cap = p.kv_capacity;
+      issue_k((uint32_t)min(t0 + n, cap - 1), t.k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        t.v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)min(t0 + 4 * kg + j, cap - 1) * row_stride));
+    }
+  }
+
+  const int T = request_len(p, b);
+  const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
+  int begin, end;
+  if (pend < 0) {
+    split_range(vis.n_vis, s, p.chunk, &begin, &end);
+  } else {
+    begin = min(pbeg, vis.n_vis);
+    end = min(pend, vis.n_vis);
+  }
+  // Score column n is virtual head n, with its own visible end (C > 1 rows).
+  // An empty split (begin == end) runs no tile and stores the empty state
+  // (m = -inf, l = 0, u = 0) through the same merge as any other.
+  const int end_n = min(end, row_limit(p, vis.n_vis, n));
+
+  // Lane l resolves the row index of tile row l%16 (one page-table lookup
+  // per row); the V rows 4kg+j take theirs from lane 4kg+j.
+  auto row_index = [&](int tile) {
+    return kv_row_index<PAGED>(p, ra, vis_pos(vis, min(tile + n, end - 1)));
   };
 
   float m_run = -INFINITY;   // running max of head n (base 2), equal in the 4 lanes of the head
@@ -192,16 +211,21 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     }
   };
 
-  MfmaTile t;
   int tile = first_tile();
   // Row indices run one tile ahead of the loads that use them, so a paged
   // cache's block-table lookup is off the load path.
   uint32_t ri = 0, ri_ahead = 0;
   if (tile < end) {
-    ri = row_index(tile);
-    issue_k(ri, t.k);
-    issue_iv(tile);
-    issue_v(ri, t.v);
+    if (spec) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (tile + 4 * kg + j >= end) t.v[j] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      ri = row_index(tile);
+      issue_k(ri, t.k);
+      issue_iv(tile);
+      issue_v(ri, t.v);
+    }
     ri_ahead = row_index(step(tile));
   }
   for (; tile < end; tile = step(tile)) {

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   static_assert(G >= 1 && G <= 16, "");
 
   int b, h, s;
-  write_partition_header(p);
+  const PartitionHeaderAtExit header_at_exit{p};
   decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
