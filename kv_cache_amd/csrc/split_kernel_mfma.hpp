@@ -100,9 +100,8 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
                                                out_row(p, b, h, n) * D + 32 * c + 8 * kg);
   }
 
-  // Row r of the tile is ordinal tile + r; rows past the split end are
-  // clamped to its last row, which is visible and finite, and then get weight
-  // 0 (score -inf), so the loads need no branches.
+  // Row addresses: lane (n, kg) loads 16 bytes of K row n at channel 8kg of
+  // each 32-channel slice, and 16 bytes of V row 4kg + j at channel 8n.
   const RowAddr ra = row_addr<PAGED>(p, b, h, D);
   const int64_t hb = ra.base;
   const uint16_t* kb = static_cast<const uint16_t*>(p.k) + hb + 8 * kg;
@@ -137,8 +136,10 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       const int cap = p.kv_capacity;
       issue_k((uint32_t)min(t0 + n, cap - 1), t.k);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        t.v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)min(t0 + 4 * kg + j, cap - 1) * row_stride));
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t rj = (uint32_t)min(t0 + 4 * kg + j, cap - 1);
+        t.v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)rj * row_stride));
+      }
     }
   }
 
@@ -156,8 +157,11 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   // (m = -inf, l = 0, u = 0) through the same merge as any other.
   const int end_n = min(end, row_limit(p, vis.n_vis, n));
 
-  // Lane l resolves the row index of tile row l%16 (one page-table lookup
-  // per row); the V rows 4kg+j take theirs from lane 4kg+j.
+  // Row r of the tile is ordinal tile + r; rows past the split end are
+  // clamped to its last row, which is visible and finite, and then get weight
+  // 0 (score -inf), so the loads need no branches.  Lane l resolves the row
+  // index of tile row l%16 (one page-table lookup per row); the V rows 4kg+j
+  // take theirs from lane 4kg+j.
   auto row_index = [&](int tile) {
     return kv_row_index<PAGED>(p, ra, vis_pos(vis, min(tile + n, end - 1)));
   };
