@@ -65,6 +65,23 @@ def test_small_contiguous_ragged(dtype, D, Hq, Hkv):
         H.check_rows(O, L, Or, Lr, TOL[dtype])
 
 
+@pytest.mark.parametrize("C", [1, 2])
+def test_first_tile_at_capacity_and_empty_splits(C):
+    # capacity equal to the longest request: first tiles reach past the
+    # capacity (clamped) and past request ends (poison rows beyond T must not
+    # leak), and splits past short requests are empty; single launch and
+    # run + combine
+    lens = [40, 33, 0, 17, 1]
+    w = synth.make_contiguous(31, len(lens), 16, 4, 128, lens, kv_capacity=40, num_queries=C)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for S in (0, 1, 2, 3):
+        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        H.check_rows(O, L, Or, Lr, TOL["bf16"])
+        O2, L2, _ = H.forward(w, num_splits=S, dw=dw)
+        H.check_rows(O2, L2, Or, Lr, TOL["bf16"])
+
+
 def test_peaky_scores_stress():
     """q scaled by sqrt(d): score std ~ 11, exercising the online rescale."""
     w = synth.make_contiguous(4, 4, 32, 8, 128, [4096, 3000, 17, 2049], q_scale=math.sqrt(128))
