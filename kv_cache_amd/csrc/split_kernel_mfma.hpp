@@ -175,8 +175,9 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     for (int e = 0; e < 8; ++e) u[i][e] = 0.f;
 
   // One tile of registers: the next tile's K rows are requested as soon as
-  // the score instructions have read the current ones, its V rows as soon as
-  // PV has read the current ones.  The requests after the last tile repeat
+  // the score instructions have read the current ones, its V rows once the
+  // current ones have arrived (PV then reads them from a copy) or, where
+  // registers are short, once PV has read them.  The requests after the last tile repeat
   // row end-1 (already cached) and keep the loop free of branches.
   // FlashMask: lane k classifies tile k of the split (a split has at most 64
   // tiles of 16 keys); SKIP tiles are never loaded, PARTIAL tiles bring the
@@ -265,16 +266,25 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = mn;
 
+    // The next tile's V rows are requested before PV reads this tile's (kept
+    // in a second set of registers), so they are in flight during PV -- where
+    // the registers allow it: not with a paged cache's table lookups at four
+    // waves per SIMD, nor with eight heads.
+    constexpr bool kEarlyV = (!PAGED || PART) && G <= 4;
+    uint4 vcur[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vcur[j] = t.v[j];
+    if constexpr (kEarlyV) issue_v(ri, t.v);
     if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w[4] = {t.v[j].x, t.v[j].y, t.v[j].z, t.v[j].w};
+      const uint32_t w[4] = {vcur[j].x, vcur[j].y, vcur[j].z, vcur[j].w};
       float vx[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) { vx[2 * e] = bf16_lo(w[e]); vx[2 * e + 1] = bf16_hi(w[e]); }
       HeadLoop<G>::accumulate(u, pr[j], vx);
     }
-    issue_v(ri, t.v);
+    if constexpr (!kEarlyV) issue_v(ri, t.v);
   }
 
   // ---- wave state: all rows of a head share m, so l and u just add ---------
