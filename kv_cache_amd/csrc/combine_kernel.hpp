@@ -36,7 +36,7 @@ namespace da {
 constexpr int kCombineThreads = 1024;
 constexpr int kCombineThreadsSmall = 256;
 constexpr int kCombineSmallS = 32;
-constexpr int kCombineSlice = 16;
+constexpr int kCombineSlice = 32;
 constexpr int kCombineSliceRows = 256;
 
 template <int D, int NT, int DS = D>
