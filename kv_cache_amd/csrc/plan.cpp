@@ -189,12 +189,13 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
   int64_t max_vis = p.max_seq_len;
   if (p.mask_kind == DA_MASK_SINK_WINDOW)
     max_vis = std::min<int64_t>(max_vis, (int64_t)p.n_sink + (int64_t)p.window);
-  // Splits cut the visible ordinals into chunks of equal length; for int8
-  // caches by weight, a residual row (bf16 K and V) counting as two int8 rows,
-  // with no tile alignment (the int8 kernel's tiles start at the split).
+  // Splits cut the visible ordinals into chunks of equal length (for int8
+  // caches by weight, a residual row (bf16 K and V) counting as two int8
+  // rows).  Tiles start at the split, so chunks need no tile alignment, except
+  // under FlashMask, whose tiles are the 16-key blocks of the summaries.
   const bool i8 = p.kv_format == DA_KV_I8;
   const int64_t split_len = max_vis + (i8 ? std::min<int64_t>(std::max(p.residual_len, 0), max_vis) : 0);
-  const int64_t align = i8 ? 1 : kRowAlign;
+  const int64_t align = p.mask_kind == DA_MASK_FLASHMASK ? kRowAlign : 1;
   int64_t chunk;
   if (max_vis == 0) {
     chunk = kRowAlign;

@@ -63,7 +63,8 @@ def test_workspace_and_auto_splits_llama_shape():
     header = (8 + 5) * 4          # partition header [W, L, B, 0, P_0..P_B]
     rup = lambda x: (x + 255) // 256 * 256
     assert ws == rup(states) + rup(counters) + rup(header) == pl.workspace_bytes
-    assert pl.chunk % 16 == 0 and S * pl.chunk >= 4096 and (S - 1) * pl.chunk < 4096
+    assert S * pl.chunk >= 4096 and (S - 1) * pl.chunk < 4096
+    assert pl.chunk == -(-4096 // S)  # equal chunks, no tile rounding: 12 x 342 rows on 256 CUs
     assert 8 * 8 * S >= 256          # at least one workgroup per CU
     assert abs(pl.problem.softmax_scale - 1 / math.sqrt(128)) < 1e-8
 
@@ -79,6 +80,14 @@ def test_uneven_splits_have_partial_tail():
     st, pl, _, _ = plan(P(batch=1, kv_capacity=131072, max_seq_len=131071, num_splits=128))
     assert st == ka.DA_OK and pl.num_splits == 128
     assert pl.chunk * 127 < 131071 < pl.chunk * 128
+
+
+def test_flashmask_chunks_stay_tile_aligned():
+    # FlashMask classifies 16-key blocks, so its splits start on block boundaries
+    st, pl, _, _ = plan(P(mask_kind="flashmask", max_seq_len=4000, kv_capacity=4000, num_splits=12))
+    assert st == ka.DA_OK and pl.chunk % 16 == 0 and pl.num_splits * pl.chunk >= 4000
+    st, pl, _, _ = plan(P(max_seq_len=4000, kv_capacity=4000, num_splits=12))
+    assert st == ka.DA_OK and pl.chunk == 334
 
 
 def test_sink_window_bounds_visible_rows():
