@@ -218,13 +218,6 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
         const int t_pb = pb + shift;
         const int g0 = t_pb >> sh;
         const int ng = ((pe - 1 + shift) >> sh) - g0 + 1;
-        if (staged) __syncthreads();                       // the previous phase has read its table
-        staged = true;
-        for (int idx = threadIdx.x; idx < ng * 16; idx += NWAVES * 64)
-          ksc[idx >> 4][idx & 15] =
-              *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
-        __syncthreads();
-
         const int8_t* kp = kc + (uint64_t)t_pb * row_stride;
         const int8_t* vp = vc + (uint64_t)t_pb * row_stride;
         const char* vsp = reinterpret_cast<const char*>(vs + (int64_t)t_pb * p.num_kv_heads);
@@ -306,6 +299,14 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
           issue_v(tile, va, sva);
           issue_v(tile + STEP, vb, svb);
         }
+        // The scale table is staged after the first tiles are requested, so its
+        // latency overlaps theirs instead of preceding it.
+        if (staged) __syncthreads();                       // the previous phase has read its table
+        staged = true;
+        for (int idx = threadIdx.x; idx < ng * 16; idx += NWAVES * 64)
+          ksc[idx >> 4][idx & 15] =
+              *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
+        __syncthreads();
         for (; tile < pe; tile += 2 * STEP) {
           const int tb = tile + STEP;
           const f32x4_t acc = scores(tile, ka);
