@@ -103,8 +103,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
 
   // q rows in the B operand layout, q[head n][32c + 8kg .. +7] (zero for
-  // n >= G), staged in LDS for the residual part (the int8 part reads q in
-  // its own channel order).
+  // n >= G), staged in LDS: the residual part uses them as they are, the int8
+  // part reads them in its own channel order.
   __shared__ uint4 q_lds[4][64];
   if (wave == 0) {
 #pragma unroll
@@ -189,12 +189,14 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   auto kch = [&](int c) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1); };
   __shared__ uint4 ksc[kI8ScaleSlots][16];
   if (begin < mid) {
+    // q in this part's channel order, read from the staged rows: channels
+    // kch(c) .. +7 of head n are 8-channel block kch(c)/8 = 4c' + kg', held by
+    // lane n + 16kg' of q_lds[c'] (zero for n >= G).
     uint4 qh[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (n < G)
-        x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + out_row(p, b, h, n) * D + kch(c));
+      const int blk = kch(c) >> 3;
+      const uint4 x = q_lds[blk >> 2][n + 16 * (blk & 3)];
       // bf16 values of N(0,1)-scale queries are exact in fp16
       qh[c] = make_uint4(pack_f16(bf16_lo(x.x), bf16_hi(x.x)), pack_f16(bf16_lo(x.y), bf16_hi(x.y)),
                          pack_f16(bf16_lo(x.z), bf16_hi(x.z)), pack_f16(bf16_lo(x.w), bf16_hi(x.w)));
