@@ -40,6 +40,9 @@ struct AppendParams {
 constexpr int kAppendThreads = 256;
 
 __device__ __forceinline__ float bf16_value(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+// the two bf16 values packed in a 32-bit word (element 2j in the low half)
+__device__ __forceinline__ float bf16_word_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_word_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Stored fp16 scale of a vector with largest magnitude amax; clears ok when it
 // is not a finite normal fp16 value.
@@ -57,15 +60,20 @@ __device__ __forceinline__ int8_t code_of(float x, uint16_t scale_bits) {
   return (int8_t)fmin(fmax(q, -127.0), 127.0);
 }
 
-template <int D>
+// MR: sweeps of the closure layout the instance holds, at least G / RS.
+template <int D, int MR>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
   static_assert(D % 64 == 0 && D <= kAppendThreads, "");
-  constexpr int CPL = D / 64;                      // channels per lane in the V row pass
-  constexpr int NW = kAppendThreads / 64;
+  // Closure layout: thread t holds the 16-byte channel group cg = t % CG of
+  // rows t / CG, t / CG + RS, ... of the G closed rows (K and V), loaded once
+  // and all at the start; K scales reduce over the threads of one channel
+  // group, V scales over the CG consecutive lanes of one row.
+  constexpr int CG = D / 8;                       // channel groups per row
+  constexpr int RS = kAppendThreads / CG;         // rows per sweep of all threads
   const int H = p.num_kv_heads;
   const int b = blockIdx.x / H;
   const int h = blockIdx.x - b * H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int G = p.group;
   const int T = p.seq_lens[b];
   if (T < 0 || T >= p.max_seq_len) {
@@ -80,54 +88,84 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   int slot = r;
 
   if (r == G) {
+    __shared__ uint32_t kmax[D];                 // per-channel amax bits (non-negative floats order as integers)
     __shared__ uint16_t ks[D];
-    __shared__ uint16_t vs[kAppendThreads];              // G <= 256 rows
+    const int cg = tid % CG, r0 = tid / CG;
+    if (tid < D) kmax[tid] = 0u;
+    uint4 kx[MR], vx[MR];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const int row = r0 + i * RS;
+      kx[i] = vx[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (row < G) {
+        kx[i] = *reinterpret_cast<const uint4*>(kres + row * row_stride + 8 * cg);
+        vx[i] = *reinterpret_cast<const uint4*>(vres + row * row_stride + 8 * cg);
+      }
+    }
+    auto elem = [](const uint4& w, int j) { return j < 2 ? (j == 0 ? w.x : w.y) : (j == 2 ? w.z : w.w); };
     bool ok = true;
-    // K: thread c owns channel c over the G rows
-    if (tid < D) {
-      float amax = 0.f;
-      for (int i = 0; i < G; ++i) {
-        const float x = bf16_value(kres[i * row_stride + tid]);
+    // K: partial amax of my 8 channels over my rows, folded into kmax
+    float kam[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kam[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = elem(kx[i], e >> 1);
+        const float x = (e & 1) ? bf16_word_hi(w) : bf16_word_lo(w);
         ok = ok && __builtin_isfinite(x);
-        amax = fmaxf(amax, fabsf(x));
+        kam[e] = fmaxf(kam[e], fabsf(x));
       }
-      ks[tid] = stored_scale(amax, ok);
     }
-    // V: wave w owns rows w, w + NW, ...; lane holds CPL channels of the row
-    for (int i = wave; i < G; i += NW) {
-      float amax = 0.f;
+    __syncthreads();                             // kmax cleared
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const float x = bf16_value(vres[i * row_stride + lane + 64 * j]);
+    for (int e = 0; e < 8; ++e) atomicMax(&kmax[8 * cg + e], __float_as_uint(kam[e]));
+    // V: amax of each of my rows over the row's CG lanes, then its scale
+    uint16_t vsc[MR];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = elem(vx[i], e >> 1);
+        const float x = (e & 1) ? bf16_word_hi(w) : bf16_word_lo(w);
         ok = ok && __builtin_isfinite(x);
-        amax = fmaxf(amax, fabsf(x));
+        a = fmaxf(a, fabsf(x));
       }
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      for (int off = 1; off < CG; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
       bool row_ok = true;
-      const uint16_t s = stored_scale(amax, row_ok);
-      ok = ok && row_ok;
-      if (lane == 0) vs[i] = s;
+      vsc[i] = stored_scale(a, row_ok);
+      if (r0 + i * RS < G) ok = ok && row_ok;
     }
+    __syncthreads();                             // kmax complete
+    if (tid < D) ks[tid] = stored_scale(__uint_as_float(kmax[tid]), ok);
     if (!__syncthreads_and(ok)) {
       if (tid == 0 && p.status) atomicOr(p.status + b, (int)DA_APPEND_BAD_SCALE);
       return;
     }
-    // codes of the closed rows, then their scales
+    // codes of the closed rows from the registers, then the scales
     int8_t* kc = p.k + ((int64_t)b * p.kv_capacity + n_q) * row_stride + (int64_t)h * D;
     int8_t* vc = p.v + ((int64_t)b * p.kv_capacity + n_q) * row_stride + (int64_t)h * D;
-    if (tid < D) {
-      const uint16_t s = ks[tid];
-      for (int i = 0; i < G; ++i) kc[i * row_stride + tid] = code_of(bf16_value(kres[i * row_stride + tid]), s);
-      p.k_scale[(((int64_t)b * p.n_groups + n_q / G) * H + h) * D + tid] = s;
-    }
-    for (int i = wave; i < G; i += NW) {
-      const uint16_t s = vs[i];
 #pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        vc[i * row_stride + lane + 64 * j] = code_of(bf16_value(vres[i * row_stride + lane + 64 * j]), s);
-      if (lane == 0) p.v_scale[((int64_t)b * p.kv_capacity + n_q + i) * H + h] = s;
+    for (int i = 0; i < MR; ++i) {
+      const int row = r0 + i * RS;
+      if (row >= G) continue;
+      uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = elem(kx[i], e >> 1), u = elem(vx[i], e >> 1);
+        const float xk = (e & 1) ? bf16_word_hi(w) : bf16_word_lo(w);
+        const float xv = (e & 1) ? bf16_word_hi(u) : bf16_word_lo(u);
+        kw[e >> 2] |= (uint32_t)(uint8_t)code_of(xk, ks[8 * cg + e]) << (8 * (e & 3));
+        vw[e >> 2] |= (uint32_t)(uint8_t)code_of(xv, vsc[i]) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(kc + row * row_stride + 8 * cg) = make_uint2(kw[0], kw[1]);
+      *reinterpret_cast<uint2*>(vc + row * row_stride + 8 * cg) = make_uint2(vw[0], vw[1]);
+      if (cg == 0) p.v_scale[((int64_t)b * p.kv_capacity + n_q + row) * H + h] = vsc[i];
     }
+    if (tid < D) p.k_scale[(((int64_t)b * p.n_groups + n_q / G) * H + h) * D + tid] = ks[tid];
     __syncthreads();      // every read of residual row 0 precedes its overwrite
     slot = 0;
   }

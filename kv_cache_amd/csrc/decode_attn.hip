@@ -337,10 +337,13 @@ extern "C" da_status decode_attn_append(const da_plan* plan, const da_append_arg
   const dim3 grid((unsigned)(p.batch * p.num_kv_heads));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (p.head_dim_qk == 128)
-    hipLaunchKernelGGL(da::append_kernel<128>, grid, dim3(da::kAppendThreads), 0, st, ap);
+  // closure rows per thread: G / (threads / (D / 8)), i.e. G / 16 (D = 128) or G / 32 (D = 64)
+  if (p.head_dim_qk == 128 && p.k_group <= 128)
+    hipLaunchKernelGGL((da::append_kernel<128, 8>), grid, dim3(da::kAppendThreads), 0, st, ap);
+  else if (p.head_dim_qk == 128)
+    hipLaunchKernelGGL((da::append_kernel<128, 16>), grid, dim3(da::kAppendThreads), 0, st, ap);
   else
-    hipLaunchKernelGGL(da::append_kernel<64>, grid, dim3(da::kAppendThreads), 0, st, ap);
+    hipLaunchKernelGGL((da::append_kernel<64, 8>), grid, dim3(da::kAppendThreads), 0, st, ap);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -19,21 +19,21 @@ def _name(request):
     H.announce(request.node.nodeid)
 
 
-def _cache(seed, lens, cap, Hq=8, Hkv=2, D=128, values=None):
+def _cache(seed, lens, cap, Hq=8, Hkv=2, D=128, values=None, g=G):
     w = synth.make_int8(seed, len(lens), Hq, Hkv, D, lens, kv_capacity=cap, residual_policy="groups",
-                        values=values)
+                        values=values, k_group=g, residual_len=g)
     w.problem.max_seq_len = cap
     return w
 
 
-def _parts(buf, b, T):
+def _parts(buf, b, T, G=G):
     n_q = quantized_count(T, "groups", G, G)
     return dict(n_q=n_q, k_codes=buf["k"][b, :n_q], k_scale=buf["k_scale"][b, :n_q // G],
                 v_codes=buf["v"][b, :n_q], v_scale=buf["v_scale"][b, :n_q],
                 k_resid_bits=buf["k_resid"][b, :T - n_q], v_resid_bits=buf["v_resid"][b, :T - n_q])
 
 
-def _apply_parts(buf, b, parts):
+def _apply_parts(buf, b, parts, G=G):
     n_q = parts["n_q"]
     r = parts["k_resid_bits"].shape[0]
     buf["k"][b, :n_q] = parts["k_codes"]
@@ -93,6 +93,35 @@ def test_append_steps_across_group_closure_byte_exact_and_attention():
     O, L, _ = H.forward(w, dw=dw)
     Or, Lr = oracle.attend(w.problem, w.buffers)
     H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+
+
+@pytest.mark.parametrize("D,g", [(64, 128), (128, 256), (128, 32), (64, 256), (64, 16)])
+def test_append_closure_other_head_dims_and_groups(D, g):
+    # the closure's layouts for other head sizes and group lengths (rows per
+    # thread from one to sixteen, partial sweeps): appends across a closure,
+    # byte-exact against the oracle's append model
+    lens = [g - 1, g, 2 * g, 0, 3 * g + 5]
+    cap = 4 * g
+    w = _cache(41 + D + g, lens, cap, D=D, g=g)
+    _, plan, _, _ = ka.decode_attn_plan(ka.problem_from(w.problem))
+    dw = H.DeviceWorkload(w)
+    ref = {k: w.buffers[k].copy() for k in ("k", "v", "k_scale", "v_scale", "k_resid", "v_resid")}
+    cur = list(lens)
+    for step in range(2):
+        k_new, v_new = synth.append_rows(300 + step, len(lens), 2, D)
+        status = _gpu_append(plan, dw.dev, k_new, v_new, cur)
+        assert not status.any()
+        for b, T in enumerate(cur):
+            st = kivi_state_from_parts(_parts(ref, b, T, g), g)
+            _apply_parts(ref, b, kivi_state_parts(kivi_append(st, k_new[b], v_new[b], g, g)), g)
+        cur = [T + 1 for T in cur]
+        got = _host(dw.dev, ref)
+        for b, T in enumerate(cur):
+            e, g_ = _parts(ref, b, T, g), _parts(got, b, T, g)
+            for key in ("k_codes", "v_codes", "k_resid_bits", "v_resid_bits"):
+                assert np.array_equal(e[key], g_[key]), (step, b, key)
+            for key in ("k_scale", "v_scale"):
+                assert np.array_equal(e[key].view(np.uint16), g_[key].view(np.uint16)), (step, b, key)
 
 
 def test_append_no_room_and_bad_scale_write_nothing():
