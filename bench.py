@@ -58,10 +58,13 @@ class GpuWorkload:
     """Device buffers, a plan and the algorithmic byte count of one workload.
 
     kinds: "contig" (bf16 or fp32), "paged" (bf16, P=16, ragged), "i8"
-    (int8 codes + fp16 scales + bf16 residual, sink+window mask)."""
+    (int8 codes + fp16 scales + bf16 residual, sink+window mask).  Contiguous
+    options: C query rows per request (bottom-right causal), the HND layout,
+    and FlashMask column intervals (seeded document/scatter runs)."""
 
     def __init__(self, torch, ka, kind, B, Hq, Hkv, D, lens, num_splits=0, min_bytes=0, seed=0,
-                 dtype="bf16", mask=None, page_size=16, k_group=128, residual=128):
+                 dtype="bf16", mask=None, page_size=16, k_group=128, residual=128, C=1, hnd=False,
+                 flashmask=False):
         import numpy as np
         import synth
         self.torch, self.ka, self.kind = torch, ka, kind
@@ -73,9 +76,12 @@ class GpuWorkload:
         eb = 4 if dtype == "f32" else 2
         tdt = torch.float32 if dtype == "f32" else torch.bfloat16
         mk = dict(mask_kind="sink_window", n_sink=mask[0], window=mask[1]) if mask else {}
+        if flashmask:
+            mk = dict(mask_kind="flashmask")
         if kind == "contig":
             prob = synth.Problem(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=dtype,
-                                 kv_format=dtype, kv_capacity=T, max_seq_len=T, num_splits=num_splits, **mk)
+                                 kv_format=dtype, kv_capacity=T, max_seq_len=T, num_splits=num_splits,
+                                 num_queries=C, layout="contig_hnd" if hnd else "contig", **mk)
             per_set = 2 * B * T * Hkv * D * eb
         elif kind == "paged":
             pages = [(t + page_size - 1) // page_size for t in self.lens]
@@ -96,12 +102,26 @@ class GpuWorkload:
         self.S = self.plan.num_splits
         self.nsets = max(1, -(-min_bytes // per_set)) if min_bytes else 1
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
+        self.mask_iv = self.mask_sum = None
+        hidden = None
+        if flashmask:
+            iv = synth.flashmask_intervals(seed, self.lens, T)
+            self.mask_iv = torch.from_numpy(np.ascontiguousarray(iv.astype(np.int32))).to("cuda")
+            nblk = (T + 15) // 16
+            self.mask_sum = torch.empty((B, nblk, 2, 4), dtype=torch.int32, device="cuda")
+            ka.decode_attn_flashmask_summarize(self.plan, self.mask_iv, self.mask_sum,
+                                               torch.cuda.current_stream().cuda_stream)
+            # keys the decode row q = T_b - 1 cannot see: q in [UTS, UTE) or [LTS, LTE)
+            hidden = [((iv[b, :t, 0] <= t - 1) & (t - 1 < iv[b, :t, 1])) |
+                      ((iv[b, :t, 2] <= t - 1) & (t - 1 < iv[b, :t, 3])) for b, t in enumerate(self.lens)]
+        qshape = (B, C, Hq, D) if C > 1 else (B, Hq, D)
         self.sets = []
         for _ in range(self.nsets):
-            d = {"q": torch.randn((B, Hq, D), device="cuda", dtype=tdt, generator=g)}
+            d = {"q": torch.randn(qshape, device="cuda", dtype=tdt, generator=g)}
             if kind == "contig":
-                d["k"] = torch.randn((B, T, Hkv, D), device="cuda", dtype=tdt, generator=g)
-                d["v"] = torch.randn((B, T, Hkv, D), device="cuda", dtype=tdt, generator=g)
+                kvshape = (B, Hkv, T, D) if hnd else (B, T, Hkv, D)
+                d["k"] = torch.randn(kvshape, device="cuda", dtype=tdt, generator=g)
+                d["v"] = torch.randn(kvshape, device="cuda", dtype=tdt, generator=g)
             elif kind == "paged":
                 d["k"] = torch.randn((n_pages, page_size, Hkv, D), device="cuda", dtype=tdt, generator=g)
                 d["v"] = torch.randn((n_pages, page_size, Hkv, D), device="cuda", dtype=tdt, generator=g)
@@ -122,8 +142,8 @@ class GpuWorkload:
                 d["v_resid"] = torch.randn((B, residual, Hkv, D), device="cuda", dtype=tdt, generator=g)
             self.sets.append(d)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
-        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
-        self.lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        self.out = torch.empty(qshape, dtype=torch.float32, device="cuda")
+        self.lse = torch.empty(qshape[:-1], dtype=torch.float32, device="cuda")
         self.order = None
         self.make_all_args()
         self.stream = torch.cuda.current_stream().cuda_stream
@@ -131,8 +151,11 @@ class GpuWorkload:
         # ---- algorithmic bytes: what the method must move once ----
         kvb = 0
         meta = B * 4
-        for t in self.lens:
+        for bi, t in enumerate(self.lens):
             vis = visible(t, mask)
+            if hidden is not None:          # FlashMask: the visible keys, plus the block summaries
+                vis = [p for p in vis if not hidden[bi][p]]
+                meta += ((t + 15) // 16) * 2 * 16
             if kind == "i8":
                 n_q = t - min(t, residual)
                 quant = [p for p in vis if p < n_q]
@@ -142,9 +165,9 @@ class GpuWorkload:
                 kvb += Hkv * len(vis) * 2 * D * eb
             if kind == "paged":
                 meta += ((t + page_size - 1) // page_size) * 4
-        q = B * Hq * D * eb
-        ws = B * Hq * self.S * (D + 2) * 4
-        out = B * Hq * (D + 1) * 4
+        q = B * C * Hq * D * eb
+        ws = B * C * Hq * self.S * (D + 2) * 4
+        out = B * C * Hq * (D + 1) * 4
         self.kv_bytes = kvb
         self.split_bytes = kvb + q + ws + meta
         self.call_bytes = self.split_bytes + ws + out
@@ -155,6 +178,7 @@ class GpuWorkload:
                                   k_scale=d.get("k_scale"), v_scale=d.get("v_scale"),
                                   k_resid=d.get("k_resid"), v_resid=d.get("v_resid"),
                                   block_table=d.get("block_table"), work_order=self.order,
+                                  mask_intervals=self.mask_iv, mask_summary=self.mask_sum,
                                   partition=getattr(self, "part", None),
                                   partition_items=getattr(self, "part_items", 0))
                      for d in self.sets]
@@ -297,6 +321,21 @@ def other_workload(torch, ka, name, steps=30, warmup=5):
                         mask=(4, 4096))
         return w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, "
                                 "4 sinks + window 4096", steps, warmup)
+    cfg2 = "B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16"
+    if name == "few_query_c2":
+        w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=6, C=2)
+        return w.report("fewq", cfg2 + " contiguous, C=2 query rows per request (bottom-right causal)",
+                        steps, warmup)
+    if name == "hnd_layout":
+        w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=7, hnd=True)
+        return w.report("hnd", cfg2 + " contiguous HND [B, H_kv, T, d], causal", steps, warmup)
+    if name == "flashmask":
+        w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=8,
+                        flashmask=True)
+        r = w.report("fm", cfg2 + " contiguous, FlashMask column intervals (seeded runs of closed "
+                             "documents, visible blocks and scattered hidden keys)", steps, warmup)
+        r["visible_kv_bytes"] = w.kv_bytes
+        return r
     if name == "tiny_fp32":
         w = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
         return w.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4", steps, warmup)
@@ -410,7 +449,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the other workloads")
     ap.add_argument("--only", default=None,
-                    choices=["long_context_128k", "paged_ragged", "int8_sink_window", "tiny_fp32"],
+                    choices=["long_context_128k", "paged_ragged", "int8_sink_window", "tiny_fp32",
+                             "few_query_c2", "hnd_layout", "flashmask"],
                     help="time one of the other workloads alone and print its report (for profiling)")
     ap.add_argument("--samples-out", default=None, help="write raw per-call samples (JSON)")
     a = ap.parse_args()
@@ -496,6 +536,8 @@ def main():
                   for name in ("long_context_128k", "paged_ragged", "int8_sink_window")}
         others["int8_append"] = append_timing(torch, ka)
         others["tiny_fp32"] = other_workload(torch, ka, "tiny_fp32")
+        for name in ("few_query_c2", "hnd_layout", "flashmask"):
+            others[name] = other_workload(torch, ka, name)
         line["other_workloads"] = others
     torch.cuda.synchronize()
     if not a.no_cpu_baseline:
