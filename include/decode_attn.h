@@ -164,7 +164,8 @@ typedef struct da_plan {
   uint64_t   key;              /* hash of every field below                         */
   da_problem problem;          /* normalized copy (softmax_scale resolved)          */
   int32_t    num_splits;       /* S launched: producer grid is B*H_kv*S workgroups  */
-  int32_t    chunk;            /* visible rows per split (multiple of 16)           */
+  int32_t    chunk;            /* visible rows per split; int8: weighted rows (a    */
+                               /* residual row counts 2); FlashMask: multiple of 16 */
   int32_t    max_visible;      /* bound on visible rows of one request              */
   int32_t    num_cus;          /* CU count the split heuristic used                 */
   uint64_t   workspace_bytes;  /* states round_up(B*H_q*S*(D + 2)*4, 256), then     */
@@ -286,7 +287,8 @@ da_status decode_attn_partition(const da_plan* plan, const int32_t* seq_lens_hos
                                 int32_t* part, uint64_t part_len, int32_t* items_out);
 
 /* Launch the split kernel: grid B*H_kv*S workgroups; workgroup (b, h_kv, s)
- * owns visible rows [s*chunk, min((s+1)*chunk, N_b)) of request b and the
+ * owns visible rows [s*chunk, min((s+1)*chunk, N_b)) of request b (int8:
+ * the rows whose weighted offsets fall there, a residual row weighing 2) and the
  * H_q/H_kv query heads sharing h_kv, reads each of its K/V rows once, and
  * writes one (m, l, u) state per query head into the workspace: u fp32
  * [B, H_q, S, D], then m fp32 [B, H_q, S] (natural-log units of the scaled
