@@ -56,3 +56,25 @@ def test_full_shape_flashmask():
     q = 4095
     hidden = ((iv[..., 0] <= q) & (q < iv[..., 1])) | ((iv[..., 2] <= q) & (q < iv[..., 3]))
     assert 0.2 < float(np.mean(hidden)) < 0.8
+
+
+@pytest.fixture(scope="module")
+def cfg3_base():
+    return synth.config(3, 1)
+
+
+@pytest.mark.parametrize("layout,table", [("paged_hnd", "dense"), ("paged", "csr")])
+def test_cfg3_layouts_sampled_rows_with_partition(cfg3_base, layout, table):
+    # the paged ragged batch of 32 requests (lengths 1 .. 32768) in the HND
+    # page layout and with a CSR page list, fixed splits and the balanced
+    # partition, on sampled rows (and the longest and shortest requests)
+    w = synth.relayout(cfg3_base, layout, page_table=table)
+    dw = H.DeviceWorkload(w)
+    g = synth.rng(78)
+    rows = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 16), g.integers(0, 32, 16))]
+    rows += [(int(np.argmax(w.buffers["seq_lens"])), 5), (int(np.argmin(w.buffers["seq_lens"])), 30)]
+    Or, Lr = oracle.attend(w.problem, w.buffers, heads=rows)
+    O, L, plan = H.run(w, dw=dw)
+    H.check_rows(O, L, Or, Lr, TOL, rows=rows)
+    O, L, _ = H.run(w, dw=dw, partition=0)
+    H.check_rows(O, L, Or, Lr, TOL, rows=rows)
