@@ -54,6 +54,36 @@ def visible(T, mask):
     return sorted(set(range(min(ns, T))) | set(range(max(0, T - W), T)))
 
 
+def algorithmic_bytes(kind, B, Hq, Hkv, D, lens, S, eb=2, mask=None, hidden=None, C=1, residual=128,
+                      k_group=128, page_size=16):
+    """Bytes the method must move once per call: every visible K/V row once per
+    K/V head (int8: codes, the row's V scale, each touched K scale row once,
+    bf16 residual rows), q, the split states written and read back, O and LSE,
+    and the metadata (lengths, block-table entries, FlashMask summaries).
+    Returns (K/V bytes, split-kernel bytes, whole-call bytes)."""
+    kvb = 0
+    meta = B * 4
+    for bi, t in enumerate(lens):
+        vis = visible(t, mask)
+        if hidden is not None:          # FlashMask: the visible keys, plus the block summaries
+            vis = [p for p in vis if not hidden[bi][p]]
+            meta += ((t + 15) // 16) * 2 * 16
+        if kind == "i8":
+            n_q = t - min(t, residual)
+            quant = [p for p in vis if p < n_q]
+            kvb += Hkv * (len(quant) * (2 * D + 2) + (len(vis) - len(quant)) * 2 * D * 2
+                          + len({p // k_group for p in quant}) * D * 2)
+        else:
+            kvb += Hkv * len(vis) * 2 * D * eb
+        if kind == "paged":
+            meta += ((t + page_size - 1) // page_size) * 4
+    q = B * C * Hq * D * eb
+    ws = B * C * Hq * S * (D + 2) * 4
+    out = B * C * Hq * (D + 1) * 4
+    split = kvb + q + ws + meta
+    return kvb, split, split + ws + out
+
+
 class GpuWorkload:
     """Device buffers, a plan and the algorithmic byte count of one workload.
 
@@ -149,28 +179,9 @@ class GpuWorkload:
         self.stream = torch.cuda.current_stream().cuda_stream
         ka.decode_attn_workspace_init(self.plan, self.ws, self.ws_bytes, self.stream)
         # ---- algorithmic bytes: what the method must move once ----
-        kvb = 0
-        meta = B * 4
-        for bi, t in enumerate(self.lens):
-            vis = visible(t, mask)
-            if hidden is not None:          # FlashMask: the visible keys, plus the block summaries
-                vis = [p for p in vis if not hidden[bi][p]]
-                meta += ((t + 15) // 16) * 2 * 16
-            if kind == "i8":
-                n_q = t - min(t, residual)
-                quant = [p for p in vis if p < n_q]
-                kvb += Hkv * (len(quant) * (2 * D + 2) + (len(vis) - len(quant)) * 2 * D * 2
-                              + len({p // k_group for p in quant}) * D * 2)
-            else:
-                kvb += Hkv * len(vis) * 2 * D * eb
-            if kind == "paged":
-                meta += ((t + page_size - 1) // page_size) * 4
-        q = B * C * Hq * D * eb
-        ws = B * C * Hq * self.S * (D + 2) * 4
-        out = B * C * Hq * (D + 1) * 4
-        self.kv_bytes = kvb
-        self.split_bytes = kvb + q + ws + meta
-        self.call_bytes = self.split_bytes + ws + out
+        self.kv_bytes, self.split_bytes, self.call_bytes = algorithmic_bytes(
+            kind, B, Hq, Hkv, D, self.lens, self.S, eb=eb, mask=mask, hidden=hidden, C=C,
+            residual=residual, k_group=k_group, page_size=page_size)
 
     def make_all_args(self):
         ka = self.ka
