@@ -28,6 +28,7 @@
 namespace da {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Broadcast lane I of each 16-lane row to the whole row.
@@ -173,6 +174,13 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   for (int i = 0; i < G; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) u[i][e] = 0.f;
+  // Eight or more (virtual) heads: PV on the matrix cores, o[c] of lane (n, kg)
+  // accumulating heads 4kg .. 4kg+3 at channel 8n + c (the VALU form would
+  // need 8 FMAs per head, row and channel group: issue-bound at G = 8).
+  constexpr bool kMfmaPV = G >= 8;
+  f32x4_t o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // One tile of registers: the next tile's K rows are requested as soon as
   // the score instructions have read the current ones, its V rows once the
@@ -275,18 +283,65 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
 #pragma unroll
     for (int j = 0; j < 4; ++j) vcur[j] = t.v[j];
     if constexpr (kEarlyV) issue_v(ri, t.v);
-    if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
+    if constexpr (kMfmaPV) {
+      // O (heads x channels) += P (heads x the tile's 16 rows) V: A = P of
+      // head n, rows 4kg .. 4kg+3, as bf16 hi + lo (together exact to about
+      // 2^-17); B block c = channel 8n + c of rows 4kg .. 4kg+3, taken from
+      // the V registers (v_mfma_f32_16x16x16_bf16: lane (n, kg) holds k rows
+      // 4kg .. 4kg+3 of column n), so no value moves between lanes.
+      if (__any(alpha != 1.f)) {      // skipped while no head max moved
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w[4] = {vcur[j].x, vcur[j].y, vcur[j].z, vcur[j].w};
-      float vx[8];
+        for (int i = 0; i < 4; ++i) {
+          const float a = __shfl(alpha, 4 * kg + i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { vx[2 * e] = bf16_lo(w[e]); vx[2 * e + 1] = bf16_hi(w[e]); }
-      HeadLoop<G>::accumulate(u, pr[j], vx);
+          for (int c = 0; c < 8; ++c) o[c][i] *= a;
+        }
+      }
+      uint32_t ah[2], al[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const float x0 = pr[2 * q2], x1 = pr[2 * q2 + 1];
+        const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
+        const float r0 = x0 - bf16_lo(hw), r1 = x1 - bf16_hi(hw);
+        ah[q2] = hw;
+        al[q2] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r1) << 16);
+      }
+      const s16x4_t a_hi = __builtin_bit_cast(s16x4_t, make_uint2(ah[0], ah[1]));
+      const s16x4_t a_lo = __builtin_bit_cast(s16x4_t, make_uint2(al[0], al[1]));
+      auto word = [](const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low half of each word
+        const uint32_t b01 = __builtin_amdgcn_perm(word(vcur[1], c >> 1), word(vcur[0], c >> 1), sel);
+        const uint32_t b23 = __builtin_amdgcn_perm(word(vcur[3], c >> 1), word(vcur[2], c >> 1), sel);
+        const s16x4_t bv = __builtin_bit_cast(s16x4_t, make_uint2(b01, b23));
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, o[c], 0, 0, 0);
+      }
+    } else {
+      if (__any(alpha != 1.f)) HeadLoop<G>::rescale(u, alpha);   // skipped while no head max moved
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w[4] = {vcur[j].x, vcur[j].y, vcur[j].z, vcur[j].w};
+        float vx[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { vx[2 * e] = bf16_lo(w[e]); vx[2 * e + 1] = bf16_hi(w[e]); }
+        HeadLoop<G>::accumulate(u, pr[j], vx);
+      }
     }
     if constexpr (!kEarlyV) issue_v(ri, t.v);
   }
 
+  if constexpr (kMfmaPV) {
+    // o in the layout of u: lane (n, kg) keeps head i at channels 8n .. 8n+7
+    // where kg = i / 4 (the sums over kg below complete it), zero elsewhere
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? o[e][i & 3] : 0.f;
+  }
   // ---- wave state: all rows of a head share m, so l and u just add ---------
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
