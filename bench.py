@@ -128,6 +128,7 @@ class GpuWorkload:
             per_set = 2 * B * T * Hkv * D
         else:
             raise ValueError(kind)
+        self.prob = prob
         _, self.plan, self.ws_bytes, _ = ka.decode_attn_plan(ka.problem_from(prob))
         self.S = self.plan.num_splits
         self.nsets = max(1, -(-min_bytes // per_set)) if min_bytes else 1
@@ -182,6 +183,19 @@ class GpuWorkload:
         self.kv_bytes, self.split_bytes, self.call_bytes = algorithmic_bytes(
             kind, B, Hq, Hkv, D, self.lens, self.S, eb=eb, mask=mask, hidden=hidden, C=C,
             residual=residual, k_group=k_group, page_size=page_size)
+
+    def host_buffers(self):
+        """Input set 0 copied to host arrays in the oracle's storage formats
+        (bf16 as uint16 bit patterns, fp16 scales as float16)."""
+        import numpy as np
+        torch = self.torch
+        out = {"seq_lens": self.seq_lens.cpu().numpy()}
+        for k, t in self.sets[0].items():
+            if t.dtype == torch.bfloat16:
+                out[k] = t.view(torch.int16).cpu().numpy().view(np.uint16)
+            else:
+                out[k] = t.cpu().numpy()
+        return out
 
     def make_all_args(self):
         ka = self.ka
@@ -305,13 +319,56 @@ class GpuWorkload:
                 "algorithmic_bytes": self.call_bytes}
 
 
-def other_workload(torch, ka, name, steps=30, warmup=5):
-    """Timing report of one of the non-headline workloads."""
+def oracle_timing(w, us_gpu, runs, single_thread=False):
+    """The fp64 NumPy oracle on input set 0 of a timed workload: wall clock
+    per call (median of `runs`), its algorithmic GB/s and the GPU speedup;
+    with `single_thread` also the same with the BLAS pool limited to one
+    thread."""
+    import oracle
+    buf = w.host_buffers()
+
+    def med():
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            oracle.attend(w.prob, buf)
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+
+    t = med()
+    r = {"runs": runs, "s_per_call": round(t, 6), "GBs": round(w.call_bytes / t / 1e9, 3),
+         "gpu_speedup": round(t / (us_gpu * 1e-6), 1)}
+    if single_thread:
+        try:
+            import threadpoolctl
+            with threadpoolctl.threadpool_limits(1):
+                t1 = med()
+            r["single_thread_s_per_call"] = round(t1, 6)
+            r["single_thread_gpu_speedup"] = round(t1 / (us_gpu * 1e-6), 1)
+        except ImportError:
+            pass
+    return r
+
+
+# oracle runs per workload when the CPU leg is on: median of 3 for the small
+# and int8 workloads, one call for the two largest
+ORACLE_RUNS = {"tiny_fp32": 3, "int8_sink_window": 3, "long_context_128k": 1, "paged_ragged": 1}
+
+
+def _with_oracle(w, r, oracle_runs, single_thread=False):
+    if oracle_runs:
+        r["oracle"] = oracle_timing(w, r["us_per_call"], oracle_runs, single_thread)
+    return r
+
+
+def other_workload(torch, ka, name, steps=30, warmup=5, oracle_runs=0):
+    """Timing report of one of the non-headline workloads; with `oracle_runs`
+    the report also carries the oracle's time on input set 0 ("oracle")."""
     import synth
     if name == "long_context_128k":
         w = GpuWorkload(torch, ka, "contig", 1, 32, 8, 128, [131072], min_bytes=600 << 20, seed=1)
-        return w.report("long", "B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal, auto splits",
-                        steps, warmup)
+        return _with_oracle(w, w.report("long", "B=1 H_q=32 H_kv=8 d=128 T=131072 bf16 contiguous causal, "
+                                                "auto splits", steps, warmup), oracle_runs)
     if name == "paged_ragged":
         lens = synth.ragged_lengths(0, 32).tolist()
         w = GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, lens, seed=2)
@@ -326,12 +383,12 @@ def other_workload(torch, ka, name, steps=30, warmup=5):
         r["partition_items_per_head"] = w.part_items
         r["fixed_splits_us_per_call"] = round(fixed * 1000, 2)
         r["fixed_splits_largest_first_us_per_call"] = round(scheduled * 1000, 2)
-        return r
+        return _with_oracle(w, r, oracle_runs)
     if name == "int8_sink_window":
         w = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
                         mask=(4, 4096))
-        return w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual 128, "
-                                "4 sinks + window 4096", steps, warmup)
+        return _with_oracle(w, w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual "
+                                                "128, 4 sinks + window 4096", steps, warmup), oracle_runs)
     cfg2 = "B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16"
     if name == "few_query_c2":
         w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=6, C=2)
@@ -349,7 +406,8 @@ def other_workload(torch, ka, name, steps=30, warmup=5):
         return r
     if name == "tiny_fp32":
         w = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
-        return w.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4", steps, warmup)
+        return _with_oracle(w, w.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4", steps,
+                                        warmup), oracle_runs, single_thread=True)
     raise ValueError(name)
 
 
@@ -423,6 +481,20 @@ def hbm_probe(torch, nbytes=512 << 20):
     torch.cuda.synchronize()
     del bufs
     return read_gbs
+
+
+def host_info():
+    """Core counts and CPU model of the host the oracle ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
 
 
 def cpu_baseline(call_bytes, seconds: float = 10.0):
@@ -541,18 +613,28 @@ def main():
         with open(a.samples_out, "w") as f:
             json.dump({"per_call_us": samples}, f)
     call_bytes = w.call_bytes
+    cpu = not a.no_cpu_baseline
+    per_config = {}
+    if cpu:
+        per_config["llama3_8b_layer"] = oracle_timing(w, ms_call * 1000, 3, single_thread=True)
     del w
     if not a.no_long:
-        others = {name: other_workload(torch, ka, name)
+        others = {name: other_workload(torch, ka, name, oracle_runs=ORACLE_RUNS[name] if cpu else 0)
                   for name in ("long_context_128k", "paged_ragged", "int8_sink_window")}
         others["int8_append"] = append_timing(torch, ka)
-        others["tiny_fp32"] = other_workload(torch, ka, "tiny_fp32")
+        others["tiny_fp32"] = other_workload(torch, ka, "tiny_fp32",
+                                             oracle_runs=ORACLE_RUNS["tiny_fp32"] if cpu else 0)
         for name in ("few_query_c2", "hnd_layout", "flashmask"):
             others[name] = other_workload(torch, ka, name)
+        for name, r in others.items():
+            if "oracle" in r:
+                per_config[name] = r.pop("oracle")
         line["other_workloads"] = others
     torch.cuda.synchronize()
-    if not a.no_cpu_baseline:
+    if cpu:
         line["cpu_baseline"] = cpu_baseline(call_bytes)
+        line["cpu_baseline"]["per_config"] = per_config
+        line["cpu_baseline"]["host"] = host_info()
     print(json.dumps(line), flush=True)
 
 
