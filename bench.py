@@ -84,6 +84,13 @@ def algorithmic_bytes(kind, B, Hq, Hkv, D, lens, S, eb=2, mask=None, hidden=None
     return kvb, split, split + ws + out
 
 
+def sample_stats(samples):
+    """count, min, median, p95 and max of sorted per-call samples (µs)."""
+    n = len(samples)
+    return {"count": n, "min": round(samples[0], 2), "median": round(samples[n // 2], 2),
+            "p95": round(samples[int(n * 0.95)], 2), "max": round(samples[-1], 2)}
+
+
 class GpuWorkload:
     """Device buffers, a plan and the algorithmic byte count of one workload.
 
@@ -316,7 +323,8 @@ class GpuWorkload:
         return {"config": config, "num_splits": self.S, "us_per_call": round(ms * 1000, 2),
                 "GBs": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
                 "two_launch_us_per_call": round(ms2 * 1000, 2),
-                "algorithmic_bytes": self.call_bytes}
+                "algorithmic_bytes": self.call_bytes,
+                "samples_us": sample_stats(self.samples(self.fwd, 100, 10))}
 
 
 def oracle_timing(w, us_gpu, runs, single_thread=False):
@@ -598,9 +606,7 @@ def main():
                      "kernel": "split_kernel_mfma<4, contiguous, fused reduction>",
                      "us_per_launch": round(ms_call * 1000, 2),
                      "algorithmic_bytes_per_launch": w.call_bytes},
-        "samples_us": {"count": len(samples), "min": round(samples[0], 2),
-                       "median": round(samples[len(samples) // 2], 2),
-                       "p95": round(samples[int(len(samples) * 0.95)], 2), "max": round(samples[-1], 2)},
+        "samples_us": sample_stats(samples),
         "graph_replay_us_per_call": round(ms_graph * 1000, 2),
         "two_launch": {"us_per_call": round(ms_two * 1000, 2),
                        "split_kernel_us": round(ms_split * 1000, 2),
