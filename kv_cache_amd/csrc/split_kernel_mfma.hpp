@@ -1,5 +1,6 @@
-// Split kernel for bf16 K/V with D = 128: QK^T on the matrix cores, PV on
-// the vector ALUs.
+// Split kernel for bf16 K/V with D = 128: QK^T on the matrix cores; PV on
+// the vector ALUs for up to 4 (virtual) heads, on the matrix cores for 8 or
+// more.
 //
 // Same ownership and output as split_kernel (workgroup (b, h_kv, s), G query
 // heads, one exact (m, l, u) state per head, "M4.5 - Decode Attention Kernels,
@@ -21,6 +22,12 @@
 //    channels 8*(l%16) .. +7 of those V rows and accumulates u for the G heads.
 //    The weight p(row 4r+j, head i) sits in lane 16r+i of the same 16-lane
 //    DPP row, so it is fetched with row_newbcast:i.
+//  * PV with 8 or more heads.  v_mfma_f32_16x16x16_bf16 per 16-row tile:
+//    A = the weights (heads x rows of the tile) as bf16 hi + lo, two
+//    instructions per block, B = V (rows x channels).  Block c takes channel
+//    8n + c of the tile's rows, i.e. element c of the 8 channels lane n
+//    already holds, so the V registers feed the matrix cores without moving
+//    between lanes.
 #pragma once
 
 #include "split_common.hpp"
