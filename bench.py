@@ -397,18 +397,18 @@ def other_workload(torch, ka, name, steps=30, warmup=5, oracle_runs=0):
                         mask=(4, 4096))
         return _with_oracle(w, w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual "
                                                 "128, 4 sinks + window 4096", steps, warmup), oracle_runs)
-    cfg2 = "B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16"
+    layer = "B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16"
     if name == "few_query_c2":
         w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=6, C=2)
-        return w.report("fewq", cfg2 + " contiguous, C=2 query rows per request (bottom-right causal)",
+        return w.report("fewq", layer + " contiguous, C=2 query rows per request (bottom-right causal)",
                         steps, warmup)
     if name == "hnd_layout":
         w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=7, hnd=True)
-        return w.report("hnd", cfg2 + " contiguous HND [B, H_kv, T, d], causal", steps, warmup)
+        return w.report("hnd", layer + " contiguous HND [B, H_kv, T, d], causal", steps, warmup)
     if name == "flashmask":
         w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=8,
                         flashmask=True)
-        r = w.report("fm", cfg2 + " contiguous, FlashMask column intervals (seeded runs of closed "
+        r = w.report("fm", layer + " contiguous, FlashMask column intervals (seeded runs of closed "
                              "documents, visible blocks and scattered hidden keys)", steps, warmup)
         r["visible_kv_bytes"] = w.kv_bytes
         return r
