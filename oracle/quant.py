@@ -1,52 +1,78 @@
 """Symmetric int8 quantizer and the int8 K/V format (test infrastructure only).
 
-M8.6 §0x02A: for a finite non-empty row x, the scale is ``amax/qmax`` stored in
-the declared qparam dtype and re-read before encoding (the stored value is the
-effective qparam); an all-zero row gets scale 1 and zero codes; codes are
-``clip(round(x/s), -qmax, qmax)`` with ties to even; a stored scale that is
-non-finite or subnormal is rejected.  qmax = 2^(bits-1) - 1 (narrow range).
+The rule (M8.6 §0x02A): the elements that share one scale are quantized with
+scale = amax / qmax, where amax is their largest magnitude and qmax =
+2^(bits-1) - 1 (narrow range, so -128 never occurs); the scale is committed
+to its storage type (fp16 here) before any code is formed, and the committed
+value is the one used; codes are x / scale rounded to the nearest integer
+(ties to even) and clipped to [-qmax, qmax]; a group of zeros uses the exact
+sentinel scale 1 and zero codes; a committed scale that is infinite or below
+the smallest normal fp16 value is refused.
 
-The K/V format applies that rule along the axes of M8.6 §0x06/§0x06A: K per
-channel over a closed group of tokens, V per token over its channels; the
-newest tokens stay in bf16 (§0x06B residual).  Decoding is ``code * scale``
-for both (§0x03B, §0x03C).  This writer is independent of the input module's
-writer; the CPU tests require both to produce identical bytes.
+The K/V format applies the rule along the axes of M8.6 §0x06/§0x06A: K shares
+a scale per channel across a closed group of tokens, V per token across its
+channels; the newest tokens stay in bf16 (§0x06B residual).  Decoding is
+``code * scale`` for both (§0x03B, §0x03C).  This writer is independent of the
+input module's writer; the CPU tests require both to produce identical bytes.
 
 Two residual policies fix which tokens are quantized (n_q of them, the oldest):
 
 * ``"window"``: the newest min(T, R) tokens are bf16, n_q = T - min(T, R)
   (a snapshot of the cache; the last K group may be partial);
-* ``"groups"``: the streaming rule of M8.6 §0x06B -- every appended row enters
-  the bf16 residual, and while the residual holds more than R rows its oldest
-  G rows are closed: K quantized per channel over those G rows, V per row.
-  Closed groups never change afterwards.  ``kivi_append`` is that rule applied
-  to one token; ``quantized_count`` is its closed form, pinned against it.
+* ``"groups"``: the streaming rule of M8.6 §0x06B: a new row always enters
+  the bf16 residual, and whenever the residual has grown past R rows its
+  oldest G rows are closed (K per channel over them, V per row) and leave it,
+  so the closed count is the smallest multiple of G that leaves at most R
+  rows open.  ``kivi_append`` applies the rule to one token by comparing that
+  count before and after the token; closed groups are never touched again.
   Rows enter as bf16, so closed groups quantize bf16 values.
 """
 from __future__ import annotations
 
 import numpy as np
 
+FP16_MAX = 65504.0
+FP16_MIN_NORMAL = 2.0 ** -14
 
-def quantize_symmetric_rows(x, bits: int = 8, qparam_dtype=np.float16):
+
+def fp16_round(v):
+    """Nearest binary16 value of each non-negative fp64 ``v`` (ties to even),
+    returned as fp64: inf past the largest finite value, subnormal values on
+    the 2^-24 grid below 2^-14.  A binary16 number in [2^(e-1), 2^e) has 11
+    significant bits, so its spacing is 2^(e-11) (never below 2^-24)."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    spacing = np.ldexp(1.0, np.maximum(e - 11, -24))
+    r = np.rint(v / spacing) * spacing
+    return np.where(r > FP16_MAX, np.inf, r)
+
+
+def quantize_symmetric(x, axis, bits: int = 8):
+    """Quantize ``x`` with one fp16 scale per slice along ``axis`` (the
+    elements along ``axis`` share a scale).  Returns ``(codes int8 with x's
+    shape, scales float16 with x's shape minus axis)``.  Raises ValueError for
+    an empty or non-finite input or a refused committed scale."""
     x = np.asarray(x, dtype=np.float64)
-    if x.ndim != 2 or 0 in x.shape or not np.isfinite(x).all():
-        raise ValueError("expected finite, non-empty [M, K] rows")
+    if x.size == 0 or not np.isfinite(x).all():
+        raise ValueError("expected finite, non-empty values")
     if not (isinstance(bits, int) and 2 <= bits <= 8):
         raise ValueError("bits must be an int in [2, 8]")
-    dt = np.dtype(qparam_dtype)
-    qmax = 2 ** (bits - 1) - 1
-    amax = np.abs(x).max(axis=1)
-    zero = amax == 0
-    ideal = np.where(zero, 1.0, amax / qmax)
-    with np.errstate(over="ignore", under="ignore"):
-        stored = ideal.astype(dt)
-    eff = stored.astype(np.float64)
-    if not np.isfinite(eff).all() or np.any(eff < np.finfo(dt).tiny):
-        raise ValueError("non-representable or subnormal stored scale")
-    codes = np.clip(np.rint(x / eff[:, None]), -qmax, qmax)
-    codes[zero] = 0
-    return codes.astype(np.int8), stored
+    qmax = (1 << (bits - 1)) - 1
+    peak = np.abs(x).max(axis=axis, keepdims=True)
+    raw = np.divide(peak, qmax, out=np.ones_like(peak), where=peak > 0)
+    committed = fp16_round(raw)
+    if not np.all(np.isfinite(committed) & (committed >= FP16_MIN_NORMAL)):
+        raise ValueError("committed fp16 scale is infinite or not normal")
+    codes = np.clip(np.rint(x / committed), -qmax, qmax).astype(np.int8)
+    return codes, np.squeeze(committed, axis=axis).astype(np.float16)
+
+
+def quantize_symmetric_rows(x, bits: int = 8):
+    """``quantize_symmetric`` of an ``[M, K]`` array with one scale per row."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2:
+        raise ValueError("expected [M, K] rows")
+    return quantize_symmetric(x, axis=1, bits=bits)
 
 
 def quantized_count(T: int, policy: str, k_group: int, residual_len: int) -> int:
@@ -60,43 +86,49 @@ def quantized_count(T: int, policy: str, k_group: int, residual_len: int) -> int
     raise ValueError(policy)
 
 
+def _close_block(k_rows, v_rows):
+    """Quantize one block of consecutive tokens (``[n, H, D]`` fp64 each) in
+    the K/V format: K shares a scale per (head, channel) over the block's
+    tokens, V per (token, head) over the channels.  Returns (K codes [n, H,
+    D], K scales [H, D], V codes [n, H, D], V scales [n, H])."""
+    kc, ks = quantize_symmetric(k_rows, axis=0)
+    vc, vs = quantize_symmetric(v_rows, axis=2)
+    return kc, ks, vc, vs
+
+
+def _via_bf16(x):
+    """fp32 values after a round trip through bf16 (nearest, ties to even)."""
+    return (_bf16_rne(x).astype(np.uint32) << 16).view(np.float32)
+
+
 def write_int8_cache_oracle(k_f32, v_f32, seq_lens, k_group: int, residual_len: int,
                             policy: str = "window"):
     """Return, per request b, the meaningful parts of the stored format:
     ``{b: dict(n_q, k_codes[n_q,H,D], k_scale[groups,H,D], v_codes[n_q,H,D],
     v_scale[n_q,H], k_resid_bits[n_res,H,D], v_resid_bits[n_res,H,D])}``.
-    With ``policy="groups"`` the rows are rounded to bf16 before anything is
-    quantized (they were appended as bf16 rows)."""
-    k_f32 = np.asarray(k_f32, dtype=np.float32)
-    v_f32 = np.asarray(v_f32, dtype=np.float32)
+    The quantized tokens are closed in blocks of ``k_group`` (the last block of
+    the window policy may be shorter).  With ``policy="groups"`` the rows are
+    rounded to bf16 first (they were appended as bf16 rows)."""
+    k = np.asarray(k_f32, dtype=np.float32)
+    v = np.asarray(v_f32, dtype=np.float32)
     if policy == "groups":
-        k_f32 = (_bf16_rne(k_f32).astype(np.uint32) << 16).view(np.float32)
-        v_f32 = (_bf16_rne(v_f32).astype(np.uint32) << 16).view(np.float32)
-    B, _, H, D = k_f32.shape
+        k, v = _via_bf16(k), _via_bf16(v)
+    H, D = k.shape[2], k.shape[3]
     out = {}
-    for b in range(B):
-        T = int(seq_lens[b])
+    for b, T in enumerate(int(t) for t in seq_lens):
         n_q = quantized_count(T, policy, k_group, residual_len)
-        n_groups = -(-n_q // k_group)
-        kc = np.zeros((n_q, H, D), np.int8)
-        ks = np.zeros((n_groups, H, D), np.float16)
-        vc = np.zeros((n_q, H, D), np.int8)
-        vs = np.zeros((n_q, H), np.float16)
-        for h in range(H):
-            for j in range(n_groups):
-                lo, hi = j * k_group, min((j + 1) * k_group, n_q)
-                # channels become rows: one scale per channel of this group
-                codes, scale = quantize_symmetric_rows(k_f32[b, lo:hi, h, :].T)
-                kc[lo:hi, h, :] = codes.T
-                ks[j, h, :] = scale
-            if n_q:
-                codes, scale = quantize_symmetric_rows(v_f32[b, :n_q, h, :])
-                vc[:, h, :] = codes
-                vs[:, h] = scale
-        kr = _bf16_rne(k_f32[b, n_q:T])
-        vr = _bf16_rne(v_f32[b, n_q:T])
-        out[b] = dict(n_q=n_q, k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs,
-                      k_resid_bits=kr, v_resid_bits=vr)
+        blocks = [_close_block(k[b, lo:min(lo + k_group, n_q)].astype(np.float64),
+                               v[b, lo:min(lo + k_group, n_q)].astype(np.float64))
+                  for lo in range(0, n_q, k_group)]
+        part = [[blk[i] for blk in blocks] for i in range(4)]
+        out[b] = dict(
+            n_q=n_q,
+            k_codes=np.concatenate(part[0]) if blocks else np.zeros((0, H, D), np.int8),
+            k_scale=np.stack(part[1]) if blocks else np.zeros((0, H, D), np.float16),
+            v_codes=np.concatenate(part[2]) if blocks else np.zeros((0, H, D), np.int8),
+            v_scale=np.concatenate(part[3]) if blocks else np.zeros((0, H), np.float16),
+            k_resid_bits=_bf16_rne(k[b, n_q:T]),
+            v_resid_bits=_bf16_rne(v[b, n_q:T]))
     return out
 
 
@@ -121,45 +153,34 @@ def _bf16_rne(x):
 
 # ---------------------------------------------------------------------------
 # Streaming append (M8.6 §0x06B, the synchronized-tail teaching state).
+#
+# A request's state: closed K groups (codes [G, H, D], scales [H, D]), closed V
+# rows (codes [H, D], scales [H]) and the open bf16 rows (bit patterns [H, D]),
+# oldest first.  The number of closed rows is a function of the token count
+# alone (``quantized_count`` under the "groups" policy), so one append closes
+# exactly the rows that count says became closed.
 # ---------------------------------------------------------------------------
 def kivi_empty_state(H: int, D: int) -> dict:
-    """One request's cache state: closed K groups (codes [G, H, D], scales
-    [H, D]), closed V rows (codes [H, D], scales [H]) and the bf16 residual
-    rows (bit patterns [H, D]), oldest first."""
     return dict(H=H, D=D, k_groups=[], v_rows=[], k_resid=[], v_resid=[])
 
 
 def kivi_append(state: dict, k_row_bits, v_row_bits, k_group: int, residual_len: int) -> dict:
-    """Append one token (bf16 bit patterns ``[H, D]`` for K and V): the row
-    joins the residual; while the residual holds more than ``residual_len``
-    rows, its oldest ``k_group`` rows are closed -- K quantized per channel
-    over those rows (one scale per channel and head), V per row (one scale per
-    row and head) -- and leave the residual.  Raises ValueError (leaving the
-    state unchanged) if a scale is not representable."""
-    k_resid = state["k_resid"] + [np.asarray(k_row_bits, np.uint16)]
-    v_resid = state["v_resid"] + [np.asarray(v_row_bits, np.uint16)]
+    """Return the state after appending one token (bf16 bit patterns
+    ``[H, D]`` for K and V).  The open rows that the new token count closes
+    are quantized in blocks of ``k_group`` and move to the closed lists.  The
+    given state is never modified; a refused scale raises ValueError."""
+    open_k = list(state["k_resid"]) + [np.asarray(k_row_bits, np.uint16)]
+    open_v = list(state["v_resid"]) + [np.asarray(v_row_bits, np.uint16)]
+    n_closed = len(state["v_rows"])
+    newly = quantized_count(n_closed + len(open_k), "groups", k_group, residual_len) - n_closed
     k_groups, v_rows = list(state["k_groups"]), list(state["v_rows"])
-    H, D = state["H"], state["D"]
-    while len(k_resid) > residual_len:
-        k_old = _bits_to_f64(np.stack(k_resid[:k_group]))          # [G, H, D]
-        v_old = _bits_to_f64(np.stack(v_resid[:k_group]))
-        kc = np.empty(k_old.shape, np.int8)
-        ks = np.empty((H, D), np.float16)
-        vc = np.empty(v_old.shape, np.int8)
-        vs = np.empty((k_old.shape[0], H), np.float16)
-        for h in range(H):
-            codes, scale = quantize_symmetric_rows(k_old[:, h, :].T)     # channels as rows
-            kc[:, h, :] = codes.T
-            ks[h] = scale
-            codes, scale = quantize_symmetric_rows(v_old[:, h, :])       # tokens as rows
-            vc[:, h, :] = codes
-            vs[:, h] = scale
+    for lo in range(0, newly, k_group):
+        kc, ks, vc, vs = _close_block(_bits_to_f64(np.stack(open_k[lo:lo + k_group])),
+                                      _bits_to_f64(np.stack(open_v[lo:lo + k_group])))
         k_groups.append((kc, ks))
-        for i in range(k_old.shape[0]):
-            v_rows.append((vc[i], vs[i]))
-        del k_resid[:k_group]
-        del v_resid[:k_group]
-    return dict(H=H, D=D, k_groups=k_groups, v_rows=v_rows, k_resid=k_resid, v_resid=v_resid)
+        v_rows.extend(zip(vc, vs))
+    return dict(H=state["H"], D=state["D"], k_groups=k_groups, v_rows=v_rows,
+                k_resid=open_k[newly:], v_resid=open_v[newly:])
 
 
 def kivi_state_parts(state: dict) -> dict:
@@ -167,16 +188,17 @@ def kivi_state_parts(state: dict) -> dict:
     dict (n_q, codes, scales, residual bits)."""
     H, D = state["H"], state["D"]
     n_q = len(state["v_rows"])
-    kc = (np.concatenate([g[0] for g in state["k_groups"]]) if state["k_groups"]
-          else np.zeros((0, H, D), np.int8))
-    ks = (np.stack([g[1] for g in state["k_groups"]]) if state["k_groups"]
-          else np.zeros((0, H, D), np.float16))
-    vc = np.stack([r[0] for r in state["v_rows"]]) if n_q else np.zeros((0, H, D), np.int8)
-    vs = np.stack([r[1] for r in state["v_rows"]]) if n_q else np.zeros((0, H), np.float16)
-    kr = np.stack(state["k_resid"]) if state["k_resid"] else np.zeros((0, H, D), np.uint16)
-    vr = np.stack(state["v_resid"]) if state["v_resid"] else np.zeros((0, H, D), np.uint16)
-    return dict(n_q=n_q, k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs,
-                k_resid_bits=kr, v_resid_bits=vr)
+
+    def cat(items, shape, dtype, join):
+        return join(items) if items else np.zeros(shape, dtype)
+    return dict(
+        n_q=n_q,
+        k_codes=cat([c for c, _ in state["k_groups"]], (0, H, D), np.int8, np.concatenate),
+        k_scale=cat([s for _, s in state["k_groups"]], (0, H, D), np.float16, np.stack),
+        v_codes=cat([c for c, _ in state["v_rows"]], (0, H, D), np.int8, np.stack),
+        v_scale=cat([s for _, s in state["v_rows"]], (0, H), np.float16, np.stack),
+        k_resid_bits=cat(state["k_resid"], (0, H, D), np.uint16, np.stack),
+        v_resid_bits=cat(state["v_resid"], (0, H, D), np.uint16, np.stack))
 
 
 def kivi_state_from_parts(parts: dict, k_group: int) -> dict:

@@ -243,16 +243,24 @@ def make_paged(seed: int, B: int, H_q: int, H_kv: int, D: int, seq_lens,
 QMAX = 127
 
 
+# Ideal scales at or above the midpoint between the largest finite fp16 value
+# (65504) and the next step (65536) round to infinity; below the midpoint
+# between the largest subnormal (2^-14 - 2^-24) and the smallest normal
+# (2^-14) they round to a subnormal.  Both are refused.
+_F16_INF_FROM = 65520.0
+_F16_NORMAL_FROM = 2.0 ** -14 - 2.0 ** -25
+
+
 def _store_scale_f16(amax: np.ndarray) -> np.ndarray:
-    """Effective stored scale: amax/127 rounded to fp16; all-zero -> 1."""
-    zero = amax == 0
-    ideal = np.where(zero, 1.0, amax / QMAX)
-    with np.errstate(over="ignore", under="ignore"):
-        s = ideal.astype(np.float16)
-    eff = s.astype(np.float64)
-    if (not np.isfinite(eff).all()) or np.any(eff < np.finfo(np.float16).tiny):
+    """fp16 scale per element of amax (>= 0): amax/127 committed to fp16,
+    and 1 where amax is 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    ideal = np.ones_like(amax)
+    nz = amax != 0
+    ideal[nz] = amax[nz] / QMAX
+    if np.any(ideal >= _F16_INF_FROM) or np.any(ideal < _F16_NORMAL_FROM):
         raise ValueError("stored fp16 scale is non-finite or subnormal")
-    return s
+    return ideal.astype(np.float16)
 
 
 def _codes(x: np.ndarray, s_eff: np.ndarray) -> np.ndarray:

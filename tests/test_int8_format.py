@@ -44,6 +44,36 @@ def test_quantizer_rejects_bad_inputs_and_scales():
         quantize_symmetric_rows(np.zeros((0, 4)))
 
 
+def test_fp16_commit_matches_ieee_binary16():
+    """The oracle's own binary16 rounding equals NumPy's IEEE conversion on
+    random magnitudes across the whole range and on the edges: the largest
+    finite value, the overflow midpoint 65520 (ties to even: inf), the
+    smallest normal 2^-14 and the midpoint below it (ties to even: 2^-14)."""
+    from oracle.quant import fp16_round
+    g = synth.rng(11)
+    v = np.exp(g.uniform(np.log(1e-9), np.log(1e6), 20000))
+    edges = [65504.0, 65519.999, 65520.0, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+             2.0 ** -14 - 2.0 ** -24, 2.0 ** -24, 2.0 ** -25, 1.0, 1.0 + 2.0 ** -11, 0.0]
+    v = np.concatenate([v, np.array(edges)])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).astype(np.float64)
+    assert np.array_equal(fp16_round(v), ref)
+
+
+def test_quantizer_axis_equals_rows_of_the_moved_axis():
+    """One scale per slice along an axis is the row quantizer applied to the
+    array with that axis moved last."""
+    from oracle.quant import quantize_symmetric
+    g = synth.rng(12)
+    x = g.standard_normal((5, 3, 7)) * np.exp(g.standard_normal((5, 3, 1)))
+    for axis in range(3):
+        c, s = quantize_symmetric(x, axis=axis)
+        moved = np.moveaxis(x, axis, -1)
+        c2, s2 = quantize_symmetric_rows(moved.reshape(-1, moved.shape[-1]))
+        assert np.array_equal(np.moveaxis(c, axis, -1).reshape(c2.shape), c2)
+        assert np.array_equal(s.reshape(-1).view(np.uint16), s2.view(np.uint16))
+
+
 def test_ties_round_to_even():
     # scale 1 (amax 127): 2.5 -> 2, 3.5 -> 4, -2.5 -> -2
     codes, s = quantize_symmetric_rows(np.array([[127.0, 2.5, 3.5, -2.5, 0.5]]))
@@ -164,3 +194,24 @@ def test_int8_sink_window_visible_rows_count_cfg5_shape():
     n_q = 16384 - 128
     assert int((A >= n_q).sum()) == 128
     assert math.ceil(n_q / 128) == 127
+
+
+@pytest.mark.parametrize("amax,ok", [(1e9, False), (65519.0 * 127, True), (65520.0 * 127, False),
+                                     (1e-7, False), ((2.0 ** -14 - 2.0 ** -25) * 127, True),
+                                     ((2.0 ** -14 - 2.0 ** -24) * 127, False)])
+def test_both_writers_refuse_the_same_scales(amax, ok):
+    """The input module's writer and the oracle's writer accept and refuse the
+    same groups at the edges of the fp16 scale range (M8.6 §0x02A)."""
+    kf = np.zeros((1, 4, 1, 8), np.float32)
+    kf[0, 0, 0, 0] = amax
+    vf = np.ones((1, 4, 1, 8), np.float32)
+    def oracle_side():
+        return write_int8_cache_oracle(kf, vf, [4], 4, 0)
+    def input_side():
+        return synth.write_int8_cache(kf, vf, [4], 4, 0, 4, synth.rng(0))
+    for fn in (oracle_side, input_side):
+        if ok:
+            fn()
+        else:
+            with pytest.raises(ValueError):
+                fn()

@@ -31,6 +31,15 @@ def test_closure_counts_follow_the_pages_rule(case):
     G, R, T = case["group"], case["residual"], case["appends"]
     assert quantized_count(T, "groups", G, R) == case["closed_rows"]
     assert T - quantized_count(T, "groups", G, R) == case["residual_rows"]
+    # the page's rule stepped on counts alone: a row joins the residual, and
+    # while the residual holds more than R rows its oldest G leave it
+    closed = open_rows = 0
+    for _ in range(T):
+        open_rows += 1
+        while open_rows > R:
+            closed += G
+            open_rows -= G
+    assert (closed, open_rows) == (case["closed_rows"], case["residual_rows"])
     if T <= 400:
         # the same counts from the append model itself, one token at a time
         st = kivi_empty_state(1, 4)

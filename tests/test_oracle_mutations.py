@@ -153,17 +153,29 @@ def test_mutation_kivi_closes_at_residual_instead_of_above(monkeypatch):
 
 
 def test_mutation_kivi_append_v_scale_per_channel(monkeypatch):
-    orig = quant_mod.quantize_symmetric_rows
-    calls = {"n": 0}
+    orig = quant_mod.quantize_symmetric
 
-    def bad(x, *a, **k):
-        # every second call (the V call of each head) quantizes the transposed
-        # block: one scale per channel instead of per token
-        calls["n"] += 1
-        if calls["n"] % 2 == 0 and x.shape[0] != x.shape[1]:
-            c, s = orig(np.asarray(x).T, *a, **k)
-            return c.T, np.resize(s, x.shape[0]).astype(s.dtype)
-        return orig(x, *a, **k)
-    monkeypatch.setattr(quant_mod, "quantize_symmetric_rows", bad)
+    def bad(x, axis, *a, **k):
+        # V (one scale per token, over the last axis) quantized with one scale
+        # per channel over the tokens instead, the scales then spread over the
+        # per-token slots
+        if axis == 2:
+            c, s = orig(x, 0, *a, **k)
+            return c, np.resize(s, np.asarray(x).shape[:2]).astype(s.dtype)
+        return orig(x, axis, *a, **k)
+    monkeypatch.setattr(quant_mod, "quantize_symmetric", bad)
     from tests import test_kivi_append as tk
-    assert _fails([lambda: tk.test_sequential_appends_equal_the_static_writer(32, 128, 300)])
+    assert _fails([lambda: tk.test_sequential_appends_equal_the_static_writer(32, 128, 300),
+                   tk.test_input_writer_matches_oracle_writer_under_groups_policy,
+                   lambda: t8.test_writers_agree_byte_for_byte([300, 128, 5])])
+
+
+def test_mutation_fp16_scale_rounded_toward_zero(monkeypatch):
+    # committing the scale by truncation instead of rounding to nearest
+    def bad(v):
+        v = np.asarray(v, dtype=np.float64)
+        _, e = np.frexp(v)
+        spacing = np.ldexp(1.0, np.maximum(e - 11, -24))
+        return np.floor(v / spacing) * spacing
+    monkeypatch.setattr(quant_mod, "fp16_round", bad)
+    assert _fails([t8.test_fp16_commit_matches_ieee_binary16])
