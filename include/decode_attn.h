@@ -21,7 +21,8 @@
  *    arguments, is a DEVICE pointer; problem, plan, reasons and
  *    workspace_bytes pointers are HOST pointers.  The caller owns every
  *    buffer; the library allocates no device memory and keeps no state
- *    beyond a per-device cache of the architecture check.
+ *    beyond a per-device cache of the architecture check, except the one
+ *    workspace array per GPU of decode_attn_forward_static.
  *  - Calls return a da_status; nothing throws across the ABI and nothing is
  *    printed.  decode_attn_run and decode_attn_combine are asynchronous on the
  *    given HIP stream (hipStream_t passed as void*, NULL = default stream) and
@@ -327,6 +328,30 @@ da_status decode_attn_combine(const da_plan* plan, const void* workspace,
  * the in-kernel fold's limit, it launches run then combine. */
 da_status decode_attn_forward(const da_plan* plan, const da_args* args, float* out, float* lse,
                               void* stream);
+
+/* ---- allocation-free forward ------------------------------------------------ */
+
+/* Size of the library's own workspace array (one per GPU, see below). */
+#define DA_STATIC_WORKSPACE_BYTES (32u << 20)
+
+/* decode_attn_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  Instead of a caller-owned workspace it uses a device array of
+ * DA_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * from the first call there until the process ends; it calls no allocating
+ * routine.  The caller still owns q, K/V, metadata, out and lse; args->workspace
+ * must be NULL and args->workspace_bytes 0 (DA_ERR_INVALID otherwise).  Every
+ * call on one GPU shares that GPU's array and finds it as the previous call
+ * left it: the call clears what must start at zero (the arrival counters, by
+ * a fill kernel on `stream`), so consecutive calls are independent, but calls
+ * that overlap on one GPU (different streams, or different host threads,
+ * without ordering between them) race on the array and must not be issued.
+ * Errors: those of decode_attn_forward, and DA_ERR_WORKSPACE when the plan's
+ * workspace_bytes exceeds DA_STATIC_WORKSPACE_BYTES (checked before anything
+ * else is read).  Results are those of decode_attn_forward for the same plan
+ * and inputs, bit for bit. */
+da_status decode_attn_forward_static(const da_plan* plan, const da_args* args, float* out, float* lse,
+                                     void* stream);
 
 /* FlashMask block summaries ("M4.5 ...", section 0x06C): for each request b
  * and block J of 16 key columns [16J, min(16J+16, max_seq_len)), write

@@ -17,7 +17,8 @@ __all__ = [
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
     "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
     "decode_attn_schedule", "decode_attn_append", "decode_attn_flashmask_summarize", "AppendArgs", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
-    "decode_attn_workspace_init", "decode_attn_trace_indices",
+    "decode_attn_workspace_init", "decode_attn_trace_indices", "decode_attn_forward_static",
+    "STATIC_WORKSPACE_BYTES",
     "decode_attn_reason", "decode_attn_status_string", "reason_names",
 ]
 
@@ -31,6 +32,7 @@ PAGE_TABLES = {"dense": 0, "csr": 1}
 MASKS = {"causal": 0, "sink_window": 1, "flashmask": 2}
 RESIDUAL_POLICIES = {"window": 0, "groups": 1}
 NUM_REASONS = 13
+STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 class Problem(ctypes.Structure):
@@ -125,6 +127,9 @@ def lib() -> ctypes.CDLL:
         L.decode_attn_forward.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.decode_attn_forward.restype = ctypes.c_int32
+        L.decode_attn_forward_static.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_attn_forward_static.restype = ctypes.c_int32
         L.decode_attn_workspace_init.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p,
                                                  ctypes.c_uint64, ctypes.c_void_p]
         L.decode_attn_workspace_init.restype = ctypes.c_int32
@@ -270,6 +275,15 @@ def decode_attn_forward(plan: Plan, args: Args, out, lse=None, stream: int = 0,
                                    stream)
     if check and st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_forward")
+    return st
+
+
+def decode_attn_forward_static(plan: Plan, args: Args, out, lse=None, stream: int = 0,
+                               check: bool = True) -> int:
+    st = lib().decode_attn_forward_static(ctypes.byref(plan), ctypes.byref(args), _ptr(out),
+                                          _ptr(lse), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_forward_static")
     return st
 
 

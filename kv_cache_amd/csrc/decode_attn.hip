@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "combine_kernel.hpp"
 #include "append_kernel.hpp"
@@ -254,6 +255,34 @@ bool dispatch_trace_d(int d, const da::SplitParams& sp, unsigned grid, int64_t* 
   return false;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is this library's own device array.
+// Each GPU the library runs on holds one copy from the module's load until
+// the process ends; its device address differs per GPU and is looked up once
+// per device (with that device current) and kept.  The array's name denotes a
+// host-side stand-in in host code, so only the looked-up address is ever
+// passed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[DA_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's array (nullptr if it cannot be
+// resolved).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream) {
@@ -483,3 +512,31 @@ extern "C" da_status decode_attn_trace_indices(const da_plan* plan, const da_arg
   if (!ok) return DA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
+
+extern "C" da_status decode_attn_forward_static(const da_plan* plan, const da_args* args, float* out,
+                                                float* lse, void* stream) {
+  if (!plan || !args) return DA_ERR_INVALID;
+  if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
+  if (plan->workspace_bytes > (uint64_t)DA_STATIC_WORKSPACE_BYTES) return DA_ERR_WORKSPACE;
+  if (args->workspace || args->workspace_bytes) return DA_ERR_INVALID;
+  const da_status chk = check_args(plan, args);
+  if (chk != DA_OK) return chk;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return DA_ERR_INVALID;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  void* ws = scratch_for_current_device();
+  if (!ws) return DA_ERR_HIP;
+  da_args a = *args;
+  a.workspace = ws;
+  a.workspace_bytes = DA_STATIC_WORKSPACE_BYTES;
+  // The array keeps whatever the previous call on this GPU left in it: the
+  // arrival counters of the single-launch fold are cleared on every call, with
+  // a fill kernel on the caller's stream.
+  if (plan->num_splits <= kFusedMaxSplits && !args->partition) {
+    const da_status st_init = decode_attn_workspace_init(plan, ws, DA_STATIC_WORKSPACE_BYTES, stream);
+    if (st_init != DA_OK) return st_init;
+  }
+  return decode_attn_forward(plan, &a, out, lse, stream);
+}
+

@@ -182,6 +182,22 @@ def test_run_rejects_null_pointers_and_small_workspace_without_gpu():
     assert ka.decode_attn_workspace_init(pl, None, ws, check=False) == ka.DA_ERR_WORKSPACE
 
 
+def test_static_forward_rejects_before_any_launch_without_gpu():
+    """The allocation-free forward refuses, on the host and before touching
+    the device, a plan whose workspace exceeds the library's array and a call
+    that brings a workspace of its own."""
+    st, pl, ws, _ = plan(P(batch=64, num_splits=64))
+    assert st == ka.DA_OK and ws > ka.STATIC_WORKSPACE_BYTES
+    assert ka.decode_attn_forward_static(pl, ka.Args(), 16, check=False) == ka.DA_ERR_WORKSPACE
+    st, pl, ws, _ = plan(P())
+    assert ws <= ka.STATIC_WORKSPACE_BYTES
+    args = ka.make_args(16, 16, 16, 16, 256, ws)
+    assert ka.decode_attn_forward_static(pl, args, 16, check=False) == ka.DA_ERR_INVALID
+    assert ka.decode_attn_forward_static(pl, ka.Args(), 16, check=False) == ka.DA_ERR_INVALID
+    pl.chunk += 1
+    assert ka.decode_attn_forward_static(pl, ka.Args(), 16, check=False) == ka.DA_ERR_PLAN_MISMATCH
+
+
 def test_reason_and_status_text():
     for i in range(ka.NUM_REASONS):
         assert ka.decode_attn_reason(i)
