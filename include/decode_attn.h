@@ -368,19 +368,40 @@ da_status decode_attn_flashmask_summarize(const da_plan* plan, const int32_t* in
 da_status decode_attn_workspace_init(const da_plan* plan, void* workspace,
                                      uint64_t workspace_bytes, void* stream);
 
-/* Debug entry point, never used on the timed path: walks exactly the rows the
- * split kernel loads, through the same device address and mask code, and
- * writes for workgroup (b, h_kv, s) and its k-th row (k < chunk):
- *   offsets  [B, H_kv, S, chunk] int64: element offset of the row's first
- *            element in the buffer it is read from (k/v, or k_resid/v_resid
- *            when positions >= n_q(b) for DA_KV_I8);
- *   positions[B, H_kv, S, chunk] int32: logical key position t.
- * Entries with no row are left untouched (callers pre-fill them with -1).
- * The walk follows the plan's fixed splits; a balanced partition reads the
- * same rows (the same visible ordinals through the same address code), cut
- * at other boundaries, so da_args.partition is ignored here. */
-da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args,
-                                    int64_t* offsets, int32_t* positions, void* stream);
+/* Index trace ("M4.5 ...", sections 0x04F and 0x04H: a kernel must read
+ * exactly the visible rows, each once, at the addresses the translation
+ * gives, and never a page tail or a table slot past the request).  Debug
+ * only, never on the timed path.  Each split kernel has a trace instance:
+ * the same code, which in addition records every K and V row load at the
+ * point where it is issued, with the address that load used.  Slots are per
+ * (b, h_kv, visible ordinal o), o < plan.max_visible; ordinal o of request b
+ * is its o-th visible key in position order (FlashMask: o = position).
+ * Arrays of B * H_kv * plan.max_visible entries, all device pointers: */
+typedef struct da_trace {
+  int64_t* k_offset;        /* element offset of the K row's first element in the buffer it was read
+                               from: k (int8: the codes) or, for DA_KV_I8 positions >= n_q(b), k_resid */
+  int64_t* v_offset;        /* the same for the V row (v or v_resid)                                  */
+  int32_t* position;        /* logical key position t of the row                                      */
+  int32_t* count;           /* caller zeroes; +1 per K row load, +(1 << 16) per V row load            */
+  int64_t* k_scale_offset;  /* DA_KV_I8 codes: element offset of the k_scale row (its channel 0) the
+                               row's dequantization used; else may be NULL                           */
+  int64_t* v_scale_offset;  /* DA_KV_I8 codes: element offset into v_scale; else may be NULL         */
+} da_trace;
+
+/* Runs the trace instance of the kernels the timed calls launch: with out ==
+ * NULL those of decode_attn_run (states into args->workspace), with out given
+ * those of decode_attn_forward (the single launch with its fold for S <= 16
+ * without a partition -- workspace counters zero on entry, as for
+ * decode_attn_forward -- else run then combine), writing out/lse as they do.
+ * A balanced partition (args->partition) runs the partition instance.  Only
+ * rows a workgroup consumes are recorded (loads issued past a split's end
+ * repeat a visible row and are weighted 0); under FlashMask the rows of
+ * PARTIAL tiles are loaded and recorded whether or not they are hidden, SKIP
+ * tiles never.  Entries never written keep their prior values (callers fill
+ * them with -1).  Errors: those of decode_attn_run / decode_attn_forward, and
+ * DA_ERR_INVALID for a NULL trace array (the scale arrays only for DA_KV_I8). */
+da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args, const da_trace* trace,
+                                    float* out, float* lse, void* stream);
 
 /* ---- streaming append for DA_KV_I8 with DA_RESIDUAL_GROUPS ------------------ */
 

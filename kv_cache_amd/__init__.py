@@ -15,7 +15,7 @@ import os
 __all__ = [
     "DA_OK", "DA_ERR_INVALID", "DA_ERR_UNSUPPORTED", "DA_ERR_WORKSPACE",
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
-    "Args", "lib", "library_path", "problem_from", "decode_attn_plan",
+    "Args", "Trace", "lib", "library_path", "problem_from", "decode_attn_plan",
     "decode_attn_schedule", "decode_attn_append", "decode_attn_flashmask_summarize", "AppendArgs", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
     "decode_attn_workspace_init", "decode_attn_trace_indices", "decode_attn_forward_static",
     "STATIC_WORKSPACE_BYTES",
@@ -60,6 +60,12 @@ class Args(ctypes.Structure):
                          ("mask_intervals", ctypes.c_void_p), ("mask_summary", ctypes.c_void_p),
                          ("partition", ctypes.c_void_p), ("partition_items", ctypes.c_int32),
                          ("reserved0", ctypes.c_int32)]
+
+
+class Trace(ctypes.Structure):
+    """da_trace: device arrays of B * H_kv * plan.max_visible entries."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_offset", "v_offset", "position", "count", "k_scale_offset", "v_scale_offset")]
 
 
 class AppendArgs(ctypes.Structure):
@@ -134,7 +140,8 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_uint64, ctypes.c_void_p]
         L.decode_attn_workspace_init.restype = ctypes.c_int32
         L.decode_attn_trace_indices.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
-                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+                                                ctypes.POINTER(Trace), ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p]
         L.decode_attn_trace_indices.restype = ctypes.c_int32
         L.decode_attn_reason.argtypes = [ctypes.c_int]
         L.decode_attn_reason.restype = ctypes.c_char_p
@@ -307,10 +314,17 @@ def decode_attn_append(plan: Plan, k_new, v_new, k, v, k_scale, v_scale, k_resid
     return st
 
 
-def decode_attn_trace_indices(plan: Plan, args: Args, offsets, positions, stream: int = 0,
-                              check: bool = True) -> int:
-    st = lib().decode_attn_trace_indices(ctypes.byref(plan), ctypes.byref(args), _ptr(offsets),
-                                         _ptr(positions), stream)
+def decode_attn_trace_indices(plan: Plan, args: Args, k_offset, v_offset, position, count,
+                              k_scale_offset=None, v_scale_offset=None, out=None, lse=None,
+                              stream: int = 0, check: bool = True) -> int:
+    """Trace instance of the timed kernels (decode_attn_run's, or with ``out``
+    decode_attn_forward's); the arrays are device tensors of B*H_kv*max_visible
+    entries (int64 offsets, int32 position and count)."""
+    tr = Trace(k_offset=_ptr(k_offset), v_offset=_ptr(v_offset), position=_ptr(position),
+               count=_ptr(count), k_scale_offset=_ptr(k_scale_offset),
+               v_scale_offset=_ptr(v_scale_offset))
+    st = lib().decode_attn_trace_indices(ctypes.byref(plan), ctypes.byref(args), ctypes.byref(tr),
+                                         _ptr(out), _ptr(lse), stream)
     if check and st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_trace_indices")
     return st

@@ -1,4 +1,5 @@
 // C-ABI launch entry points: decode_attn_run, decode_attn_combine,
+// decode_attn_forward and its allocation-free form, decode_attn_append,
 // decode_attn_trace_indices.  Argument and plan checks happen on the host
 // before any launch; the launches are asynchronous on the caller's stream.
 #include <hip/hip_runtime.h>
@@ -38,13 +39,6 @@ template <> struct Unroll<DA_KV_I8> { static constexpr int value = DA_UNROLL_I8;
 
 template <int FMT, int D>
 constexpr bool use_mfma() { return DA_MFMA_QK && (FMT == DA_KV_BF16 || FMT == DA_KV_I8) && D == 128; }
-
-// Rows per wave tile of the kernel that serves (FMT, D); the trace walk uses
-// the same value.
-template <int FMT, int D>
-constexpr int tile_rows() {
-  return use_mfma<FMT, D>() ? 16 : (64 / (D / da::KvTraits<FMT>::EPL)) * Unroll<FMT>::value;
-}
 
 int log2_exact(int x) {
   if (x <= 0 || (x & (x - 1))) return -1;
@@ -158,59 +152,54 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   return sp;
 }
 
-template <int FMT, int D, int G, bool PAGED, bool FUSED, bool FM>
+// TRACE selects the index-trace instance of the same kernel (debug entry
+// point only).
+template <int FMT, int D, int G, bool PAGED, bool FUSED, bool FM, bool TRACE>
 void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8) {
     static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
-    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED>), dim3(grid), dim3(kWaves * 64), 0,
+    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED, TRACE>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
   } else if constexpr (use_mfma<FMT, D>()) {
     if constexpr (!FUSED && !FM) {
       if (sp.partition) {
-        hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, false, false, true>), dim3(grid),
+        hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, false, false, true, TRACE>), dim3(grid),
                            dim3(kWaves * 64), 0, st, sp);
         return;
       }
     }
-    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED, FM>), dim3(grid),
+    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED, FM, false, TRACE>), dim3(grid),
                        dim3(kWaves * 64), 0, st, sp);
   } else {
     static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
-    hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value, FUSED>),
+    hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value, FUSED, TRACE>),
                        dim3(grid), dim3(kWaves * 64), 0, st, sp);
   }
 }
 
-template <int FMT, int D, bool PAGED>
-void launch_trace(const da::SplitParams& sp, unsigned grid, int64_t* off, int32_t* pos,
-                  hipStream_t st) {
-  hipLaunchKernelGGL((da::trace_kernel<FMT == DA_KV_I8, D, PAGED, kWaves, tile_rows<FMT, D>()>),
-                     dim3(grid), dim3(kWaves * 64), 0, st, sp, off, pos);
-}
-
-template <int FMT, int D, bool PAGED, bool FUSED, bool FM>
+template <int FMT, int D, bool PAGED, bool FUSED, bool FM, bool TRACE>
 bool dispatch_g(int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   switch (g) {
-    case 1: launch_split<FMT, D, 1, PAGED, FUSED, FM>(sp, grid, st); return true;
-    case 2: launch_split<FMT, D, 2, PAGED, FUSED, FM>(sp, grid, st); return true;
-    case 4: launch_split<FMT, D, 4, PAGED, FUSED, FM>(sp, grid, st); return true;
-    case 8: launch_split<FMT, D, 8, PAGED, FUSED, FM>(sp, grid, st); return true;
+    case 1: launch_split<FMT, D, 1, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
+    case 2: launch_split<FMT, D, 2, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
+    case 4: launch_split<FMT, D, 4, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
+    case 8: launch_split<FMT, D, 8, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
     default: return false;
   }
 }
 
-template <int FMT, bool PAGED, bool FUSED, bool FM = false>
+template <int FMT, bool PAGED, bool FUSED, bool FM, bool TRACE>
 bool dispatch_d(int d, int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   if constexpr (FM) {
-    return d == 128 && dispatch_g<FMT, 128, PAGED, FUSED, true>(g, sp, grid, st);
+    return d == 128 && dispatch_g<FMT, 128, PAGED, FUSED, true, TRACE>(g, sp, grid, st);
   } else {
-    if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED, false>(g, sp, grid, st);
-    if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED, false>(g, sp, grid, st);
+    if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED, false, TRACE>(g, sp, grid, st);
+    if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED, false, TRACE>(g, sp, grid, st);
     return false;
   }
 }
 
-template <bool FUSED>
+template <bool FUSED, bool TRACE = false>
 bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   // A workgroup serves the C query rows of each of its H_q/H_kv heads: C*g
   // "virtual heads" sharing one K/V head.
@@ -219,17 +208,17 @@ bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned gri
   switch (p.kv_format) {
     case DA_KV_F32:
       if (p.mask_kind == DA_MASK_FLASHMASK) return false;
-      return paged ? dispatch_d<DA_KV_F32, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
-                   : dispatch_d<DA_KV_F32, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
+      return paged ? dispatch_d<DA_KV_F32, true, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st)
+                   : dispatch_d<DA_KV_F32, false, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st);
     case DA_KV_BF16:
       if (p.mask_kind == DA_MASK_FLASHMASK)
-        return paged ? dispatch_d<DA_KV_BF16, true, FUSED, true>(p.head_dim_qk, g, sp, grid, st)
-                     : dispatch_d<DA_KV_BF16, false, FUSED, true>(p.head_dim_qk, g, sp, grid, st);
-      return paged ? dispatch_d<DA_KV_BF16, true, FUSED>(p.head_dim_qk, g, sp, grid, st)
-                   : dispatch_d<DA_KV_BF16, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
+        return paged ? dispatch_d<DA_KV_BF16, true, FUSED, true, TRACE>(p.head_dim_qk, g, sp, grid, st)
+                     : dispatch_d<DA_KV_BF16, false, FUSED, true, TRACE>(p.head_dim_qk, g, sp, grid, st);
+      return paged ? dispatch_d<DA_KV_BF16, true, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st)
+                   : dispatch_d<DA_KV_BF16, false, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st);
     case DA_KV_I8:
       if (p.mask_kind == DA_MASK_FLASHMASK) return false;
-      return !paged && dispatch_d<DA_KV_I8, false, FUSED>(p.head_dim_qk, g, sp, grid, st);
+      return !paged && dispatch_d<DA_KV_I8, false, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st);
     default:
       return false;
   }
@@ -245,14 +234,6 @@ static_assert(kFusedMaxSplits <= da::kFoldMaxSplits, "fold handles at most 64 st
 __global__ void zero_words(uint32_t* w, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) w[i] = 0u;
-}
-
-template <int FMT, bool PAGED>
-bool dispatch_trace_d(int d, const da::SplitParams& sp, unsigned grid, int64_t* off, int32_t* pos,
-                      hipStream_t st) {
-  if (d == 64) { launch_trace<FMT, 64, PAGED>(sp, grid, off, pos, st); return true; }
-  if (d == 128) { launch_trace<FMT, 128, PAGED>(sp, grid, off, pos, st); return true; }
-  return false;
 }
 
 // ---------------------------------------------------------------------------
@@ -480,37 +461,44 @@ extern "C" da_status decode_attn_combine(const da_plan* plan, const void* worksp
 }
 
 extern "C" da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args,
-                                               int64_t* offsets, int32_t* positions,
+                                               const da_trace* trace, float* out, float* lse,
                                                void* stream) {
   const da_status chk = check_args(plan, args);
   if (chk != DA_OK) return chk;
   const da_problem& p = plan->problem;
   if (p.batch == 0) return DA_OK;
-  if (!offsets || !positions) return DA_ERR_INVALID;
+  if (!trace || !trace->k_offset || !trace->v_offset || !trace->position || !trace->count)
+    return DA_ERR_INVALID;
+  if (p.kv_format == DA_KV_I8 && (!trace->k_scale_offset || !trace->v_scale_offset)) return DA_ERR_INVALID;
+  if (out && (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return DA_ERR_INVALID;
+  if (!args->workspace || args->workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(args->workspace) & 15u) != 0) return DA_ERR_WORKSPACE;
   if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
-  const da::SplitParams sp = make_params(plan, args);
-  const unsigned grid = (unsigned)((uint64_t)p.batch * p.num_kv_heads * plan->num_splits);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  da::SplitParams sp = make_params(plan, args);
+  sp.tr.k_off = trace->k_offset;
+  sp.tr.v_off = trace->v_offset;
+  sp.tr.pos = trace->position;
+  sp.tr.count = trace->count;
+  sp.tr.ks_off = trace->k_scale_offset;
+  sp.tr.vs_off = trace->v_scale_offset;
+  sp.tr.stride = plan->max_visible;
+  const uint64_t grid64 = args->partition
+                              ? (uint64_t)std::max(args->partition_items, 1) * p.num_kv_heads
+                              : (uint64_t)p.batch * p.num_kv_heads * plan->num_splits;
+  if (grid64 > 0x7fffffffull) return DA_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  bool ok = false;
-  const bool paged = p.layout == DA_LAYOUT_PAGED_NHD || p.layout == DA_LAYOUT_PAGED_HND;
-  switch (p.kv_format) {
-    case DA_KV_F32:
-      ok = paged ? dispatch_trace_d<DA_KV_F32, true>(p.head_dim_qk, sp, grid, offsets, positions, st)
-                 : dispatch_trace_d<DA_KV_F32, false>(p.head_dim_qk, sp, grid, offsets, positions, st);
-      break;
-    case DA_KV_BF16:
-      ok = paged ? dispatch_trace_d<DA_KV_BF16, true>(p.head_dim_qk, sp, grid, offsets, positions, st)
-                 : dispatch_trace_d<DA_KV_BF16, false>(p.head_dim_qk, sp, grid, offsets, positions, st);
-      break;
-    case DA_KV_I8:
-      ok = !paged && dispatch_trace_d<DA_KV_I8, false>(p.head_dim_qk, sp, grid, offsets, positions, st);
-      break;
-    default:
-      ok = false;
+  // The launches of decode_attn_forward (out given) or of decode_attn_run,
+  // each with the trace instance of the same kernel.
+  if (out && plan->num_splits <= kFusedMaxSplits && !args->partition) {
+    sp.out = out;
+    sp.lse = lse;
+    if (!dispatch_split<true, true>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
   }
-  if (!ok) return DA_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+  if (!dispatch_split<false, true>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
+  if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
+  return out ? decode_attn_combine(plan, args->workspace, args->workspace_bytes, out, lse, stream) : DA_OK;
 }
 
 extern "C" da_status decode_attn_forward_static(const da_plan* plan, const da_args* args, float* out,

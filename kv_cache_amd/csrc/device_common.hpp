@@ -1,5 +1,6 @@
-// Device-side address and mask code shared by the split kernel and the index
-// trace kernel (one source of truth for which K/V rows a workgroup reads).
+// Device-side address and mask code shared by the split kernels and their
+// index-trace instances (one source of truth for which K/V rows a workgroup
+// reads).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,7 +10,19 @@
 
 namespace da {
 
-// Kernel arguments of the split and trace kernels (passed by value).
+// Index trace outputs of a split kernel's trace instance, one slot per
+// (b, h_kv, visible ordinal), `stride` ordinals per (b, h_kv).
+struct TraceOut {
+  int64_t* k_off;    // element offset of the K row's first element
+  int64_t* v_off;    // element offset of the V row's first element
+  int32_t* pos;      // logical key position
+  int32_t* count;    // +1 per K row load, +(1 << 16) per V row load
+  int64_t* ks_off;   // int8 codes: element offset of the K scale row used (else unused)
+  int64_t* vs_off;   // int8 codes: element offset of the V scale used (else unused)
+  int32_t stride;
+};
+
+// Kernel arguments of the split kernels (passed by value).
 struct SplitParams {
   const void* q;
   const void* k;
@@ -58,8 +71,9 @@ struct SplitParams {
   int32_t num_page_entries;  // CSR table entries
   uint32_t row_stride;       // elements between consecutive row indices
   uint32_t page_rows;        // paged: row indices per page (P for NHD, H_kv*P for HND)
-  int32_t n_mask_blocks;     // FlashMask: ceil(max_seq_len / 16)         // paged: page ids are clamped to [0, num_pages)
+  int32_t n_mask_blocks;     // FlashMask: ceil(max_seq_len / 16)
   float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
+  TraceOut tr;               // trace instances only
 };
 
 // ---------------------------------------------------------------------------
@@ -318,6 +332,34 @@ __device__ __forceinline__ int64_t kv_row_offset(const SplitParams& p, const Row
 // Quantization: Activations and KV Cache", section 0x06B).
 __device__ __forceinline__ int64_t resid_row_offset(const SplitParams& p, int b, int tr, int h, int D) {
   return (((int64_t)b * p.residual_len + tr) * p.num_kv_heads + h) * (int64_t)D;
+}
+
+// ---------------------------------------------------------------------------
+// Index trace ("M4.5 ...", sections 0x04F and 0x04H: the rows a kernel reads
+// must be exactly the visible rows, each once, at their translated
+// addresses).  A split kernel's trace instance calls these where it issues
+// each K and V row load, with the offset that load used; the product
+// instances compile them out.  Slots outside the trace buffer are dropped.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t trace_slot(const SplitParams& p, int b, int h, int o) {
+  return o >= 0 && o < p.tr.stride ? ((int64_t)b * p.num_kv_heads + h) * p.tr.stride + o : -1;
+}
+__device__ __forceinline__ void trace_k(const SplitParams& p, int b, int h, int o, int t, int64_t k_off,
+                                        int64_t ks_off = -1) {
+  const int64_t i = trace_slot(p, b, h, o);
+  if (i < 0) return;
+  p.tr.k_off[i] = k_off;
+  p.tr.pos[i] = t;
+  if (ks_off >= 0) p.tr.ks_off[i] = ks_off;
+  atomicAdd(p.tr.count + i, 1);
+}
+__device__ __forceinline__ void trace_v(const SplitParams& p, int b, int h, int o, int64_t v_off,
+                                        int64_t vs_off = -1) {
+  const int64_t i = trace_slot(p, b, h, o);
+  if (i < 0) return;
+  p.tr.v_off[i] = v_off;
+  if (vs_off >= 0) p.tr.vs_off[i] = vs_off;
+  atomicAdd(p.tr.count + i, 1 << 16);
 }
 
 // ---------------------------------------------------------------------------

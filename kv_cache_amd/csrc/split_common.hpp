@@ -1,6 +1,6 @@
-// Pieces shared by the split kernels and the index trace kernel: streaming
-// loads, the empty-split identity, the cross-wave merge of partial states and
-// their store into the workspace, and the trace walk.
+// Pieces shared by the split kernels: streaming loads, the empty-split
+// identity, the cross-wave merge of partial states and their store into the
+// workspace, and the single-launch fold.
 #pragma once
 
 #include "device_common.hpp"
@@ -225,55 +225,6 @@ __device__ __forceinline__ void finish_split(const SplitParams& p, int b, int h)
     const int wave = threadIdx.x >> 6;
     for (int i = wave; i < G; i += NWAVES) fold_row<D>(p, out_row(p, b, h, i));
     if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Index trace: the workgroup decomposition, tile walk (TW rows per wave tile,
-// tiles dealt round-robin to NWAVES waves) and address code of the split
-// kernels, recording each row instead of consuming it.
-template <bool I8, int D, bool PAGED, int NWAVES, int TW>
-__global__ __launch_bounds__(NWAVES * 64) void trace_kernel(SplitParams p, int64_t* offsets,
-                                                            int32_t* positions) {
-  int b, h, s;
-  decode_workgroup(p, &b, &h, &s);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int T = request_len(p, b);
-  const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
-  const int n_q = I8 ? quantized_len(p, T) : T;
-  int begin, end;
-  if (I8)
-    split_range_weighted(vis.n_vis, residual_ordinal(vis, n_q), s, p.chunk, &begin, &end);
-  else
-    split_range(vis.n_vis, s, p.chunk, &begin, &end);
-  const int64_t base = (((int64_t)b * p.num_kv_heads + h) * p.num_splits + s) * p.chunk;
-  const RowAddr ra = row_addr<PAGED && !I8>(p, b, h, D);
-  const bool fm = !I8 && p.mask_kind == DA_MASK_FLASHMASK;
-  const int q_row = vis.n_vis - 1;
-  for (int tile = begin + wave * TW; tile < end; tile += NWAVES * TW) {
-    // FlashMask: the tile walk of the split kernel (16-key tiles; SKIP tiles
-    // are not read, PARTIAL tiles drop their hidden rows)
-    int cls = kTileFull;
-    if (fm) {
-      cls = fm_tile_class(p, b, q_row, tile);
-      if (cls == kTileSkip) continue;
-    }
-    for (int j = lane; j < TW; j += 64) {
-      const int o = tile + j;
-      if (fm && cls == kTilePartial && o < end &&
-          fm_hidden(p.mask_iv[(int64_t)b * p.max_seq_len + o], q_row))
-        continue;
-      if (o < end) {
-        const int t = vis_pos(vis, o);
-        int64_t off;
-        if (I8)
-          off = t < n_q ? kv_row_offset<false>(p, ra, t) : resid_row_offset(p, b, t - n_q, h, D);
-        else
-          off = kv_row_offset<PAGED>(p, ra, t);
-        offsets[base + (o - begin)] = off;
-        positions[base + (o - begin)] = t;
-      }
-    }
   }
 }
 

@@ -42,15 +42,21 @@ struct RawRow {
   bool valid;
 };
 
-template <int FMT, int D, bool PAGED>
-__device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra, int b, int h, int t,
-                                         int n_q, int col0, RawRow& raw) {
+// Loads this lane's slice of the K and V rows of visible ordinal o (position
+// t).  TRACE: lane `rec` also records the row loads (trace instances only).
+template <int FMT, int D, bool PAGED, bool TRACE>
+__device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra, int b, int h, int o, int t,
+                                         int n_q, int col0, bool rec, RawRow& raw) {
   constexpr int EB = FMT == DA_KV_F32 ? 4 : FMT == DA_KV_BF16 ? 2 : 1;
   if (FMT != DA_KV_I8) {
     const int64_t off = kv_row_offset<PAGED>(p, ra, t) + col0;
     raw.k = stream_load(reinterpret_cast<const uint4*>(static_cast<const char*>(p.k) + off * EB));
     raw.v = stream_load(reinterpret_cast<const uint4*>(static_cast<const char*>(p.v) + off * EB));
     raw.region = 0;
+    if (TRACE && rec) {
+      trace_k(p, b, h, o, t, off - col0);
+      trace_v(p, b, h, o, off - col0);
+    }
   } else {
     if (t < n_q) {
       const int64_t off = kv_row_offset<false>(p, ra, t) + col0;
@@ -61,14 +67,23 @@ __device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra
       const int grp = t >> p.k_group_shift;
       const int64_t soff = (((int64_t)b * ((p.kv_capacity + (1 << p.k_group_shift) - 1) >> p.k_group_shift) + grp)
                                 * p.num_kv_heads + h) * (int64_t)D + col0;
+      const int64_t vsoff = ((int64_t)b * p.kv_capacity + t) * p.num_kv_heads + h;
       raw.ks = *reinterpret_cast<const uint4*>(p.k_scale + soff);
-      raw.vs = p.v_scale[((int64_t)b * p.kv_capacity + t) * p.num_kv_heads + h];
+      raw.vs = p.v_scale[vsoff];
       raw.region = 0;
+      if (TRACE && rec) {
+        trace_k(p, b, h, o, t, off - col0, soff - col0);
+        trace_v(p, b, h, o, off - col0, vsoff);
+      }
     } else {
       const int64_t off = resid_row_offset(p, b, t - n_q, h, D) + col0;
       raw.k = stream_load(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k_resid) + off));
       raw.v = stream_load(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v_resid) + off));
       raw.region = 1;
+      if (TRACE && rec) {
+        trace_k(p, b, h, o, t, off - col0);
+        trace_v(p, b, h, o, off - col0);
+      }
     }
   }
 }
@@ -115,7 +130,9 @@ __device__ __forceinline__ float decode_v(const RawRow& raw, float* x) {
   }
 }
 
-template <int FMT, int D, int G, bool PAGED, int NWAVES, int U, bool FUSED>
+// TRACE: the index-trace instance, which also records each row load where it
+// is issued; otherwise identical.
+template <int FMT, int D, int G, bool PAGED, int NWAVES, int U, bool FUSED, bool TRACE = false>
 __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   constexpr int EPL = KvTraits<FMT>::EPL;
   constexpr int LPR = D / EPL;           // lanes per row
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
       rr[j].ks = make_uint4(0u, 0u, 0u, 0u);
       rr[j].vs = 0u;
       rr[j].region = 0;
-      if (rr[j].valid) load_row<FMT, D, PAGED>(p, ra, b, h, vis_pos(vis, o), n_q, col0, rr[j]);
+      if (rr[j].valid) load_row<FMT, D, PAGED, TRACE>(p, ra, b, h, o, vis_pos(vis, o), n_q, col0, cg == 0, rr[j]);
     }
   };
 

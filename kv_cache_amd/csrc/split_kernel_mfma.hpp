@@ -81,7 +81,9 @@ template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 
 // (the host's default item count uses the same figure).
 constexpr int kPartitionWgPerCu = 3;
 
-template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM, bool PART = false>
+// TRACE: the index-trace instance, which also records each row load where it
+// is issued (trace_k / trace_v); otherwise identical.
+template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM, bool PART = false, bool TRACE = false>
 __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
@@ -115,19 +117,6 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   const uint16_t* kb = static_cast<const uint16_t*>(p.k) + hb + 8 * kg;
   const uint16_t* vb = static_cast<const uint16_t*>(p.v) + hb + 8 * n;
   const uint32_t row_stride = p.row_stride;
-  auto issue_k = [&](uint32_t ri, uint4 (&k)[4]) {
-    const uint16_t* row = kb + (uint64_t)ri * row_stride;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
-  };
-  auto issue_v = [&](uint32_t ri, uint4 (&v)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t rj = (uint32_t)__shfl((int)ri, 4 * kg + j);
-      v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)rj * row_stride));
-    }
-  };
-
   // Speculative first tile: with a plain contiguous cache and the causal mask
   // the first tile's rows (ordinals s*chunk + wave*16 + r, positions equal to
   // ordinals) do not depend on the request length, so they are requested
@@ -142,7 +131,9 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     if (spec) {
       const int t0 = s * p.chunk + wave * TW;
       const int cap = p.kv_capacity;
-      issue_k((uint32_t)min(t0 + n, cap - 1), t.k);
+      const uint16_t* row = kb + (uint64_t)(uint32_t)min(t0 + n, cap - 1) * row_stride;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t.k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t rj = (uint32_t)min(t0 + 4 * kg + j, cap - 1);
@@ -160,6 +151,32 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     begin = min(pbeg, vis.n_vis);
     end = min(pend, vis.n_vis);
   }
+
+  // K rows of tile tl: lane (n, kg) loads row tl + n, whose row index is ri.
+  // The trace instance records the rows inside the split (loads past its end
+  // repeat a visible row and are weighted 0).
+  auto issue_k = [&](int tl, uint32_t ri, uint4 (&k)[4]) {
+    const uint16_t* row = kb + (uint64_t)ri * row_stride;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
+    if constexpr (TRACE) {
+      if (kg == 0 && tl + n >= begin && tl + n < end)
+        trace_k(p, b, h, tl + n, vis_pos(vis, tl + n), hb + (int64_t)((uint64_t)ri * row_stride));
+    }
+  };
+  // V rows of tile tl: lane (n, kg) loads rows tl + 4kg + j, whose row
+  // indices lanes 4kg + j hold.
+  auto issue_v = [&](int tl, uint32_t ri, uint4 (&v)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t rj = (uint32_t)__shfl((int)ri, 4 * kg + j);
+      v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)rj * row_stride));
+      if constexpr (TRACE) {
+        const int o = tl + 4 * kg + j;
+        if (n == 0 && o >= begin && o < end) trace_v(p, b, h, o, hb + (int64_t)((uint64_t)rj * row_stride));
+      }
+    }
+  };
   // Score column n is virtual head n, with its own visible end (C > 1 rows).
   // An empty split (begin == end) runs no tile and stores the empty state
   // (m = -inf, l = 0, u = 0) through the same merge as any other.
@@ -237,14 +254,28 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   uint32_t ri = 0, ri_ahead = 0;
   if (tile < end) {
     if (spec) {
+      // the first tile (tile == t0) was requested above; trace its rows now
+      // that the split end is known, with the row indices those loads used
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
         if (tile + 4 * kg + j >= end) t.v[j] = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (TRACE) {
+          // tile == s*chunk + wave*16 here, the first row of the loads above
+          const int o = tile + 4 * kg + j;
+          const uint32_t rj = (uint32_t)min(o, p.kv_capacity - 1);
+          if (n == 0 && o < end) trace_v(p, b, h, o, hb + (int64_t)((uint64_t)rj * row_stride));
+        }
+      }
+      if constexpr (TRACE) {
+        const uint32_t rk = (uint32_t)min(tile + n, p.kv_capacity - 1);
+        if (kg == 0 && tile + n < end)
+          trace_k(p, b, h, tile + n, vis_pos(vis, tile + n), hb + (int64_t)((uint64_t)rk * row_stride));
+      }
     } else {
       ri = row_index(tile);
-      issue_k(ri, t.k);
+      issue_k(tile, ri, t.k);
       issue_iv(tile);
-      issue_v(ri, t.v);
+      issue_v(tile, ri, t.v);
     }
     ri_ahead = row_index(step(tile));
   }
@@ -262,7 +293,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
                                                     __builtin_bit_cast(bf16x8_t, qop[c]), acc, 0, 0, 0);
     ri = ri_ahead;
     ri_ahead = row_index(step(next_tile));
-    issue_k(ri, t.k);
+    issue_k(next_tile, ri, t.k);
     issue_iv(next_tile);
     float sc[4];
 #pragma unroll
@@ -289,7 +320,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     uint4 vcur[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vcur[j] = t.v[j];
-    if constexpr (kEarlyV) issue_v(ri, t.v);
+    if constexpr (kEarlyV) issue_v(next_tile, ri, t.v);
     if constexpr (kMfmaPV) {
       // O (heads x channels) += P (heads x the tile's 16 rows) V: A = P of
       // head n, rows 4kg .. 4kg+3, as bf16 hi + lo (together exact to about
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
         HeadLoop<G>::accumulate(u, pr[j], vx);
       }
     }
-    if constexpr (!kEarlyV) issue_v(ri, t.v);
+    if constexpr (!kEarlyV) issue_v(next_tile, ri, t.v);
   }
 
   if constexpr (kMfmaPV) {

@@ -87,7 +87,9 @@ __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) { return (ui
 constexpr int kI8ScaleSlots = 24;
 
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
-template <int G, int NWAVES, bool FUSED>
+// TRACE: the index-trace instance, which also records each row load (codes,
+// scales, residual rows) where it is issued; otherwise identical.
+template <int G, int NWAVES, bool FUSED, bool TRACE = false>
 __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma_i8(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
@@ -141,8 +143,10 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const uint16_t* kr = static_cast<const uint16_t*>(p.k_resid) + res_base + 8 * kg;
   const uint16_t* vr = static_cast<const uint16_t*>(p.v_resid) + res_base + 8 * n;
   const int n_groups = (p.kv_capacity + (1 << p.k_group_shift) - 1) >> p.k_group_shift;
-  const uint16_t* ks = p.k_scale + ((int64_t)b * n_groups * p.num_kv_heads + h) * D;
-  const uint16_t* vs = p.v_scale + (int64_t)b * p.kv_capacity * p.num_kv_heads + h;
+  const int64_t ks_base = ((int64_t)b * n_groups * p.num_kv_heads + h) * D;
+  const int64_t vs_base = (int64_t)b * p.kv_capacity * p.num_kv_heads + h;
+  const uint16_t* ks = p.k_scale + ks_base;
+  const uint16_t* vs = p.v_scale + vs_base;
 
   float m_run = -INFINITY;   // running max of head n (base 2)
   float l_run = 0.f;         // partial denominator over rows 4kg .. 4kg+3 of every tile
@@ -226,10 +230,19 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
         const uint32_t last = (uint32_t)(pe - 1 - pb);
         // row of ordinal o within the phase, clamped to its last row
         auto rel = [&](int o) { return min((uint32_t)(o - pb), last); };
+        auto slot = [&](int tile) { return (int)((t_pb + rel(tile + n)) >> sh) - g0; };
         auto issue_k = [&](int tile, uint4 (&k)[2]) {
           const uint32_t off = mul_u24(rel(tile + n), row_stride) + 16 * kg;
           k[0] = stream_load(reinterpret_cast<const uint4*>(kp + off));
           k[1] = stream_load(reinterpret_cast<const uint4*>(kp + off + 64));
+          if constexpr (TRACE) {
+            // the row's codes, and the scale row its dequantization reads
+            // (staged from k_scale row g0 + slot)
+            if (kg == 0 && tile + n < pe)
+              trace_k(p, b, h, tile + n, t_pb + (int)rel(tile + n),
+                      code_base + (int64_t)t_pb * row_stride + (off - 16 * kg),
+                      ks_base + (int64_t)(g0 + slot(tile)) * row_stride);
+          }
         };
         auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
 #pragma unroll
@@ -237,9 +250,13 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
             const uint32_t r = rel(tile + 4 * kg + j);
             v[j] = stream_load(reinterpret_cast<const uint2*>(vp + (mul_u24(r, row_stride) + 8 * (uint32_t)n)));
             sv[j] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
+            if constexpr (TRACE) {
+              if (n == 0 && tile + 4 * kg + j < pe)
+                trace_v(p, b, h, tile + 4 * kg + j, code_base + (int64_t)t_pb * row_stride + mul_u24(r, row_stride),
+                        vs_base + (int64_t)t_pb * p.num_kv_heads + mul_u24(r, vs_stride) / 2);
+            }
           }
         };
-        auto slot = [&](int tile) { return (int)((t_pb + rel(tile + n)) >> sh) - g0; };
         auto scores = [&](int tile, const uint4 (&k)[2]) {
           const int sl = slot(tile);
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -361,11 +378,22 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
       const uint16_t* row = kr + (uint64_t)rrow(tile + n) * row_stride;
 #pragma unroll
       for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
+      if constexpr (TRACE) {
+        if (kg == 0 && tile + n < end)
+          trace_k(p, b, h, tile + n, vis_pos(vis, tile + n),
+                  res_base + (int64_t)((uint64_t)rrow(tile + n) * row_stride));
+      }
     };
     auto issue_v = [&](int tile, uint4 (&v)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
         v[j] = stream_load(reinterpret_cast<const uint4*>(vr + (uint64_t)rrow(tile + 4 * kg + j) * row_stride));
+        if constexpr (TRACE) {
+          if (n == 0 && tile + 4 * kg + j < end)
+            trace_v(p, b, h, tile + 4 * kg + j,
+                    res_base + (int64_t)((uint64_t)rrow(tile + 4 * kg + j) * row_stride));
+        }
+      }
     };
     MfmaTile t;
     int tile = mid + wave * TW;

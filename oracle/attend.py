@@ -41,11 +41,14 @@ def _scale(prob) -> float:
     return float(prob.softmax_scale) if prob.softmax_scale else 1.0 / math.sqrt(prob.head_dim)
 
 
-def gather_rows(prob, buf, b: int, h_kv: int, positions):
+def gather_rows(prob, buf, b: int, h_kv: int, positions, scale_offsets=None):
     """K and V rows (fp64, ``[n, D]``) of the given logical positions of
     request b and K/V head h_kv, plus the element offset of each row inside the
     buffer it was read from and the region tag (0: main cache or int8 codes,
-    1: bf16 residual)."""
+    1: bf16 residual).  For the int8 format, ``scale_offsets`` (a dict, if
+    given) receives the element offsets of the scales each row was decoded
+    with: ``"k"`` the first element of its K scale row in ``k_scale``, ``"v"``
+    its V scale in ``v_scale`` (-1 for residual rows)."""
     D = prob.head_dim
     H = prob.num_kv_heads
     positions = np.asarray(positions, dtype=np.int64)
@@ -96,16 +99,24 @@ def gather_rows(prob, buf, b: int, h_kv: int, positions):
         quant = positions < n_q
         region[~quant] = 1
         tq = positions[quant]
+        ks_off = np.full(n, -1, dtype=np.int64)
+        vs_off = np.full(n, -1, dtype=np.int64)
         if tq.size:
             o = nhd_offset(b, tq, h_kv, 0, prob.kv_capacity, H, D)
             offs[quant] = o
             idx = o[:, None] + lane[None, :]
             kc = buf["k"].reshape(-1)[idx].astype(np.float64)
             vc = buf["v"].reshape(-1)[idx].astype(np.float64)
-            ks = decode_f16(buf["k_scale"][b, tq // G, h_kv, :])          # [n, D]
-            vs = decode_f16(buf["v_scale"][b, tq, h_kv])                   # [n]
+            # K scale row of the token's group, V scale of the token (M8.6 §0x06A)
+            n_groups = -(-prob.kv_capacity // G)
+            ks_off[quant] = ((b * n_groups + tq // G) * H + h_kv) * D
+            vs_off[quant] = (b * prob.kv_capacity + tq) * H + h_kv
+            ks = decode_f16(buf["k_scale"].reshape(-1)[ks_off[quant][:, None] + lane[None, :]])  # [n, D]
+            vs = decode_f16(buf["v_scale"].reshape(-1)[vs_off[quant]])                            # [n]
             K[quant] = kc * ks
             V[quant] = vc * vs[:, None]
+        if scale_offsets is not None:
+            scale_offsets["k"], scale_offsets["v"] = ks_off, vs_off
         tr = positions[~quant]
         if tr.size:
             o = nhd_offset(b, tr - n_q, h_kv, 0, R, H, D)
@@ -121,7 +132,9 @@ def attend(prob, buf, heads=None, with_trace: bool = False):
     """Exact decode attention.
 
     Returns ``(O [B, H_q, D], LSE [B, H_q])`` in fp64, and with ``with_trace``
-    also ``{(b, h_kv): (positions, offsets, regions)}`` of every row read.
+    also ``{(b, h_kv): dict(positions, offsets, regions, k_scale_offsets,
+    v_scale_offsets)}`` of every row read (in position order; the scale
+    offsets are those of ``gather_rows``, -1 outside the int8 codes).
     ``heads`` optionally restricts the work to a list of ``(b, h_q)`` rows
     (the other rows are returned as NaN).
 
@@ -162,11 +175,17 @@ def attend(prob, buf, heads=None, with_trace: bool = False):
                         O[b, qi, h * g + i] = 0.0
                         LSE[b, qi, h * g + i] = -math.inf
                     if with_trace and last:
-                        trace[(b, h)] = (A, np.zeros(0, np.int64), np.zeros(0, np.int8))
+                        none = np.zeros(0, np.int64)
+                        trace[(b, h)] = dict(positions=A, offsets=none, regions=np.zeros(0, np.int8),
+                                             k_scale_offsets=none, v_scale_offsets=none)
                     continue
-                K, V, offs, region = gather_rows(prob, buf, b, h, A)
+                so = {}
+                K, V, offs, region = gather_rows(prob, buf, b, h, A, scale_offsets=so)
                 if with_trace and last:
-                    trace[(b, h)] = (A, offs, region)
+                    minus = np.full(A.size, -1, np.int64)
+                    trace[(b, h)] = dict(positions=A, offsets=offs, regions=region,
+                                         k_scale_offsets=so.get("k", minus),
+                                         v_scale_offsets=so.get("v", minus))
                 for i in rows:
                     s = (K @ q[b, qi, h * g + i]) * scale
                     m = np.max(s)

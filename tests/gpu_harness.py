@@ -159,20 +159,90 @@ def split_workspace(ws_bytes: np.ndarray, plan):
     return u, m, l
 
 
-def trace(w, num_splits=None, dw=None):
+def trace(w, num_splits=None, dw=None, forward=False, partition=None):
+    """Runs the trace instance of the timed kernels: decode_attn_run's (then
+    the combine), or with ``forward`` decode_attn_forward's; ``partition`` as
+    in run().  Returns (trace dict of [B, H_kv, max_visible] arrays, plan, O,
+    LSE)."""
     t = torch()
     dw = dw or DeviceWorkload(w)
     plan, ws_bytes = plan_for(w, num_splits)
+    if partition is not None:
+        dw.partition(plan, partition)
+    elif getattr(dw, "part", None) is not None:
+        dw.part, dw.part_items = None, 0
     ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+    ws.fill_(0xFF)
+    s = t.cuda.current_stream().cuda_stream
+    if forward:
+        ka.decode_attn_workspace_init(plan, ws, ws_bytes, s)
     p = w.problem
-    n = p.batch * p.num_kv_heads * plan.num_splits * plan.chunk
-    offs = t.full((max(n, 1),), -1, dtype=t.int64, device="cuda")
-    pos = t.full((max(n, 1),), -1, dtype=t.int32, device="cuda")
-    ka.decode_attn_trace_indices(plan, dw.args(ws, ws_bytes), offs, pos,
-                                 t.cuda.current_stream().cuda_stream)
+    n = max(p.batch * p.num_kv_heads * plan.max_visible, 1)
+    arr = dict(k_offset=t.full((n,), -1, dtype=t.int64, device="cuda"),
+               v_offset=t.full((n,), -1, dtype=t.int64, device="cuda"),
+               position=t.full((n,), -1, dtype=t.int32, device="cuda"),
+               count=t.zeros((n,), dtype=t.int32, device="cuda"),
+               k_scale_offset=t.full((n,), -1, dtype=t.int64, device="cuda"),
+               v_scale_offset=t.full((n,), -1, dtype=t.int64, device="cuda"))
+    out, lse = _outputs(w)
+    if forward:
+        ka.decode_attn_trace_indices(plan, dw.args(ws, ws_bytes), **arr, out=out, lse=lse, stream=s)
+    else:
+        ka.decode_attn_trace_indices(plan, dw.args(ws, ws_bytes), **arr, stream=s)
+        ka.decode_attn_combine(plan, ws, ws_bytes, out, lse, s)
     t.cuda.synchronize()
-    shape = (p.batch, p.num_kv_heads, plan.num_splits, plan.chunk)
-    return offs.cpu().numpy()[:n].reshape(shape), pos.cpu().numpy()[:n].reshape(shape), plan
+    shape = (p.batch, p.num_kv_heads, plan.max_visible)
+    m = p.batch * p.num_kv_heads * plan.max_visible
+    res = {k: v.cpu().numpy()[:m].reshape(shape) for k, v in arr.items()}
+    return res, plan, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+ONCE = 1 + (1 << 16)     # one K row load and one V row load
+
+
+def check_trace(w, tr, fm_partial=None, ref=None):
+    """The rows the timed kernel loaded are exactly the oracle's visible rows,
+    each once as K and once as V, at the oracle's offsets (element offsets in
+    the buffer each row comes from; int8: also the K scale row and the V
+    scale), in the slot of their visible ordinal.  FlashMask (slots are
+    positions): hidden rows may be loaded only inside tiles the classifier
+    calls PARTIAL; ``fm_partial(b, pos) -> bool`` says which.  ``ref``: the
+    oracle's trace, if already computed."""
+    if ref is None:
+        _, _, ref = oracle_attend_trace(w)
+    i8 = w.problem.kv_format == "i8"
+    for (b, h), r in ref.items():
+        pos = r["positions"]
+        cnt = tr["count"][b, h]
+        slots = pos if fm_partial is not None else np.arange(pos.size)
+        assert np.all(cnt[slots] == ONCE), (b, h, "a visible row not loaded exactly once")
+        other = np.ones(cnt.size, bool)
+        other[slots] = False
+        if fm_partial is None:
+            assert not cnt[other].any(), (b, h, "a row outside the visible set was loaded")
+        else:
+            extra = np.nonzero(other & (cnt != 0))[0]
+            assert np.all(cnt[extra] == ONCE)
+            assert all(fm_partial(b, int(x)) for x in extra), (b, h, "hidden row outside PARTIAL tiles")
+        assert np.array_equal(tr["position"][b, h][slots], pos), (b, h)
+        assert np.array_equal(tr["k_offset"][b, h][slots], r["offsets"]), (b, h)
+        assert np.array_equal(tr["v_offset"][b, h][slots], r["offsets"]), (b, h)
+        if i8:
+            assert np.array_equal(tr["k_scale_offset"][b, h][slots], r["k_scale_offsets"]), (b, h)
+            assert np.array_equal(tr["v_scale_offset"][b, h][slots], r["v_scale_offsets"]), (b, h)
+    return sum(r["positions"].size for r in ref.values())
+
+
+def oracle_attend_trace(w):
+    import oracle
+    return oracle.attend(w.problem, w.buffers, with_trace=True)
+
+
+def errors(O, L, Or, Lr):
+    """(max|O - O_ref|, max|LSE - LSE_ref| over rows with a finite reference)."""
+    fin = np.isfinite(Lr)
+    lerr = float(np.max(np.abs(L[fin] - Lr[fin]))) if fin.any() else 0.0
+    return max_abs(O, Or), lerr
 
 
 def max_abs(a, b):

@@ -1,7 +1,8 @@
 """GPU parity for the FlashMask mask program (M4.5 §0x06A-§0x06D): library
 block summaries equal the oracle's, attention equals the oracle over the
-visible columns of the decode row, and the traced rows (SKIP tiles unread,
-hidden rows of PARTIAL tiles dropped) equal the oracle's visible set."""
+visible columns of the decode row, and the rows the timed kernel loads (its
+trace instance) are the oracle's visible set plus, at most, hidden rows of
+PARTIAL tiles: SKIP tiles are never read."""
 import numpy as np
 import pytest
 
@@ -62,6 +63,7 @@ def test_flashmask_trace_contiguous():
     w = _masked(synth.make_contiguous(63, len(lens), 8, 2, 128, lens, kv_capacity=2000), 3)
     dw = _ready(w, 3)
     _trace_rows_fm(w, dw, 3)
+    _trace_rows_fm(w, dw, 3, forward=True)
 
 
 def test_flashmask_everything_hidden():
@@ -77,13 +79,16 @@ def test_flashmask_everything_hidden():
     assert np.all(O == 0) and not np.signbit(O).any() and np.all(np.isneginf(L))
 
 
-def _trace_rows_fm(w, dw, S):
-    offs, pos, plan = H.trace(w, num_splits=S, dw=dw)
-    _, _, tr = oracle.attend(w.problem, w.buffers, with_trace=True)
-    for (b, h), (p_ref, o_ref, _) in tr.items():
-        got_p = pos[b, h].reshape(-1)
-        got_o = offs[b, h].reshape(-1)
-        sel = got_p >= 0
-        order = np.argsort(got_p[sel], kind="stable")
-        assert np.array_equal(got_p[sel][order], p_ref), (b, h)
-        assert np.array_equal(got_o[sel][order], o_ref), (b, h)
+def _trace_rows_fm(w, dw, S, forward=False):
+    """The timed kernel's trace instance loads every visible column once and
+    hidden columns only inside PARTIAL tiles (never a SKIP tile)."""
+    summ = [fm.block_summary(w.buffers["mask_intervals"][b], 16) for b in range(w.problem.batch)]
+    lens = w.buffers["seq_lens"]
+
+    def partial(b, pos):
+        q = int(lens[b]) - 1
+        return pos < lens[b] and fm.classify_tile(q, q + 1, summ[b][pos // 16]) == "PARTIAL"
+    tr, plan, O, L = H.trace(w, num_splits=S, dw=dw, forward=forward)
+    H.check_trace(w, tr, fm_partial=partial)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    H.check_rows(O, L, Or, Lr, 2e-3)

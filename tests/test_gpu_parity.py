@@ -170,17 +170,6 @@ def test_paged_other_page_sizes(P):
     H.check_rows(O, L, Or, Lr, TOL["bf16"])
 
 
-def test_cfg3_full_sampled_rows():
-    w = synth.config(3, 0)
-    O, L, plan = H.run(w)
-    g = synth.rng(77)
-    rows = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 24), g.integers(0, 32, 24))]
-    rows += [(int(np.argmax(w.buffers["seq_lens"])), 0), (int(np.argmin(w.buffers["seq_lens"])), 31)]
-    Or, Lr = oracle.attend(w.problem, w.buffers, heads=rows)
-    H.check_rows(O, L, Or, Lr, TOL["bf16"], rows=rows)
-    assert np.all(np.isfinite(O))      # poisoned tails and spare pages never reached
-
-
 # ---------------------------------------------------------------- masks
 MASK_CASES = [
     # (lens, n_sink, window): window >= T, sinks overlapping the window, S > T
@@ -260,55 +249,42 @@ def test_int8_scale_table_edges():
             H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_cfg5_full(seed):
-    w = synth.config(5, seed)
-    O, L, plan = H.run(w)
-    Or, Lr = oracle.attend(w.problem, w.buffers)
-    err = H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
-    H.announce(f"cfg5 seed {seed}: max|dO| = {err:.3e}, S = {plan.num_splits}")
-
-
 # ---------------------------------------------------------------- exact indices
-def _trace_rows(w, S):
-    offs, pos, plan = H.trace(w, num_splits=S)
-    _, _, tr = oracle.attend(w.problem, w.buffers, with_trace=True)
-    for (b, h), (p_ref, o_ref, _) in tr.items():
-        got_p = pos[b, h].reshape(-1)
-        got_o = offs[b, h].reshape(-1)
-        sel = got_p >= 0
-        gp, go = got_p[sel], got_o[sel]
-        order = np.argsort(gp, kind="stable")
-        assert np.array_equal(gp[order], p_ref), (b, h)          # no missing / extra / duplicate
-        assert np.array_equal(go[order], o_ref), (b, h)
-        assert np.all(got_o[~sel] == -1)
+def _trace_rows(w, S, forward=False, partition=None):
+    """The trace instance of the kernel the timed call runs loads exactly the
+    oracle's rows, and computes the same output as the product instance."""
+    tr, plan, O, L = H.trace(w, num_splits=S, forward=forward, partition=partition)
+    n = H.check_trace(w, tr)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    tol = 1e-5 if w.problem.kv_format == "f32" else 2e-3
+    if w.problem.kv_format == "i8":
+        H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+    else:
+        H.check_rows(O, L, Or, Lr, tol)
+    return n
 
 
-def test_trace_indices_contiguous_and_mask():
+@pytest.mark.parametrize("forward", [False, True])
+def test_trace_indices_contiguous_and_mask(forward):
     _trace_rows(synth.make_contiguous(12, 3, 8, 4, 128, [500, 0, 77], mask_kind="sink_window",
-                                      n_sink=3, window=64, kv_capacity=500), 5)
-    _trace_rows(synth.make_contiguous(13, 2, 4, 4, 64, [33, 257], dtype="f32", kv_capacity=260), 3)
+                                      n_sink=3, window=64, kv_capacity=500), 5, forward)
+    _trace_rows(synth.make_contiguous(13, 2, 4, 4, 64, [33, 257], dtype="f32", kv_capacity=260), 3,
+                forward)
+    # causal contiguous NHD: the speculative first tile, including a capacity-bound one
+    _trace_rows(synth.make_contiguous(16, 3, 8, 2, 128, [1000, 1, 777], kv_capacity=1000), 4, forward)
 
 
 def test_trace_indices_paged_cfg3_shape():
     lens = [1, 16, 17, 4099, 0, 250]
-    _trace_rows(synth.make_paged(14, len(lens), 32, 8, 128, lens, page_size=16,
-                                 max_pages_per_seq=260), 8)
+    w = synth.make_paged(14, len(lens), 32, 8, 128, lens, page_size=16, max_pages_per_seq=260)
+    _trace_rows(w, 8)
+    _trace_rows(w, 8, forward=True)
+    _trace_rows(w, 8, partition=0)
 
 
-def test_trace_indices_int8():
+@pytest.mark.parametrize("forward", [False, True])
+def test_trace_indices_int8(forward):
     _trace_rows(synth.make_int8(15, 2, 16, 4, 128, [1000, 60], mask_kind="sink_window", n_sink=4,
-                                window=300, kv_capacity=1000), 4)
-
-
-def test_trace_indices_cfg5_full_sampled():
-    w = synth.config(5, 0)
-    offs, pos, plan = H.trace(w)
-    _, _, tr = oracle.attend(w.problem, w.buffers, heads=[(0, 0), (7, 13), (15, 31)], with_trace=True)
-    for (b, h), (p_ref, o_ref, _) in tr.items():
-        gp, go = pos[b, h].reshape(-1), offs[b, h].reshape(-1)
-        sel = gp >= 0
-        order = np.argsort(gp[sel], kind="stable")
-        assert np.array_equal(gp[sel][order], p_ref)
-        assert np.array_equal(go[sel][order], o_ref)
-        assert len(p_ref) == 4100
+                                window=300, kv_capacity=1000), 4, forward)
+    # long splits: several scale-staging phases per split, causal over codes and residual
+    _trace_rows(synth.make_int8(17, 2, 32, 8, 128, [7000, 3000], kv_capacity=7000), 1, forward)

@@ -77,15 +77,3 @@ def test_partition_and_fixed_splits_share_a_workspace():
         H.check_rows(b.astype(np.float64), L2.cpu().numpy().astype(np.float64), Or, Lr, TOL)
         outs.append(a)
     assert np.array_equal(outs[0], outs[2])       # fixed plan + fixed partition: bitwise repeatable
-
-
-def test_partition_cfg3_full_sampled_rows():
-    w = synth.config(3, 0)
-    H.announce("partition cfg3 full")
-    O, L, plan = H.run(w, partition=0)
-    g = synth.rng(78)
-    rows = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 24), g.integers(0, 32, 24))]
-    rows += [(int(np.argmax(w.buffers["seq_lens"])), 0), (int(np.argmin(w.buffers["seq_lens"])), 31)]
-    Or, Lr = oracle.attend(w.problem, w.buffers, heads=rows)
-    H.check_rows(O, L, Or, Lr, TOL, rows=rows)
-    assert np.all(np.isfinite(O))

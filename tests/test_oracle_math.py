@@ -248,13 +248,37 @@ def test_trace_lists_each_visible_row_once():
     w = synth.make_paged(4, 2, 4, 2, 8, [19, 7], page_size=4, mask_kind="sink_window",
                          n_sink=2, window=6, max_pages_per_seq=8)
     _, _, tr = oracle.attend(w.problem, w.buffers, with_trace=True)
-    for (b, h), (pos, offs, _) in tr.items():
+    for (b, h), t in tr.items():
+        pos, offs = t["positions"], t["offsets"]
         T = int(w.buffers["seq_lens"][b])
         assert list(pos) == [t for t in range(T) if t < 2 or t >= T - 6]
         assert len(set(offs.tolist())) == len(offs)
         for t, o in zip(pos, offs):
             page = w.buffers["block_table"][b, t // 4]
             assert o == ((page * 4 + t % 4) * 2 + h) * 8
+
+
+def test_trace_int8_rows_and_scales_are_the_stored_elements():
+    """Every traced int8 row, K scale row and V scale points at the element
+    the format stores for (b, t, h) (NumPy's own multi-index flattening), and
+    residual rows at row t - n_q of the residual buffer."""
+    lens = [300, 130, 5]
+    w = synth.make_int8(9, 3, 4, 2, 16, lens, k_group=32, residual_len=16, kv_capacity=320,
+                        mask_kind="sink_window", n_sink=3, window=100)
+    _, _, tr = oracle.attend(w.problem, w.buffers, with_trace=True)
+    kc, ks, vs, kr = (w.buffers[x] for x in ("k", "k_scale", "v_scale", "k_resid"))
+    for (b, h), t in tr.items():
+        n_q = lens[b] - min(lens[b], 16)
+        for pos, off, reg, ko, vo in zip(t["positions"], t["offsets"], t["regions"],
+                                         t["k_scale_offsets"], t["v_scale_offsets"]):
+            if pos < n_q:
+                assert reg == 0
+                assert off == np.ravel_multi_index((b, pos, h, 0), kc.shape)
+                assert ko == np.ravel_multi_index((b, pos // 32, h, 0), ks.shape)
+                assert vo == np.ravel_multi_index((b, pos, h), vs.shape)
+            else:
+                assert reg == 1 and ko == -1 and vo == -1
+                assert off == np.ravel_multi_index((b, pos - n_q, h, 0), kr.shape)
 
 
 @pytest.mark.parametrize("C,T_list", [(3, [8, 3, 0]), (2, [5, 1]), (4, [6, 9])])

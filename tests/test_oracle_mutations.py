@@ -40,9 +40,9 @@ def test_mutation_missing_softmax_scale(monkeypatch):
 def test_mutation_wrong_gqa_map(monkeypatch):
     orig = attend_mod.gather_rows
 
-    def bad(prob, buf, b, h_kv, positions):
+    def bad(prob, buf, b, h_kv, positions, **kw):
         # query group i of head h reads head (h+1) mod H_kv
-        return orig(prob, buf, b, (h_kv + 1) % prob.num_kv_heads, positions)
+        return orig(prob, buf, b, (h_kv + 1) % prob.num_kv_heads, positions, **kw)
     monkeypatch.setattr(attend_mod, "gather_rows", bad)
     assert _fails([_bf_all])
 
@@ -104,10 +104,10 @@ def test_mutation_int8_scale_axis(monkeypatch):
     """K scale indexed by token instead of by 128-token group."""
     orig = attend_mod.gather_rows
 
-    def bad(prob, buf, b, h_kv, positions):
+    def bad(prob, buf, b, h_kv, positions, **kw):
         if prob.kv_format != "i8":
-            return orig(prob, buf, b, h_kv, positions)
-        K, V, offs, reg = orig(prob, buf, b, h_kv, positions)
+            return orig(prob, buf, b, h_kv, positions, **kw)
+        K, V, offs, reg = orig(prob, buf, b, h_kv, positions, **kw)
         pos = np.asarray(positions)
         q = reg == 0
         G = prob.k_group
