@@ -187,7 +187,13 @@ typedef struct da_plan {
  *               DA_KV_I8: int8 codes [B, T_cap, H_kv, D] of tokens t < n_q(b) (contiguous NHD)
  *   k_scale     DA_KV_I8: fp16 [B, ceil(T_cap/k_group), H_kv, D]; group j scales
  *               tokens [j*k_group, (j+1)*k_group), one scale per channel
- *   v_scale     DA_KV_I8: fp16 [B, T_cap, H_kv]; one scale per token
+ *   v_scale     DA_KV_I8: fp16 [B, T_cap, H_kv]; one scale per token.
+ *               Domain: any finite normal fp16 scales (the writer rule of "M8.6 ...",
+ *               section 0x02A) with any finite bf16 q; the matrix-core int8 kernel
+ *               scales q (per head) and the K and V scales (per run of at most 2048
+ *               rows) by powers of two into fp16's range and undoes them exactly, so
+ *               K values up to 127 * 65504 and |q| beyond 65504 stay finite.  Scores
+ *               must be finite in fp32.
  *   k_resid,
  *   v_resid     DA_KV_I8: bf16 [B, R, H_kv, D]; row t - n_q(b) holds token t for
  *               t >= n_q(b) = seq_lens[b] - min(seq_lens[b], R)

@@ -77,6 +77,31 @@ __device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
 }
 
+// Largest magnitude bit pattern (sign cleared) of the eight fp16 values in x.
+__device__ __forceinline__ uint32_t f16_absmax_bits(uint4 x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  return m;
+}
+// The eight fp16 values of x times 2^-e (exact while the results stay normal).
+__device__ __forceinline__ uint4 f16_scale_pow2(uint4 x, int e) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_f16(ldexpf(f16_bits_to_f32(w[i] & 0xffffu), -e), ldexpf(f16_bits_to_f32(w[i] >> 16), -e));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+// floor(log2 x) of a normal fp16 magnitude bit pattern (subnormals: -14)
+__device__ __forceinline__ int f16_exponent(uint32_t bits) { return max((int)(bits >> 10), 1) - 15; }
+
 // a * b for a, b < 2^24 with a product below 2^32 (v_mul_u32_u24), unsigned so
 // that it extends to an address offset by zero extension
 __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) { return (uint32_t)__umul24(a, b); }
@@ -150,6 +175,17 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 
   float m_run = -INFINITY;   // running max of head n (base 2)
   float l_run = 0.f;         // partial denominator over rows 4kg .. 4kg+3 of every tile
+  // fp16 range of the int8 part's matrix-core operands.  Each operand is
+  // brought into range by a power of two that the scores or the weights undo
+  // exactly: q per head (largest |q| in [2^14, 2^15)), the K scale rows of a
+  // phase (largest in [2^8, 2^9), so code * scale < 2^16), the V scales of a
+  // phase (largest in [2^14, 2^15), so weight * scale < 2^15).  Scores are
+  // acc * sfac with sfac = scale * log2(e) * 2^(e_q + e_k); the weights
+  // p * sigma_V enter PV times vinv = 2^-e_v (the denominator takes p), so o
+  // holds u * 2^-e_v and is multiplied by vpow = 2^e_v at the end.
+  float sfac = p.qscale;
+  int e_v = 0;
+  float vpow = 1.f, vinv = 1.f;
   f32x4_t o[8];              // int8 part: PV accumulators in the matrix-core layout
 #pragma unroll
   for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -161,8 +197,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     const int l = min(lim, lim_n);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sc[i] = (ta + 4 * kg + i < l) ? acc[i] * p.qscale : -INFINITY;
-      sc[4 + i] = (tb + 4 * kg + i < l) ? acc2[i] * p.qscale : -INFINITY;
+      sc[i] = (ta + 4 * kg + i < l) ? acc[i] * sfac : -INFINITY;
+      sc[4 + i] = (tb + 4 * kg + i < l) ? acc2[i] * sfac : -INFINITY;
     }
     float mt = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                      fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -196,14 +232,30 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     // q in this part's channel order, read from the staged rows: channels
     // kch(c) .. +7 of head n are 8-channel block kch(c)/8 = 4c' + kg', held by
     // lane n + 16kg' of q_lds[c'] (zero for n >= G).
-    uint4 qh[4];
+    // Head n's channels are spread over the lanes n + 16kg; its largest |q|
+    // (bf16 bit pattern) sets e_q, and q * 2^-e_q (exact in fp16 down to
+    // 2^-28 of the largest) feeds the matrix cores.
+    uint4 qx[4];
+    uint32_t qmx = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int blk = kch(c) >> 3;
-      const uint4 x = q_lds[blk >> 2][n + 16 * (blk & 3)];
-      // bf16 values of N(0,1)-scale queries are exact in fp16
-      qh[c] = make_uint4(pack_f16(bf16_lo(x.x), bf16_hi(x.x)), pack_f16(bf16_lo(x.y), bf16_hi(x.y)),
-                         pack_f16(bf16_lo(x.z), bf16_hi(x.z)), pack_f16(bf16_lo(x.w), bf16_hi(x.w)));
+      qx[c] = q_lds[blk >> 2][n + 16 * (blk & 3)];
+      const uint32_t w[4] = {qx[c].x, qx[c].y, qx[c].z, qx[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qmx = max(qmx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    }
+    qmx = max(qmx, (uint32_t)__shfl_xor((int)qmx, 16));
+    qmx = max(qmx, (uint32_t)__shfl_xor((int)qmx, 32));
+    const int e_q = qmx ? min(max((int)(qmx >> 7) - 127 - 14, -100), 100) : 0;
+    uint4 qh[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 x = qx[c];
+      auto cv = [&](uint32_t wd) {
+        return pack_f16(ldexpf(bf16_lo(wd), -e_q), ldexpf(bf16_hi(wd), -e_q));
+      };
+      qh[c] = make_uint4(cv(x.x), cv(x.y), cv(x.z), cv(x.w));
     }
     const int sh = p.k_group_shift;
     // Ordinals map to positions by a constant shift inside each run (sinks:
@@ -214,7 +266,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     // (slots - 1) groups' length touches at most `slots` scale rows.
     const int phase = min((kI8ScaleSlots - 1) << sh, 2048);
     const uint32_t vs_stride = 2 * (uint32_t)p.num_kv_heads;   // V scale bytes per position
-    bool staged = false;
+    __shared__ uint32_t smax[NWAVES][2];   // per-wave largest K and V scale of a phase
     for (int run = 0; run < 2; ++run) {
       const int rb = run == 0 ? begin : max(begin, vis.ns);
       const int re = run == 0 ? min(mid, vis.ns) : mid;
@@ -286,10 +338,13 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
         auto pv2 = [&](const uint2 (&a)[4], const uint32_t (&sa)[4], const uint2 (&bv)[4],
                        const uint32_t (&sb)[4], const float (&pr)[8]) {
           uint4 w;
-          w.x = pack_f16(pr[0] * f16_bits_to_f32(sa[0]), pr[1] * f16_bits_to_f32(sa[1]));
-          w.y = pack_f16(pr[2] * f16_bits_to_f32(sa[2]), pr[3] * f16_bits_to_f32(sa[3]));
-          w.z = pack_f16(pr[4] * f16_bits_to_f32(sb[0]), pr[5] * f16_bits_to_f32(sb[1]));
-          w.w = pack_f16(pr[6] * f16_bits_to_f32(sb[2]), pr[7] * f16_bits_to_f32(sb[3]));
+          float ps[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ps[i] = pr[i] * vinv;
+          w.x = pack_f16(ps[0] * f16_bits_to_f32(sa[0]), ps[1] * f16_bits_to_f32(sa[1]));
+          w.y = pack_f16(ps[2] * f16_bits_to_f32(sa[2]), ps[3] * f16_bits_to_f32(sa[3]));
+          w.z = pack_f16(ps[4] * f16_bits_to_f32(sb[0]), ps[5] * f16_bits_to_f32(sb[1]));
+          w.w = pack_f16(ps[6] * f16_bits_to_f32(sb[2]), ps[7] * f16_bits_to_f32(sb[3]));
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const uint4 vcol = make_uint4(v_pair_word(a[0], a[1], c), v_pair_word(a[2], a[3], c),
@@ -319,13 +374,54 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
           issue_v(tile + STEP, vb, svb);
         }
         // The scale table is staged after the first tiles are requested, so its
-        // latency overlaps theirs instead of preceding it.
-        if (staged) __syncthreads();                       // the previous phase has read its table
-        staged = true;
-        for (int idx = threadIdx.x; idx < ng * 16; idx += NWAVES * 64)
-          ksc[idx >> 4][idx & 15] =
-              *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
+        // latency overlaps theirs instead of preceding it.  The phase's
+        // largest K and V scales set e_k and e_v (see above); the K scale rows
+        // are stored times 2^-e_k.
+        static_assert(kI8ScaleSlots * 16 <= 2 * NWAVES * 64, "two scale quads per thread");
+        uint4 kreg[2];
+        uint32_t kmx = 0, vmx = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int idx = threadIdx.x + k2 * NWAVES * 64;
+          kreg[k2] = make_uint4(0u, 0u, 0u, 0u);
+          if (idx < ng * 16) {
+            kreg[k2] = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
+            kmx = max(kmx, f16_absmax_bits(kreg[k2]));
+          }
+        }
+        for (int r = threadIdx.x; r < pe - pb; r += NWAVES * 64)
+          vmx = max(vmx, (uint32_t)*reinterpret_cast<const uint16_t*>(vsp + mul_u24((uint32_t)r, vs_stride)) & 0x7fffu);
+        kmx = wave_max_u32(kmx);
+        vmx = wave_max_u32(vmx);
+        if (lane == 0) {
+          smax[wave][0] = kmx;
+          smax[wave][1] = vmx;
+        }
+        __syncthreads();        // also: every wave has finished the previous phase's table
+        kmx = 0;
+        vmx = 0;
+#pragma unroll
+        for (int w8 = 0; w8 < NWAVES; ++w8) {
+          kmx = max(kmx, smax[w8][0]);
+          vmx = max(vmx, smax[w8][1]);
+        }
+        const int e_k = kmx ? f16_exponent(kmx) - 8 : 0;
+        const int e_v_new = vmx ? f16_exponent(vmx) - 14 : 0;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int idx = threadIdx.x + k2 * NWAVES * 64;
+          if (idx < ng * 16) ksc[idx >> 4][idx & 15] = f16_scale_pow2(kreg[k2], e_k);
+        }
         __syncthreads();
+        sfac = ldexpf(p.qscale, e_q + e_k);
+        if (e_v_new != e_v) {        // o to the new phase's units (o is 0 before the first)
+          const float f = ldexpf(1.f, e_v - e_v_new);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[c] *= f;
+          e_v = e_v_new;
+          vpow = ldexpf(1.f, e_v);
+          vinv = ldexpf(1.f, -e_v);
+        }
         for (; tile < pe; tile += 2 * STEP) {
           const int tb = tile + STEP;
           const f32x4_t acc = scores(tile, ka);
@@ -350,7 +446,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? o[e][i & 3] : 0.f;
+    for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? o[e][i & 3] * vpow : 0.f;
 
   // Online softmax over the 4 scores of this lane (rows 4kg+i, head n);
   // returns the weights and rescales l and u.

@@ -70,3 +70,34 @@ def test_residual_only_int8_equals_bf16():
     H.check_rows(O8, L8, Ob, Lb, 2e-3)
     e, le = H.errors(O8, L8, Ob, Lb)
     H.announce(f"residual-only pin: int8 vs bf16 GPU max|dO| = {e:.3e}, max|dLSE| = {le:.3e}")
+
+
+def test_int8_operands_outside_fp16_range():
+    """The int8 kernel feeds fp16 matrix-core operands, whose range ends at
+    65504.  Inputs the format allows beyond that range give finite results
+    that match the oracle: a K value of 1e5 (its group's channel scale is
+    787.5, so code * scale reaches 1e5), query elements of +-7e4, a request
+    whose K scales are all large, and a request with small V values (|V| ~
+    0.03, whose weighted scales would fall below fp16's normal range)."""
+    B, T, Hkv, D = 4, 2048, 8, 128
+    g = synth.rng(33)
+    kf = g.standard_normal((B, T, Hkv, D), dtype=np.float32)
+    vf = g.standard_normal((B, T, Hkv, D), dtype=np.float32)
+    kf[0, 100, 3, 7] = 1e5
+    kf[1] *= 3e4
+    vf[2] *= 0.01
+    lens = [2048, 2000, 1900, 1500]
+    w = synth.make_int8(33, B, 32, Hkv, D, lens, kv_capacity=T, values=(kf, vf))
+    assert float(w.buffers["k_scale"][0, 0, 3, 7]) == 787.5
+    q = w.buffers["q"]
+    q[3, 5, 11] = synth.bf16_bits(np.float32(7e4))
+    q[1, 20, 3] = synth.bf16_bits(np.float32(-7e4))
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    for fn in (H.forward, H.run):
+        O, L, _ = fn(w)
+        assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+        for b in range(B):       # each request against its own output scale
+            H.check_rows(O[b:b + 1], L[b:b + 1], Or[b:b + 1], Lr[b:b + 1], 0.0, rtol=1e-2)
+            e, le = H.errors(O[b:b + 1], L[b:b + 1], Or[b:b + 1], Lr[b:b + 1])
+            H.announce(f"range case request {b}: max|dO| = {e:.3e} (max|O_ref| = "
+                       f"{float(np.max(np.abs(Or[b]))):.3g}), max|dLSE| = {le:.3e}")
