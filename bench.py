@@ -33,9 +33,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_fused_llama3_8b_layer_traffic.json")
-KERNEL_SOURCES = ["kv_cache_amd/csrc/split_kernel_mfma.hpp", "kv_cache_amd/csrc/split_common.hpp",
-                  "kv_cache_amd/csrc/device_common.hpp", "kv_cache_amd/csrc/decode_attn.hip"]
+PROFILES = os.path.join(ROOT, "profiles")
+# every source that decides what the timed kernels do (the split count too)
+KERNEL_SOURCES = ["kv_cache_amd/csrc/split_kernel_mfma.hpp", "kv_cache_amd/csrc/split_kernel_mfma_i8.hpp",
+                  "kv_cache_amd/csrc/split_kernel.hpp", "kv_cache_amd/csrc/split_common.hpp",
+                  "kv_cache_amd/csrc/combine_kernel.hpp", "kv_cache_amd/csrc/device_common.hpp",
+                  "kv_cache_amd/csrc/decode_attn.hip", "kv_cache_amd/csrc/plan.cpp"]
+# the kernel that moves the call's bytes, per workload (substring of its name)
+DOMINANT = {"llama3_8b_layer": "split_kernel_mfma<4, false, 4, true, false, false, 0>",
+            "long_context_128k": "split_kernel_mfma<4, false, 4, false, false, false, 0>",
+            "int8_sink_window": "split_kernel_mfma_i8<4, 4, true, 0>",
+            "paged_ragged": "split_kernel_mfma<4, true, 4, false, false, true, 0>"}
 
 
 def kernel_source_hash() -> str:
@@ -44,6 +52,50 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def profile_record(workload):
+    """The machine-readable block of profiles/<workload>_kernel_trace.md (written
+    by ``bench.py --summarize``), or None."""
+    path = os.path.join(PROFILES, f"{workload}_kernel_trace.md")
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    tag = "<!-- bench-data "
+    i = text.find(tag)
+    if i < 0:
+        return None
+    try:
+        return json.loads(text[i + len(tag):text.index(" -->", i)])
+    except ValueError:
+        return None
+
+
+def profiled_roofline(workload, call_bytes, num_splits):
+    """Roofline of the workload's dominant kernel from its committed rocprofv3
+    summary: its average duration and counter traffic, only when the summary
+    was taken on the current kernel sources and split count."""
+    rec = profile_record(workload)
+    if not rec:
+        return None, "no profile summary"
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None, f"profile taken on other kernel sources ({rec.get('kernel_source_hash')})"
+    if rec.get("num_splits") != num_splits:
+        return None, f"profile taken at {rec.get('num_splits')} splits"
+    k = rec["kernels"].get(rec["dominant"])
+    if not k:
+        return None, "dominant kernel missing from the profile"
+    us = k["avg_ns"] / 1000.0
+    ach = call_bytes / (us * 1e-6) / 1e9
+    out = {"kernel": rec["dominant"], "us_per_launch": round(us, 2), "calls": k["calls"],
+           "achieved": round(ach, 1), "frac": round(ach / PEAK_GBS, 4),
+           "source_hash": rec["kernel_source_hash"], "file": f"profiles/{workload}_kernel_trace.md"}
+    tr = rec.get("traffic")
+    if tr:
+        out["traffic"] = tr["hbm_bytes_per_launch"]
+    return out, None
 
 
 def visible(T, mask):
@@ -190,6 +242,36 @@ class GpuWorkload:
         self.kv_bytes, self.split_bytes, self.call_bytes = algorithmic_bytes(
             kind, B, Hq, Hkv, D, self.lens, self.S, eb=eb, mask=mask, hidden=hidden, C=C,
             residual=residual, k_group=k_group, page_size=page_size)
+
+    def replan(self, num_splits):
+        """Plan the same buffers for another split count (fresh workspace,
+        arguments and byte count)."""
+        ka, torch = self.ka, self.torch
+        self.prob.num_splits = num_splits
+        _, self.plan, self.ws_bytes, _ = ka.decode_attn_plan(ka.problem_from(self.prob))
+        S_old, self.S = self.S, self.plan.num_splits
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.make_all_args()
+        ka.decode_attn_workspace_init(self.plan, self.ws, self.ws_bytes, self.stream)
+        d_ws = self.B * self.prob.num_queries * self.Hq * (self.S - S_old) * (self.D + 2) * 4
+        self.split_bytes += d_ws
+        self.call_bytes += 2 * d_ws
+        return self
+
+    def sweep(self, splits, steps=30, warmup=5):
+        """Per-call time of decode_attn_forward for each split count (0:
+        the planner's choice), restoring the original plan afterwards."""
+        S0 = self.prob.num_splits
+        out = []
+        for S in splits:
+            self.replan(S)
+            ms = self.time(self.fwd, steps, warmup)
+            gbs = self.call_bytes / (ms * 1e-3) / 1e9
+            out.append({"requested": S, "num_splits": self.S, "chunk": self.plan.chunk,
+                        "us_per_call": round(ms * 1000, 2), "GBs": round(gbs, 1),
+                        "pct_of_peak": round(100 * gbs / PEAK_GBS, 1)})
+        self.replan(S0)
+        return out
 
     def host_buffers(self):
         """Input set 0 copied to host arrays in the oracle's storage formats
@@ -491,6 +573,52 @@ def hbm_probe(torch, nbytes=512 << 20):
     return read_gbs
 
 
+def pattern_probe(torch, w, steps=100, warmup=10, stamp_calls=20):
+    """The split kernel's read pattern without its arithmetic (hbm_probe.hip
+    pattern_kernel) on the headline workload's input sets, same grid and
+    split length: the read ceiling of that access pattern on this machine, and
+    its per-XCD completion (the median over calls of each XCD's last
+    workgroup end, from the start of the earliest)."""
+    import ctypes
+    import numpy as np
+    L = ctypes.CDLL(os.path.join(ROOT, "kv_cache_amd", "libhbm_probe.so"))
+    L.hbm_probe_pattern.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + \
+        [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    T = max(w.lens)
+    grid = w.B * w.Hkv * w.S
+    sink = torch.empty(grid, dtype=torch.int32, device="cuda")
+    st = torch.zeros((grid, 2), dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call(i, stamps=None):
+        d = w.sets[i % w.nsets]
+        rc = L.hbm_probe_pattern(d["k"].data_ptr(), d["v"].data_ptr(), w.B, T, w.Hkv, w.S, w.plan.chunk,
+                                 sink.data_ptr(), stamps, stream)
+        assert rc == 0
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1000
+    ends = []
+    for i in range(stamp_calls):
+        call(i, st.data_ptr())
+        torch.cuda.synchronize()
+        a = st.cpu().numpy().view(np.uint64)
+        e = (a[:, 0] - a[:, 0].min()).astype(np.float64) / 100.0      # 100 MHz counter -> us
+        x = a[:, 1].astype(int)
+        ends.append([float(e[x == k].max()) if (x == k).any() else 0.0 for k in range(8)])
+    kv = 2 * w.B * T * w.Hkv * w.D * 2
+    return {"us_per_launch": round(us, 2), "GBs": round(kv / (us * 1e-6) / 1e9, 1), "bytes": kv,
+            "grid": grid, "chunk": w.plan.chunk,
+            "xcd_last_end_spread_us_median": [round(float(np.median([c[k] for c in ends])), 2) for k in range(8)]}
+
+
 def host_info():
     """Core counts and CPU model of the host the oracle ran on."""
     model = None
@@ -531,6 +659,160 @@ def cpu_baseline(call_bytes, seconds: float = 10.0):
                       f"{dt:.1f} s wall"}
 
 
+def headline(torch, ka, num_splits=0):
+    """The Llama-3-8B-shaped layer: B=8, H_q=32, H_kv=8, d=128, S_k=4096, bf16."""
+    return GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, num_splits=num_splits,
+                       min_bytes=600 << 20, seed=0)
+
+
+def make_workload(torch, ka, name):
+    """Device workload of one of the named timed workloads (for --stamps)."""
+    import synth
+    if name == "llama3_8b_layer":
+        return headline(torch, ka)
+    if name == "long_context_128k":
+        return GpuWorkload(torch, ka, "contig", 1, 32, 8, 128, [131072], min_bytes=600 << 20, seed=1)
+    if name == "int8_sink_window":
+        return GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
+                           mask=(4, 4096))
+    if name == "paged_ragged":
+        return GpuWorkload(torch, ka, "paged", 32, 32, 8, 128, synth.ragged_lengths(0, 32).tolist(), seed=2)
+    raise ValueError(name)
+
+
+def stamps_summary(torch, ka, name, calls=20, warmup=5):
+    """Per-workgroup timestamps of decode_attn_forward's launches
+    (decode_attn_timestamps) over `calls` calls: when workgroups start and
+    store their states, how the 8 XCDs finish, and how long the folds take."""
+    import numpy as np
+    w = make_workload(torch, ka, name)
+    grid = w.B * w.Hkv * w.S
+    st = torch.zeros((grid, 4), dtype=torch.int64, device="cuda")
+    rows = []
+    hz = 0
+    for i in range(warmup + calls):
+        _, hz = ka.decode_attn_timestamps(w.plan, w.args[i % w.nsets], w.out, w.lse, st, w.stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            rows.append(st.cpu().numpy().view(np.uint64).copy())
+    us = 1e6 / hz
+    res = {"workload": name, "num_splits": w.S, "workgroups": grid, "clock_hz": hz, "calls": calls}
+    per = []
+    for a in rows:
+        t0 = a[:, 0].min()
+        start, stored, end = ((a[:, k] - t0) * us for k in range(3))
+        xcc = (a[:, 3] & 0xF).astype(int)
+        hw = ((a[:, 3] >> 8) & 0xFFFFFFFF).astype(np.int64)
+        folded = (a[:, 3] >> 63).astype(bool)
+        # (XCC, SE_ID, SH_ID, CU_ID) from HW_ID: CU_ID bits 8..11, SH_ID 12, SE_ID 13..15
+        cu = ((hw >> 8) & 0x1F) | (((hw >> 13) & 0x7) << 5) | (xcc.astype(np.int64) << 8)
+        per.append({"span": float(end.max()), "last_start": float(start.max()),
+                    "stored_median": float(np.median(stored)), "stored_max": float(stored.max()),
+                    "xcd_last_store": [float(stored[xcc == x].max()) if (xcc == x).any() else 0.0
+                                       for x in range(8)],
+                    "xcd_wgs": [int((xcc == x).sum()) for x in range(8)],
+                    "cu_last_store_p10_p90": [float(np.percentile([stored[cu == c].max() for c in np.unique(cu)], q))
+                                              for q in (10, 90)],
+                    "fold_us_median": float(np.median((end - stored)[folded])) if folded.any() else None,
+                    "fold_us_max": float((end - stored)[folded].max()) if folded.any() else None,
+                    "end_after_last_store": float(end.max() - stored.max()),
+                    "cus": int(len(np.unique(cu)))})
+    med = lambda k: round(float(np.median([p[k] for p in per])), 2)
+    res.update({k: med(k) for k in ("span", "last_start", "stored_median", "stored_max",
+                                    "end_after_last_store", "cus")})
+    res["xcd_last_store_median"] = [round(float(np.median([p["xcd_last_store"][x] for p in per])), 2)
+                                    for x in range(8)]
+    res["xcd_workgroups"] = per[0]["xcd_wgs"]
+    res["cu_last_store_p10_p90_median"] = [round(float(np.median([p["cu_last_store_p10_p90"][j] for p in per])), 2)
+                                           for j in range(2)]
+    if per[0]["fold_us_median"] is not None:
+        res["fold_us_median"] = med("fold_us_median")
+        res["fold_us_max_median"] = med("fold_us_max")
+    return res
+
+
+def summarize(a):
+    """Write profiles/<workload>_kernel_trace.md from a rocprofv3 --stats
+    kernel summary (and, when given, FETCH_SIZE / WRITE_SIZE counter passes
+    calibrated by the probe's 256 MiB copy), with a machine-readable block
+    that the bench line reads back."""
+    import csv
+    import re
+    import statistics
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "").replace("void ", "")
+        return re.sub(r"\bda::", "", re.sub(r"\(.*", "", n))
+
+    def one(d, suffix):
+        for root, _, files in os.walk(d):
+            for f in files:
+                if f.endswith(suffix):
+                    return os.path.join(root, f)
+        raise FileNotFoundError(f"{suffix} under {d}")
+    def ours(name):       # this library's kernels and the probe's (not torch's input generation)
+        return bool(re.search(r"\bda::", name)) or any(
+            k in name for k in ("read_kernel", "copy_kernel", "pattern_kernel", "zero_words"))
+    stats = [r for r in csv.DictReader(open(one(a.trace, "kernel_stats.csv"))) if ours(r["Name"])]
+    kernels = {short(r["Name"]): {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                                  "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+                                  "std_ns": float(r["StdDev"])} for r in stats}
+    dom = DOMINANT[a.summarize]
+    dominant = [k for k in kernels if k.startswith(dom)]
+    line = None
+    if a.bench_log:
+        for ln in open(a.bench_log):
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    rec = {"workload": a.summarize, "kernel_source_hash": a.source_hash or kernel_source_hash(),
+           "dominant": dominant[0] if dominant else dom, "kernels": kernels,
+           "num_splits": a.num_splits}
+    traffic_txt = ""
+    if a.fetch and a.write:
+        def counters(d):
+            g = {}
+            for r in csv.DictReader(open(one(d, "counter_collection.csv"))):
+                g.setdefault(short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+            return g
+        fetch, write = counters(a.fetch), counters(a.write)
+        copy_kib = 256 * 1024
+        rf = copy_kib / statistics.median(fetch["copy_kernel"])
+        wf = copy_kib / statistics.median(write["copy_kernel"])
+        fk = statistics.median(fetch[rec["dominant"]])
+        wk = statistics.median(write[rec["dominant"]])
+        hbm = int(round((fk * rf + wk * wf) * 1024))
+        rec["traffic"] = {"fetch_kib": fk, "write_kib": wk, "fetch_factor": round(rf, 4),
+                          "write_factor": round(wf, 4), "hbm_bytes_per_launch": hbm,
+                          "commands": a.pmc_command}
+        traffic_txt = (f"\nCounters (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, medians) of `{rec['dominant']}`: "
+                       f"{fk:.1f} / {wk:.1f}.  Calibration: the probe's copy of 256 MiB reads "
+                       f"{statistics.median(fetch['copy_kernel']):.0f} / writes {statistics.median(write['copy_kernel']):.0f} KiB "
+                       f"-> factors {rf:.3f} / {wf:.3f}.  HBM bytes per launch: {hbm}.\n\nCounter commands:\n\n"
+                       + "".join(f"    {c}\n" for c in a.pmc_command))
+    out = os.path.join(PROFILES, f"{a.summarize}_kernel_trace.md")
+    with open(out, "w") as f:
+        f.write(f"# Kernel trace: {a.title}\n\nCommand:\n\n    {a.trace_command}\n\n")
+        f.write("rocprofv3 --kernel-trace --stats summary (durations in ns):\n\n"
+                "| kernel | calls | average | min | max | stddev |\n|---|---|---|---|---|---|\n")
+        for k, v in kernels.items():
+            f.write(f"| `{k}` | {v['calls']} | {v['avg_ns']:.0f} | {v['min_ns']:.0f} | {v['max_ns']:.0f} | "
+                    f"{v['std_ns']:.0f} |\n")
+        f.write(f"\nDominant kernel: `{rec['dominant']}`; kernel sources hash {rec['kernel_source_hash']}; "
+                f"{a.num_splits} splits.\n")
+        if line:
+            f.write(f"\nbench.py line of the same run: {json.dumps(line.get(a.summarize, line))[:600]}\n")
+        f.write(traffic_txt)
+        if a.variant_trace:
+            vst = [r for r in csv.DictReader(open(one(a.variant_trace, "kernel_stats.csv"))) if ours(r["Name"])]
+            f.write(f"\n## Variant: {a.variant_label}\n\nCommand:\n\n    {a.variant_command}\n\n"
+                    "| kernel | calls | average | min | max | stddev |\n|---|---|---|---|---|---|\n")
+            for r in vst:
+                f.write(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                        f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | {float(r['StdDev']):.0f} |\n")
+        f.write(f"\n<!-- bench-data {json.dumps(rec)} -->\n")
+    print(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,12 +821,33 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the other workloads")
-    ap.add_argument("--only", default=None,
-                    choices=["long_context_128k", "paged_ragged", "int8_sink_window", "tiny_fp32",
-                             "few_query_c2", "hnd_layout", "flashmask"],
-                    help="time one of the other workloads alone and print its report (for profiling)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the split-count sweeps")
+    names = ["llama3_8b_layer", "long_context_128k", "paged_ragged", "int8_sink_window", "tiny_fp32",
+             "few_query_c2", "hnd_layout", "flashmask"]
+    ap.add_argument("--only", default=None, choices=names,
+                    help="time one workload alone and print its report (for profiling)")
+    ap.add_argument("--stamps", default=None, choices=list(DOMINANT),
+                    help="per-workgroup timestamps of one workload's forward launches (JSON)")
     ap.add_argument("--samples-out", default=None, help="write raw per-call samples (JSON)")
+    ap.add_argument("--summarize", default=None, choices=list(DOMINANT),
+                    help="write profiles/<workload>_kernel_trace.md from rocprofv3 output (no GPU)")
+    ap.add_argument("--trace", help="--summarize: directory of the --kernel-trace --stats run")
+    ap.add_argument("--fetch", help="--summarize: directory of the FETCH_SIZE counter run")
+    ap.add_argument("--write", help="--summarize: directory of the WRITE_SIZE counter run")
+    ap.add_argument("--bench-log", help="--summarize: log holding the profiled run's JSON line")
+    ap.add_argument("--title", default="", help="--summarize: title")
+    ap.add_argument("--trace-command", default="", help="--summarize: the profiled command")
+    ap.add_argument("--pmc-command", action="append", default=[], help="--summarize: counter commands")
+    ap.add_argument("--source-hash", default=None,
+                    help="--summarize: kernel sources hash of the profiled run (default: the tree's)")
+    ap.add_argument("--variant-trace", help="--summarize: kernel-trace directory of a library variant")
+    ap.add_argument("--variant-label", default="", help="--summarize: what the variant changes")
+    ap.add_argument("--variant-command", default="", help="--summarize: the variant's commands")
     a = ap.parse_args()
+    if a.summarize:
+        a.num_splits = a.num_splits or 0
+        summarize(a)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path has no multi-GPU mode "
               "(it shards by request and K/V head with no exchange; see the design notes)",
@@ -555,13 +858,22 @@ def main():
     import kv_cache_amd as ka
     ka.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.stamps:
+        print(json.dumps({"stamps": stamps_summary(torch, ka, a.stamps)}), flush=True)
+        return
+    if a.only == "llama3_8b_layer":
+        hbm_probe(torch)      # the copy of known size that calibrates the byte counters
+        w = headline(torch, ka, a.num_splits)
+        print(json.dumps({a.only: w.report("llama", "headline", a.steps, a.warmup)}), flush=True)
+        return
     if a.only:
+        if a.only in ("long_context_128k", "int8_sink_window", "paged_ragged"):
+            hbm_probe(torch)
         print(json.dumps({a.only: other_workload(torch, ka, a.only, a.steps, a.warmup)}), flush=True)
         return
 
     ceiling = hbm_probe(torch)
-    w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, num_splits=a.num_splits,
-                    min_bytes=600 << 20, seed=0)
+    w = headline(torch, ka, a.num_splits)
     torch.cuda.synchronize()
     ms_call = w.time(w.fwd, a.steps, a.warmup)         # timed region: K steps
     ms_two = w.time(w.call, a.steps, a.warmup)          # run + combine, same stream
@@ -571,16 +883,13 @@ def main():
     ms_graph_two = w.graph_time(False)
     value = w.call_bytes / (ms_call * 1e-3) / 1e9
     # The dominant kernel is the forward launch itself: one kernel moves every
-    # algorithmic byte of the call.
-    achieved = value
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("num_splits") == w.S:
-            traffic = tr.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        traffic = None
+    # algorithmic byte of the call.  Its roofline is reported from the HIP
+    # events of the timed region and from the committed rocprofv3 summary of
+    # the same kernel (when taken on these sources); the headline is the lower.
+    event = {"us_per_launch": round(ms_call * 1000, 2), "achieved": round(value, 1),
+             "frac": round(value / PEAK_GBS, 4)}
+    prof, why = profiled_roofline("llama3_8b_layer", w.call_bytes, w.S)
+    achieved = min(value, prof["achieved"]) if prof else value
 
     line = {
         "metric": "decode-attn us/call + achieved HBM GB/s (% of peak), GQA 32q/8kv d128",
@@ -602,28 +911,38 @@ def main():
                    "num_splits": w.S, "chunk": w.plan.chunk, "input_sets": w.nsets,
                    "algorithmic_bytes_per_call": w.call_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "split_kernel_mfma<4, contiguous, fused reduction>",
-                     "us_per_launch": round(ms_call * 1000, 2),
-                     "algorithmic_bytes_per_launch": w.call_bytes},
+                     "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": prof.get("traffic") if prof else None,
+                     "kernel": DOMINANT["llama3_8b_layer"],
+                     "algorithmic_bytes_per_launch": w.call_bytes,
+                     "event": event, "profiled": prof if prof else {"unavailable": why}},
         "samples_us": sample_stats(samples),
+        "samples_raw_us": [round(x, 2) for x in samples],
         "graph_replay_us_per_call": round(ms_graph * 1000, 2),
         "two_launch": {"us_per_call": round(ms_two * 1000, 2),
                        "split_kernel_us": round(ms_split * 1000, 2),
                        "split_kernel_GBs": round(w.split_bytes / (ms_split * 1e-3) / 1e9, 1),
                        "graph_replay_us_per_call": round(ms_graph_two * 1000, 2)},
         "hbm_read_probe_GBs": round(ceiling, 1),
+        "pattern_probe": pattern_probe(torch, w),
         "kernel_source_hash": kernel_source_hash(),
     }
     if a.samples_out:
         with open(a.samples_out, "w") as f:
             json.dump({"per_call_us": samples}, f)
+    if not a.no_sweep:
+        sweep = {"llama3_8b_layer": w.sweep([1, 2, 4, 8, 12, 16, 24, 32, 0])}
     call_bytes = w.call_bytes
     cpu = not a.no_cpu_baseline
     per_config = {}
     if cpu:
         per_config["llama3_8b_layer"] = oracle_timing(w, ms_call * 1000, 3, single_thread=True)
     del w
+    if not a.no_sweep:
+        wl = make_workload(torch, ka, "long_context_128k")
+        sweep["long_context_128k"] = wl.sweep([1, 8, 32, 128, 0], steps=10, warmup=3)
+        del wl
+        line["split_sweep"] = sweep
     if not a.no_long:
         others = {name: other_workload(torch, ka, name, oracle_runs=ORACLE_RUNS[name] if cpu else 0)
                   for name in ("long_context_128k", "paged_ragged", "int8_sink_window")}

@@ -221,7 +221,8 @@ typedef struct da_plan {
  *               NULL: the plan's fixed splits.  With a partition the producer grid is
  *               partition_items*H_kv workgroups of equal work (see decode_attn_partition).
  *   partition_items  the descriptor's item count W (host value; 0 without partition)
- * q, k, v, k_resid and v_resid must be 16-byte aligned. */
+ * q, k, v, k_resid, v_resid and k_scale must be 16-byte aligned, v_scale 2-byte
+ * aligned (DA_ERR_INVALID otherwise). */
 typedef struct da_args {
   const void*    q;
   const void*    k;
@@ -408,6 +409,21 @@ typedef struct da_trace {
  * DA_ERR_INVALID for a NULL trace array (the scale arrays only for DA_KV_I8). */
 da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args, const da_trace* trace,
                                     float* out, float* lse, void* stream);
+
+/* Per-workgroup timestamps of the launches decode_attn_forward makes, for
+ * schedule analysis (debug only, never on the timed path): a timestamp
+ * instance of the same kernels, in which thread 0 of each workgroup reads the
+ * device's constant-rate clock (s_memrealtime) at its start, when its states
+ * are stored, and at its end.  stamps: device uint64 [B*H_kv*S, 4] per
+ * workgroup index: start, states stored, end, and the XCC_ID register (bits
+ * 0..3) | the HW_ID register << 8 (CU, shader engine) | 1 << 63 when the
+ * workgroup folded the states of its (b, h_kv).  *clock_hz (host) receives
+ * the clock's rate.  With S above the single-launch limit the split kernel is
+ * stamped and the combine follows.  Matrix-core kernels (bf16 / int8,
+ * head_dim 128) without a partition or FlashMask; else DA_ERR_UNSUPPORTED.
+ * Other errors as decode_attn_forward. */
+da_status decode_attn_timestamps(const da_plan* plan, const da_args* args, float* out, float* lse,
+                                 uint64_t* stamps, uint64_t* clock_hz, void* stream);
 
 /* ---- streaming append for DA_KV_I8 with DA_RESIDUAL_GROUPS ------------------ */
 

@@ -17,7 +17,7 @@ __all__ = [
     "DA_ERR_PLAN_MISMATCH", "DA_ERR_HIP", "DecodeAttnError", "Problem", "Plan",
     "Args", "Trace", "lib", "library_path", "problem_from", "decode_attn_plan",
     "decode_attn_schedule", "decode_attn_append", "decode_attn_flashmask_summarize", "AppendArgs", "decode_attn_run", "decode_attn_combine", "decode_attn_forward",
-    "decode_attn_workspace_init", "decode_attn_trace_indices", "decode_attn_forward_static",
+    "decode_attn_workspace_init", "decode_attn_trace_indices", "decode_attn_forward_static", "decode_attn_timestamps",
     "STATIC_WORKSPACE_BYTES",
     "decode_attn_reason", "decode_attn_status_string", "reason_names",
 ]
@@ -88,7 +88,10 @@ class DecodeAttnError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecode_attn.so")
+    """The in-tree library, or the variant named by KV_CACHE_AMD_LIB (a build
+    of the same sources with other compile-time switches, for comparisons)."""
+    return os.environ.get("KV_CACHE_AMD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libdecode_attn.so")
 
 
 _LIB = None
@@ -143,6 +146,10 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(Trace), ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p]
         L.decode_attn_trace_indices.restype = ctypes.c_int32
+        L.decode_attn_timestamps.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.POINTER(ctypes.c_uint64), ctypes.c_void_p]
+        L.decode_attn_timestamps.restype = ctypes.c_int32
         L.decode_attn_reason.argtypes = [ctypes.c_int]
         L.decode_attn_reason.restype = ctypes.c_char_p
         L.decode_attn_status_string.argtypes = [ctypes.c_int32]
@@ -312,6 +319,18 @@ def decode_attn_append(plan: Plan, k_new, v_new, k, v, k_scale, v_scale, k_resid
     if check and st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_append")
     return st
+
+
+def decode_attn_timestamps(plan: Plan, args: Args, out, lse, stamps, stream: int = 0,
+                           check: bool = True):
+    """Timestamp instance of decode_attn_forward's launches; ``stamps`` is a
+    device uint64 tensor of [grid, 4].  Returns (status, clock rate in Hz)."""
+    hz = ctypes.c_uint64(0)
+    st = lib().decode_attn_timestamps(ctypes.byref(plan), ctypes.byref(args), _ptr(out), _ptr(lse),
+                                      _ptr(stamps), ctypes.byref(hz), stream)
+    if check and st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_timestamps")
+    return st, hz.value
 
 
 def decode_attn_trace_indices(plan: Plan, args: Args, k_offset, v_offset, position, count,

@@ -84,7 +84,8 @@ da_status check_args(const da_plan* plan, const da_args* a) {
     if (p.residual_len > 0 && (!a->k_resid || !a->v_resid)) return DA_ERR_INVALID;
     if ((a->k_resid && !aligned16(a->k_resid)) || (a->v_resid && !aligned16(a->v_resid)))
       return DA_ERR_INVALID;
-    if ((reinterpret_cast<uintptr_t>(a->k_scale) & 15u) != 0) return DA_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(a->k_scale) & 15u) != 0 || (reinterpret_cast<uintptr_t>(a->v_scale) & 1u) != 0)
+      return DA_ERR_INVALID;
   }
   return DA_OK;
 }
@@ -126,6 +127,8 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
                    : nullptr;
   sp.out = nullptr;
   sp.lse = nullptr;
+  sp.tr = da::TraceOut{};
+  sp.stamps = nullptr;
   sp.num_q_heads = p.num_q_heads;
   sp.num_kv_heads = p.num_kv_heads;
   sp.batch = p.batch;
@@ -152,54 +155,68 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   return sp;
 }
 
-// TRACE selects the index-trace instance of the same kernel (debug entry
-// point only).
-template <int FMT, int D, int G, bool PAGED, bool FUSED, bool FM, bool TRACE>
-void launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
+// INSTR selects an instrumentation instance of the same kernel (debug entry
+// points only): da::kInstrRows the index trace, da::kInstrStamps per-workgroup
+// timestamps (matrix-core kernels without a partition or FlashMask only).
+// Returns false when no such instance exists.
+template <int FMT, int D, int G, bool PAGED, bool FUSED, bool FM, int INSTR>
+bool launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
+  constexpr bool kStamps = INSTR == da::kInstrStamps;
   if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8) {
     static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
-    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED, TRACE>), dim3(grid), dim3(kWaves * 64), 0,
+    hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED, INSTR>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
+    return true;
   } else if constexpr (use_mfma<FMT, D>()) {
-    if constexpr (!FUSED && !FM) {
+    if constexpr (!FUSED && !FM && !kStamps) {
       if (sp.partition) {
-        hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, false, false, true, TRACE>), dim3(grid),
+        hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, false, false, true, INSTR>), dim3(grid),
                            dim3(kWaves * 64), 0, st, sp);
-        return;
+        return true;
       }
     }
-    hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED, FM, false, TRACE>), dim3(grid),
-                       dim3(kWaves * 64), 0, st, sp);
+    if constexpr (kStamps && FM) {
+      return false;
+    } else {
+      if (kStamps && sp.partition) return false;
+      hipLaunchKernelGGL((da::split_kernel_mfma<G, PAGED, kWaves, FUSED, FM, false, INSTR>), dim3(grid),
+                         dim3(kWaves * 64), 0, st, sp);
+      return true;
+    }
   } else {
-    static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
-    hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value, FUSED, TRACE>),
-                       dim3(grid), dim3(kWaves * 64), 0, st, sp);
+    if constexpr (kStamps || FM) {   // FlashMask runs on the bf16 matrix-core kernel only
+      return false;
+    } else {
+      hipLaunchKernelGGL((da::split_kernel<FMT, D, G, PAGED, kWaves, Unroll<FMT>::value, FUSED, INSTR>),
+                         dim3(grid), dim3(kWaves * 64), 0, st, sp);
+      return true;
+    }
   }
 }
 
-template <int FMT, int D, bool PAGED, bool FUSED, bool FM, bool TRACE>
+template <int FMT, int D, bool PAGED, bool FUSED, bool FM, int INSTR>
 bool dispatch_g(int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   switch (g) {
-    case 1: launch_split<FMT, D, 1, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
-    case 2: launch_split<FMT, D, 2, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
-    case 4: launch_split<FMT, D, 4, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
-    case 8: launch_split<FMT, D, 8, PAGED, FUSED, FM, TRACE>(sp, grid, st); return true;
+    case 1: return launch_split<FMT, D, 1, PAGED, FUSED, FM, INSTR>(sp, grid, st);
+    case 2: return launch_split<FMT, D, 2, PAGED, FUSED, FM, INSTR>(sp, grid, st);
+    case 4: return launch_split<FMT, D, 4, PAGED, FUSED, FM, INSTR>(sp, grid, st);
+    case 8: return launch_split<FMT, D, 8, PAGED, FUSED, FM, INSTR>(sp, grid, st);
     default: return false;
   }
 }
 
-template <int FMT, bool PAGED, bool FUSED, bool FM, bool TRACE>
+template <int FMT, bool PAGED, bool FUSED, bool FM, int INSTR>
 bool dispatch_d(int d, int g, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   if constexpr (FM) {
-    return d == 128 && dispatch_g<FMT, 128, PAGED, FUSED, true, TRACE>(g, sp, grid, st);
+    return d == 128 && dispatch_g<FMT, 128, PAGED, FUSED, true, INSTR>(g, sp, grid, st);
   } else {
-    if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED, false, TRACE>(g, sp, grid, st);
-    if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED, false, TRACE>(g, sp, grid, st);
+    if (d == 64) return dispatch_g<FMT, 64, PAGED, FUSED, false, INSTR>(g, sp, grid, st);
+    if (d == 128) return dispatch_g<FMT, 128, PAGED, FUSED, false, INSTR>(g, sp, grid, st);
     return false;
   }
 }
 
-template <bool FUSED, bool TRACE = false>
+template <bool FUSED, int INSTR = da::kInstrNone>
 bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   // A workgroup serves the C query rows of each of its H_q/H_kv heads: C*g
   // "virtual heads" sharing one K/V head.
@@ -208,17 +225,17 @@ bool dispatch_split(const da_problem& p, const da::SplitParams& sp, unsigned gri
   switch (p.kv_format) {
     case DA_KV_F32:
       if (p.mask_kind == DA_MASK_FLASHMASK) return false;
-      return paged ? dispatch_d<DA_KV_F32, true, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st)
-                   : dispatch_d<DA_KV_F32, false, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st);
+      return paged ? dispatch_d<DA_KV_F32, true, FUSED, false, INSTR>(p.head_dim_qk, g, sp, grid, st)
+                   : dispatch_d<DA_KV_F32, false, FUSED, false, INSTR>(p.head_dim_qk, g, sp, grid, st);
     case DA_KV_BF16:
       if (p.mask_kind == DA_MASK_FLASHMASK)
-        return paged ? dispatch_d<DA_KV_BF16, true, FUSED, true, TRACE>(p.head_dim_qk, g, sp, grid, st)
-                     : dispatch_d<DA_KV_BF16, false, FUSED, true, TRACE>(p.head_dim_qk, g, sp, grid, st);
-      return paged ? dispatch_d<DA_KV_BF16, true, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st)
-                   : dispatch_d<DA_KV_BF16, false, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st);
+        return paged ? dispatch_d<DA_KV_BF16, true, FUSED, true, INSTR>(p.head_dim_qk, g, sp, grid, st)
+                     : dispatch_d<DA_KV_BF16, false, FUSED, true, INSTR>(p.head_dim_qk, g, sp, grid, st);
+      return paged ? dispatch_d<DA_KV_BF16, true, FUSED, false, INSTR>(p.head_dim_qk, g, sp, grid, st)
+                   : dispatch_d<DA_KV_BF16, false, FUSED, false, INSTR>(p.head_dim_qk, g, sp, grid, st);
     case DA_KV_I8:
       if (p.mask_kind == DA_MASK_FLASHMASK) return false;
-      return !paged && dispatch_d<DA_KV_I8, false, FUSED, false, TRACE>(p.head_dim_qk, g, sp, grid, st);
+      return !paged && dispatch_d<DA_KV_I8, false, FUSED, false, INSTR>(p.head_dim_qk, g, sp, grid, st);
     default:
       return false;
   }
@@ -493,12 +510,46 @@ extern "C" da_status decode_attn_trace_indices(const da_plan* plan, const da_arg
   if (out && plan->num_splits <= kFusedMaxSplits && !args->partition) {
     sp.out = out;
     sp.lse = lse;
-    if (!dispatch_split<true, true>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
+    if (!dispatch_split<true, da::kInstrRows>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
   }
-  if (!dispatch_split<false, true>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
+  if (!dispatch_split<false, da::kInstrRows>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
   if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
   return out ? decode_attn_combine(plan, args->workspace, args->workspace_bytes, out, lse, stream) : DA_OK;
+}
+
+extern "C" da_status decode_attn_timestamps(const da_plan* plan, const da_args* args, float* out,
+                                            float* lse, uint64_t* stamps, uint64_t* clock_hz,
+                                            void* stream) {
+  const da_status chk = check_args(plan, args);
+  if (chk != DA_OK) return chk;
+  const da_problem& p = plan->problem;
+  if (p.batch == 0) return DA_OK;
+  if (!out || !stamps || !clock_hz || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return DA_ERR_INVALID;
+  if (args->partition || p.mask_kind == DA_MASK_FLASHMASK) return DA_ERR_UNSUPPORTED;
+  if (!args->workspace || args->workspace_bytes < plan->workspace_bytes) return DA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(args->workspace) & 15u) != 0) return DA_ERR_WORKSPACE;
+  if (!da::current_device_is_gfx950()) return DA_ERR_UNSUPPORTED;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return DA_ERR_HIP;
+  *clock_hz = (uint64_t)khz * 1000u;
+  da::SplitParams sp = make_params(plan, args);
+  sp.stamps = stamps;
+  const uint64_t grid64 = (uint64_t)p.batch * p.num_kv_heads * plan->num_splits;
+  if (grid64 > 0x7fffffffull) return DA_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (plan->num_splits <= kFusedMaxSplits) {
+    sp.out = out;
+    sp.lse = lse;
+    if (!dispatch_split<true, da::kInstrStamps>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+  }
+  if (!dispatch_split<false, da::kInstrStamps>(p, sp, (unsigned)grid64, st)) return DA_ERR_UNSUPPORTED;
+  if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
+  return decode_attn_combine(plan, args->workspace, args->workspace_bytes, out, lse, stream);
 }
 
 extern "C" da_status decode_attn_forward_static(const da_plan* plan, const da_args* args, float* out,

@@ -10,6 +10,11 @@
 
 namespace da {
 
+// Instrumentation instances of a split kernel (a template parameter): the
+// product code, the index trace (every row load recorded where it is
+// issued), or per-workgroup timestamps.
+constexpr int kInstrNone = 0, kInstrRows = 1, kInstrStamps = 2;
+
 // Index trace outputs of a split kernel's trace instance, one slot per
 // (b, h_kv, visible ordinal), `stride` ordinals per (b, h_kv).
 struct TraceOut {
@@ -74,6 +79,7 @@ struct SplitParams {
   int32_t n_mask_blocks;     // FlashMask: ceil(max_seq_len / 16)
   float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
   TraceOut tr;               // trace instances only
+  uint64_t* stamps;          // timestamp instances only: [grid, 4]
 };
 
 // ---------------------------------------------------------------------------

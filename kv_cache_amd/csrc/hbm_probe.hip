@@ -6,6 +6,8 @@
 
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // Each thread streams 16-byte words with a grid stride, folding them into a
 // checksum that is stored once per thread block so the loads cannot be
 // removed.
@@ -33,7 +35,62 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// The read pattern of the decode split kernel without its arithmetic: workgroup
+// (b, h, s) of a [B, T, H, row] cache (row = 256 bytes per token and head, two
+// buffers K and V) reads rows [s*chunk, min((s+1)*chunk, T)) of head h, the
+// split index rotated by (b, h) as the decode kernel does; each wave takes
+// 16-row tiles round-robin, lane l reading 16 bytes of row l % 16 at 16-byte
+// column l / 16 (K) and the matching V bytes.  With `stamps`, thread 0 writes
+// the workgroup's end time (s_memrealtime) and XCC_ID.
+__global__ __launch_bounds__(256) void pattern_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                                      int B, int T, int H, int S, int chunk,
+                                                      uint32_t* __restrict__ sink, uint64_t* __restrict__ stamps) {
+  const int wg = blockIdx.x;
+  const int bh = wg / S;
+  const int s = (wg - bh * S + bh) % S;
+  const int h = bh % H, b = bh / H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, c = lane >> 4;
+  const int begin = min(s * chunk, T), end = min(begin + chunk, T);
+  // 16-byte words: row (b, t, h) starts at ((b*T + t)*H + h)*16, 16 words per row
+  const size_t base = ((size_t)b * T * H + h) * 16;
+  uint32_t acc = 0;
+  for (int t = begin + wave * 16; t < end; t += 64) {
+    const int row = min(t + r, end - 1);
+    const size_t off = base + (size_t)row * H * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k + off + 4 * q + c));
+      const u32x4_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v + off + 4 * q + c));
+      acc ^= x.x ^ x.w ^ y.y ^ y.z;
+    }
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < 256; ++i) t ^= red[i];
+    sink[wg] = t;
+    if (stamps) {
+      stamps[2 * (size_t)wg] = __builtin_amdgcn_s_memrealtime();
+      stamps[2 * (size_t)wg + 1] = (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xfu;   // XCC_ID
+    }
+  }
+}
+
 }  // namespace
+
+// K and V [B, T, H, 128] bf16 (256-byte rows); grid B*H*S workgroups; sink
+// holds one uint32 per workgroup; stamps (optional) two uint64 per workgroup.
+extern "C" int hbm_probe_pattern(const void* k, const void* v, int B, int T, int H, int S, int chunk,
+                                 uint32_t* sink, uint64_t* stamps, void* stream) {
+  if (!k || !v || !sink || B <= 0 || T <= 0 || H <= 0 || S <= 0 || chunk <= 0) return -1;
+  if ((reinterpret_cast<uintptr_t>(k) & 15u) || (reinterpret_cast<uintptr_t>(v) & 15u)) return -1;
+  hipLaunchKernelGGL(pattern_kernel, dim3((unsigned)(B * H * S)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), B, T, H, S, chunk, sink, stamps);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // bytes must be a multiple of 16; sink holds `grid` uint32 values.
 extern "C" int hbm_probe_read(const void* src, uint64_t bytes, uint32_t* sink, int grid,

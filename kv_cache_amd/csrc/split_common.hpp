@@ -210,8 +210,9 @@ __device__ __forceinline__ void fold_row(const SplitParams& p, int64_t row) {
   if (p.lse && lane == 0) p.lse[row] = valid ? M + __logf(L) : -INFINITY;
 }
 
+// Returns whether this workgroup folded (single-launch mode).
 template <int G, int D, int NWAVES, bool FUSED>
-__device__ __forceinline__ void finish_split(const SplitParams& p, int b, int h) {
+__device__ __forceinline__ bool finish_split(const SplitParams& p, int b, int h) {
   if constexpr (FUSED) {
     __shared__ int is_last;
     uint32_t* cnt = p.counters + (int64_t)b * p.num_kv_heads + h;
@@ -221,11 +222,58 @@ __device__ __forceinline__ void finish_split(const SplitParams& p, int b, int h)
       is_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 (uint32_t)(p.num_splits - 1);
     __syncthreads();
-    if (!is_last) return;
+    if (!is_last) return false;
     const int wave = threadIdx.x >> 6;
     for (int i = wave; i < G; i += NWAVES) fold_row<D>(p, out_row(p, b, h, i));
     if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
   }
+  return false;
 }
+
+// Per-workgroup timestamps (timestamp instances only).  Thread 0 writes
+// stamps[4 * workgroup + k]: k = 0 the kernel's start, 1 the split's states
+// stored (just before the arrival protocol), 2 the end (after any fold), from
+// the constant-rate counter read by s_memrealtime; k = 3 the XCC_ID register
+// (bits 0..3), the HW_ID register (bits 8..39) and bit 63 set when the
+// workgroup folded.  Product instances compile all of it out.
+template <int INSTR>
+struct WgStamps {
+  const SplitParams& p;
+  bool folded = false;
+  // The start and states-stored times wait in LDS, so no register holds them
+  // through the kernel (and no global store precedes the metadata reads).
+  __device__ static uint64_t* slots() {
+    __shared__ uint64_t t[2];
+    return t;
+  }
+  __device__ explicit WgStamps(const SplitParams& pp) : p(pp) {
+    if constexpr (INSTR == kInstrStamps) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      if (threadIdx.x == 0) slots()[0] = t0;
+    }
+  }
+  __device__ void states_stored() {
+    if constexpr (INSTR == kInstrStamps) {
+      const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+      if (threadIdx.x == 0) slots()[1] = t1;
+    }
+  }
+  __device__ ~WgStamps() {
+    if constexpr (INSTR == kInstrStamps) {
+      const uint64_t t2 = __builtin_amdgcn_s_memrealtime();
+      if (threadIdx.x == 0) {
+        // s_getreg operands: (size - 1) << 11 | offset << 6 | register id
+        const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xfu;   // XCC_ID
+        const uint32_t hw = (uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 4);          // HW_ID
+        uint64_t* st = p.stamps + 4 * (uint64_t)blockIdx.x;
+        st[0] = slots()[0];
+        st[1] = slots()[1];
+        st[2] = t2;
+        st[3] = (uint64_t)xcc | ((uint64_t)hw << 8) | ((uint64_t)folded << 63);
+      }
+    }
+  }
+};
 
 }  // namespace da

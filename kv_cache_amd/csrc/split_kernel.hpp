@@ -43,8 +43,8 @@ struct RawRow {
 };
 
 // Loads this lane's slice of the K and V rows of visible ordinal o (position
-// t).  TRACE: lane `rec` also records the row loads (trace instances only).
-template <int FMT, int D, bool PAGED, bool TRACE>
+// t).  kInstrRows: lane `rec` also records the row loads (trace instances only).
+template <int FMT, int D, bool PAGED, int INSTR>
 __device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra, int b, int h, int o, int t,
                                          int n_q, int col0, bool rec, RawRow& raw) {
   constexpr int EB = FMT == DA_KV_F32 ? 4 : FMT == DA_KV_BF16 ? 2 : 1;
@@ -53,7 +53,7 @@ __device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra
     raw.k = stream_load(reinterpret_cast<const uint4*>(static_cast<const char*>(p.k) + off * EB));
     raw.v = stream_load(reinterpret_cast<const uint4*>(static_cast<const char*>(p.v) + off * EB));
     raw.region = 0;
-    if (TRACE && rec) {
+    if (INSTR == kInstrRows && rec) {
       trace_k(p, b, h, o, t, off - col0);
       trace_v(p, b, h, o, off - col0);
     }
@@ -71,7 +71,7 @@ __device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra
       raw.ks = *reinterpret_cast<const uint4*>(p.k_scale + soff);
       raw.vs = p.v_scale[vsoff];
       raw.region = 0;
-      if (TRACE && rec) {
+      if (INSTR == kInstrRows && rec) {
         trace_k(p, b, h, o, t, off - col0, soff - col0);
         trace_v(p, b, h, o, off - col0, vsoff);
       }
@@ -80,7 +80,7 @@ __device__ __forceinline__ void load_row(const SplitParams& p, const RowAddr& ra
       raw.k = stream_load(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k_resid) + off));
       raw.v = stream_load(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v_resid) + off));
       raw.region = 1;
-      if (TRACE && rec) {
+      if (INSTR == kInstrRows && rec) {
         trace_k(p, b, h, o, t, off - col0);
         trace_v(p, b, h, o, off - col0);
       }
@@ -130,9 +130,9 @@ __device__ __forceinline__ float decode_v(const RawRow& raw, float* x) {
   }
 }
 
-// TRACE: the index-trace instance, which also records each row load where it
-// is issued; otherwise identical.
-template <int FMT, int D, int G, bool PAGED, int NWAVES, int U, bool FUSED, bool TRACE = false>
+// INSTR: kInstrRows is the index-trace instance, which also records each row
+// load where it is issued; otherwise identical (no timestamp instance).
+template <int FMT, int D, int G, bool PAGED, int NWAVES, int U, bool FUSED, int INSTR = 0>
 __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
   constexpr int EPL = KvTraits<FMT>::EPL;
   constexpr int LPR = D / EPL;           // lanes per row
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NWAVES * 64) void split_kernel(SplitParams p) {
       rr[j].ks = make_uint4(0u, 0u, 0u, 0u);
       rr[j].vs = 0u;
       rr[j].region = 0;
-      if (rr[j].valid) load_row<FMT, D, PAGED, TRACE>(p, ra, b, h, o, vis_pos(vis, o), n_q, col0, cg == 0, rr[j]);
+      if (rr[j].valid) load_row<FMT, D, PAGED, INSTR>(p, ra, b, h, o, vis_pos(vis, o), n_q, col0, cg == 0, rr[j]);
     }
   };
 

@@ -81,14 +81,16 @@ template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 
 // (the host's default item count uses the same figure).
 constexpr int kPartitionWgPerCu = 3;
 
-// TRACE: the index-trace instance, which also records each row load where it
-// is issued (trace_k / trace_v); otherwise identical.
-template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM, bool PART = false, bool TRACE = false>
+// INSTR: kInstrRows is the index-trace instance, which also records each row
+// load where it is issued (trace_k / trace_v); kInstrStamps records
+// per-workgroup timestamps; otherwise identical.
+template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM, bool PART = false, int INSTR = 0>
 __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
   static_assert(G >= 1 && G <= 16, "");
 
+  WgStamps<INSTR> stamps(p);
   const PartitionHeaderAtExit header_at_exit{p};
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     const uint16_t* row = kb + (uint64_t)ri * row_stride;
 #pragma unroll
     for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
-    if constexpr (TRACE) {
+    if constexpr (INSTR == kInstrRows) {
       if (kg == 0 && tl + n >= begin && tl + n < end)
         trace_k(p, b, h, tl + n, vis_pos(vis, tl + n), hb + (int64_t)((uint64_t)ri * row_stride));
     }
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     for (int j = 0; j < 4; ++j) {
       const uint32_t rj = (uint32_t)__shfl((int)ri, 4 * kg + j);
       v[j] = stream_load(reinterpret_cast<const uint4*>(vb + (uint64_t)rj * row_stride));
-      if constexpr (TRACE) {
+      if constexpr (INSTR == kInstrRows) {
         const int o = tl + 4 * kg + j;
         if (n == 0 && o >= begin && o < end) trace_v(p, b, h, o, hb + (int64_t)((uint64_t)rj * row_stride));
       }
@@ -259,14 +261,14 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (tile + 4 * kg + j >= end) t.v[j] = make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (TRACE) {
+        if constexpr (INSTR == kInstrRows) {
           // tile == s*chunk + wave*16 here, the first row of the loads above
           const int o = tile + 4 * kg + j;
           const uint32_t rj = (uint32_t)min(o, p.kv_capacity - 1);
           if (n == 0 && o < end) trace_v(p, b, h, o, hb + (int64_t)((uint64_t)rj * row_stride));
         }
       }
-      if constexpr (TRACE) {
+      if constexpr (INSTR == kInstrRows) {
         const uint32_t rk = (uint32_t)min(tile + n, p.kv_capacity - 1);
         if (kg == 0 && tile + n < end)
           trace_k(p, b, h, tile + n, vis_pos(vis, tile + n), hb + (int64_t)((uint64_t)rk * row_stride));
@@ -403,7 +405,8 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   }
   __syncthreads();
   merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
-  finish_split<G, D, NWAVES, FUSED>(p, b, h);
+  stamps.states_stored();
+  stamps.folded = finish_split<G, D, NWAVES, FUSED>(p, b, h);
   };
 
   if constexpr (!PART) {

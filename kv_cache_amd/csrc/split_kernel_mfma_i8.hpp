@@ -77,7 +77,8 @@ __device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
 }
 
-// Largest magnitude bit pattern (sign cleared) of the eight fp16 values in x.
+// Largest magnitude bit pattern (sign cleared) of the eight 16-bit floats
+// (fp16 or bf16: ordering by magnitude is ordering of these bits) in x.
 __device__ __forceinline__ uint32_t f16_absmax_bits(uint4 x) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
   uint32_t m = 0;
@@ -94,10 +95,20 @@ __device__ __forceinline__ uint4 f16_scale_pow2(uint4 x, int e) {
     r[i] = pack_f16(ldexpf(f16_bits_to_f32(w[i] & 0xffffu), -e), ldexpf(f16_bits_to_f32(w[i] >> 16), -e));
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
+// Wave-wide maximum (wave-uniform result): DPP inside each 16-lane row, then
+// the four row maxima read into scalar registers.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
-  return x;
+  x = max(x, dpp_u32<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = max(x, dpp_u32<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = max(x, dpp_u32<0x141>(x));   // row_half_mirror
+  x = max(x, dpp_u32<0x140>(x));   // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
 }
 // floor(log2 x) of a normal fp16 magnitude bit pattern (subnormals: -14)
 __device__ __forceinline__ int f16_exponent(uint32_t bits) { return max((int)(bits >> 10), 1) - 15; }
@@ -112,15 +123,17 @@ __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) { return (ui
 constexpr int kI8ScaleSlots = 24;
 
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
-// TRACE: the index-trace instance, which also records each row load (codes,
-// scales, residual rows) where it is issued; otherwise identical.
-template <int G, int NWAVES, bool FUSED, bool TRACE = false>
+// INSTR: kInstrRows is the index-trace instance, which also records each row
+// load (codes, scales, residual rows) where it is issued; kInstrStamps
+// records per-workgroup timestamps; otherwise identical.
+template <int G, int NWAVES, bool FUSED, int INSTR = 0>
 __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma_i8(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
   constexpr int STEP = NWAVES * TW;
   static_assert(G >= 1 && G <= 16, "");
 
+  WgStamps<INSTR> stamps(p);
   int b, h, s;
   const PartitionHeaderAtExit header_at_exit{p};
   decode_workgroup(p, &b, &h, &s);
@@ -155,7 +168,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const int lim_n = row_limit(p, vis.n_vis, n);
   if (begin >= end) {
     write_identity<G, D, NWAVES, FUSED>(p, b, h, s);
-    finish_split<G, D, NWAVES, FUSED>(p, b, h);
+    stamps.states_stored();
+    stamps.folded = finish_split<G, D, NWAVES, FUSED>(p, b, h);
     return;
   }
   const int mid = min(max(o_res, begin), end);
@@ -177,12 +191,17 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   float l_run = 0.f;         // partial denominator over rows 4kg .. 4kg+3 of every tile
   // fp16 range of the int8 part's matrix-core operands.  Each operand is
   // brought into range by a power of two that the scores or the weights undo
-  // exactly: q per head (largest |q| in [2^14, 2^15)), the K scale rows of a
-  // phase (largest in [2^8, 2^9), so code * scale < 2^16), the V scales of a
-  // phase (largest in [2^14, 2^15), so weight * scale < 2^15).  Scores are
-  // acc * sfac with sfac = scale * log2(e) * 2^(e_q + e_k); the weights
-  // p * sigma_V enter PV times vinv = 2^-e_v (the denominator takes p), so o
-  // holds u * 2^-e_v and is multiplied by vpow = 2^e_v at the end.
+  // exactly, per wave and per phase of the split, where it needs it:
+  //  * q per head, when its largest |q| is below 2^-4 or 2^15 or more: into
+  //    [2^14, 2^15) (q * 2^-e_q);
+  //  * the phase's K scale rows, when their largest scale is 2^9 or more:
+  //    into [2^8, 2^9) (times 2^-e_k), so code * scale < 2^16;
+  //  * the V scales of the wave's rows of the phase, when their largest is
+  //    below 2^-3: into [2^14, 2^15) (times 2^-e_v), so small scales do not
+  //    fall to fp16 subnormals (weight * scale never exceeds the scale).
+  // Scores are acc * sfac with sfac = scale * log2(e) * 2^(e_q + e_k); the
+  // weights p * sigma_V enter PV times vinv = 2^-e_v (the denominator takes
+  // p), so o holds u * 2^-e_v and is multiplied by vpow = 2^e_v at the end.
   float sfac = p.qscale;
   int e_v = 0;
   float vpow = 1.f, vinv = 1.f;
@@ -227,31 +246,27 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   // tile in flight holds only codes and V scales and each wave keeps two
   // tiles in flight.  A split is one phase per run unless it is long.
   auto kch = [&](int c) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1); };
-  __shared__ uint4 ksc[kI8ScaleSlots][16];
+  __shared__ uint4 ksc[NWAVES][kI8ScaleSlots][16];   // one scale table per wave
   if (begin < mid) {
     // q in this part's channel order, read from the staged rows: channels
     // kch(c) .. +7 of head n are 8-channel block kch(c)/8 = 4c' + kg', held by
     // lane n + 16kg' of q_lds[c'] (zero for n >= G).
-    // Head n's channels are spread over the lanes n + 16kg; its largest |q|
-    // (bf16 bit pattern) sets e_q, and q * 2^-e_q (exact in fp16 down to
-    // 2^-28 of the largest) feeds the matrix cores.
-    uint4 qx[4];
+    // Head n's largest |q| (bf16 bit pattern, read by each of its lanes from
+    // all 16 staged blocks, so the four lanes of a head agree) sets e_q, and
+    // q * 2^-e_q (exact in fp16 down to 2^-28 of the largest) feeds the
+    // matrix cores.
     uint32_t qmx = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int blk = kch(c) >> 3;
-      qx[c] = q_lds[blk >> 2][n + 16 * (blk & 3)];
-      const uint32_t w[4] = {qx[c].x, qx[c].y, qx[c].z, qx[c].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qmx = max(qmx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
-    }
-    qmx = max(qmx, (uint32_t)__shfl_xor((int)qmx, 16));
-    qmx = max(qmx, (uint32_t)__shfl_xor((int)qmx, 32));
-    const int e_q = qmx ? min(max((int)(qmx >> 7) - 127 - 14, -100), 100) : 0;
+    for (int blk = 0; blk < 16; ++blk) qmx = max(qmx, f16_absmax_bits(q_lds[blk >> 2][n + 16 * (blk & 3)]));
+    // (bf16 exponent of the largest |q|; q of magnitude in [2^-4, 2^15) is
+    // used as it is)
+    const int eq_max = (int)(qmx >> 7) - 127;
+    const int e_q = (qmx == 0 || (eq_max >= -4 && eq_max < 15)) ? 0 : min(max(eq_max - 14, -100), 100);
     uint4 qh[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 x = qx[c];
+      const int blk = kch(c) >> 3;
+      const uint4 x = q_lds[blk >> 2][n + 16 * (blk & 3)];
       auto cv = [&](uint32_t wd) {
         return pack_f16(ldexpf(bf16_lo(wd), -e_q), ldexpf(bf16_hi(wd), -e_q));
       };
@@ -266,7 +281,6 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     // (slots - 1) groups' length touches at most `slots` scale rows.
     const int phase = min((kI8ScaleSlots - 1) << sh, 2048);
     const uint32_t vs_stride = 2 * (uint32_t)p.num_kv_heads;   // V scale bytes per position
-    __shared__ uint32_t smax[NWAVES][2];   // per-wave largest K and V scale of a phase
     for (int run = 0; run < 2; ++run) {
       const int rb = run == 0 ? begin : max(begin, vis.ns);
       const int re = run == 0 ? min(mid, vis.ns) : mid;
@@ -287,7 +301,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
           const uint32_t off = mul_u24(rel(tile + n), row_stride) + 16 * kg;
           k[0] = stream_load(reinterpret_cast<const uint4*>(kp + off));
           k[1] = stream_load(reinterpret_cast<const uint4*>(kp + off + 64));
-          if constexpr (TRACE) {
+          if constexpr (INSTR == kInstrRows) {
             // the row's codes, and the scale row its dequantization reads
             // (staged from k_scale row g0 + slot)
             if (kg == 0 && tile + n < pe)
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
             const uint32_t r = rel(tile + 4 * kg + j);
             v[j] = stream_load(reinterpret_cast<const uint2*>(vp + (mul_u24(r, row_stride) + 8 * (uint32_t)n)));
             sv[j] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
-            if constexpr (TRACE) {
+            if constexpr (INSTR == kInstrRows) {
               if (n == 0 && tile + 4 * kg + j < pe)
                 trace_v(p, b, h, tile + 4 * kg + j, code_base + (int64_t)t_pb * row_stride + mul_u24(r, row_stride),
                         vs_base + (int64_t)t_pb * p.num_kv_heads + mul_u24(r, vs_stride) / 2);
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
             const uint4 w = k[c >> 1];
             const uint2 codes = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
             uint4 hi, lo;
-            dequant_f16(codes, ksc[sl][kch(c) >> 3], hi, lo);
+            dequant_f16(codes, ksc[wave][sl][kch(c) >> 3], hi, lo);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hi),
                                                          __builtin_bit_cast(f16x8_t, qh[c]), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, lo),
@@ -362,59 +376,71 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
             for (int c = 0; c < 8; ++c) o[c][i] *= a;
           }
         };
+        // Phase start, per wave (no workgroup barrier): the wave stages its own
+        // copy of the phase's K scale rows and finds the largest K scale of
+        // the phase and the largest V scale of its own rows, which set its
+        // e_k and e_v (see above).  The scale loads are issued first and the
+        // first tiles after them (addresses clamped into the phase, so all
+        // loads are unconditional), so the scales, returned first, are reduced
+        // and staged while the tiles are in flight.  Duplicates from clamping
+        // change no maximum.
+        // K scale quads idx = lane + 64k of the phase's rows (two requested
+        // here, clamped; longer phases fetch the rest below)
+        uint4 kq0, kq1;
+        {
+          const int i0 = min(lane, ng * 16 - 1), i1 = min(lane + 64, ng * 16 - 1);
+          kq0 = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (i0 >> 4)) * row_stride + 8 * (i0 & 15));
+          kq1 = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (i1 >> 4)) * row_stride + 8 * (i1 & 15));
+        }
+        // this wave's rows: tiles pb + 16*wave + 64k, 16 rows each; lane l
+        // takes row 16*wave + 64*(4j + l/16) + l%16 of the phase for load j
+        uint32_t vsv[8];
+#pragma unroll
+        for (int j8 = 0; j8 < 8; ++j8) {
+          const uint32_t r = min((uint32_t)(16 * wave + 64 * (4 * j8 + (lane >> 4)) + (lane & 15)), last);
+          vsv[j8] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
+        }
         uint4 ka[2], kb[2];
         uint2 va[4], vb[4];
         uint32_t sva[4], svb[4];
         int tile = pb + wave * TW;
         // the loop's request order (K, K, V, V), so its waits leave newer requests in flight
-        if (tile < pe) {
-          issue_k(tile, ka);
-          issue_k(tile + STEP, kb);
-          issue_v(tile, va, sva);
-          issue_v(tile + STEP, vb, svb);
+        issue_k(tile, ka);
+        issue_k(tile + STEP, kb);
+        issue_v(tile, va, sva);
+        issue_v(tile + STEP, vb, svb);
+        uint32_t kmx = max(f16_absmax_bits(kq0), f16_absmax_bits(kq1)), vmx = 0;
+        if (lane < ng * 16) ksc[wave][lane >> 4][lane & 15] = kq0;
+        if (lane + 64 < ng * 16) ksc[wave][(lane + 64) >> 4][lane & 15] = kq1;
+        for (int idx = lane + 128; idx < ng * 16; idx += 64) {
+          const uint4 x = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
+          kmx = max(kmx, f16_absmax_bits(x));
+          ksc[wave][idx >> 4][idx & 15] = x;
         }
-        // The scale table is staged after the first tiles are requested, so its
-        // latency overlaps theirs instead of preceding it.  The phase's
-        // largest K and V scales set e_k and e_v (see above); the K scale rows
-        // are stored times 2^-e_k.
-        static_assert(kI8ScaleSlots * 16 <= 2 * NWAVES * 64, "two scale quads per thread");
-        uint4 kreg[2];
-        uint32_t kmx = 0, vmx = 0;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int idx = threadIdx.x + k2 * NWAVES * 64;
-          kreg[k2] = make_uint4(0u, 0u, 0u, 0u);
-          if (idx < ng * 16) {
-            kreg[k2] = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
-            kmx = max(kmx, f16_absmax_bits(kreg[k2]));
-          }
-        }
-        for (int r = threadIdx.x; r < pe - pb; r += NWAVES * 64)
-          vmx = max(vmx, (uint32_t)*reinterpret_cast<const uint16_t*>(vsp + mul_u24((uint32_t)r, vs_stride)) & 0x7fffu);
+        for (int j8 = 0; j8 < 8; ++j8) vmx = max(vmx, vsv[j8] & 0x7fffu);
         kmx = wave_max_u32(kmx);
         vmx = wave_max_u32(vmx);
-        if (lane == 0) {
-          smax[wave][0] = kmx;
-          smax[wave][1] = vmx;
+        // K rows are scaled only where code * scale could reach fp16's range
+        const int e_k = max(f16_exponent(kmx) - 8, 0);
+        // V scales of 2^-3 or more need no scaling: weights below fp16's
+        // normal range then carry at most 2^-10 of the output
+        const int e_v_new = f16_exponent(vmx) >= -3 ? 0 : f16_exponent(vmx) - 14;
+        // the wave reads its table only after all of its lanes have written it
+        auto wave_lds_sync = [] {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the table stores have completed
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        wave_lds_sync();
+        if (e_k > 0) {               // rare: the table times 2^-e_k, in place
+          for (int idx = lane; idx < ng * 16; idx += 64)
+            ksc[wave][idx >> 4][idx & 15] = f16_scale_pow2(ksc[wave][idx >> 4][idx & 15], e_k);
+          wave_lds_sync();
         }
-        __syncthreads();        // also: every wave has finished the previous phase's table
-        kmx = 0;
-        vmx = 0;
-#pragma unroll
-        for (int w8 = 0; w8 < NWAVES; ++w8) {
-          kmx = max(kmx, smax[w8][0]);
-          vmx = max(vmx, smax[w8][1]);
-        }
-        const int e_k = kmx ? f16_exponent(kmx) - 8 : 0;
-        const int e_v_new = vmx ? f16_exponent(vmx) - 14 : 0;
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int idx = threadIdx.x + k2 * NWAVES * 64;
-          if (idx < ng * 16) ksc[idx >> 4][idx & 15] = f16_scale_pow2(kreg[k2], e_k);
-        }
-        __syncthreads();
         sfac = ldexpf(p.qscale, e_q + e_k);
-        if (e_v_new != e_v) {        // o to the new phase's units (o is 0 before the first)
+        if (e_v_new != e_v) {        // o to the new units (o is 0 before the first phase)
           const float f = ldexpf(1.f, e_v - e_v_new);
 #pragma unroll
           for (int c = 0; c < 8; ++c) o[c] *= f;
@@ -474,7 +500,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
       const uint16_t* row = kr + (uint64_t)rrow(tile + n) * row_stride;
 #pragma unroll
       for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
-      if constexpr (TRACE) {
+      if constexpr (INSTR == kInstrRows) {
         if (kg == 0 && tile + n < end)
           trace_k(p, b, h, tile + n, vis_pos(vis, tile + n),
                   res_base + (int64_t)((uint64_t)rrow(tile + n) * row_stride));
@@ -484,7 +510,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[j] = stream_load(reinterpret_cast<const uint4*>(vr + (uint64_t)rrow(tile + 4 * kg + j) * row_stride));
-        if constexpr (TRACE) {
+        if constexpr (INSTR == kInstrRows) {
           if (n == 0 && tile + 4 * kg + j < end)
             trace_v(p, b, h, tile + 4 * kg + j,
                     res_base + (int64_t)((uint64_t)rrow(tile + 4 * kg + j) * row_stride));
@@ -542,7 +568,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   }
   __syncthreads();
   merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
-  finish_split<G, D, NWAVES, FUSED>(p, b, h);
+  stamps.states_stored();
+  stamps.folded = finish_split<G, D, NWAVES, FUSED>(p, b, h);
 }
 
 }  // namespace da

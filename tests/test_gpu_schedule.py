@@ -47,5 +47,8 @@ def test_schedule_int8_sink_window():
 
 def test_schedule_trace_indices_unchanged():
     w = synth.make_paged(23, 4, 8, 2, 128, [700, 33, 0, 1500], page_size=16)
-    (o1, p1, _), (o2, p2, _) = _pair(w, H.trace, 6)
-    assert np.array_equal(o1, o2) and np.array_equal(p1, p2)
+    (t1, _, O1, L1), (t2, _, O2, L2) = _pair(w, H.trace, 6)
+    assert t1.keys() == t2.keys()
+    for key in t1:
+        assert np.array_equal(t1[key], t2[key]), key
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
