@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
+SETTLE_S = 0.25          # untimed calls before every timed region (GPU clock ramp)
 PROFILES = os.path.join(ROOT, "profiles")
 # every source that decides what the timed kernels do (the split count too)
 KERNEL_SOURCES = ["kv_cache_amd/csrc/split_kernel_mfma.hpp", "kv_cache_amd/csrc/split_kernel_mfma_i8.hpp",
@@ -334,8 +335,24 @@ class GpuWorkload:
         self.ka.decode_attn_forward(self.plan, self.args[i % self.nsets], self.out, self.lse,
                                     self.stream)
 
+    def settle(self, fn, seconds=SETTLE_S):
+        """Untimed calls for `seconds` of wall time.  After the GPU has idled
+        (allocation, host work, the oracle) its clocks need several
+        milliseconds of work to come back up: the first 200 calls of the
+        headline workload run about 6 % slower than the next 200.  Every timed
+        region therefore starts from steady state."""
+        torch = self.torch
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(50):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+
     def time(self, fn, steps, warmup):
         torch = self.torch
+        self.settle(fn)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -351,6 +368,7 @@ class GpuWorkload:
     def samples(self, fn, n, warmup):
         """Per-call event pairs for the sample statistics."""
         torch = self.torch
+        self.settle(fn)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -578,7 +596,9 @@ def pattern_probe(torch, w, steps=100, warmup=10, stamp_calls=20):
     pattern_kernel) on the headline workload's input sets, same grid and
     split length: the read ceiling of that access pattern on this machine, and
     its per-XCD completion (the median over calls of each XCD's last
-    workgroup end, from the start of the earliest)."""
+    workgroup end, counted from the earliest workgroup end).  Then the same
+    bytes read in address order (hbm_probe.hip read2_kernel): the ceiling of
+    one launch that reads them, whatever its pattern."""
     import ctypes
     import numpy as np
     L = ctypes.CDLL(os.path.join(ROOT, "kv_cache_amd", "libhbm_probe.so"))
@@ -614,9 +634,28 @@ def pattern_probe(torch, w, steps=100, warmup=10, stamp_calls=20):
         x = a[:, 1].astype(int)
         ends.append([float(e[x == k].max()) if (x == k).any() else 0.0 for k in range(8)])
     kv = 2 * w.B * T * w.Hkv * w.D * 2
+    # the same K and V bytes read in address order (grid-stride, 1024 workgroups)
+    L.hbm_probe_read2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                  ctypes.c_int, ctypes.c_void_p]
+    sink2 = torch.empty(1024, dtype=torch.int32, device="cuda")
+
+    def call2(i):
+        d = w.sets[i % w.nsets]
+        assert L.hbm_probe_read2(d["k"].data_ptr(), d["v"].data_ptr(), kv // 2, sink2.data_ptr(), 1024,
+                                 stream) == 0
+    for i in range(warmup):
+        call2(i)
+    e0.record()
+    for i in range(steps):
+        call2(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us2 = e0.elapsed_time(e1) / steps * 1000
     return {"us_per_launch": round(us, 2), "GBs": round(kv / (us * 1e-6) / 1e9, 1), "bytes": kv,
             "grid": grid, "chunk": w.plan.chunk,
-            "xcd_last_end_spread_us_median": [round(float(np.median([c[k] for c in ends])), 2) for k in range(8)]}
+            "xcd_last_end_spread_us_median": [round(float(np.median([c[k] for c in ends])), 2) for k in range(8)],
+            "contiguous_read": {"us_per_launch": round(us2, 2), "GBs": round(kv / (us2 * 1e-6) / 1e9, 1),
+                                "grid": 1024}}
 
 
 def host_info():

@@ -39,9 +39,12 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
 // (b, h, s) of a [B, T, H, row] cache (row = 256 bytes per token and head, two
 // buffers K and V) reads rows [s*chunk, min((s+1)*chunk, T)) of head h, the
 // split index rotated by (b, h) as the decode kernel does; each wave takes
-// 16-row tiles round-robin, lane l reading 16 bytes of row l % 16 at 16-byte
-// column l / 16 (K) and the matching V bytes.  With `stamps`, thread 0 writes
-// the workgroup's end time (s_memrealtime) and XCC_ID.
+// 16-row tiles round-robin.  Per tile, lane (n = l%16, g = l/16) reads, like
+// the matrix-core kernel: K 16 bytes of row n at byte 64c + 16g for c = 0..3
+// (each instruction: 16 rows x 64 bytes, plain loads), V 16 bytes of row
+// 4g + j at byte 16n for j = 0..3 (each instruction: 4 whole rows,
+// non-temporal).  With `stamps`, thread 0 writes the workgroup's end time
+// (s_memrealtime) and XCC_ID.
 __global__ __launch_bounds__(256) void pattern_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                       int B, int T, int H, int S, int chunk,
                                                       uint32_t* __restrict__ sink, uint64_t* __restrict__ stamps) {
@@ -50,18 +53,18 @@ __global__ __launch_bounds__(256) void pattern_kernel(const uint4* __restrict__ 
   const int s = (wg - bh * S + bh) % S;
   const int h = bh % H, b = bh / H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, c = lane >> 4;
+  const int n = lane & 15, g = lane >> 4;
   const int begin = min(s * chunk, T), end = min(begin + chunk, T);
   // 16-byte words: row (b, t, h) starts at ((b*T + t)*H + h)*16, 16 words per row
   const size_t base = ((size_t)b * T * H + h) * 16;
   uint32_t acc = 0;
   for (int t = begin + wave * 16; t < end; t += 64) {
-    const int row = min(t + r, end - 1);
-    const size_t off = base + (size_t)row * H * 16;
+    const size_t koff = base + (size_t)min(t + n, end - 1) * H * 16 + g;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k + off + 4 * q + c));
-      const u32x4_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v + off + 4 * q + c));
+    for (int c = 0; c < 4; ++c) {
+      const uint4 x = k[koff + 4 * c];
+      const size_t voff = base + (size_t)min(t + 4 * g + c, end - 1) * H * 16 + n;
+      const u32x4_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v + voff));
       acc ^= x.x ^ x.w ^ y.y ^ y.z;
     }
   }
@@ -79,6 +82,28 @@ __global__ __launch_bounds__(256) void pattern_kernel(const uint4* __restrict__ 
   }
 }
 
+// Contiguous streaming read of two buffers of n16 16-byte words each (the
+// same K and V bytes as a decode call, in address order): the read ceiling
+// of those bytes in one launch, whatever the access pattern.
+__global__ __launch_bounds__(256) void read2_kernel(const uint4* __restrict__ a, const uint4* __restrict__ b,
+                                                    size_t n16, uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a + i));
+    const u32x4_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b + i));
+    acc ^= x.x ^ x.w ^ y.y ^ y.z;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < 256; ++i) t ^= red[i];
+    sink[blockIdx.x] = t;
+  }
+}
+
 }  // namespace
 
 // K and V [B, T, H, 128] bf16 (256-byte rows); grid B*H*S workgroups; sink
@@ -89,6 +114,16 @@ extern "C" int hbm_probe_pattern(const void* k, const void* v, int B, int T, int
   if ((reinterpret_cast<uintptr_t>(k) & 15u) || (reinterpret_cast<uintptr_t>(v) & 15u)) return -1;
   hipLaunchKernelGGL(pattern_kernel, dim3((unsigned)(B * H * S)), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(k), static_cast<const uint4*>(v), B, T, H, S, chunk, sink, stamps);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Two buffers of bytes_each (a multiple of 16) bytes; sink holds `grid` uint32 values.
+extern "C" int hbm_probe_read2(const void* a, const void* b, uint64_t bytes_each, uint32_t* sink, int grid,
+                               void* stream) {
+  if (!a || !b || !sink || grid <= 0 || (bytes_each & 15u)) return -1;
+  if ((reinterpret_cast<uintptr_t>(a) & 15u) || (reinterpret_cast<uintptr_t>(b) & 15u)) return -1;
+  hipLaunchKernelGGL(read2_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(a), static_cast<const uint4*>(b), (size_t)(bytes_each / 16), sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -7,31 +7,41 @@
 
 namespace da {
 
-// K/V rows are read exactly once per call: the loads carry the non-temporal
-// hint so they do not displace lines that are reused (q, block table, scales).
+// K/V rows are read exactly once per call.  Loads whose lanes cover whole
+// 128-byte lines carry the non-temporal hint (they stream past the caches);
+// loads that take half lines (a tile's 16 rows at 64 bytes each, the other
+// half following in the next instruction) are plain, so the second half
+// finds the line the first one brought in.
 #ifndef DA_NT_LOADS
 #define DA_NT_LOADS 1
+#endif
+#ifndef DA_K_NT
+#define DA_K_NT 0
 #endif
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+template <bool NT = true>
 __device__ __forceinline__ uint4 stream_load(const uint4* p) {
-#if DA_NT_LOADS
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *p;
-#endif
+  if constexpr (NT && DA_NT_LOADS) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
 }
 
+template <bool NT = true>
 __device__ __forceinline__ uint2 stream_load(const uint2* p) {
-#if DA_NT_LOADS
-  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-  return make_uint2(v.x, v.y);
-#else
-  return *p;
-#endif
+  if constexpr (NT && DA_NT_LOADS) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *p;
+  }
 }
+// the half-line K loads of the matrix-core kernels
+constexpr bool kHalfLineNT = DA_K_NT != 0;
 
 // The empty identity (m = -inf, l = 0, u = 0) for the G query heads of an
 // empty split ("M4.5 - Decode Attention Kernels, Mask Programs, and Backend

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       const int cap = p.kv_capacity;
       const uint16_t* row = kb + (uint64_t)(uint32_t)min(t0 + n, cap - 1) * row_stride;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) t.k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
+      for (int c = 0; c < 4; ++c) t.k[c] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(row + 32 * c));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t rj = (uint32_t)min(t0 + 4 * kg + j, cap - 1);
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   auto issue_k = [&](int tl, uint32_t ri, uint4 (&k)[4]) {
     const uint16_t* row = kb + (uint64_t)ri * row_stride;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
+    for (int c = 0; c < 4; ++c) k[c] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(row + 32 * c));
     if constexpr (INSTR == kInstrRows) {
       if (kg == 0 && tl + n >= begin && tl + n < end)
         trace_k(p, b, h, tl + n, vis_pos(vis, tl + n), hb + (int64_t)((uint64_t)ri * row_stride));

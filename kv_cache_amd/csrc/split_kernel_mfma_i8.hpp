@@ -299,8 +299,8 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
         auto slot = [&](int tile) { return (int)((t_pb + rel(tile + n)) >> sh) - g0; };
         auto issue_k = [&](int tile, uint4 (&k)[2]) {
           const uint32_t off = mul_u24(rel(tile + n), row_stride) + 16 * kg;
-          k[0] = stream_load(reinterpret_cast<const uint4*>(kp + off));
-          k[1] = stream_load(reinterpret_cast<const uint4*>(kp + off + 64));
+          k[0] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(kp + off));
+          k[1] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(kp + off + 64));
           if constexpr (INSTR == kInstrRows) {
             // the row's codes, and the scale row its dequantization reads
             // (staged from k_scale row g0 + slot)
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
     auto issue_k = [&](int tile, uint4 (&k)[4]) {
       const uint16_t* row = kr + (uint64_t)rrow(tile + n) * row_stride;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) k[c] = stream_load(reinterpret_cast<const uint4*>(row + 32 * c));
+      for (int c = 0; c < 4; ++c) k[c] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(row + 32 * c));
       if constexpr (INSTR == kInstrRows) {
         if (kg == 0 && tile + n < end)
           trace_k(p, b, h, tile + n, vis_pos(vis, tile + n),
