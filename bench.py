@@ -511,12 +511,30 @@ def other_workload(torch, ka, name, steps=30, warmup=5, oracle_runs=0):
         r = w.report("fm", layer + " contiguous, FlashMask column intervals (seeded runs of closed "
                              "documents, visible blocks and scattered hidden keys)", steps, warmup)
         r["visible_kv_bytes"] = w.kv_bytes
+        r["nonskip_tile_kv_bytes"] = flashmask_loaded_bytes(w)
         return r
     if name == "tiny_fp32":
         w = GpuWorkload(torch, ka, "contig", 1, 4, 4, 64, [256], num_splits=4, seed=4, dtype="f32")
         return _with_oracle(w, w.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4", steps,
                                         warmup), oracle_runs, single_thread=True)
     raise ValueError(name)
+
+
+def flashmask_loaded_bytes(w):
+    """K and V bytes of the rows the kernel loads under FlashMask: the rows
+    (< T_b) of every 16-key tile its block summary does not mark SKIP for the
+    decode row q = T_b - 1 (all columns hidden by one interval family: q at or
+    past the family's largest start and before its smallest end)."""
+    import numpy as np
+    sm = w.mask_sum.cpu().numpy()          # [B, nblk, 2, 4]: per family (start min, max, end min, max)
+    rows = 0
+    for b, T in enumerate(w.lens):
+        q = T - 1
+        for j in range((T + 15) // 16):
+            skip = any(q >= sm[b, j, f, 1] and q + 1 <= sm[b, j, f, 2] for f in range(2))
+            if not skip:
+                rows += min(16, T - 16 * j)
+    return rows * w.Hkv * w.D * 2 * 2
 
 
 def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, steps=50):
@@ -990,6 +1008,10 @@ def main():
                                              oracle_runs=ORACLE_RUNS["tiny_fp32"] if cpu else 0)
         for name in ("few_query_c2", "hnd_layout", "flashmask"):
             others[name] = other_workload(torch, ka, name)
+        fmr = others["flashmask"]
+        # the loaded tiles' bytes at the causal headline's achieved rate: what
+        # the masked call would take if SKIP tiles cost nothing
+        fmr["us_at_headline_rate"] = round(fmr["nonskip_tile_kv_bytes"] / (value * 1e3), 2)
         for name, r in others.items():
             if "oracle" in r:
                 per_config[name] = r.pop("oracle")

@@ -101,7 +101,10 @@ typedef int32_t da_status;
                                   hidden when q = T-1 lies in [UTS_t, UTE_t) or [LTS_t, LTE_t)
                                   (da_args mask_intervals); 16-key tiles are classified SKIP /
                                   FULL / PARTIAL from mask_summary and SKIP tiles are never
-                                  loaded.  bf16 K/V, head_dim 128, one query row.             */
+                                  loaded; splits share the non-SKIP tiles evenly.  bf16 K/V,
+                                  head_dim 128, one query row, max_seq_len <=
+                                  DA_FLASHMASK_MAX_SEQ.                                       */
+#define DA_FLASHMASK_MAX_SEQ 131072
 
 /* admission reason bits (DA_ERR_UNSUPPORTED) */
 #define DA_R_HEAD_DIM    (1ull << 0)   /* head_dim_qk not in {64, 128}                 */

@@ -124,6 +124,7 @@ __device__ __forceinline__ VisProgram make_vis(int T, int kind, int n_sink, int 
 // ---------------------------------------------------------------------------
 constexpr int kMaskBlock = 16;
 enum { kTileSkip = 0, kTileFull = 1, kTilePartial = 2 };
+constexpr int kFmMaxTiles = DA_FLASHMASK_MAX_SEQ / kMaskBlock;   // tiles a request may have under FlashMask
 
 __device__ __forceinline__ bool fm_hidden(const int4& iv, int q) {
   return (iv.x <= q && q < iv.y) || (iv.z <= q && q < iv.w);
@@ -134,14 +135,18 @@ __device__ __forceinline__ int fm_family(int q, int s_min, int s_max, int e_min,
   if (q + 1 > s_min && q < e_max) return 1;
   return 2;
 }
-__device__ __forceinline__ int fm_tile_class(const SplitParams& p, int b, int q, int tile) {
-  const int4* sm = p.mask_sum + ((int64_t)b * p.n_mask_blocks + tile / kMaskBlock) * 2;
-  const int4 u = sm[0], l = sm[1];      // (UTS min, max, UTE min, max), (LTS ..., LTE ...)
+// class of a tile from its block summary (u, l) = (UTS min, max, UTE min, max),
+// (LTS ..., LTE ...) for decode row q
+__device__ __forceinline__ int fm_class(int q, const int4& u, const int4& l) {
   const int fu = fm_family(q, u.x, u.y, u.z, u.w);
   const int fl = fm_family(q, l.x, l.y, l.z, l.w);
   if (fu == 0 || fl == 0) return kTileSkip;
   if (fu == 2 && fl == 2) return kTileFull;
   return kTilePartial;
+}
+__device__ __forceinline__ int fm_tile_class(const SplitParams& p, int b, int q, int tile) {
+  const int4* sm = p.mask_sum + ((int64_t)b * p.n_mask_blocks + tile / kMaskBlock) * 2;
+  return fm_class(q, sm[0], sm[1]);
 }
 
 __device__ __forceinline__ int vis_pos(const VisProgram& v, int o) {

@@ -170,7 +170,8 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
       p.mask_kind != DA_MASK_FLASHMASK)
     reasons |= DA_R_MASK_KIND;
   if (p.mask_kind == DA_MASK_FLASHMASK &&
-      (p.kv_format != DA_KV_BF16 || p.head_dim_qk != 128 || p.num_queries != 1))
+      (p.kv_format != DA_KV_BF16 || p.head_dim_qk != 128 || p.num_queries != 1 ||
+       p.max_seq_len > DA_FLASHMASK_MAX_SEQ))
     reasons |= DA_R_MASK_KIND;
   if (p.num_splits > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;
 

@@ -30,6 +30,8 @@
 //    between lanes.
 #pragma once
 
+#include <type_traits>
+
 #include "split_common.hpp"
 
 namespace da {
@@ -81,6 +83,90 @@ template <int G> struct MfmaOccupancy { static constexpr int value = G <= 4 ? 4 
 // (the host's default item count uses the same figure).
 constexpr int kPartitionWgPerCu = 3;
 
+// FlashMask tile numbering ("M4.5 ...", sections 0x06C-0x06F: SKIP blocks
+// are never visited, and the work a split does should follow the blocks that
+// are not skipped, not the positions they cover).  The workgroup classifies
+// all of the request's 16-key tiles for the decode row from the block
+// summaries and numbers the non-SKIP ones in position order; split s takes
+// numbers [s*ct, (s+1)*ct) with ct = ceil(count / S), so the splits share the
+// tiles to load evenly whatever the mask hides, as the sink+window mask is
+// compiled into visible ordinals.  Every workgroup of the request derives the
+// same numbering, so the splits stay a disjoint exact cover of the non-SKIP
+// tiles.
+struct Empty {};
+template <int NWAVES>
+struct FmCompact {
+  static constexpr int kEntries = kFmMaxTiles / 64;   // 64 tiles per entry
+  uint64_t ns[kEntries];    // entry e: non-SKIP bits of tiles 64e .. 64e+63
+  uint64_t pa[kEntries];    // PARTIAL bits of the same tiles
+  int pre[kEntries];        // non-SKIP tiles before entry e
+  uint32_t list[64];        // the split's tiles in order: tile | PARTIAL << 31
+  int count;                // non-SKIP tiles of the request
+};
+
+// The summaries of tiles 64*wave + lane (this wave's entry of the first
+// pass), requested before the request length is known.
+struct FmFirst {
+  int4 u, l;
+};
+template <int NWAVES>
+__device__ __forceinline__ FmFirst fm_prefetch(const SplitParams& p, int b, int wave, int lane) {
+  if (p.n_mask_blocks <= 0) return FmFirst{};
+  const int t = min(64 * wave + lane, p.n_mask_blocks - 1);
+  const int4* sm = p.mask_sum + ((int64_t)b * p.n_mask_blocks + t) * 2;
+  return FmFirst{sm[0], sm[1]};
+}
+
+// Fills f.list with split s's tiles and returns how many there are (<= 64:
+// ct <= ceil(ceil(T/16) / S) <= plan chunk / 16).  Contains three workgroup
+// barriers: every wave calls it.
+template <int NWAVES>
+__device__ __forceinline__ int fm_compact(const SplitParams& p, int b, int q_row, int n_vis, int s,
+                                          const FmFirst& first, FmCompact<NWAVES>& f, int wave, int lane) {
+  const int nblk = min((n_vis + 15) / 16, kFmMaxTiles);   // the plan admits n_vis <= 16 * kFmMaxTiles
+  const int ne = (nblk + 63) / 64;
+  for (int e = wave; e < ne; e += NWAVES) {
+    const int t = 64 * e + lane;
+    int cls = kTileSkip;
+    if (t < nblk) cls = e == wave ? fm_class(q_row, first.u, first.l) : fm_tile_class(p, b, q_row, 16 * t);
+    const uint64_t ns = __ballot(cls != kTileSkip);
+    const uint64_t pa = __ballot(cls == kTilePartial);
+    if (lane == 0) {
+      f.ns[e] = ns;
+      f.pa[e] = pa;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int run = 0;     // exclusive prefix of the entries' counts, 64 entries per pass
+    for (int e0 = 0; e0 < ne; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < ne ? __popcll(f.ns[e]) : 0;
+      int x = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      if (e < ne) f.pre[e] = run + x - c;
+      run += __shfl(x, 63);
+    }
+    if (lane == 0) f.count = run;
+  }
+  __syncthreads();
+  const int total = f.count;
+  const int ct = (total + p.num_splits - 1) / p.num_splits;
+  const int j0 = min(s * ct, total), j1 = min(j0 + ct, total);
+  for (int e = wave; e < ne; e += NWAVES) {
+    const uint64_t ns = f.ns[e];
+    const int idx = f.pre[e] + __popcll(ns & ((1ull << lane) - 1));
+    if (((ns >> lane) & 1) && idx >= j0 && idx < j1 && idx - j0 < 64)
+      f.list[idx - j0] = (uint32_t)(64 * e + lane) | ((uint32_t)((f.pa[e] >> lane) & 1) << 31);
+  }
+  __syncthreads();
+  return min(j1 - j0, 64);
+}
+
 // INSTR: kInstrRows is the index-trace instance, which also records each row
 // load where it is issued (trace_k / trace_v); kInstrStamps records
 // per-workgroup timestamps; otherwise identical.
@@ -97,6 +183,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   const int n = lane & 15;     // K row of the tile / score column (head)
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
   __shared__ WaveStates<G, D, NWAVES> sh;
+  __shared__ std::conditional_t<FM, FmCompact<NWAVES>, Empty> fmc;
 
   // One piece of work: visible ordinals [pbeg, pend) of request b for K/V
   // head h, stored as split slot s.  pend < 0: the plan's split s.
@@ -144,10 +231,15 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     }
   }
 
+  FmFirst fm_first{};
+  if constexpr (FM) fm_first = fm_prefetch<NWAVES>(p, b, wave, lane);
   const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   int begin, end;
-  if (pend < 0) {
+  if (FM) {
+    begin = 0;            // the split's share is its tile list (below)
+    end = vis.n_vis;
+  } else if (pend < 0) {
     split_range(vis.n_vis, s, p.chunk, &begin, &end);
   } else {
     begin = min(pbeg, vis.n_vis);
@@ -213,40 +305,41 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   // current ones have arrived (PV then reads them from a copy) or, where
   // registers are short, once PV has read them.  The requests after the last tile repeat
   // row end-1 (already cached) and keep the loop free of branches.
-  // FlashMask: lane k classifies tile k of the split (a split has at most 64
-  // tiles of 16 keys); SKIP tiles are never loaded, PARTIAL tiles bring the
-  // interval vectors of their rows with their K rows.  The wave walks its
-  // tiles (k = wave mod NWAVES) that are not SKIP.
+  // FlashMask: the split's non-SKIP tiles come from fm_compact in position
+  // order; the wave walks entries wave, wave + NWAVES, ... of that list, its
+  // k-th tile held by lane k (read with v_readlane).  PARTIAL tiles bring the
+  // interval vectors of their rows with their K rows.
   const int q_row = vis.n_vis - 1;
-  uint64_t walk = 0, partial = 0;
-  if constexpr (FM) {
-    const int nt = (end - begin + TW - 1) / TW;
-    const int cls = lane < nt ? fm_tile_class(p, b, q_row, begin + TW * lane) : kTileSkip;
-    uint64_t every = 0;
-    for (int k = wave; k < 64; k += NWAVES) every |= 1ull << k;
-    walk = __ballot(cls != kTileSkip) & every;
-    partial = __ballot(cls == kTilePartial);
-  }
   const int past = end + NWAVES * TW * 2;     // any ordinal >= end: row_index clamps it
+  int n_mine = 0, kc = 0;                     // FlashMask: the wave's tiles, index of the current one
+  uint32_t mine = 0;                          // lane k: the wave's k-th list entry
+  if constexpr (FM) {
+    const int n_list = fm_compact<NWAVES>(p, b, q_row, vis.n_vis, s, fm_first, fmc, wave, lane);
+    n_mine = n_list > wave ? (n_list - wave + NWAVES - 1) / NWAVES : 0;   // <= 16
+    if (lane < n_mine) mine = fmc.list[wave + NWAVES * lane];
+  }
+  auto entry_at = [&](int k) -> uint32_t { return (uint32_t)__builtin_amdgcn_readlane((int)mine, k & 63); };
+  auto tile_at = [&](int k) -> int {          // FlashMask: first position of the wave's tile k
+    if constexpr (FM) return k < n_mine ? TW * (int)(entry_at(k) & 0x7fffffffu) : past;
+    else return past;
+  };
+  auto partial_at = [&](int k) -> bool {
+    if constexpr (FM) return k < n_mine && (entry_at(k) >> 31) != 0u;
+    else return false;
+  };
   auto first_tile = [&]() -> int {
     if constexpr (!FM) return begin + wave * TW;
-    else return walk ? begin + TW * __builtin_ctzll(walk) : past;
+    else return tile_at(0);
   };
-  auto step = [&](int tile) -> int {
-    if constexpr (!FM) {
-      return tile + NWAVES * TW;
-    } else {
-      if (tile >= end) return past;
-      const int k = (tile - begin) / TW;
-      const uint64_t rest = k >= 63 ? 0ull : walk & (~0ull << (k + 1));
-      return rest ? begin + TW * __builtin_ctzll(rest) : past;
-    }
+  // The wave's tile d steps after the current one (d = 1, 2).
+  auto ahead = [&](int tile, int d) -> int {
+    if constexpr (!FM) return tile + d * NWAVES * TW;
+    else return tile_at(kc + d);
   };
   int4 ivt = make_int4(0, 0, 0, 0);   // FlashMask intervals of row tile + n (PARTIAL tiles)
-  auto issue_iv = [&](int tile) {
+  auto issue_iv = [&](int tile, bool part) {
     if constexpr (FM) {
-      if (tile < end && ((partial >> ((tile - begin) / TW)) & 1))
-        ivt = p.mask_iv[(int64_t)b * p.max_seq_len + min(tile + n, end - 1)];
+      if (tile < end && part) ivt = p.mask_iv[(int64_t)b * p.max_seq_len + min(tile + n, end - 1)];
     }
   };
 
@@ -276,17 +369,16 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     } else {
       ri = row_index(tile);
       issue_k(tile, ri, t.k);
-      issue_iv(tile);
+      issue_iv(tile, partial_at(kc));
       issue_v(tile, ri, t.v);
     }
-    ri_ahead = row_index(step(tile));
+    ri_ahead = row_index(ahead(tile, 1));
   }
-  for (; tile < end; tile = step(tile)) {
-    const int next_tile = step(tile);
+  while (tile < end) {
+    const int next_tile = ahead(tile, 1);
     uint32_t hidden = 0;                  // rows of this tile hidden by FlashMask (bit r)
     if constexpr (FM) {
-      if ((partial >> ((tile - begin) / TW)) & 1)
-        hidden = (uint32_t)__ballot(fm_hidden(ivt, q_row)) & 0xFFFFu;
+      if (partial_at(kc)) hidden = (uint32_t)__ballot(fm_hidden(ivt, q_row)) & 0xFFFFu;
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -294,9 +386,9 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[c]),
                                                     __builtin_bit_cast(bf16x8_t, qop[c]), acc, 0, 0, 0);
     ri = ri_ahead;
-    ri_ahead = row_index(step(next_tile));
+    ri_ahead = row_index(ahead(tile, 2));
     issue_k(next_tile, ri, t.k);
-    issue_iv(next_tile);
+    issue_iv(next_tile, partial_at(kc + 1));
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -372,6 +464,8 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       }
     }
     if constexpr (!kEarlyV) issue_v(next_tile, ri, t.v);
+    tile = next_tile;
+    ++kc;
   }
 
   if constexpr (kMfmaPV) {

@@ -300,11 +300,14 @@ def test_flashmask_plan_domain():
     st, pl, _, rs = plan(P(mask_kind="flashmask"))
     assert st == ka.DA_OK and pl.chunk <= 1024
     for kw in (dict(kv_format="f32", q_dtype="f32"), dict(head_dim=64), dict(num_queries=2),
-               dict(num_splits=2)):                       # 4096 / 2 keys per split > 1024
+               dict(num_splits=2),                        # 4096 / 2 keys per split > 1024
+               dict(max_seq_len=131073, kv_capacity=131073, num_splits=256)):   # > DA_FLASHMASK_MAX_SEQ
         st, _, _, rs = plan(P(mask_kind="flashmask", **kw))
         assert st == ka.DA_ERR_UNSUPPORTED and rs & (1 << 11), kw
     st, _, _, _ = plan(P(mask_kind="flashmask", window=4))
     assert st == ka.DA_ERR_INVALID
+    st, _, _, _ = plan(P(mask_kind="flashmask", max_seq_len=131072, kv_capacity=131072, num_splits=256))
+    assert st == ka.DA_OK
 
 
 # ---------------------------------------------------------------- balanced partition

@@ -66,6 +66,18 @@ def test_flashmask_trace_contiguous():
     _trace_rows_fm(w, dw, 3, forward=True)
 
 
+def test_flashmask_long_request_tile_numbering():
+    """A request of more than 4096 tiles: the non-SKIP numbering spans several
+    passes of the prefix scan and many entries per wave."""
+    lens = [70001, 4099]
+    w = _masked(synth.make_contiguous(65, len(lens), 8, 2, 128, lens, kv_capacity=70016), 4)
+    dw = _ready(w)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.forward(w, dw=dw)
+    H.check_rows(O, L, Or, Lr, 2e-3)
+    _trace_rows_fm(w, dw, None)
+
+
 def test_flashmask_everything_hidden():
     lens = [400, 64]
     w = synth.make_contiguous(64, 2, 8, 2, 128, lens, kv_capacity=400)
