@@ -537,14 +537,16 @@ def flashmask_loaded_bytes(w):
     return rows * w.Hkv * w.D * 2 * 2
 
 
-def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, steps=50):
+def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, R=128, steps=50):
     """decode_attn_append on the int8 cache shape of the sink+window workload
-    (group-closing residual, R = G = 128): one call where no request closes a
-    group and one where every request closes one (all of its residual)."""
+    (group-closing residual of R rows, K groups of G): one call where no
+    request closes a group and one where every request closes one (its
+    oldest G residual rows; the other R - G move down)."""
     import synth
-    cap = T + G
+    assert (T - R) % G == 0 and G > 28
+    cap = T + R
     prob = synth.Problem(batch=B, num_q_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=D, kv_format="i8",
-                         kv_capacity=cap, max_seq_len=cap, k_group=G, residual_len=G,
+                         kv_capacity=cap, max_seq_len=cap, k_group=G, residual_len=R,
                          residual_policy="groups")
     _, plan, _, _ = ka.decode_attn_plan(ka.problem_from(prob))
     g = torch.Generator(device="cuda")
@@ -553,14 +555,14 @@ def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, steps=50):
     v = torch.randint(-127, 128, (B, cap, Hkv, D), device="cuda", dtype=torch.int8, generator=g)
     ks = (torch.rand((B, cap // G + 1, Hkv, D), device="cuda", generator=g) * 0.04 + 0.005).half()
     vs = (torch.rand((B, cap, Hkv), device="cuda", generator=g) * 0.04 + 0.005).half()
-    kr = torch.randn((B, G, Hkv, D), device="cuda", generator=g).bfloat16()
-    vr = torch.randn((B, G, Hkv, D), device="cuda", generator=g).bfloat16()
+    kr = torch.randn((B, R, Hkv, D), device="cuda", generator=g).bfloat16()
+    vr = torch.randn((B, R, Hkv, D), device="cuda", generator=g).bfloat16()
     kn = torch.randn((B, Hkv, D), device="cuda", generator=g).bfloat16()
     vn = torch.randn((B, Hkv, D), device="cuda", generator=g).bfloat16()
     status = torch.zeros(B, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
     out = {}
-    # lengths before the append: residual 100 rows (no closure) / 128 rows (closure)
+    # lengths before the append: residual R - 28 rows (no closure) / R rows (closure)
     for name, t in (("no_closure", T - 28), ("closure", T)):
         sl = torch.full((B,), t, dtype=torch.int32, device="cuda")
         call = lambda: ka.decode_attn_append(plan, kn, vn, k, v, ks, vs, kr, vr, sl, status, st)
@@ -575,8 +577,9 @@ def append_timing(torch, ka, B=16, Hkv=8, D=128, T=16384, G=128, steps=50):
         torch.cuda.synchronize()
         out[name + "_us"] = round(e0.elapsed_time(e1) / steps * 1000, 2)
     assert int(status.max()) == 0
-    out["config"] = (f"B={B} H_kv={Hkv} d={D} int8 cache T={T}, R=G={G}; closure = quantize "
-                     f"{G} residual rows per (b, h_kv): K per channel, V per row")
+    out["config"] = (f"B={B} H_kv={Hkv} d={D} int8 cache T={T}, G={G}, R={R}; closure = quantize "
+                     f"the oldest {G} residual rows per (b, h_kv) (K per channel, V per row)"
+                     + (f" and move the other {R - G} down" if R > G else ""))
     return out
 
 
@@ -1004,6 +1007,7 @@ def main():
         others = {name: other_workload(torch, ka, name, oracle_runs=ORACLE_RUNS[name] if cpu else 0)
                   for name in ("long_context_128k", "paged_ragged", "int8_sink_window")}
         others["int8_append"] = append_timing(torch, ka)
+        others["int8_append_g32_r128"] = append_timing(torch, ka, G=32, R=128)
         others["tiny_fp32"] = other_workload(torch, ka, "tiny_fp32",
                                              oracle_runs=ORACLE_RUNS["tiny_fp32"] if cpu else 0)
         for name in ("few_query_c2", "hnd_layout", "flashmask"):

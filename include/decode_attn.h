@@ -68,7 +68,7 @@ typedef int32_t da_status;
 #define DA_RESIDUAL_WINDOW 0  /* n_q = T - min(T, R): the newest min(T, R) tokens are bf16     */
 #define DA_RESIDUAL_GROUPS 1  /* n_q = G * max(0, ceil((T - R) / G)): whole K groups close as
                                  soon as more than R tokens are unclosed (the streaming rule
-                                 decode_attn_append maintains; requires R == G there)       */
+                                 decode_attn_append maintains; requires G <= R)             */
 
 /* cache layouts ("M4.5 ...", sections 0x04B and 0x04D) */
 #define DA_LAYOUT_CONTIG_NHD 0  /* [B_c, T_cap, H_kv, D]; element ((c*T_cap + t)*H_kv + h)*D + x  */
@@ -449,18 +449,20 @@ typedef struct da_append_args {
 } da_append_args;
 
 /* Append one token to every request of an int8 cache that follows
- * DA_RESIDUAL_GROUPS with residual_len == k_group ("M8.6 ...", sections 0x05B
+ * DA_RESIDUAL_GROUPS with k_group <= residual_len ("M8.6 ...", sections 0x05B
  * and 0x06B).  For request b of length T = seq_lens[b]: if its residual holds
- * R rows, they are closed first -- K quantized per channel over the R = G rows
- * into scale group n_q/G, V quantized per row (scale per token), codes at
- * positions n_q .. n_q+G-1 -- then the new rows go to residual row T - n_q(T+1).
+ * R rows, its oldest G are closed first -- K quantized per channel over the G
+ * rows into scale group n_q/G, V quantized per row (scale per token), codes at
+ * positions n_q .. n_q+G-1 -- and the other R - G rows move down to residual
+ * rows 0 .. R-G-1 (residual row i always holds token n_q + i); then the new
+ * rows go to residual row T - n_q(T+1).
  * The quantizer is that of the int8 format (section 0x02A).  One workgroup per
  * (b, h_kv), asynchronous on `stream`; nothing is written for a request whose
  * status gets an error bit (the heads of one request may then disagree, so
  * the request must be dropped).  The same plan serves attention over the
  * cache after seq_lens has been advanced.  Errors: DA_ERR_INVALID (NULL
  * buffer, altered key -> DA_ERR_PLAN_MISMATCH), DA_ERR_UNSUPPORTED (not
- * int8 + contiguous + DA_RESIDUAL_GROUPS with residual_len == k_group <= 256,
+ * int8 + contiguous + DA_RESIDUAL_GROUPS with k_group <= residual_len and k_group <= 256,
  * or head_dim not 64/128), DA_ERR_HIP. */
 da_status decode_attn_append(const da_plan* plan, const da_append_args* args, void* stream);
 

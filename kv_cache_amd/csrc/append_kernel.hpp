@@ -1,9 +1,10 @@
 // Streaming append for the int8 K/V format under the group-closing residual
 // policy ("M8.6 - Live-Data Quantization: Activations and KV Cache",
 // sections 0x05B, 0x06B): the new token's bf16 K and V rows enter the
-// residual; when the residual already holds R rows (R == G), those G rows are
-// closed first -- K quantized per channel over the G rows into one new scale
-// group, V quantized per row -- and the new row takes residual slot 0.
+// residual; when the residual already holds R rows (G <= R), its oldest G
+// rows are closed first -- K quantized per channel over the G rows into one
+// new scale group, V quantized per row -- the other R - G rows move down by G
+// (residual row i holds token n_q + i), and the new row takes slot R - G.
 // Quantizer rule (section 0x02A): scale = fp16(amax / 127) re-read as the
 // effective scale (1 for an all-zero vector), code = clip(rint(x / scale),
 // -127, 127) with ties to even; a non-finite input or a non-finite or
@@ -33,7 +34,8 @@ struct AppendParams {
   int32_t num_kv_heads;
   int32_t kv_capacity;
   int32_t max_seq_len;
-  int32_t group;           // G == R
+  int32_t group;           // G
+  int32_t resid_len;       // R >= G
   int32_t n_groups;        // ceil(T_cap / G)
 };
 
@@ -75,19 +77,20 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   const int h = blockIdx.x - b * H;
   const int tid = threadIdx.x;
   const int G = p.group;
+  const int R = p.resid_len;
   const int T = p.seq_lens[b];
   if (T < 0 || T >= p.max_seq_len) {
     if (tid == 0 && p.status) atomicOr(p.status + b, (int)DA_APPEND_NO_ROOM);
     return;
   }
-  const int n_q = T > G ? (T - G + G - 1) / G * G : 0;  // closed rows (R == G)
-  const int r = T - n_q;                                  // residual rows, 0 .. G
+  const int n_q = T > R ? (T - R + G - 1) / G * G : 0;  // closed rows
+  const int r = T - n_q;                                  // residual rows, 0 .. R
   const int64_t row_stride = (int64_t)H * D;
-  uint16_t* kres = p.k_resid + ((int64_t)b * G * H + h) * D;
-  uint16_t* vres = p.v_resid + ((int64_t)b * G * H + h) * D;
+  uint16_t* kres = p.k_resid + ((int64_t)b * R * H + h) * D;
+  uint16_t* vres = p.v_resid + ((int64_t)b * R * H + h) * D;
   int slot = r;
 
-  if (r == G) {
+  if (r == R) {
     __shared__ uint32_t kmax[D];                 // per-channel amax bits (non-negative floats order as integers)
     __shared__ uint16_t ks[D];
     const int cg = tid % CG, r0 = tid / CG;
@@ -166,8 +169,25 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
       if (cg == 0) p.v_scale[((int64_t)b * p.kv_capacity + n_q + row) * H + h] = vsc[i];
     }
     if (tid < D) p.k_scale[(((int64_t)b * p.n_groups + n_q / G) * H + h) * D + tid] = ks[tid];
-    __syncthreads();      // every read of residual row 0 precedes its overwrite
-    slot = 0;
+    __syncthreads();      // every read of the closed rows precedes their overwrite
+    // rows G .. R-1 move to 0 .. R-G-1, RS rows per pass in ascending order: a
+    // pass writes rows below every row a later pass reads, and its barrier
+    // keeps its writes after every thread's reads of the previous pass
+    for (int base = 0; base < R - G; base += RS) {
+      const int row = base + r0;
+      uint4 kw4 = make_uint4(0u, 0u, 0u, 0u), vw4 = kw4;
+      if (row < R - G) {
+        kw4 = *reinterpret_cast<const uint4*>(kres + (row + G) * row_stride + 8 * cg);
+        vw4 = *reinterpret_cast<const uint4*>(vres + (row + G) * row_stride + 8 * cg);
+      }
+      __syncthreads();
+      if (row < R - G) {
+        *reinterpret_cast<uint4*>(kres + row * row_stride + 8 * cg) = kw4;
+        *reinterpret_cast<uint4*>(vres + row * row_stride + 8 * cg) = vw4;
+      }
+    }
+    __syncthreads();      // every read of residual row R - G precedes its overwrite
+    slot = R - G;
   }
   if (tid < D) {
     kres[slot * row_stride + tid] = p.k_new[((int64_t)b * H + h) * D + tid];

@@ -337,7 +337,7 @@ extern "C" da_status decode_attn_append(const da_plan* plan, const da_append_arg
   if (!da::plan_intact(plan)) return DA_ERR_PLAN_MISMATCH;
   const da_problem& p = plan->problem;
   if (p.kv_format != DA_KV_I8 || p.layout != DA_LAYOUT_CONTIG_NHD || p.cache_rows != 0 ||
-      p.residual_policy != DA_RESIDUAL_GROUPS || p.residual_len != p.k_group ||
+      p.residual_policy != DA_RESIDUAL_GROUPS || p.residual_len < p.k_group ||
       p.k_group > da::kAppendThreads || (p.head_dim_qk != 64 && p.head_dim_qk != 128))
     return DA_ERR_UNSUPPORTED;
   if (p.batch == 0) return DA_OK;
@@ -360,6 +360,7 @@ extern "C" da_status decode_attn_append(const da_plan* plan, const da_append_arg
   ap.kv_capacity = p.kv_capacity;
   ap.max_seq_len = p.max_seq_len;
   ap.group = p.k_group;
+  ap.resid_len = p.residual_len;
   ap.n_groups = (p.kv_capacity + p.k_group - 1) / p.k_group;
   const dim3 grid((unsigned)(p.batch * p.num_kv_heads));
   const hipStream_t st = static_cast<hipStream_t>(stream);

@@ -263,6 +263,13 @@ def test_append_rejects_unsupported_plans_and_null_buffers_without_gpu():
     assert ka.decode_attn_append(pl, *([16] * 8), None, check=False) == ka.DA_ERR_INVALID
     pl.chunk += 16
     assert ka.decode_attn_append(pl, *([16] * 9), check=False) == ka.DA_ERR_PLAN_MISMATCH
+    # G < R is accepted (a NULL buffer is then the error); G above 256 is not
+    st, pl, ws, _ = plan(P(kv_format="i8", k_group=32, residual_len=128, residual_policy="groups"))
+    assert st == ka.DA_OK
+    assert ka.decode_attn_append(pl, *([16] * 8), None, check=False) == ka.DA_ERR_INVALID
+    st, pl, ws, _ = plan(P(kv_format="i8", k_group=512, residual_len=512, residual_policy="groups"))
+    assert st == ka.DA_OK
+    assert ka.decode_attn_append(pl, *([16] * 9), check=False) == ka.DA_ERR_UNSUPPORTED
 
 
 def test_groups_policy_plan_checks():

@@ -19,15 +19,15 @@ def _name(request):
     H.announce(request.node.nodeid)
 
 
-def _cache(seed, lens, cap, Hq=8, Hkv=2, D=128, values=None, g=G):
+def _cache(seed, lens, cap, Hq=8, Hkv=2, D=128, values=None, g=G, R=None):
     w = synth.make_int8(seed, len(lens), Hq, Hkv, D, lens, kv_capacity=cap, residual_policy="groups",
-                        values=values, k_group=g, residual_len=g)
+                        values=values, k_group=g, residual_len=g if R is None else R)
     w.problem.max_seq_len = cap
     return w
 
 
-def _parts(buf, b, T, G=G):
-    n_q = quantized_count(T, "groups", G, G)
+def _parts(buf, b, T, G=G, R=None):
+    n_q = quantized_count(T, "groups", G, G if R is None else R)
     return dict(n_q=n_q, k_codes=buf["k"][b, :n_q], k_scale=buf["k_scale"][b, :n_q // G],
                 v_codes=buf["v"][b, :n_q], v_scale=buf["v_scale"][b, :n_q],
                 k_resid_bits=buf["k_resid"][b, :T - n_q], v_resid_bits=buf["v_resid"][b, :T - n_q])
@@ -122,6 +122,44 @@ def test_append_closure_other_head_dims_and_groups(D, g):
                 assert np.array_equal(e[key], g_[key]), (step, b, key)
             for key in ("k_scale", "v_scale"):
                 assert np.array_equal(e[key].view(np.uint16), g_[key].view(np.uint16)), (step, b, key)
+
+
+@pytest.mark.parametrize("D,g,R", [(128, 32, 128), (64, 16, 48), (128, 64, 96), (128, 128, 256),
+                                   (64, 256, 300)])
+def test_append_residual_longer_than_group(D, g, R):
+    # G < R (the page's teaching state closes 32-token groups behind a
+    # 128-token residual): a closure takes the oldest G residual rows and the
+    # other R - G move down; byte-exact against the oracle's append model over
+    # several appends, then attention over the appended cache
+    lens = [R - 1, R, R + 1, R + g, 0, 2 * g + R - 2, 3 * g + R + 5]
+    cap = 4 * g + R + 16
+    w = _cache(51 + D + g + R, lens, cap, D=D, g=g, R=R)
+    _, plan, _, _ = ka.decode_attn_plan(ka.problem_from(w.problem))
+    dw = H.DeviceWorkload(w)
+    ref = {k: w.buffers[k].copy() for k in ("k", "v", "k_scale", "v_scale", "k_resid", "v_resid")}
+    cur = list(lens)
+    for step in range(3):
+        k_new, v_new = synth.append_rows(400 + step, len(lens), 2, D)
+        status = _gpu_append(plan, dw.dev, k_new, v_new, cur)
+        assert not status.any()
+        for b, T in enumerate(cur):
+            st = kivi_state_from_parts(_parts(ref, b, T, g, R), g)
+            _apply_parts(ref, b, kivi_state_parts(kivi_append(st, k_new[b], v_new[b], g, R)), g)
+        cur = [T + 1 for T in cur]
+        got = _host(dw.dev, ref)
+        for b, T in enumerate(cur):
+            e, g_ = _parts(ref, b, T, g, R), _parts(got, b, T, g, R)
+            assert e["n_q"] == g_["n_q"]
+            for key in ("k_codes", "v_codes", "k_resid_bits", "v_resid_bits"):
+                assert np.array_equal(e[key], g_[key]), (step, b, key)
+            for key in ("k_scale", "v_scale"):
+                assert np.array_equal(e[key].view(np.uint16), g_[key].view(np.uint16)), (step, b, key)
+    w.buffers.update(ref)
+    w.buffers["seq_lens"] = np.asarray(cur, np.int32)
+    dw.dev["seq_lens"] = H.to_dev(w.buffers["seq_lens"])
+    O, L, _ = H.forward(w, dw=dw)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
 def test_append_no_room_and_bad_scale_write_nothing():
