@@ -249,7 +249,11 @@ typedef struct da_args {
 } da_args;
 
 /* Validate the problem (semantic checks first, then every capability
- * predicate), choose the split count, size the workspace and freeze the plan.
+ * predicate), choose the split count, size the workspace and freeze the plan
+ * ("M4.5 ...", sections 0x07A-0x07B: the dispatch key is frozen before
+ * selection, admission is a conjunction and a rejection reports every failed
+ * predicate; 0x07F: the plan is a second immutable key; 0x03B and 0x03D-0x03E:
+ * split bounds and the workspace follow from the problem).
  * Host only: touches the device only to read its CU count and architecture
  * when problem->num_cus == 0.  plan, workspace_bytes and reasons may each be
  * NULL; *reasons receives the complete bit vector of failed predicates. */
@@ -297,7 +301,9 @@ da_status decode_attn_schedule(const da_plan* plan, const int32_t* seq_lens_host
 da_status decode_attn_partition(const da_plan* plan, const int32_t* seq_lens_host, int32_t items_per_head,
                                 int32_t* part, uint64_t part_len, int32_t* items_out);
 
-/* Launch the split kernel: grid B*H_kv*S workgroups; workgroup (b, h_kv, s)
+/* Launch the split kernel ("M4.5 ...", sections 0x02A, 0x02C, 0x03C and
+ * 0x03D: the producer grid, one state per split and query head, the empty
+ * identity, the workspace shapes): grid B*H_kv*S workgroups; workgroup (b, h_kv, s)
  * owns visible rows [s*chunk, min((s+1)*chunk, N_b)) of request b (int8:
  * the rows whose weighted offsets fall there, a residual row weighing 2) and the
  * H_q/H_kv query heads sharing h_kv, reads each of its K/V rows once, and
@@ -311,7 +317,9 @@ da_status decode_attn_partition(const da_plan* plan, const int32_t* seq_lens_hos
  * (W = 0 without a partition), which the combine reads. */
 da_status decode_attn_run(const da_plan* plan, const da_args* args, void* stream);
 
-/* Launch the combine kernel: for each (b, i, h_q), fold its S states (with
+/* Launch the combine kernel ("M4.5 ...", sections 0x02B-0x02C, 0x03C and
+ * 0x03I: the reducer grid, the binary merge, the empty-aware fold): for each
+ * (b, i, h_q), fold its S states (with
  * a partition: its pieces, as the workspace's partition header written by
  * the preceding run says) in ascending split order and write out fp32
  * [B, C, H_q, D] = u/l and, when lse
@@ -322,8 +330,10 @@ da_status decode_attn_combine(const da_plan* plan, const void* workspace,
                               uint64_t workspace_bytes, float* out, float* lse,
                               void* stream);
 
-/* Single-launch form of run + combine: the same split kernel, with the
- * reduction of section 0x02B folded into it.  Each workgroup stores its
+/* Single-launch form of run + combine ("M4.5 ...", sections 0x02B, 0x03F and
+ * 0x09B: Flash-Decoding's second reduction level, here without the second
+ * launch): the same split kernel, with the reduction of section 0x02B folded
+ * into it.  Each workgroup stores its
  * states, makes them visible device-wide, and increments the arrival counter
  * of its (b, h_kv); the workgroup that arrives last (the S-th) reads the S
  * states of its H_q/H_kv rows, folds them in ascending split order exactly as
@@ -372,7 +382,8 @@ da_status decode_attn_forward_static(const da_plan* plan, const da_args* args, f
 da_status decode_attn_flashmask_summarize(const da_plan* plan, const int32_t* intervals,
                                           int32_t* summary, void* stream);
 
-/* Zero the arrival counters of a workspace sized for `plan` (a fill kernel on
+/* Zero the arrival counters ("M4.5 ...", section 0x03E: temporary storage
+ * derived from the ABI) of a workspace sized for `plan` (a fill kernel on
  * `stream`, so it may be captured into a graph).  Needed once per workspace
  * before its first decode_attn_forward. */
 da_status decode_attn_workspace_init(const da_plan* plan, void* workspace,
@@ -414,7 +425,9 @@ da_status decode_attn_trace_indices(const da_plan* plan, const da_args* args, co
                                     float* out, float* lse, void* stream);
 
 /* Per-workgroup timestamps of the launches decode_attn_forward makes, for
- * schedule analysis (debug only, never on the timed path): a timestamp
+ * schedule analysis ("M4.5 ...", sections 0x0BF and 0x0BH: a trace shows
+ * what ran; raw synchronized samples close the measurement).  Debug only,
+ * never on the timed path: a timestamp
  * instance of the same kernels, in which thread 0 of each workgroup reads the
  * device's constant-rate clock (s_memrealtime) at its start, when its states
  * are stored, and at its end.  stamps: device uint64 [B*H_kv*S, 4] per
@@ -466,7 +479,8 @@ typedef struct da_append_args {
  * or head_dim not 64/128), DA_ERR_HIP. */
 da_status decode_attn_append(const da_plan* plan, const da_append_args* args, void* stream);
 
-/* Static text for one reason bit index (0 .. DA_NUM_REASONS-1) or status. */
+/* Static text for one reason bit index (0 .. DA_NUM_REASONS-1) or status
+ * ("M4.5 ...", section 0x07B: a rejection is a vector of named predicates). */
 const char* decode_attn_reason(int bit);
 const char* decode_attn_status_string(da_status status);
 
