@@ -1002,6 +1002,9 @@ def main():
         wl = make_workload(torch, ka, "long_context_128k")
         sweep["long_context_128k"] = wl.sweep([1, 8, 32, 128, 0], steps=10, warmup=3)
         del wl
+        w8 = make_workload(torch, ka, "int8_sink_window")
+        sweep["int8_sink_window"] = w8.sweep([2, 3, 4, 6, 8, 12, 16, 0], steps=50, warmup=5)
+        del w8
         line["split_sweep"] = sweep
     if not a.no_long:
         others = {name: other_workload(torch, ka, name, oracle_runs=ORACLE_RUNS[name] if cpu else 0)
