@@ -495,8 +495,10 @@ def other_workload(torch, ka, name, steps=30, warmup=5, oracle_runs=0):
     if name == "int8_sink_window":
         w = GpuWorkload(torch, ka, "i8", 16, 32, 8, 128, [16384] * 16, min_bytes=600 << 20, seed=3,
                         mask=(4, 4096))
-        return _with_oracle(w, w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual "
-                                                "128, 4 sinks + window 4096", steps, warmup), oracle_runs)
+        r = w.report("int8", "B=16 H_q=32 H_kv=8 d=128 T=16384 int8 K/V + bf16 residual "
+                             "128, 4 sinks + window 4096", steps, warmup)
+        r["code_pattern_probe"] = i8_pattern_probe(torch, w, 4096)
+        return _with_oracle(w, r, oracle_runs)
     layer = "B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16"
     if name == "few_query_c2":
         w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=6, C=2)
@@ -518,6 +520,31 @@ def other_workload(torch, ka, name, steps=30, warmup=5, oracle_runs=0):
         return _with_oracle(w, w.report("tiny", "B=1 H_q=H_kv=4 d=64 T=256 fp32 contiguous, S=4", steps,
                                         warmup), oracle_runs, single_thread=True)
     raise ValueError(name)
+
+
+def i8_pattern_probe(torch, w, window, steps=100, warmup=10):
+    """The int8 split kernel's code loads without its arithmetic
+    (hbm_probe.hip i8_pattern_kernel) over the window's K and V codes of the
+    workload's input sets, with its grid: the read ceiling of that access
+    pattern (the sinks, residual rows and scales, a few percent of the bytes,
+    left out)."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "kv_cache_amd", "libhbm_probe.so"))
+    L.hbm_probe_i8_pattern.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 6 + \
+        [ctypes.c_void_p, ctypes.c_void_p]
+    T = max(w.lens)
+    S = w.S
+    chunk = -(-window // S)
+    sink = torch.empty(w.B * w.Hkv * S, dtype=torch.int32, device="cuda")
+
+    def call(i):
+        d = w.sets[i % w.nsets]
+        assert L.hbm_probe_i8_pattern(d["k"].data_ptr(), d["v"].data_ptr(), w.B, T, w.Hkv, S, chunk, window,
+                                      sink.data_ptr(), w.stream) == 0
+    ms = w.time(call, steps, warmup)
+    nbytes = 2 * w.B * w.Hkv * window * w.D
+    return {"us_per_launch": round(ms * 1000, 2), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "code_bytes": nbytes, "grid": w.B * w.Hkv * S, "chunk": chunk}
 
 
 def flashmask_loaded_bytes(w):

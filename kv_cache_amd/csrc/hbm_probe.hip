@@ -7,6 +7,7 @@
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Each thread streams 16-byte words with a grid stride, folding them into a
 // checksum that is stored once per thread block so the loads cannot be
@@ -104,6 +105,48 @@ __global__ __launch_bounds__(256) void read2_kernel(const uint4* __restrict__ a,
   }
 }
 
+
+// The int8 split kernel's code loads without its arithmetic: codes [B, T, H,
+// 128] (128-byte rows), workgroup (b, h, s) reads rows [s*chunk, ..) of the
+// window [T - W, T) (split index rotated by (b, h)); per 16-row tile, lane
+// (n, g) reads K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row n
+// (plain) and V bytes [8n, 8n+8) of rows 4g + j (non-temporal).
+__global__ __launch_bounds__(256) void i8_pattern_kernel(const int8_t* __restrict__ k, const int8_t* __restrict__ v,
+                                                         int B, int T, int H, int S, int chunk, int W,
+                                                         uint32_t* __restrict__ sink) {
+  const int wg = blockIdx.x;
+  const int bh = wg / S;
+  const int s = (wg - bh * S + bh) % S;
+  const int h = bh % H, b = bh / H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int w0 = T - W;
+  const int begin = min(s * chunk, W), end = min(begin + chunk, W);
+  const size_t base = ((size_t)b * T * H + h) * 128;
+  const size_t rs = (size_t)H * 128;
+  uint32_t acc = 0;
+  for (int t = begin + wave * 16; t < end; t += 64) {
+    const size_t kr = base + (size_t)(w0 + min(t + n, end - 1)) * rs;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(k + kr + 16 * g);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(k + kr + 64 + 16 * g);
+    acc ^= x0.x ^ x1.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t vr = base + (size_t)(w0 + min(t + 4 * g + j, end - 1)) * rs + 8 * n;
+      const u32x2_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(v + vr));
+      acc ^= y.x ^ y.y;
+    }
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < 256; ++i) t ^= red[i];
+    sink[wg] = t;
+  }
+}
+
 }  // namespace
 
 // K and V [B, T, H, 128] bf16 (256-byte rows); grid B*H*S workgroups; sink
@@ -114,6 +157,17 @@ extern "C" int hbm_probe_pattern(const void* k, const void* v, int B, int T, int
   if ((reinterpret_cast<uintptr_t>(k) & 15u) || (reinterpret_cast<uintptr_t>(v) & 15u)) return -1;
   hipLaunchKernelGGL(pattern_kernel, dim3((unsigned)(B * H * S)), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(k), static_cast<const uint4*>(v), B, T, H, S, chunk, sink, stamps);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// int8 codes K and V [B, T, H, 128]; grid B*H*S workgroups over the last W
+// rows of each request; sink holds one uint32 per workgroup.
+extern "C" int hbm_probe_i8_pattern(const void* k, const void* v, int B, int T, int H, int S, int chunk, int W,
+                                    uint32_t* sink, void* stream) {
+  if (!k || !v || !sink || B <= 0 || H <= 0 || S <= 0 || chunk <= 0 || W <= 0 || W > T) return -1;
+  if ((reinterpret_cast<uintptr_t>(k) & 15u) || (reinterpret_cast<uintptr_t>(v) & 15u)) return -1;
+  hipLaunchKernelGGL(i8_pattern_kernel, dim3((unsigned)(B * H * S)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const int8_t*>(k), static_cast<const int8_t*>(v), B, T, H, S, chunk, W, sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
