@@ -499,6 +499,17 @@ def other_workload(torch, ka, name, steps=30, warmup=5, oracle_runs=0):
                              "128, 4 sinks + window 4096", steps, warmup)
         r["code_pattern_probe"] = i8_pattern_probe(torch, w, 4096)
         return _with_oracle(w, r, oracle_runs)
+    if name == "int8_ragged":
+        lens = synth.ragged_lengths(4, 32, 1, 16384).tolist()
+        w = GpuWorkload(torch, ka, "i8", 32, 32, 8, 128, lens, min_bytes=600 << 20, seed=9)
+        fixed = w.time(w.fwd, steps, warmup)
+        w.use_partition()
+        r = w.report("int8r", "B=32 H_q=32 H_kv=8 d=128 int8 K/V + bf16 residual 128, causal, "
+                              "T~U[1,16384] (seed 4), balanced partition from decode_attn_partition",
+                     steps, warmup)
+        r["partition_items_per_head"] = w.part_items
+        r["fixed_splits_us_per_call"] = round(fixed * 1000, 2)
+        return r
     layer = "B=8 H_q=32 H_kv=8 d=128 S_k=4096 bf16"
     if name == "few_query_c2":
         w = GpuWorkload(torch, ka, "contig", 8, 32, 8, 128, [4096] * 8, min_bytes=600 << 20, seed=6, C=2)
@@ -910,7 +921,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-sweep", action="store_true", help="skip the split-count sweeps")
     names = ["llama3_8b_layer", "long_context_128k", "paged_ragged", "int8_sink_window", "tiny_fp32",
-             "few_query_c2", "hnd_layout", "flashmask"]
+             "few_query_c2", "hnd_layout", "flashmask", "int8_ragged"]
     ap.add_argument("--only", default=None, choices=names,
                     help="time one workload alone and print its report (for profiling)")
     ap.add_argument("--stamps", default=None, choices=list(DOMINANT),
@@ -1040,7 +1051,7 @@ def main():
         others["int8_append_g32_r128"] = append_timing(torch, ka, G=32, R=128)
         others["tiny_fp32"] = other_workload(torch, ka, "tiny_fp32",
                                              oracle_runs=ORACLE_RUNS["tiny_fp32"] if cpu else 0)
-        for name in ("few_query_c2", "hnd_layout", "flashmask"):
+        for name in ("int8_ragged", "few_query_c2", "hnd_layout", "flashmask"):
             others[name] = other_workload(torch, ka, name)
         fmr = others["flashmask"]
         # the loaded tiles' bytes at the causal headline's achieved rate: what

@@ -289,13 +289,16 @@ da_status decode_attn_schedule(const da_plan* plan, const int32_t* seq_lens_host
  * folds exactly those pieces, in ascending order; the arithmetic is the same
  * split/merge, so the result matches the oracle to the same tolerance (but is
  * not bitwise equal to the fixed-split result).
- *   items_per_head  target W (0: 3 workgroups per CU of the plan / H_kv, one round)
+ *   items_per_head  target W (0: one dispatch round, 3 workgroups per CU of the plan / H_kv
+ *                   for bf16, 2 for int8)
  *   part            host int32 [5 + B + W_max] with W_max = the target W:
  *                   [W, L, B, 0, P_0 .. P_B, first request of item 0 .. W-1]
  *   *items_out      W (may be 0 when every request is empty)
  * Copy part to the device and pass it with W as da_args.partition /
- * partition_items.  Supported by the bf16 D = 128 matrix-core kernel with the
- * causal or sink+window mask (any layout).  Errors: DA_ERR_INVALID for a NULL
+ * partition_items.  Supported by the bf16 (any layout) and int8 D = 128
+ * matrix-core kernels with the causal or sink+window mask; items count visible
+ * rows (an int8 cache's bf16 residual rows, at most R per request, count as one
+ * row each although they carry twice the bytes).  Errors: DA_ERR_INVALID for a NULL
  * pointer, a length outside [0, max_seq_len], part_len too small, or N >= 2^31;
  * DA_ERR_UNSUPPORTED for S < 2; DA_ERR_PLAN_MISMATCH for an altered plan. */
 da_status decode_attn_partition(const da_plan* plan, const int32_t* seq_lens_host, int32_t items_per_head,

@@ -72,9 +72,9 @@ da_status check_args(const da_plan* plan, const da_args* a) {
     return DA_ERR_INVALID;
   if (a->partition) {
     if (a->partition_items < 0) return DA_ERR_INVALID;
-    // balanced partitions run on the bf16 D = 128 matrix-core kernel, without FlashMask
-    if (p.kv_format != DA_KV_BF16 || p.head_dim_qk != 128 || p.mask_kind == DA_MASK_FLASHMASK ||
-        plan->num_splits < 2 || !DA_MFMA_QK)
+    // balanced partitions run on the bf16 and int8 D = 128 matrix-core kernels, without FlashMask
+    if ((p.kv_format != DA_KV_BF16 && p.kv_format != DA_KV_I8) || p.head_dim_qk != 128 ||
+        p.mask_kind == DA_MASK_FLASHMASK || plan->num_splits < 2 || !DA_MFMA_QK)
       return DA_ERR_UNSUPPORTED;
   } else if (a->partition_items != 0) {
     return DA_ERR_INVALID;
@@ -164,6 +164,14 @@ bool launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
   constexpr bool kStamps = INSTR == da::kInstrStamps;
   if constexpr (use_mfma<FMT, D>() && FMT == DA_KV_I8) {
     static_assert(!FM, "FlashMask runs on the bf16 matrix-core kernel only");
+    if constexpr (!FUSED && !kStamps) {
+      if (sp.partition) {
+        hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, false, INSTR, true>), dim3(grid),
+                           dim3(kWaves * 64), 0, st, sp);
+        return true;
+      }
+    }
+    if (kStamps && sp.partition) return false;
     hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED, INSTR>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
     return true;

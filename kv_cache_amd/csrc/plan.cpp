@@ -63,6 +63,7 @@ constexpr int kRowAlign = 16;
 // Workgroups per CU a balanced partition targets by default: one round of the
 // partitioned split kernel (its launch bound allows this many per CU).
 constexpr int kPartitionWgPerCu = 3;
+constexpr int kI8PartitionWgPerCu = 2;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ceil(a / b) for b > 0 and any sign of a
@@ -333,7 +334,10 @@ extern "C" da_status decode_attn_partition(const da_plan* plan, const int32_t* s
   const int64_t B = p.batch, H = p.num_kv_heads, S = plan->num_splits;
   if (items_per_head < 0) return DA_ERR_INVALID;
   int64_t target = items_per_head;
-  if (target == 0) target = std::max<int64_t>(1, (kPartitionWgPerCu * (int64_t)plan->num_cus) / std::max<int64_t>(H, 1));
+  // default: one dispatch round of the partition instance (bf16: 3 workgroups
+  // per CU; int8: 2, the register budget of its partition instance)
+  const int64_t per_cu = p.kv_format == DA_KV_I8 ? kI8PartitionWgPerCu : kPartitionWgPerCu;
+  if (target == 0) target = std::max<int64_t>(1, (per_cu * (int64_t)plan->num_cus) / std::max<int64_t>(H, 1));
   if (part_len < (uint64_t)(5 + B + target)) return DA_ERR_INVALID;
   if (S < 2) return DA_ERR_UNSUPPORTED;
   std::vector<int64_t> n(B);

@@ -122,30 +122,40 @@ __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) { return (ui
 // 24 of them.
 constexpr int kI8ScaleSlots = 24;
 
+// A partitioned run keeps the state of several pieces' walk live: it gets
+// the register budget of 2 waves per SIMD, and the host sizes its default
+// partition for 2 workgroups per CU.
+constexpr int kI8PartitionWgPerCu = 2;
+
 // 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
 // INSTR: kInstrRows is the index-trace instance, which also records each row
 // load (codes, scales, residual rows) where it is issued; kInstrStamps
-// records per-workgroup timestamps; otherwise identical.
-template <int G, int NWAVES, bool FUSED, int INSTR = 0>
-__global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma_i8(SplitParams p) {
+// records per-workgroup timestamps; otherwise identical.  PART: the balanced
+// partition instance (workgroup (item, h_kv) runs the request pieces of its
+// item, as in split_kernel_mfma).
+template <int G, int NWAVES, bool FUSED, int INSTR = 0, bool PART = false>
+__global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ? 3 : 2)) void split_kernel_mfma_i8(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
   constexpr int STEP = NWAVES * TW;
   static_assert(G >= 1 && G <= 16, "");
 
   WgStamps<INSTR> stamps(p);
-  int b, h, s;
   const PartitionHeaderAtExit header_at_exit{p};
-  decode_workgroup(p, &b, &h, &s);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int n = lane & 15;     // K row of the tile / score column (head)
   const int kg = lane >> 4;    // channel group of the MFMA slice / V row slot
+  __shared__ uint4 q_lds[4][64];
+  __shared__ uint4 ksc[NWAVES][kI8ScaleSlots][16];   // one K scale table per wave
+  __shared__ WaveStates<G, D, NWAVES> sh;
 
+  // One piece of work: visible ordinals [pbeg, pend) of request b for K/V
+  // head h, stored as split slot s.  pend < 0: the plan's split s.
+  auto piece = [&](int b, int h, int s, int pbeg, int pend) {
   // q rows in the B operand layout, q[head n][32c + 8kg .. +7] (zero for
   // n >= G), staged in LDS: the residual part uses them as they are, the int8
   // part reads them in its own channel order.
-  __shared__ uint4 q_lds[4][64];
   if (wave == 0) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -163,7 +173,12 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   const int n_q = quantized_len(p, T);
   const int o_res = residual_ordinal(vis, n_q);
   int begin, end;
-  split_range_weighted(vis.n_vis, o_res, s, p.chunk, &begin, &end);
+  if (pend < 0) {
+    split_range_weighted(vis.n_vis, o_res, s, p.chunk, &begin, &end);
+  } else {
+    begin = min(pbeg, vis.n_vis);
+    end = min(pend, vis.n_vis);
+  }
   // Score column n is virtual head n, with its own visible end (C > 1 rows).
   const int lim_n = row_limit(p, vis.n_vis, n);
   if (begin >= end) {
@@ -246,7 +261,6 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   // tile in flight holds only codes and V scales and each wave keeps two
   // tiles in flight.  A split is one phase per run unless it is long.
   auto kch = [&](int c) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1); };
-  __shared__ uint4 ksc[NWAVES][kI8ScaleSlots][16];   // one scale table per wave
   if (begin < mid) {
     // q in this part's channel order, read from the staged rows: channels
     // kch(c) .. +7 of head n are 8-channel block kch(c)/8 = 4c' + kg', held by
@@ -555,7 +569,6 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
       u[i][e] += __shfl_xor(u[i][e], 16);
       u[i][e] += __shfl_xor(u[i][e], 32);
     }
-  __shared__ WaveStates<G, D, NWAVES> sh;
   if (kg == 0) {
 #pragma unroll
     for (int i = 0; i < G; ++i)
@@ -570,6 +583,35 @@ __global__ __launch_bounds__(NWAVES * 64, G <= 4 ? 3 : 2) void split_kernel_mfma
   merge_waves_and_store<G, D, NWAVES, FUSED>(p, b, h, s, sh);
   stamps.states_stored();
   stamps.folded = finish_split<G, D, NWAVES, FUSED>(p, b, h);
+  };
+
+  if constexpr (!PART) {
+    int b, h, s;
+    decode_workgroup(p, &b, &h, &s);
+    piece(b, h, s, 0, -1);
+  } else {
+    // Balanced partition: workgroup (item, h) takes ordinals [item*L,
+    // (item+1)*L) of the requests' visible ordinals laid end to end, one piece
+    // per request it meets, stored as split slot (items since the request's
+    // first); descriptor values are checked against the plan.
+    static_assert(!FUSED, "partitions fold in the combine kernel");
+    const int32_t* part = p.partition;
+    const int h = (int)(blockIdx.x % (unsigned)p.num_kv_heads);
+    const int item = (int)(blockIdx.x / (unsigned)p.num_kv_heads);
+    const int L = part[1];
+    if (part[2] != p.batch || L <= 0 || item >= part[0]) return;
+    int x = item * L;
+    const int xe = min(x + L, part[4 + p.batch]);
+    for (int b = part[5 + p.batch + item]; x < xe && b >= 0 && b < p.batch; ++b) {
+      const int pb = part[4 + b], pb1 = part[5 + b];
+      if (pb1 <= x) continue;                     // empty request
+      const int j = item - pb / L;
+      if (j < 0 || j >= p.num_splits || x < pb) return;
+      if (x != item * L) __syncthreads();          // the previous piece has read the shared tables
+      piece(b, h, j, x - pb, min(xe, pb1) - pb);
+      x = min(xe, pb1);
+    }
+  }
 }
 
 }  // namespace da

@@ -77,3 +77,48 @@ def test_partition_and_fixed_splits_share_a_workspace():
         H.check_rows(b.astype(np.float64), L2.cpu().numpy().astype(np.float64), Or, Lr, TOL)
         outs.append(a)
     assert np.array_equal(outs[0], outs[2])       # fixed plan + fixed partition: bitwise repeatable
+
+
+@pytest.mark.parametrize("mask", ["causal", "sink_window"])
+def test_partition_int8_ragged(mask):
+    # int8 codes + bf16 residual under a balanced partition: pieces cut through
+    # the int8 part, the seam between sinks and window, and the residual rows
+    lens = [0, 1, 100, 128, 200, 1000, 5000, 3000]
+    mk = dict(mask_kind="sink_window", n_sink=4, window=900) if mask == "sink_window" else {}
+    w = synth.make_int8(91, len(lens), 16, 4, 128, lens, residual_len=128, kv_capacity=5000, **mk)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    dw = H.DeviceWorkload(w)
+    for items in (1, 3, 0, 100):
+        H.announce(f"int8 partition {mask} items={items}")
+        O, L, _ = H.run(w, num_splits=8, dw=dw, partition=items)
+        H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+        O2, L2, _ = H.run(w, num_splits=8, dw=dw, partition=items)
+        assert np.array_equal(O, O2) and np.array_equal(L, L2)      # fixed partition: bitwise repeatable
+
+
+def test_partition_int8_trace_exact():
+    # the partition instance's own loads: every visible row once, at the
+    # oracle's code, residual and scale offsets
+    lens = [700, 0, 2100, 300, 40]
+    w = synth.make_int8(92, len(lens), 8, 2, 128, lens, residual_len=128, kv_capacity=2100,
+                        mask_kind="sink_window", n_sink=4, window=1000)
+    dw = H.DeviceWorkload(w)
+    tr, plan, O, L = H.trace(w, num_splits=6, dw=dw, partition=5)
+    H.check_trace(w, tr)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+
+
+def test_partition_int8_full_ragged_batch():
+    # the config-5 shape with ragged lengths (B = 16, 32q/8kv, 4 sinks + window
+    # 4096, residual 128), default partition, every row against the oracle
+    lens = [int(x) for x in synth.rng(93).integers(129 + 128, 16300, size=16)]
+    # no 1-15-row trailing K group (its per-channel scales of a few N(0,1)
+    # values can fall below fp16's normal range, which the writer refuses)
+    lens = [T + 16 if 0 < (T - 128) % 128 < 16 else T for T in lens]
+    lens[3] = 0
+    w = synth.make_int8(93, 16, 32, 8, 128, lens, residual_len=128, kv_capacity=16384,
+                        mask_kind="sink_window", n_sink=4, window=4096)
+    Or, Lr = oracle.attend(w.problem, w.buffers)
+    O, L, _ = H.run(w, num_splits=0, partition=0)
+    H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
