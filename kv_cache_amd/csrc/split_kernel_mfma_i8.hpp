@@ -20,8 +20,10 @@
 //    own 128-token group's scales (staged in LDS per phase of the split), so
 //    groups never need special handling.  The V scale of a row multiplies
 //    that row's softmax weight (section 0x03C) before PV, which runs on
-//    v_mfma_f32_16x16x32_f16 with the V codes as exact fp16; the denominator
-//    uses the unscaled weight.  Each wave keeps two tiles in flight.
+//    v_mfma_f32_16x16x32_f16 with the V codes as exact fp16 subnormals
+//    (c + 128) * 2^-24 (one v_perm per pair) and removes the 128 * sum(weights)
+//    bias with one more MFMA against a constant; the denominator uses the
+//    unscaled weight.  Each wave keeps two tiles in flight.
 //  * residual part: exactly the bf16 kernel's tile (A = bf16 K rows, B = q).
 #pragma once
 
@@ -65,17 +67,19 @@ __device__ __forceinline__ void dequant_f16(uint2 codes, uint4 scales, uint4& hi
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
 }
 
-// V codes of channel e (0..7) of two rows a, b as one exact fp16 pair
-// (c_a[e], c_b[e]): v_perm places the two code bytes under zero bytes, the
-// xor turns them into fp16 1024 + c + 128, the packed subtract removes the
-// bias.
-__device__ __forceinline__ uint32_t v_pair_word(uint2 a, uint2 b, int e) {
-  const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+// V codes of channel e (0..7) of two rows a, b as one fp16 pair of exact
+// subnormals ((c_a[e] + 128) * 2^-24, (c_b[e] + 128) * 2^-24): the code words
+// arrive with every byte xor 0x80 (so a byte is c + 128, in [1, 255]) and
+// v_perm places the two bytes under zero bytes, the fp16 subnormal whose
+// mantissa is the byte.  PV over these values is 2^-24 (sum w c + 128 sum w);
+// the bias term is accumulated beside it and removed at the end.
+__device__ __forceinline__ uint32_t v_pair_biased(uint2 a, uint2 b, int e) {
   const uint32_t wa = e < 4 ? a.x : a.y, wb = e < 4 ? b.x : b.y;
   const uint32_t sel = (uint32_t)(e & 3) | 0x0C00u | ((uint32_t)(4 + (e & 3)) << 16) | 0x0C000000u;
-  const uint32_t bits = __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, bits) - bias);
+  return __builtin_amdgcn_perm(wb, wa, sel);
 }
+// 128 * 2^-24 = 2^-17 as an fp16 subnormal pair: the B operand of the bias term
+constexpr uint32_t kVBiasPair = 0x00800080u;
 
 // Largest magnitude bit pattern (sign cleared) of the eight 16-bit floats
 // (fp16 or bf16: ordering by magnitude is ordering of these bits) in x.
@@ -223,6 +227,9 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
   f32x4_t o[8];              // int8 part: PV accumulators in the matrix-core layout
 #pragma unroll
   for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // 2^-17 * (sum of the weights) per head, in o's layout (every channel
+  // block carries the same bias term); o - obias is 2^-24 * u
+  f32x4_t obias = {0.f, 0.f, 0.f, 0.f};
 
   // Online softmax over the 8 scores of this lane for two tiles (rows
   // 4kg+i of tiles ta and tb, head n).
@@ -373,13 +380,22 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
           w.y = pack_f16(ps[2] * f16_bits_to_f32(sa[2]), ps[3] * f16_bits_to_f32(sa[3]));
           w.z = pack_f16(ps[4] * f16_bits_to_f32(sb[0]), ps[5] * f16_bits_to_f32(sb[1]));
           w.w = pack_f16(ps[6] * f16_bits_to_f32(sb[2]), ps[7] * f16_bits_to_f32(sb[3]));
+          uint2 ax[4], bx[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            ax[j] = make_uint2(a[j].x ^ 0x80808080u, a[j].y ^ 0x80808080u);
+            bx[j] = make_uint2(bv[j].x ^ 0x80808080u, bv[j].y ^ 0x80808080u);
+          }
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            const uint4 vcol = make_uint4(v_pair_word(a[0], a[1], c), v_pair_word(a[2], a[3], c),
-                                          v_pair_word(bv[0], bv[1], c), v_pair_word(bv[2], bv[3], c));
+            const uint4 vcol = make_uint4(v_pair_biased(ax[0], ax[1], c), v_pair_biased(ax[2], ax[3], c),
+                                          v_pair_biased(bx[0], bx[1], c), v_pair_biased(bx[2], bx[3], c));
             o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, w),
                                                           __builtin_bit_cast(f16x8_t, vcol), o[c], 0, 0, 0);
           }
+          const uint4 kb4 = make_uint4(kVBiasPair, kVBiasPair, kVBiasPair, kVBiasPair);
+          obias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, w),
+                                                         __builtin_bit_cast(f16x8_t, kb4), obias, 0, 0, 0);
         };
         // running-maximum rescale of o: lane (n, kg) scales heads 4kg .. 4kg+3
         auto rescale_o = [&](float alpha) {
@@ -388,6 +404,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
             const float a = __shfl(alpha, 4 * kg + i);
 #pragma unroll
             for (int c = 0; c < 8; ++c) o[c][i] *= a;
+            obias[i] *= a;
           }
         };
         // Phase start, per wave (no workgroup barrier): the wave stages its own
@@ -458,6 +475,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
           const float f = ldexpf(1.f, e_v - e_v_new);
 #pragma unroll
           for (int c = 0; c < 8; ++c) o[c] *= f;
+          obias *= f;
           e_v = e_v_new;
           vpow = ldexpf(1.f, e_v);
           vinv = ldexpf(1.f, -e_v);
@@ -486,7 +504,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? o[e][i & 3] * vpow : 0.f;
+    for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? (o[e][i & 3] - obias[i & 3]) * (vpow * 16777216.f) : 0.f;
 
   // Online softmax over the 4 scores of this lane (rows 4kg+i, head n);
   // returns the weights and rescales l and u.
