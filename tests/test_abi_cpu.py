@@ -396,13 +396,27 @@ def test_partition_bounds_pieces_by_the_plan_and_rejects_bad_arguments():
 
 
 def test_partition_rejected_where_unsupported_without_gpu():
-    # int8 (and fp32, FlashMask) run only on the fixed splits; a partition item
+    # fp32 (and FlashMask) run only on the fixed splits; a partition item
     # count without a descriptor is malformed.  Both fail before any device work.
-    st, pl, ws, _ = plan(P(kv_format="i8", k_group=128, residual_len=128))
+    st, pl, ws, _ = plan(P(kv_format="f32", q_dtype="f32"))
     assert st == ka.DA_OK
-    a = ka.make_args(16, 16, 16, 16, 16, ws, k_scale=16, v_scale=16, k_resid=16, v_resid=16,
-                     partition=16, partition_items=1)
+    a = ka.make_args(16, 16, 16, 16, 16, ws, partition=16, partition_items=1)
     assert ka.decode_attn_run(pl, a, check=False) == ka.DA_ERR_UNSUPPORTED
+
+
+def test_partition_default_item_count_follows_the_kernel():
+    # one dispatch round of the partition instance: 3 workgroups per CU for
+    # bf16, 2 for int8 (its partition instance's register budget)
+    lens = [4096] * 8
+    for fmt, per_cu in (("bf16", 3), ("i8", 2)):
+        kw = dict(batch=8, max_seq_len=4096, kv_capacity=4096)
+        if fmt == "i8":
+            kw.update(kv_format="i8", k_group=128, residual_len=128)
+        st, pl, ws, _ = plan(P(**kw))
+        assert st == ka.DA_OK
+        part, W = ka.decode_attn_partition(pl, lens)
+        want = per_cu * pl.num_cus // pl.problem.num_kv_heads
+        assert W <= want and W >= want - want // 8, (fmt, W, want)
     st, pl, ws, _ = plan(P())
     a = ka.make_args(16, 16, 16, 16, 16, ws, partition_items=3)
     assert ka.decode_attn_run(pl, a, check=False) == ka.DA_ERR_INVALID
