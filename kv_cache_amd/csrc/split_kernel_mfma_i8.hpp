@@ -331,12 +331,16 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
                       ks_base + (int64_t)(g0 + slot(tile)) * row_stride);
           }
         };
-        auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t (&sv)[4]) {
+        // V rows 4kg + j of the tile, and one V scale per lane: lane (n, kg)
+        // with n < 4 reads the scale of row 4kg + n, which PV broadcasts
+        // across its 16-lane row (row_newbcast:j gives row 4kg + j); the other
+        // lanes repeat a row of theirs.
+        auto issue_v = [&](int tile, uint2 (&v)[4], uint32_t& sv) {
+          sv = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(rel(tile + 4 * kg + (n & 3)), vs_stride));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t r = rel(tile + 4 * kg + j);
             v[j] = stream_load(reinterpret_cast<const uint2*>(vp + (mul_u24(r, row_stride) + 8 * (uint32_t)n)));
-            sv[j] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
             if constexpr (INSTR == kInstrRows) {
               if (n == 0 && tile + 4 * kg + j < pe)
                 trace_v(p, b, h, tile + 4 * kg + j, code_base + (int64_t)t_pb * row_stride + mul_u24(r, row_stride),
@@ -370,16 +374,25 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
         // block c is channel 8n + c and no code moves between lanes.  The
         // accumulator o[c] of lane (n, kg) holds heads 4kg .. 4kg+3 at channel
         // 8n + c.  The denominator uses the unscaled weights.
-        auto pv2 = [&](const uint2 (&a)[4], const uint32_t (&sa)[4], const uint2 (&bv)[4],
-                       const uint32_t (&sb)[4], const float (&pr)[8]) {
+        auto pv2 = [&](const uint2 (&a)[4], uint32_t sa, const uint2 (&bv)[4], uint32_t sb,
+                       const float (&pr)[8]) {
           uint4 w;
           float ps[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) ps[i] = pr[i] * vinv;
-          w.x = pack_f16(ps[0] * f16_bits_to_f32(sa[0]), ps[1] * f16_bits_to_f32(sa[1]));
-          w.y = pack_f16(ps[2] * f16_bits_to_f32(sa[2]), ps[3] * f16_bits_to_f32(sa[3]));
-          w.z = pack_f16(ps[4] * f16_bits_to_f32(sb[0]), ps[5] * f16_bits_to_f32(sb[1]));
-          w.w = pack_f16(ps[6] * f16_bits_to_f32(sb[2]), ps[7] * f16_bits_to_f32(sb[3]));
+          // scale of row 4kg + j: lane j of this lane's 16-lane row
+          auto sc = [](uint32_t x, auto J) {
+            return f16_bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + decltype(J)::value,
+                                                                          0xF, 0xF, false));
+          };
+          using J0 = std::integral_constant<int, 0>;
+          using J1 = std::integral_constant<int, 1>;
+          using J2 = std::integral_constant<int, 2>;
+          using J3 = std::integral_constant<int, 3>;
+          w.x = pack_f16(ps[0] * sc(sa, J0{}), ps[1] * sc(sa, J1{}));
+          w.y = pack_f16(ps[2] * sc(sa, J2{}), ps[3] * sc(sa, J3{}));
+          w.z = pack_f16(ps[4] * sc(sb, J0{}), ps[5] * sc(sb, J1{}));
+          w.w = pack_f16(ps[6] * sc(sb, J2{}), ps[7] * sc(sb, J3{}));
           uint2 ax[4], bx[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -433,7 +446,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
         }
         uint4 ka[2], kb[2];
         uint2 va[4], vb[4];
-        uint32_t sva[4], svb[4];
+        uint32_t sva, svb;
         int tile = pb + wave * TW;
         // the loop's request order (K, K, V, V), so its waits leave newer requests in flight
         issue_k(tile, ka);
