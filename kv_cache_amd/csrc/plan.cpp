@@ -49,16 +49,28 @@ bool current_device_is_gfx950() {
 namespace {
 
 // Automatic split choice.  A K/V head of one request is an independent
-// stream; B*H_kv of them rarely fill 256 CUs, so the visible rows are cut into
-// splits until about kWgPerCu workgroups per CU exist, but never into splits
-// shorter than kMinChunk rows: each extra split adds one (m, l, u) state per
-// query head to the workspace round trip and to the reducer fan-in.  Splits
-// are also never longer than kMaxChunk rows: the plan knows only the longest
-// request, and with ragged lengths short splits let the hardware dispatcher
-// balance the work (splits past a short request's end exit at once).
-constexpr int kWgPerCu = 3;
+// stream of rows, and the plan knows only the longest request.
+//  * When B*H_kv is below the CU count, the rows are cut into splits until
+//    about one workgroup per CU exists (kWgPerCu): the split kernels run 4
+//    waves per workgroup with two tiles in flight per wave, which keeps
+//    enough bytes in flight per CU, and every extra split adds one (m, l, u)
+//    state per query head to the workspace round trip and to the reducer's
+//    fan-in (measured on the 8 x 4096 GQA shape: 4 splits 27.0 us per
+//    single-launch call, 12 splits 28.0 us; int8 sink+window shape: 2 splits
+//    31.4 us, 6 splits 32.7 us; 128k context: 32 splits 88.9 us, 128 splits
+//    90.9 us).  Splits are at most kMaxChunk rows long.
+//  * When B*H_kv alone fills the CUs, splits only balance ragged lengths:
+//    about kBalanceWgPerCu workgroups per CU and never more than
+//    kBalanceChunk rows, so that the hardware dispatcher can even out the
+//    work (splits past a short request's end exit at once; measured on the
+//    32-request ragged paged batch: 1024-row splits 383 us, 4096-row splits
+//    456 us per call).
+// Splits are never shorter than kMinChunk rows.
+constexpr int kWgPerCu = 1;
+constexpr int kMaxChunk = 4096;
+constexpr int kBalanceWgPerCu = 3;
+constexpr int kBalanceChunk = 1024;
 constexpr int kMinChunk = 256;
-constexpr int kMaxChunk = 1024;
 constexpr int kRowAlign = 16;
 // Workgroups per CU a balanced partition targets by default: one round of the
 // partitioned split kernel (its launch bound allows this many per CU).
@@ -205,9 +217,12 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
     chunk = round_up(ceil_div(split_len, p.num_splits), align);
   } else {
     const int64_t units = std::max<int64_t>(1, (int64_t)p.batch * p.num_kv_heads);
-    const int64_t s0 = std::max<int64_t>(1, ceil_div((int64_t)kWgPerCu * num_cus, units));
+    const bool fills = units >= num_cus;
+    const int64_t s0 = std::max<int64_t>(1, ceil_div((int64_t)(fills ? kBalanceWgPerCu : kWgPerCu) * num_cus, units));
     chunk = round_up(ceil_div(split_len, s0), align);
-    chunk = std::min<int64_t>(chunk, kMaxChunk);
+    chunk = std::min<int64_t>(chunk, fills ? kBalanceChunk : kMaxChunk);
+    // FlashMask splits hold at most 64 tiles of 16 keys
+    if (p.mask_kind == DA_MASK_FLASHMASK) chunk = std::min<int64_t>(chunk, 64 * kRowAlign);
     chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinChunk, round_up(split_len, align)));
   }
   int64_t S = max_vis == 0 ? 1 : ceil_div(split_len, chunk);

@@ -64,7 +64,7 @@ def test_workspace_and_auto_splits_llama_shape():
     rup = lambda x: (x + 255) // 256 * 256
     assert ws == rup(states) + rup(counters) + rup(header) == pl.workspace_bytes
     assert S * pl.chunk >= 4096 and (S - 1) * pl.chunk < 4096
-    assert pl.chunk == -(-4096 // S)  # equal chunks, no tile rounding: 12 x 342 rows on 256 CUs
+    assert pl.chunk == -(-4096 // S)  # equal chunks, no tile rounding: 4 x 1024 rows on 256 CUs
     assert 8 * 8 * S >= 256          # at least one workgroup per CU
     assert abs(pl.problem.softmax_scale - 1 / math.sqrt(128)) < 1e-8
 
@@ -407,9 +407,11 @@ def test_partition_rejected_where_unsupported_without_gpu():
 def test_partition_default_item_count_follows_the_kernel():
     # one dispatch round of the partition instance: 3 workgroups per CU for
     # bf16, 2 for int8 (its partition instance's register budget)
+    # (the plan's split count caps a request's pieces, L >= n_max / (S - 1), so
+    # the plan reserves 12 states per row here)
     lens = [4096] * 8
     for fmt, per_cu in (("bf16", 3), ("i8", 2)):
-        kw = dict(batch=8, max_seq_len=4096, kv_capacity=4096)
+        kw = dict(batch=8, max_seq_len=4096, kv_capacity=4096, num_splits=12)
         if fmt == "i8":
             kw.update(kv_format="i8", k_group=128, residual_len=128)
         st, pl, ws, _ = plan(P(**kw))

@@ -34,13 +34,13 @@ def _check_both(w, dw=None):
 def test_full_shape_two_query_rows():
     w = synth.make_contiguous(71, 8, 32, 8, 128, LENS, kv_capacity=4096, num_queries=2)
     plan = _check_both(w)
-    assert plan.num_splits == 12
+    assert plan.num_splits == 4
 
 
 def test_full_shape_hnd_layout():
     w = synth.relayout(synth.make_contiguous(72, 8, 32, 8, 128, LENS, kv_capacity=4096), "contig_hnd")
     plan = _check_both(w)
-    assert plan.num_splits == 12
+    assert plan.num_splits == 4
 
 
 def test_full_shape_flashmask():
