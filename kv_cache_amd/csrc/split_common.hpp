@@ -181,9 +181,14 @@ __device__ __forceinline__ void fold_row(const SplitParams& p, int64_t row) {
   const int sl = min(lane, S - 1);
   float ls = get_shared_state(p.ws_l + row * S + sl);
   const float ms = get_shared_state(p.ws_m + row * S + sl);
+  // only the quad loads that hold states are issued (wave-uniform guard);
+  // the others stay zero and get weight 0 below
   float4 x[NI];
 #pragma unroll
-  for (int k = 0; k < NI; ++k) x[k] = get_shared_state4(u + (int64_t)min(k * SPI + sub, S - 1) * D);
+  for (int k = 0; k < NI; ++k) {
+    x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k * SPI < S) x[k] = get_shared_state4(u + (int64_t)min(k * SPI + sub, S - 1) * D);
+  }
   if (lane >= S) ls = 0.f;
   const float M = wave_max(ls > 0.f ? ms : -INFINITY);
   const float w = ls > 0.f ? __expf(ms - M) : 0.f;        // 0 for invalid and absent states
@@ -202,8 +207,10 @@ __device__ __forceinline__ void fold_row(const SplitParams& p, int64_t row) {
     j0 += NB;
     if (j0 >= S) break;
 #pragma unroll
-    for (int k = 0; k < NI; ++k)
-      x[k] = get_shared_state4(u + (int64_t)min(j0 + k * SPI + sub, S - 1) * D);
+    for (int k = 0; k < NI; ++k) {
+      x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + k * SPI < S) x[k] = get_shared_state4(u + (int64_t)min(j0 + k * SPI + sub, S - 1) * D);
+    }
   }
 #pragma unroll
   for (int off = QPS; off < 64; off <<= 1) {
