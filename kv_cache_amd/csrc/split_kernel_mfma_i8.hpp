@@ -123,8 +123,10 @@ __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) { return (ui
 
 // K scale rows staged in LDS per workgroup (256 B each for D = 128): a phase
 // of at most 23 groups' length starting anywhere in a group touches at most
-// 24 of them.
+// 24 of them.  A phase is at most kI8PhaseRows rows (the V-scale pre-pass of
+// a phase start reads 12 scales per lane: 3072 rows over the 4 waves' tiles).
 constexpr int kI8ScaleSlots = 24;
+constexpr int kI8PhaseRows = 3072;
 
 // A partitioned run keeps the state of several pieces' walk live: it gets
 // the register budget of 2 waves per SIMD, and the host sizes its default
@@ -297,10 +299,12 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
     // Ordinals map to positions by a constant shift inside each run (sinks:
     // 0, window: gap), so a phase never spans the seam: its rows are the
     // positions t_pb + r, r in [0, pe - pb), addressed from wave-uniform bases
-    // with lane offsets r * row_stride formed by 24-bit multiplies (r < 2048
-    // and row_stride <= 2^20 bytes keep them below 2^31).  A phase of at most
-    // (slots - 1) groups' length touches at most `slots` scale rows.
-    const int phase = min((kI8ScaleSlots - 1) << sh, 2048);
+    // with unsigned lane offsets r * row_stride formed by 24-bit multiplies
+    // (r < kI8PhaseRows = 3072 and row_stride <= 2^20 bytes keep them below
+    // 2^32).  A phase of at most (slots - 1) groups' length touches at most
+    // `slots` scale rows.  Every phase start costs one round trip to memory
+    // (its scale rows), so phases are as long as the table allows.
+    const int phase = min((kI8ScaleSlots - 1) << sh, kI8PhaseRows);
     const uint32_t vs_stride = 2 * (uint32_t)p.num_kv_heads;   // V scale bytes per position
     for (int run = 0; run < 2; ++run) {
       const int rb = run == 0 ? begin : max(begin, vis.ns);
@@ -428,19 +432,20 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
         // loads are unconditional), so the scales, returned first, are reduced
         // and staged while the tiles are in flight.  Duplicates from clamping
         // change no maximum.
-        // K scale quads idx = lane + 64k of the phase's rows (two requested
-        // here, clamped; longer phases fetch the rest below)
-        uint4 kq0, kq1;
-        {
-          const int i0 = min(lane, ng * 16 - 1), i1 = min(lane + 64, ng * 16 - 1);
-          kq0 = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (i0 >> 4)) * row_stride + 8 * (i0 & 15));
-          kq1 = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (i1 >> 4)) * row_stride + 8 * (i1 & 15));
+        // K scale quads idx = lane + 64k of the phase's rows, all requested
+        // here (clamped: a phase touches at most kI8ScaleSlots rows of 16 quads)
+        constexpr int kKq = kI8ScaleSlots * 16 / 64;
+        uint4 kq[kKq];
+#pragma unroll
+        for (int k = 0; k < kKq; ++k) {
+          const int i = min(lane + 64 * k, ng * 16 - 1);
+          kq[k] = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (i >> 4)) * row_stride + 8 * (i & 15));
         }
         // this wave's rows: tiles pb + 16*wave + 64k, 16 rows each; lane l
         // takes row 16*wave + 64*(4j + l/16) + l%16 of the phase for load j
-        uint32_t vsv[8];
+        uint32_t vsv[kI8PhaseRows / 256];
 #pragma unroll
-        for (int j8 = 0; j8 < 8; ++j8) {
+        for (int j8 = 0; j8 < kI8PhaseRows / 256; ++j8) {
           const uint32_t r = min((uint32_t)(16 * wave + 64 * (4 * j8 + (lane >> 4)) + (lane & 15)), last);
           vsv[j8] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
         }
@@ -453,16 +458,15 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
         issue_k(tile + STEP, kb);
         issue_v(tile, va, sva);
         issue_v(tile + STEP, vb, svb);
-        uint32_t kmx = max(f16_absmax_bits(kq0), f16_absmax_bits(kq1)), vmx = 0;
-        if (lane < ng * 16) ksc[wave][lane >> 4][lane & 15] = kq0;
-        if (lane + 64 < ng * 16) ksc[wave][(lane + 64) >> 4][lane & 15] = kq1;
-        for (int idx = lane + 128; idx < ng * 16; idx += 64) {
-          const uint4 x = *reinterpret_cast<const uint4*>(ks + (uint64_t)(g0 + (idx >> 4)) * row_stride + 8 * (idx & 15));
-          kmx = max(kmx, f16_absmax_bits(x));
-          ksc[wave][idx >> 4][idx & 15] = x;
+        uint32_t kmx = 0, vmx = 0;
+#pragma unroll
+        for (int k = 0; k < kKq; ++k) {
+          kmx = max(kmx, f16_absmax_bits(kq[k]));
+          const int idx = lane + 64 * k;
+          if (idx < ng * 16) ksc[wave][idx >> 4][idx & 15] = kq[k];
         }
 #pragma unroll
-        for (int j8 = 0; j8 < 8; ++j8) vmx = max(vmx, vsv[j8] & 0x7fffu);
+        for (int j8 = 0; j8 < kI8PhaseRows / 256; ++j8) vmx = max(vmx, vsv[j8] & 0x7fffu);
         kmx = wave_max_u32(kmx);
         vmx = wave_max_u32(vmx);
         // K rows are scaled only where code * scale could reach fp16's range
