@@ -152,6 +152,7 @@ da::SplitParams make_params(const da_plan* plan, const da_args* a) {
   sp.max_seq_len = p.max_seq_len;
   sp.num_pages = p.num_pages;
   sp.qscale = p.softmax_scale * 1.4426950408889634f;
+  sp.num_cus = plan->num_cus;
   return sp;
 }
 
@@ -172,6 +173,15 @@ bool launch_split(const da::SplitParams& sp, unsigned grid, hipStream_t st) {
       }
     }
     if (kStamps && sp.partition) return false;
+    // At most 2 workgroups per CU: the instance with the larger register
+    // budget (it folds the sinks into the first window phase).
+    if constexpr (G <= 4) {
+      if ((uint64_t)grid <= 2ull * (uint64_t)std::max(sp.num_cus, 1)) {
+        hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED, INSTR, false, true>), dim3(grid),
+                           dim3(kWaves * 64), 0, st, sp);
+        return true;
+      }
+    }
     hipLaunchKernelGGL((da::split_kernel_mfma_i8<G, kWaves, FUSED, INSTR>), dim3(grid), dim3(kWaves * 64), 0,
                        st, sp);
     return true;

@@ -78,6 +78,7 @@ struct SplitParams {
   uint32_t page_rows;        // paged: row indices per page (P for NHD, H_kv*P for HND)
   int32_t n_mask_blocks;     // FlashMask: ceil(max_seq_len / 16)
   float qscale;              // softmax_scale * log2(e): scores are kept in base-2 units
+  int32_t num_cus;           // the plan's CU count (host-side launch choices only)
   TraceOut tr;               // trace instances only
   uint64_t* stamps;          // timestamp instances only: [grid, 4]
 };

@@ -133,15 +133,20 @@ constexpr int kI8PhaseRows = 3072;
 // partition for 2 workgroups per CU.
 constexpr int kI8PartitionWgPerCu = 2;
 
-// 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads.
+// 3 waves per SIMD (<= 168 VGPRs) up to 4 heads per group, 2 for 8 heads;
+// OCC2: the instance for grids of at most 2 workgroups per CU, with the
+// register budget of 2 waves per SIMD (<= 256 VGPRs).
 // INSTR: kInstrRows is the index-trace instance, which also records each row
 // load (codes, scales, residual rows) where it is issued; kInstrStamps
 // records per-workgroup timestamps; otherwise identical.  PART: the balanced
 // partition instance (workgroup (item, h_kv) runs the request pieces of its
 // item, as in split_kernel_mfma).
-template <int G, int NWAVES, bool FUSED, int INSTR = 0, bool PART = false>
-__global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ? 3 : 2)) void split_kernel_mfma_i8(SplitParams p) {
+template <int G, int NWAVES, bool FUSED, int INSTR = 0, bool PART = false, bool OCC2 = false>
+__global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 && !OCC2 ? 3 : 2)) void split_kernel_mfma_i8(SplitParams p) {
   constexpr int D = 128;
+  // The sink tile (below) keeps another tile's registers live at a phase
+  // start: only instances with the 2-waves-per-SIMD budget take it.
+  constexpr bool kMergeSinks = PART || OCC2 || G > 4;
   constexpr int TW = 16;
   constexpr int STEP = NWAVES * TW;
   static_assert(G >= 1 && G <= 16, "");
@@ -301,12 +306,22 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
     // positions t_pb + r, r in [0, pe - pb), addressed from wave-uniform bases
     // with unsigned lane offsets r * row_stride formed by 24-bit multiplies
     // (r < kI8PhaseRows = 3072 and row_stride <= 2^20 bytes keep them below
-    // 2^32).  A phase of at most (slots - 1) groups' length touches at most
-    // `slots` scale rows.  Every phase start costs one round trip to memory
-    // (its scale rows), so phases are as long as the table allows.
-    const int phase = min((kI8ScaleSlots - 1) << sh, kI8PhaseRows);
+    // 2^32).  A phase of at most (slots - 2) groups' length touches at most
+    // `slots - 1` scale rows (the last slot holds the sink tile's row, below).
+    // Every phase start costs one round trip to memory (its scale rows), so
+    // phases are as long as the table allows.
+    const int phase = min((kI8ScaleSlots - 2) << sh, kI8PhaseRows);
     const uint32_t vs_stride = 2 * (uint32_t)p.num_kv_heads;   // V scale bytes per position
-    for (int run = 0; run < 2; ++run) {
+    // Sink tile: when the split's sink ordinals [s_b, s_e) fit one tile
+    // inside one K group and the split also has int8 window rows, wave 0
+    // takes the sinks as one extra tile of the first window phase (their K
+    // scale row in the table's last slot, their V scales in the wave's
+    // normalization), so the split pays one phase start instead of two.
+    const int s_b = begin, s_e = min(mid, vis.ns), w_b = max(begin, vis.ns);
+    const bool sink_tile = kMergeSinks && s_b < s_e && w_b < mid && s_e - s_b <= TW &&
+                           (s_b >> sh) == ((s_e - 1) >> sh);
+    constexpr int kSinkSlot = kI8ScaleSlots - 1;
+    for (int run = sink_tile ? 1 : 0; run < 2; ++run) {
       const int rb = run == 0 ? begin : max(begin, vis.ns);
       const int re = run == 0 ? min(mid, vis.ns) : mid;
       const int shift = run == 0 ? 0 : vis.gap;
@@ -352,8 +367,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
             }
           }
         };
-        auto scores = [&](int tile, const uint4 (&k)[2]) {
-          const int sl = slot(tile);
+        auto scores_sl = [&](int sl, const uint4 (&k)[2]) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -368,6 +382,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
           }
           return acc;
         };
+        auto scores = [&](int tile, const uint4 (&k)[2]) { return scores_sl(slot(tile), k); };
         // PV on the matrix cores, O (heads x channels) += P (heads x rows) V
         // (rows x channels) over the 32 rows of the two tiles: A = the weights
         // p * sigma_V in fp16 (relative error 2^-11, far inside the int8 format's
@@ -449,6 +464,35 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
           const uint32_t r = min((uint32_t)(16 * wave + 64 * (4 * j8 + (lane >> 4)) + (lane & 15)), last);
           vsv[j8] = *reinterpret_cast<const uint16_t*>(vsp + mul_u24(r, vs_stride));
         }
+        // The sink tile (wave 0 of the first window phase): its K scale row
+        // (lanes 0..15), codes and V scales, requested before the phase's tiles.
+        const bool sink_here = sink_tile && run == 1 && pb == w_b && wave == 0;   // wave-uniform
+        uint4 kqs = make_uint4(0u, 0u, 0u, 0u), sk[2];
+        uint2 sv4[4];
+        uint32_t svs = 0;
+        if (sink_here) {
+          if (lane < 16) kqs = *reinterpret_cast<const uint4*>(ks + (uint64_t)(s_b >> sh) * row_stride + 8 * lane);
+          const uint32_t rk = (uint32_t)min(s_b + n, s_e - 1);
+          const uint32_t rs = (uint32_t)min(s_b + 4 * kg + (n & 3), s_e - 1);
+          svs = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vs) + (uint64_t)rs * vs_stride);
+          sk[0] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(kc + (uint64_t)rk * row_stride + 16 * kg));
+          sk[1] = stream_load<kHalfLineNT>(reinterpret_cast<const uint4*>(kc + (uint64_t)rk * row_stride + 64 + 16 * kg));
+          if constexpr (INSTR == kInstrRows) {
+            if (kg == 0 && s_b + n < s_e)
+              trace_k(p, b, h, s_b + n, s_b + n, code_base + (int64_t)rk * row_stride,
+                      ks_base + (int64_t)(s_b >> sh) * row_stride);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t rv = (uint32_t)min(s_b + 4 * kg + j, s_e - 1);
+            sv4[j] = stream_load(reinterpret_cast<const uint2*>(vc + (uint64_t)rv * row_stride + 8 * (uint32_t)n));
+            if constexpr (INSTR == kInstrRows) {
+              if (n == 0 && s_b + 4 * kg + j < s_e)
+                trace_v(p, b, h, s_b + 4 * kg + j, code_base + (int64_t)rv * row_stride,
+                        vs_base + (int64_t)rv * p.num_kv_heads);
+            }
+          }
+        }
         uint4 ka[2], kb[2];
         uint2 va[4], vb[4];
         uint32_t sva, svb;
@@ -467,6 +511,11 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
         }
 #pragma unroll
         for (int j8 = 0; j8 < kI8PhaseRows / 256; ++j8) vmx = max(vmx, vsv[j8] & 0x7fffu);
+        if (sink_here) {
+          kmx = max(kmx, f16_absmax_bits(kqs));        // lanes >= 16 hold zeros
+          vmx = max(vmx, svs & 0x7fffu);
+          if (lane < 16) ksc[0][kSinkSlot][lane] = kqs;
+        }
         kmx = wave_max_u32(kmx);
         vmx = wave_max_u32(vmx);
         // K rows are scaled only where code * scale could reach fp16's range
@@ -485,6 +534,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
         if (e_k > 0) {               // rare: the table times 2^-e_k, in place
           for (int idx = lane; idx < ng * 16; idx += 64)
             ksc[wave][idx >> 4][idx & 15] = f16_scale_pow2(ksc[wave][idx >> 4][idx & 15], e_k);
+          if (sink_here && lane < 16) ksc[0][kSinkSlot][lane] = f16_scale_pow2(ksc[0][kSinkSlot][lane], e_k);
           wave_lds_sync();
         }
         sfac = ldexpf(p.qscale, e_q + e_k);
@@ -496,6 +546,15 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 ?
           e_v = e_v_new;
           vpow = ldexpf(1.f, e_v);
           vinv = ldexpf(1.f, -e_v);
+        }
+        if (sink_here) {
+          // one tile of sink rows (the second tile of the pair is empty: its
+          // ordinals start at s_e, all masked, weight 0)
+          const f32x4_t acc = scores_sl(kSinkSlot, sk);
+          float pr[8];
+          const float alpha = softmax2(acc, acc, s_b, s_e, s_e, pr);
+          if (__any(alpha != 1.f)) rescale_o(alpha);
+          pv2(sv4, svs, sv4, svs, pr);
         }
         for (; tile < pe; tile += 2 * STEP) {
           const int tb = tile + STEP;
