@@ -43,7 +43,7 @@ KERNEL_SOURCES = ["kv_cache_amd/csrc/split_kernel_mfma.hpp", "kv_cache_amd/csrc/
 # the kernel that moves the call's bytes, per workload (substring of its name)
 DOMINANT = {"llama3_8b_layer": "split_kernel_mfma<4, false, 4, true, false, false, 0>",
             "long_context_128k": "split_kernel_mfma<4, false, 4, false, false, false, 0>",
-            "int8_sink_window": "split_kernel_mfma_i8<4, 4, true, 0, false>",
+            "int8_sink_window": "split_kernel_mfma_i8<4, 4, true, 0, false, true>",
             "paged_ragged": "split_kernel_mfma<4, true, 4, false, false, true, 0>"}
 
 
