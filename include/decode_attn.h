@@ -148,7 +148,10 @@ typedef struct da_problem {
   int32_t n_sink;            /* DA_MASK_SINK_WINDOW: sink positions >= 0            */
   int32_t window;            /* DA_MASK_SINK_WINDOW: recent window W > 0            */
   float   softmax_scale;     /* 0 -> 1/sqrt(head_dim_qk); must be finite and >= 0   */
-  int32_t num_splits;        /* 0 -> automatic; otherwise the requested split count */
+  int32_t num_splits;        /* 0 -> automatic (B*H_kv below the CU count: about one
+                                 workgroup per CU, splits of 256..4096 rows; otherwise
+                                 about 3 per CU, splits of 256..1024 rows); otherwise
+                                 the requested split count */
   int32_t k_group;           /* DA_KV_I8: tokens per K-scale group (128); else 0   */
   int32_t residual_len;      /* DA_KV_I8: bf16 residual rows R >= 0; else 0        */
   int32_t num_cus;           /* 0 -> query the current device; > 0: plan for this many CUs */
