@@ -81,21 +81,24 @@ def _outputs(w):
     return out, lse
 
 
-def plan_for(w, num_splits=None):
+def plan_for(w, num_splits=None, num_cus=0):
+    """num_cus > 0 plans for that many CUs instead of the device's (the launch
+    picks the int8 kernel's instance by workgroups per CU of the plan)."""
     p = w.problem
     if num_splits is not None:
         p.num_splits = num_splits
-    _, plan, ws, _ = ka.decode_attn_plan(ka.problem_from(p))
+    _, plan, ws, _ = ka.decode_attn_plan(ka.problem_from(p, num_cus=num_cus))
     return plan, ws
 
 
-def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None, partition=None):
+def run(w, num_splits=None, dw=None, poison_ws=True, want_ws=False, stream=None, partition=None,
+        num_cus=0):
     """Plan, run, combine.  Returns (O, LSE, plan[, workspace numpy]).
     partition: None (fixed splits) or a target item count per K/V head for the
     balanced partition (0: the library's default)."""
     t = torch()
     dw = dw or DeviceWorkload(w)
-    plan, ws_bytes = plan_for(w, num_splits)
+    plan, ws_bytes = plan_for(w, num_splits, num_cus)
     if partition is not None:
         dw.partition(plan, partition)
     elif getattr(dw, "part", None) is not None:
@@ -120,13 +123,13 @@ def states_bytes(plan):
     return (raw + 255) // 256 * 256
 
 
-def forward(w, num_splits=None, dw=None, ws=None, want_ws=False, init=True):
+def forward(w, num_splits=None, dw=None, ws=None, want_ws=False, init=True, num_cus=0):
     """Plan and run the single-launch path (split kernel with the fused
     reduction).  A fresh workspace is filled with 0xFF (NaN states, counters
     garbage) and then initialised through decode_attn_workspace_init."""
     t = torch()
     dw = dw or DeviceWorkload(w)
-    plan, ws_bytes = plan_for(w, num_splits)
+    plan, ws_bytes = plan_for(w, num_splits, num_cus)
     if ws is None:
         ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
         ws.fill_(0xFF)
@@ -159,14 +162,14 @@ def split_workspace(ws_bytes: np.ndarray, plan):
     return u, m, l
 
 
-def trace(w, num_splits=None, dw=None, forward=False, partition=None):
+def trace(w, num_splits=None, dw=None, forward=False, partition=None, num_cus=0):
     """Runs the trace instance of the timed kernels: decode_attn_run's (then
     the combine), or with ``forward`` decode_attn_forward's; ``partition`` as
     in run().  Returns (trace dict of [B, H_kv, max_visible] arrays, plan, O,
     LSE)."""
     t = torch()
     dw = dw or DeviceWorkload(w)
-    plan, ws_bytes = plan_for(w, num_splits)
+    plan, ws_bytes = plan_for(w, num_splits, num_cus)
     if partition is not None:
         dw.partition(plan, partition)
     elif getattr(dw, "part", None) is not None:

@@ -75,3 +75,19 @@ def test_cfg3_full_trace_fixed_splits_and_partition():
         assert rows == 8 * int(np.sum(w.buffers["seq_lens"]))
         _check(3, 0, f"trace instance ({'partition' if part is not None else 'fixed'}), {rows} rows",
                O, L, Or, Lr)
+
+
+def test_cfg5_larger_grid_instance():
+    """Config 5 at S = 6 (768 workgroups, 3 per CU) runs the int8 kernel's
+    168-VGPR instance (separate sink phase) instead of the auto plan's; every
+    row and every load against the oracle."""
+    H.announce("full cfg5 S=6")
+    w = synth.config(5, 0)
+    Or, Lr, ref = oracle.attend(w.problem, w.buffers, with_trace=True)
+    dw = H.DeviceWorkload(w)
+    O, L, plan = H.forward(w, num_splits=6, dw=dw)
+    assert plan.num_splits == 6
+    _check(5, 0, "forward S=6", O, L, Or, Lr)
+    tr, plan, O, L = H.trace(w, num_splits=6, dw=dw, forward=True)
+    assert H.check_trace(w, tr, ref=ref) == 16 * 8 * 4100
+    _check(5, 0, "trace instance S=6", O, L, Or, Lr)

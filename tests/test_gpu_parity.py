@@ -201,13 +201,23 @@ def test_sink_window_paged():
 
 
 # ---------------------------------------------------------------- int8 (config 5)
-def test_int8_small_with_residual_and_mask():
+# The int8 kernel has two instances for one or few heads per group: grids of
+# at most 2 workgroups per CU of the plan run the one with the larger register
+# budget (which takes the sinks as an extra tile of the first window phase),
+# larger grids the other.  A plan for 1 CU forces the second on any grid.
+I8_CUS = [0, 1]
+
+
+@pytest.mark.parametrize("cus", I8_CUS)
+def test_int8_small_with_residual_and_mask(cus):
     w = synth.make_int8(10, 3, 16, 4, 128, [1000, 100, 250], mask_kind="sink_window",
                         n_sink=4, window=300, kv_capacity=1000)
     Or, Lr = oracle.attend(w.problem, w.buffers)
     dw = H.DeviceWorkload(w)
     for S in (0, 1, 4):
-        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        O, L, _ = H.run(w, num_splits=S, dw=dw, num_cus=cus)
+        H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
+        O, L, _ = H.forward(w, num_splits=S, dw=dw, num_cus=cus)
         H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
@@ -218,7 +228,8 @@ def test_int8_causal_small():
     H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
-def test_int8_scale_table_edges():
+@pytest.mark.parametrize("cus", I8_CUS)
+def test_int8_scale_table_edges(cus):
     # many 64-token groups in one split (several phases of the staged scale
     # table) and a window whose first group is the sinks' last group (the two
     # position runs share a scale row)
@@ -227,14 +238,14 @@ def test_int8_scale_table_edges():
     Or, Lr = oracle.attend(w.problem, w.buffers)
     dw = H.DeviceWorkload(w)
     for S in (1, 2, 0):
-        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        O, L, _ = H.run(w, num_splits=S, dw=dw, num_cus=cus)
         H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
     w = synth.make_int8(15, 2, 8, 2, 128, [1000, 700], mask_kind="sink_window", n_sink=100,
                         window=890, k_group=64, residual_len=64, kv_capacity=1000)
     Or, Lr = oracle.attend(w.problem, w.buffers)
     dw = H.DeviceWorkload(w)
     for S in (1, 3, 0):
-        O, L, _ = H.run(w, num_splits=S, dw=dw)
+        O, L, _ = H.run(w, num_splits=S, dw=dw, num_cus=cus)
         H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
     # no sinks (one run), and sinks covering whole requests (T <= n_sink) next
     # to a request whose sink run ends inside a tile
@@ -245,15 +256,15 @@ def test_int8_scale_table_edges():
         Or, Lr = oracle.attend(w.problem, w.buffers)
         dw = H.DeviceWorkload(w)
         for S in (1, 2, 0):
-            O, L, _ = H.run(w, num_splits=S, dw=dw)
+            O, L, _ = H.run(w, num_splits=S, dw=dw, num_cus=cus)
             H.check_rows(O, L, Or, Lr, 0.0, rtol=1e-2)
 
 
 # ---------------------------------------------------------------- exact indices
-def _trace_rows(w, S, forward=False, partition=None):
+def _trace_rows(w, S, forward=False, partition=None, num_cus=0):
     """The trace instance of the kernel the timed call runs loads exactly the
     oracle's rows, and computes the same output as the product instance."""
-    tr, plan, O, L = H.trace(w, num_splits=S, forward=forward, partition=partition)
+    tr, plan, O, L = H.trace(w, num_splits=S, forward=forward, partition=partition, num_cus=num_cus)
     n = H.check_trace(w, tr)
     Or, Lr = oracle.attend(w.problem, w.buffers)
     tol = 1e-5 if w.problem.kv_format == "f32" else 2e-3
@@ -282,9 +293,14 @@ def test_trace_indices_paged_cfg3_shape():
     _trace_rows(w, 8, partition=0)
 
 
+@pytest.mark.parametrize("cus", I8_CUS)
 @pytest.mark.parametrize("forward", [False, True])
-def test_trace_indices_int8(forward):
+def test_trace_indices_int8(forward, cus):
     _trace_rows(synth.make_int8(15, 2, 16, 4, 128, [1000, 60], mask_kind="sink_window", n_sink=4,
-                                window=300, kv_capacity=1000), 4, forward)
+                                window=300, kv_capacity=1000), 4, forward, num_cus=cus)
+    # sinks split over two splits, and sinks that end inside a tile next to the window
+    _trace_rows(synth.make_int8(18, 3, 8, 2, 128, [1000, 700, 30], mask_kind="sink_window", n_sink=20,
+                                window=500, kv_capacity=1000), 0, forward, num_cus=cus)
     # long splits: several scale-staging phases per split, causal over codes and residual
-    _trace_rows(synth.make_int8(17, 2, 32, 8, 128, [7000, 3000], kv_capacity=7000), 1, forward)
+    _trace_rows(synth.make_int8(17, 2, 32, 8, 128, [7000, 3000], kv_capacity=7000), 1, forward,
+                num_cus=cus)
