@@ -69,6 +69,31 @@ def test_workspace_and_auto_splits_llama_shape():
     assert abs(pl.problem.softmax_scale - 1 / math.sqrt(128)) < 1e-8
 
 
+def test_auto_split_regimes():
+    # B*H_kv below the CU count: about one workgroup per CU, splits of 256..4096 rows
+    st, pl, _, _ = plan(P(batch=1, kv_capacity=131072, max_seq_len=131072))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (32, 4096)
+    st, pl, _, _ = plan(P(batch=16, kv_format="i8", kv_capacity=16384, max_seq_len=16384,
+                          mask_kind="sink_window", n_sink=4, window=4096, k_group=128,
+                          residual_len=128))
+    # weighted chunk: (4100 visible + 128 residual rows counted twice) / 2
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (2, 2114)
+    st, pl, _, _ = plan(P(batch=2, max_seq_len=300, kv_capacity=300))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (2, 256)      # never below 256 rows
+    # FlashMask splits hold at most 64 tiles of 16 keys
+    st, pl, _, _ = plan(P(batch=1, mask_kind="flashmask", max_seq_len=32768, kv_capacity=32768))
+    assert st == ka.DA_OK and pl.chunk == 1024 and pl.num_splits == 32
+    # B*H_kv filling the CUs: about 3 workgroups per CU, splits of at most 1024 rows
+    st, pl, _, _ = plan(P(batch=32, layout="paged", page_size=16, max_pages_per_seq=2048,
+                          num_pages=40000, kv_capacity=0, max_seq_len=32768))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (32, 1024)
+    st, pl, _, _ = plan(P(batch=64, max_seq_len=4096, kv_capacity=4096))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (4, 1024)
+    # the same problem on a device with more CUs than B*H_kv: the first regime again
+    st, pl, _, _ = plan(P(batch=64, max_seq_len=4096, kv_capacity=4096), cus=1024)
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (2, 2048)
+
+
 @pytest.mark.parametrize("S", [1, 8, 32, 128])
 def test_explicit_split_counts_long_context(S):
     st, pl, ws, _ = plan(P(batch=1, kv_capacity=131072, max_seq_len=131072, num_splits=S))
