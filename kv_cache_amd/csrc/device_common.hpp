@@ -210,6 +210,18 @@ __device__ __forceinline__ void decode_workgroup(const SplitParams& p, int* b, i
   *b = bh / p.num_kv_heads;
 }
 
+// First step (of `steps` equal steps) at which the split (b, s) starts its
+// sweep, wrapping around to cover every step.  Equal splits of a contiguous
+// cache start at byte offsets that differ by multiples of large powers of two
+// (the request and split strides), so sweeps that all start at their first
+// row request, at any moment, addresses that agree in their low bits; starting
+// at staggered eighths of the split ((2b + s) mod 8) spreads the concurrent
+// requests over those bits.  Any order visits the same rows, so results
+// change only in the order of the fp32 sums.
+__device__ __forceinline__ int sweep_start(int b, int s, int steps) {
+  return ((2 * b + s) & 7) * (steps >> 3);
+}
+
 // A workgroup of K/V head h serves "virtual heads" j = 0 .. C*g-1: query row
 // i = j / g of request b, query head h*g + j % g (g = H_q/H_kv).  Its row of
 // q, of the split states and of O/LSE, ordered (b, i, h_q):

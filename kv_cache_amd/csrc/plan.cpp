@@ -72,6 +72,7 @@ constexpr int kBalanceWgPerCu = 3;
 constexpr int kBalanceChunk = 1024;
 constexpr int kMinChunk = 256;
 constexpr int kRowAlign = 16;
+constexpr int kStepRows = 64;
 // Workgroups per CU a balanced partition targets by default: one round of the
 // partitioned split kernel (its launch bound allows this many per CU).
 constexpr int kPartitionWgPerCu = 3;
@@ -224,6 +225,13 @@ extern "C" da_status decode_attn_plan(const da_problem* problem, da_plan* plan_o
     // FlashMask splits hold at most 64 tiles of 16 keys
     if (p.mask_kind == DA_MASK_FLASHMASK) chunk = std::min<int64_t>(chunk, 64 * kRowAlign);
     chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinChunk, round_up(split_len, align)));
+    // bf16 and fp32 splits of whole steps (the split kernels' 4 waves x 16-row
+    // tiles) where that keeps the split count: a split ending inside a step
+    // leaves some waves a tile without rows
+    if (!i8 && p.mask_kind != DA_MASK_FLASHMASK) {
+      const int64_t whole = round_up(chunk, kStepRows);
+      if (ceil_div(split_len, whole) == ceil_div(split_len, chunk)) chunk = whole;
+    }
   }
   int64_t S = max_vis == 0 ? 1 : ceil_div(split_len, chunk);
   if (S > DA_MAX_SPLITS) reasons |= DA_R_SPLITS;

@@ -174,6 +174,7 @@ template <int G, bool PAGED, int NWAVES, bool FUSED, bool FM, bool PART = false,
 __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupancy<G>::value) void split_kernel_mfma(SplitParams p) {
   constexpr int D = 128;
   constexpr int TW = 16;
+  constexpr int kStep = NWAVES * TW;   // rows of one step of the workgroup's waves
   static_assert(G >= 1 && G <= 16, "");
 
   WgStamps<INSTR> stamps(p);
@@ -214,11 +215,14 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   // those of any row past the end.
   MfmaTile t;
   bool spec = false;
+  int spec_t0 = 0;
   if constexpr (!PAGED && !FM && !PART) {
     spec = p.mask_kind == DA_MASK_CAUSAL && p.layout == DA_LAYOUT_CONTIG_NHD && !p.cache_batch_idx &&
            p.kv_capacity > 0;
     if (spec) {
-      const int t0 = s * p.chunk + wave * TW;
+      // the first tile of a full split under the sweep rotation below
+      const int t0 = s * p.chunk + kStep * sweep_start(b, s, (p.chunk + kStep - 1) / kStep) + wave * TW;
+      spec_t0 = t0;
       const int cap = p.kv_capacity;
       const uint16_t* row = kb + (uint64_t)(uint32_t)min(t0 + n, cap - 1) * row_stride;
 #pragma unroll
@@ -319,22 +323,40 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     if (lane < n_mine) mine = fmc.list[wave + NWAVES * lane];
   }
   auto entry_at = [&](int k) -> uint32_t { return (uint32_t)__builtin_amdgcn_readlane((int)mine, k & 63); };
-  auto tile_at = [&](int k) -> int {          // FlashMask: first position of the wave's tile k
-    if constexpr (FM) return k < n_mine ? TW * (int)(entry_at(k) & 0x7fffffffu) : past;
-    else return past;
+  // Sweep order (no FlashMask): the split's steps of NWAVES tiles are visited
+  // from step j0 on and wrap around, wave w taking tile w of each step that
+  // has one (only the last step can lack it).  j0 staggers the splits' starts
+  // (sweep_start), or is 0 where the wave has fewer steps than the staggered
+  // start.
+  const int n_steps = (end - begin + kStep - 1) / kStep;
+  int j0 = 0;
+  if constexpr (!FM && !PAGED) {
+    // (contiguous NHD: the request and split strides are the large powers of
+    // two; paged and HND caches are read in step order)
+    const int ref = (pend < 0 && !PART) ? (p.chunk + kStep - 1) / kStep : n_steps;
+    j0 = p.layout == DA_LAYOUT_CONTIG_NHD ? sweep_start(b, s, ref) : 0;
+    if (j0 >= n_steps) j0 = 0;
+  }
+  auto tile_at = [&](int k) -> int {          // first position of the wave's tile k
+    if constexpr (FM) {
+      return k < n_mine ? TW * (int)(entry_at(k) & 0x7fffffffu) : past;
+    } else {
+      if (k >= n_steps) return past;
+      const int j = j0 + k;
+      return begin + kStep * (j >= n_steps ? j - n_steps : j) + wave * TW;
+    }
   };
   auto partial_at = [&](int k) -> bool {
     if constexpr (FM) return k < n_mine && (entry_at(k) >> 31) != 0u;
     else return false;
   };
-  auto first_tile = [&]() -> int {
-    if constexpr (!FM) return begin + wave * TW;
-    else return tile_at(0);
-  };
+  auto first_tile = [&]() -> int { return tile_at(0); };
   // The wave's tile d steps after the current one (d = 1, 2).
-  auto ahead = [&](int tile, int d) -> int {
-    if constexpr (!FM) return tile + d * NWAVES * TW;
-    else return tile_at(kc + d);
+  auto ahead = [&](int, int d) -> int { return tile_at(kc + d); };
+  // whether the wave has a tile at step k (FlashMask: a listed tile)
+  auto has_step = [&](int tile, int k) -> bool {
+    if constexpr (FM) return tile < end;
+    else return k < n_steps;
   };
   int4 ivt = make_int4(0, 0, 0, 0);   // FlashMask intervals of row tile + n (PARTIAL tiles)
   auto issue_iv = [&](int tile, bool part) {
@@ -347,15 +369,15 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
   // Row indices run one tile ahead of the loads that use them, so a paged
   // cache's block-table lookup is off the load path.
   uint32_t ri = 0, ri_ahead = 0;
-  if (tile < end) {
-    if (spec) {
-      // the first tile (tile == t0) was requested above; trace its rows now
-      // that the split end is known, with the row indices those loads used
+  if (has_step(tile, 0)) {
+    if (spec && tile == spec_t0) {
+      // the first tile (t0) was requested above; trace its rows now that the
+      // split end is known, with the row indices those loads used
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (tile + 4 * kg + j >= end) t.v[j] = make_uint4(0u, 0u, 0u, 0u);
         if constexpr (INSTR == kInstrRows) {
-          // tile == s*chunk + wave*16 here, the first row of the loads above
+          // tile == t0 here, the first row of the loads above
           const int o = tile + 4 * kg + j;
           const uint32_t rj = (uint32_t)min(o, p.kv_capacity - 1);
           if (n == 0 && o < end) trace_v(p, b, h, o, hb + (int64_t)((uint64_t)rj * row_stride));
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
     }
     ri_ahead = row_index(ahead(tile, 1));
   }
-  while (tile < end) {
+  while (has_step(tile, kc)) {
     const int next_tile = ahead(tile, 1);
     uint32_t hidden = 0;                  // rows of this tile hidden by FlashMask (bit r)
     if constexpr (FM) {
