@@ -496,7 +496,21 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 &
         uint4 ka[2], kb[2];
         uint2 va[4], vb[4];
         uint32_t sva, svb;
-        int tile = pb + wave * TW;
+        // Sweep order: the phase's pairs of steps (wave w takes tiles w and
+        // w + NWAVES of each pair) are visited from pair q0 on and wrap around,
+        // q0 staggering requests and splits (sweep_start; K/V codes of equal
+        // requests lie a power of two apart); the requests after the last pair
+        // repeat the phase's last row.
+        const int n_pairs = (pe - pb + 2 * STEP - 1) / (2 * STEP);
+        const int n_mine = max(0, (pe - pb - wave * TW + 2 * STEP - 1) / (2 * STEP));   // pairs with a tile of this wave
+        int q0 = sweep_start(b, s, n_pairs);
+        if (q0 >= n_mine) q0 = 0;
+        auto pair_tile = [&](int k) -> int {
+          if (k >= n_mine) return pe + wave * TW;
+          const int q = q0 + k;
+          return pb + 2 * STEP * (q >= n_mine ? q - n_mine : q) + wave * TW;
+        };
+        int tile = pair_tile(0);
         // the loop's request order (K, K, V, V), so its waits leave newer requests in flight
         issue_k(tile, ka);
         issue_k(tile + STEP, kb);
@@ -556,18 +570,20 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 &
           if (__any(alpha != 1.f)) rescale_o(alpha);
           pv2(sv4, svs, sv4, svs, pr);
         }
-        for (; tile < pe; tile += 2 * STEP) {
+        for (int k = 0; k < n_mine; ++k) {
           const int tb = tile + STEP;
+          const int next = pair_tile(k + 1);
           const f32x4_t acc = scores(tile, ka);
           const f32x4_t acc2 = scores(tb, kb);
-          issue_k(tile + 2 * STEP, ka);
-          issue_k(tb + 2 * STEP, kb);
+          issue_k(next, ka);
+          issue_k(next + STEP, kb);
           float pr[8];
           const float alpha = softmax2(acc, acc2, tile, tb, pe, pr);
           if (__any(alpha != 1.f)) rescale_o(alpha);   // skipped while no head maximum moves
           pv2(va, sva, vb, svb, pr);
-          issue_v(tile + 2 * STEP, va, sva);
-          issue_v(tb + 2 * STEP, vb, svb);
+          issue_v(next, va, sva);
+          issue_v(next + STEP, vb, svb);
+          tile = next;
         }
       }
     }
