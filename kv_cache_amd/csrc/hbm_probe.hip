@@ -44,8 +44,9 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
 // the matrix-core kernel: K 16 bytes of row n at byte 64c + 16g for c = 0..3
 // (each instruction: 16 rows x 64 bytes, plain loads), V 16 bytes of row
 // 4g + j at byte 16n for j = 0..3 (each instruction: 4 whole rows,
-// non-temporal).  With `stamps`, thread 0 writes the workgroup's end time
-// (s_memrealtime) and XCC_ID.
+// non-temporal).  Like the kernel, a split of whole 64-row steps starts its
+// sweep at step ((2b + s) mod 8) * (steps / 8) and wraps.  With `stamps`,
+// thread 0 writes the workgroup's end time (s_memrealtime) and XCC_ID.
 __global__ __launch_bounds__(256) void pattern_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                       int B, int T, int H, int S, int chunk,
                                                       uint32_t* __restrict__ sink, uint64_t* __restrict__ stamps) {
@@ -58,8 +59,12 @@ __global__ __launch_bounds__(256) void pattern_kernel(const uint4* __restrict__ 
   const int begin = min(s * chunk, T), end = min(begin + chunk, T);
   // 16-byte words: row (b, t, h) starts at ((b*T + t)*H + h)*16, 16 words per row
   const size_t base = ((size_t)b * T * H + h) * 16;
+  const int ntiles = (end - begin + 15) / 16;
+  const int r0 = (end - begin) % 64 == 0 ? 4 * (((2 * b + s) & 7) * (ntiles / 4 >> 3)) : 0;
   uint32_t acc = 0;
-  for (int t = begin + wave * 16; t < end; t += 64) {
+  for (int i = wave; i < ntiles; i += 4) {
+    const int ti = i + r0 >= ntiles ? i + r0 - ntiles : i + r0;
+    const int t = begin + 16 * ti;
     const size_t koff = base + (size_t)min(t + n, end - 1) * H * 16 + g;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -110,7 +115,9 @@ __global__ __launch_bounds__(256) void read2_kernel(const uint4* __restrict__ a,
 // 128] (128-byte rows), workgroup (b, h, s) reads rows [s*chunk, ..) of the
 // window [T - W, T) (split index rotated by (b, h)); per 16-row tile, lane
 // (n, g) reads K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row n
-// (plain) and V bytes [8n, 8n+8) of rows 4g + j (non-temporal).
+// (plain) and V bytes [8n, 8n+8) of rows 4g + j (non-temporal).  Like the
+// kernel, the split's pairs of 64-row steps are visited from pair
+// ((2b + s) mod 8) * (pairs / 8) on, wrapping.
 __global__ __launch_bounds__(256) void i8_pattern_kernel(const int8_t* __restrict__ k, const int8_t* __restrict__ v,
                                                          int B, int T, int H, int S, int chunk, int W,
                                                          uint32_t* __restrict__ sink) {
@@ -124,8 +131,12 @@ __global__ __launch_bounds__(256) void i8_pattern_kernel(const int8_t* __restric
   const int begin = min(s * chunk, W), end = min(begin + chunk, W);
   const size_t base = ((size_t)b * T * H + h) * 128;
   const size_t rs = (size_t)H * 128;
+  const int ntiles = (end - begin + 15) / 16;
+  const int r0 = 8 * (((2 * b + s) & 7) * ((end - begin + 127) / 128 >> 3));   // in tiles, whole pairs
   uint32_t acc = 0;
-  for (int t = begin + wave * 16; t < end; t += 64) {
+  for (int i = wave; i < ntiles; i += 4) {
+    const int ti = i + r0 >= ntiles ? i + r0 - ntiles : i + r0;
+    const int t = begin + 16 * ti;
     const size_t kr = base + (size_t)(w0 + min(t + n, end - 1)) * rs;
     const uint4 x0 = *reinterpret_cast<const uint4*>(k + kr + 16 * g);
     const uint4 x1 = *reinterpret_cast<const uint4*>(k + kr + 64 + 16 * g);
