@@ -80,6 +80,14 @@ def test_auto_split_regimes():
     assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (2, 2114)
     st, pl, _, _ = plan(P(batch=2, max_seq_len=300, kv_capacity=300))
     assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (2, 256)      # never below 256 rows
+    # bf16 chunks of whole 64-row steps where the split count stays: 3000 / 4 = 750 -> 768
+    st, pl, _, _ = plan(P(max_seq_len=3000, kv_capacity=3000))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (4, 768)
+    st, pl, _, _ = plan(P(max_seq_len=4100, kv_capacity=4100))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (4, 1088)
+    # ... but not where the split count would drop: 8224 / 32 = 257, and 320-row splits would be 26
+    st, pl, _, _ = plan(P(batch=1, max_seq_len=8224, kv_capacity=8224))
+    assert st == ka.DA_OK and (pl.num_splits, pl.chunk) == (32, 257)
     # FlashMask splits hold at most 64 tiles of 16 keys
     st, pl, _, _ = plan(P(batch=1, mask_kind="flashmask", max_seq_len=32768, kv_capacity=32768))
     assert st == ka.DA_OK and pl.chunk == 1024 and pl.num_splits == 32
