@@ -285,6 +285,19 @@ def test_trace_indices_contiguous_and_mask(forward):
     _trace_rows(synth.make_contiguous(16, 3, 8, 2, 128, [1000, 1, 777], kv_capacity=1000), 4, forward)
 
 
+@pytest.mark.parametrize("forward", [False, True])
+def test_trace_indices_staggered_sweeps(forward):
+    # splits of whole 64-row steps start their sweep at staggered steps and
+    # wrap (requests 0 and 1); request 2's second split is shorter and keeps the
+    # plain order, so the first tile requested before its length arrived (at
+    # the staggered start of a full split) is not the one it uses
+    lens = [2048, 2048, 1500]
+    w = synth.make_contiguous(19, 3, 8, 2, 128, lens, kv_capacity=2048)
+    _trace_rows(w, 2, forward)
+    w = synth.make_contiguous(20, 2, 16, 4, 128, [4096, 4000], kv_capacity=4096, num_queries=2)
+    _trace_rows(w, 4, forward)
+
+
 def test_trace_indices_paged_cfg3_shape():
     lens = [1, 16, 17, 4099, 0, 250]
     w = synth.make_paged(14, len(lens), 32, 8, 128, lens, page_size=16, max_pages_per_seq=260)
