@@ -411,6 +411,38 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// x combined with the lane 16 (32) apart in the same 32 (64) lanes, as
+// x + (or max with) __shfl_xor(x, 16 or 32) gives it, without LDS and without
+// lane-index registers: v_permlane16_swap / v_permlane32_swap exchange rows
+// between two copies of x, so each lane holds its own value and its partner's
+// in the two results, whichever copy took which (the sum and the max are
+// symmetric in the two).  The second copy is an identity DPP move, which the
+// compiler does not see as equal to x, so it does not take the swap of two
+// equal operands for two equal results.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t b) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0xE4, 0xF, 0xF, false);   // quad_perm [0,1,2,3]
+}
+template <bool MAX, int ROWS>
+__device__ __forceinline__ float xor_rows(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  uint32_t r0, r1;
+  if constexpr (ROWS == 1) {
+    const auto r = __builtin_amdgcn_permlane16_swap(b, opaque_copy(b), false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(b, opaque_copy(b), false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  const float a = __builtin_bit_cast(float, r0), c = __builtin_bit_cast(float, r1);
+  return MAX ? fmaxf(a, c) : a + c;
+}
+__device__ __forceinline__ float xor16_sum(float x) { return xor_rows<false, 1>(x); }
+__device__ __forceinline__ float xor32_sum(float x) { return xor_rows<false, 2>(x); }
+__device__ __forceinline__ float xor16_max(float x) { return xor_rows<true, 1>(x); }
+__device__ __forceinline__ float xor32_max(float x) { return xor_rows<true, 2>(x); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

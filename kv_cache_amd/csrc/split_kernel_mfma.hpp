@@ -417,8 +417,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       sc[i] = (tile + 4 * kg + i < end_n && !((hidden >> (4 * kg + i)) & 1u)) ? acc[i] * p.qscale
                                                                              : -INFINITY;
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = xor32_max(xor16_max(mt));
     const float mn = fmaxf(m_run, mt);
     const float mz = mn == -INFINITY ? 0.f : mn;     // no -inf - -inf
     const float alpha = fast_exp2(m_run - mz);
@@ -499,14 +498,12 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kPartitionWgPerCu : MfmaOccupan
       for (int e = 0; e < 8; ++e) u[i][e] = kg == (i >> 2) ? o[e][i & 3] : 0.f;
   }
   // ---- wave state: all rows of a head share m, so l and u just add ---------
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = xor32_sum(xor16_sum(l_run));
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      u[i][e] += __shfl_xor(u[i][e], 16);
-      u[i][e] += __shfl_xor(u[i][e], 32);
+      u[i][e] = xor32_sum(xor16_sum(u[i][e]));
     }
 
   if (kg == 0) {

@@ -250,8 +250,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 &
     }
     float mt = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                      fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = xor32_max(xor16_max(mt));
     const float mn = fmaxf(m_run, mt);
     const float mz = mn == -INFINITY ? 0.f : mn;
     const float alpha = fast_exp2(m_run - mz);
@@ -605,8 +604,7 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 &
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = (tile + 4 * kg + i < min(lim, lim_n)) ? acc[i] * p.qscale : -INFINITY;
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = xor32_max(xor16_max(mt));
     const float mn = fmaxf(m_run, mt);
     const float mz = mn == -INFINITY ? 0.f : mn;
     const float alpha = fast_exp2(m_run - mz);
@@ -670,14 +668,12 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 &
   }
 
   // ---- wave state: all rows of a head share m, so l and u just add ---------
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = xor32_sum(xor16_sum(l_run));
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      u[i][e] += __shfl_xor(u[i][e], 16);
-      u[i][e] += __shfl_xor(u[i][e], 32);
+      u[i][e] = xor32_sum(xor16_sum(u[i][e]));
     }
   if (kg == 0) {
 #pragma unroll
