@@ -813,6 +813,12 @@ def stamps_summary(torch, ka, name, calls=20, warmup=5):
                                               for q in (10, 90)],
                     "fold_us_median": float(np.median((end - stored)[folded])) if folded.any() else None,
                     "fold_us_max": float((end - stored)[folded].max()) if folded.any() else None,
+                    # the workgroups that did not fold: store wait + arrival atomic only
+                    "arrival_us_median": float(np.median((end - stored)[~folded])) if (~folded).any() else None,
+                    # the first fold on each XCD (the fold code's first run there)
+                    "first_fold_us": float(np.median([(end - stored)[m][np.argmin(stored[m])] for m in
+                                                      (folded & (xcc == x) for x in range(8)) if m.any()]))
+                    if folded.any() else None,
                     "end_after_last_store": float(end.max() - stored.max()),
                     "cus": int(len(np.unique(cu)))})
     med = lambda k: round(float(np.median([p[k] for p in per])), 2)
@@ -826,6 +832,9 @@ def stamps_summary(torch, ka, name, calls=20, warmup=5):
     if per[0]["fold_us_median"] is not None:
         res["fold_us_median"] = med("fold_us_median")
         res["fold_us_max_median"] = med("fold_us_max")
+        res["first_fold_on_xcd_us_median"] = med("first_fold_us")
+    if per[0]["arrival_us_median"] is not None and per[0]["fold_us_median"] is not None:
+        res["arrival_us_median"] = med("arrival_us_median")
     return res
 
 
