@@ -138,18 +138,23 @@ __device__ __forceinline__ int fm_compact(const SplitParams& p, int b, int q_row
   }
   __syncthreads();
   if (wave == 0) {
-    int run = 0;     // exclusive prefix of the entries' counts, 64 entries per pass
+    // Exclusive prefix of the entries' counts, 64 entries per pass, by bit
+    // planes: a count c <= 64 is the sum of its bits (c >> k & 1) << k, and
+    // the lanes below this one holding bit k number mbcnt(ballot of bit k).
+    // No cross-lane data movement, so no LDS round trips.
+    int run = 0;
     for (int e0 = 0; e0 < ne; e0 += 64) {
       const int e = e0 + lane;
       const int c = e < ne ? __popcll(f.ns[e]) : 0;
-      int x = c;
+      int x = 0, sum = 0;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
+      for (int k = 0; k < 7; ++k) {
+        const uint64_t bk = __ballot((c >> k) & 1);
+        x += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bk, 0u)) << k;
+        sum += __popcll(bk) << k;
       }
-      if (e < ne) f.pre[e] = run + x - c;
-      run += __shfl(x, 63);
+      if (e < ne) f.pre[e] = run + x;
+      run += sum;
     }
     if (lane == 0) f.count = run;
   }
