@@ -164,22 +164,24 @@ __global__ __launch_bounds__(NWAVES * 64, PART ? kI8PartitionWgPerCu : (G <= 4 &
   // One piece of work: visible ordinals [pbeg, pend) of request b for K/V
   // head h, stored as split slot s.  pend < 0: the plan's split s.
   auto piece = [&](int b, int h, int s, int pbeg, int pend) {
+  // The request length is requested first, so its round trip overlaps the
+  // q staging below instead of following its barrier.
+  const int T = request_len(p, b);
   // q rows in the B operand layout, q[head n][32c + 8kg .. +7] (zero for
   // n >= G), staged in LDS: the residual part uses them as they are, the int8
   // part reads them in its own channel order.
   if (wave == 0) {
+    // all four loads in flight at once (lanes n >= G read head 0's row and
+    // store zeros), so the staging costs one round trip
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + out_row(p, b, h, n < G ? n : 0) * D + 8 * kg;
+    uint4 x[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (n < G)
-        x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
-                                            out_row(p, b, h, n) * D + 32 * c + 8 * kg);
-      q_lds[c][lane] = x;
-    }
+    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q_lds[c][lane] = n < G ? x[c] : make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
 
-  const int T = request_len(p, b);
   const VisProgram vis = make_vis(T, p.mask_kind, p.n_sink, p.window);
   const int n_q = quantized_len(p, T);
   const int o_res = residual_ordinal(vis, n_q);
